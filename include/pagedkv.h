@@ -1,0 +1,172 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) batched paged-attention decode step.
+ *
+ * One decode step of a paged KV cache, as the nanoserve pages describe it:
+ *
+ *   1. pkv_kv_write: every running row's new K/V vector is scattered into its
+ *      pool slot; a padding row aims at the sink slot, a legal address past every
+ *      slot the allocator hands out (Day 55, "the capture list moved to startup,
+ *      and the dummy batch was all padding", section "Why it matters").
+ *   2. pkv_paged_attention: for every (row, query head) the row's history is read
+ *      through its block table, block id times block size plus offset (Day 51,
+ *      "the read rectangle stopped being built ...", section "Why it matters"),
+ *      in cdiv(context_len, block) tiles folded into an online softmax (Day 59,
+ *      "the rectangle the read builds, and the tile that replaces it", sections
+ *      "What I added today" and "What I learned" 3-4).  The result equals the
+ *      masked [rows, heads, 1, max_ctx] softmax rectangle of the reference read
+ *      (same page, "What I added today").  A row whose context_len is 0 is a
+ *      padding row: its output is zero and no K/V, block-table entry or pool slot
+ *      of it is read.
+ *
+ * Conventions for every call:
+ *   - Pointers named k_cache, v_cache, k, v, q, out, slot_mapping, block_tables,
+ *     context_lens and workspace are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or keeps them.  The host-check entry points
+ *     (pkv_check_*_host) take HOST pointers instead.
+ *   - All arrays are dense, row-major, with no padding between rows.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.  Calls
+ *     are asynchronous on that stream unless `validate` is non-zero.
+ *   - Every entry point returns a pkv_status.  On a refusal nothing is launched
+ *     and no memory is touched; pkv_last_error_detail() names the offending row,
+ *     entry or argument (thread-local, valid until the next call on the thread).
+ *   - Device-side safety: with validate == 0 the kernels still never read or write
+ *     outside the pool: a context_len is clamped to [0, max_blocks_per_row *
+ *     block_size], a live block id outside [0, num_blocks) is skipped and a write
+ *     slot outside [0, sink] is skipped.  Such inputs give unspecified output values
+ *     (not a fault) and raise a bit in the device status word (pkv_device_status).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* Element type of q, out, the new K/V and both pools. */
+typedef enum pkv_dtype {
+  PKV_F32 = 0,   /* IEEE binary32 */
+  PKV_BF16 = 1   /* bfloat16; accumulation is float32 */
+} pkv_dtype;
+
+/* Order of the axes of one pool block.  Both describe the same slot-indexed pool
+ * [slots, kv_heads, head_dim] with slot = block * block_size + offset.
+ *   HND: [num_blocks + 1][num_kv_heads][block_size][head_dim]
+ *        (one block of one KV head is block_size * head_dim contiguous elements)
+ *   NHD: [num_blocks + 1][block_size][num_kv_heads][head_dim]
+ *        (one slot of all KV heads is num_kv_heads * head_dim contiguous elements) */
+typedef enum pkv_layout {
+  PKV_LAYOUT_HND = 0,
+  PKV_LAYOUT_NHD = 1
+} pkv_layout;
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_EMPTY = 1,          /* zero rows, or zero tokens to write */
+  PKV_ERR_DTYPE = 2,          /* unknown dtype code */
+  PKV_ERR_SHAPE = 3,          /* inconsistent dimensions (e.g. heads % kv_heads != 0) */
+  PKV_ERR_CONTEXT_BOUNDS = 4, /* a context_len < 0, > max_blocks_per_row*block_size,
+                                 or > num_blocks*block_size */
+  PKV_ERR_BLOCK_ID = 5,       /* a live block-table entry outside [0, num_blocks) */
+  PKV_ERR_SLOT = 6,           /* a slot_mapping entry outside [0, sink] */
+  PKV_ERR_UNSUPPORTED = 7,    /* legal, but not a shape this library was built for */
+  PKV_ERR_WORKSPACE = 8,      /* workspace missing or smaller than pkv_workspace_bytes */
+  PKV_ERR_NULL = 9,           /* a required pointer is NULL */
+  PKV_ERR_HIP = 10            /* the HIP runtime reported an error */
+} pkv_status;
+
+/* The pool both caches share.  num_blocks counts the blocks a block table may name;
+ * storage holds one more block, whose first slot is the sink. */
+typedef struct pkv_pool_desc {
+  int64_t num_blocks;    /* NB >= 1 */
+  int32_t block_size;    /* BS: 16, 32, 64, 128 or 256 */
+  int32_t num_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;      /* D: 64, 128 or 256 */
+  int32_t dtype;         /* pkv_dtype */
+  int32_t layout;        /* pkv_layout */
+} pkv_pool_desc;
+
+/* Device status bits raised by kernels run with validate == 0 on bad inputs. */
+#define PKV_DEVERR_SLOT 1u            /* a write slot outside [0, sink] was skipped */
+#define PKV_DEVERR_CONTEXT_BOUNDS 2u  /* a context_len was clamped */
+#define PKV_DEVERR_BLOCK_ID 4u        /* a live block id outside [0, num_blocks) was skipped */
+
+int32_t pkv_abi_version(void);
+const char* pkv_status_str(pkv_status status);
+const char* pkv_last_error_detail(void);
+
+/* The sink slot, num_blocks * block_size (Day 55, "Why it matters": one past the
+ * pool the allocator hands out).  Returns -1 for an invalid descriptor. */
+int64_t pkv_sink_slot(const pkv_pool_desc* pool);
+
+/* Elements of one pool (K or V): (num_blocks + 1) * block_size * num_kv_heads * head_dim.
+ * Returns -1 for an invalid descriptor. */
+int64_t pkv_pool_elements(const pkv_pool_desc* pool);
+
+/* Checks a descriptor: DTYPE, SHAPE or UNSUPPORTED, else OK. */
+pkv_status pkv_check_pool(const pkv_pool_desc* pool);
+
+/* Host-side refusal checks on HOST arrays, in the order EMPTY, DTYPE, SHAPE, SLOT
+ * (write) and EMPTY, DTYPE, SHAPE, CONTEXT_BOUNDS, BLOCK_ID (attention).  The first
+ * offending entry is reported.  Entries of a table row past its live prefix
+ * cdiv(context_len, block_size) are never checked (they may hold -1).  These are the
+ * checks validate != 0 runs; they launch nothing and need no GPU. */
+pkv_status pkv_check_write_host(const pkv_pool_desc* pool, const int64_t* slot_mapping,
+                                int64_t num_tokens);
+pkv_status pkv_check_attention_host(const pkv_pool_desc* pool, const int32_t* block_tables,
+                                    int32_t max_blocks_per_row, const int32_t* context_lens,
+                                    int64_t num_rows, int32_t num_heads);
+
+/* The slot scatter (Day 55, "Why it matters": the padded batch is written with one
+ * indexed assignment, pad rows into the sink).
+ *   k, v          [num_tokens][num_kv_heads][head_dim], pool dtype
+ *   slot_mapping  [num_tokens] int64, each in [0, sink]
+ *   k_cache, v_cache  pools in the descriptor's layout, updated in place
+ * Token i's vectors are copied bit-exactly into slot slot_mapping[i].  Distinct tokens
+ * must name distinct slots, except that any number may name the sink (its contents
+ * afterwards are one of those tokens' vectors).
+ * validate != 0 copies slot_mapping to the host first (synchronising `stream`) and
+ * refuses bad slots before launching. */
+pkv_status pkv_kv_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
+                        const void* k, const void* v, const int64_t* slot_mapping,
+                        int64_t num_tokens, int32_t validate, void* stream);
+
+/* Device workspace bytes pkv_paged_attention needs for this batch shape (may be 0).
+ * Depends only on the arguments, never on the lengths. */
+size_t pkv_workspace_bytes(const pkv_pool_desc* pool, int64_t num_rows, int32_t num_heads,
+                           int32_t max_blocks_per_row);
+
+/* The batched decode read (Day 59, "What I added today").
+ *   q, out        [num_rows][num_heads][head_dim], pool dtype; query head h reads KV
+ *                 head h / (num_heads / num_kv_heads)
+ *   block_tables  [num_rows][max_blocks_per_row] int32; entry j of row r names the
+ *                 pool block holding positions j*block_size .. j*block_size+block_size-1
+ *   context_lens  [num_rows] int32; 0 marks a padding row (output zero, nothing read)
+ *   scale         multiplies q.k before the softmax
+ *   workspace     device scratch of at least pkv_workspace_bytes(...) bytes, owned by
+ *                 the caller; its contents on entry do not matter and are undefined
+ *                 on return.  Two calls in flight at once need two workspaces.
+ * out[r,h,:] = sum_t softmax_t(scale * q[r,h,:].K[t]) V[t] over t < context_lens[r],
+ * accumulated in float32, rounded once to the pool dtype.
+ * validate != 0 copies context_lens and block_tables to the host first (synchronising
+ * `stream`) and refuses bad lengths and block ids before launching. */
+pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int32_t max_blocks_per_row,
+                               const int32_t* context_lens, int64_t num_rows,
+                               int32_t num_heads, float scale, void* workspace,
+                               size_t workspace_bytes, int32_t validate, void* stream);
+
+/* Reads (and if `clear` is non-zero, resets) the current device's status word, a
+ * bitwise OR of PKV_DEVERR_* raised since the last clear.  Synchronises `stream`. */
+pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

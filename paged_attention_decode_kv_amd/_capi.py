@@ -1,0 +1,60 @@
+"""ctypes declarations of libpagedkv.so (include/pagedkv.h).  Loading only; no logic."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+F32, BF16 = 0, 1
+LAYOUT_CODES = {"HND": 0, "NHD": 1}
+STATUS_NAMES = ("OK", "EMPTY", "DTYPE", "SHAPE", "CONTEXT_BOUNDS", "BLOCK_ID", "SLOT",
+                "UNSUPPORTED", "WORKSPACE", "NULL", "HIP")
+DEVERR_SLOT, DEVERR_CONTEXT_BOUNDS, DEVERR_BLOCK_ID = 1, 2, 4
+
+# every function include/pagedkv.h declares: name -> (restype, argtypes)
+_i32, _i64, _sz, _p, _f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p,
+                           ctypes.c_float)
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+_PD = ctypes.POINTER(PoolDesc)
+SIGNATURES = {
+    "pkv_abi_version": (_i32, []),
+    "pkv_status_str": (ctypes.c_char_p, [_i32]),
+    "pkv_last_error_detail": (ctypes.c_char_p, []),
+    "pkv_sink_slot": (_i64, [_PD]),
+    "pkv_pool_elements": (_i64, [_PD]),
+    "pkv_check_pool": (_i32, [_PD]),
+    "pkv_check_write_host": (_i32, [_PD, _p, _i64]),
+    "pkv_check_attention_host": (_i32, [_PD, _p, _i32, _p, _i64, _i32]),
+    "pkv_kv_write": (_i32, [_PD, _p, _p, _p, _p, _p, _i64, _i32, _p]),
+    "pkv_workspace_bytes": (_sz, [_PD, _i64, _i32, _i32]),
+    "pkv_paged_attention": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32, _f, _p,
+                                   _sz, _i32, _p]),
+    "pkv_device_status": (_i32, [ctypes.POINTER(ctypes.c_uint32), _i32, _p]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib

@@ -1,0 +1,200 @@
+"""Python face of libpagedkv.so: torch tensors in, device pointers and sizes out.
+
+Argument marshalling only.  Every step of the decode path runs in the library's HIP
+kernels; this module checks tensor types and shapes, turns them into the C ABI's
+plain pointers and sizes, and raises ``PagedKVError`` on any status but OK.  There is
+no CPU fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _capi
+
+_DTYPES = {torch.float32: _capi.F32, torch.bfloat16: _capi.BF16}
+
+
+class PagedKVError(ValueError):
+    """A refusal or failure of the library; ``code`` is the status name."""
+
+    def __init__(self, code: str, detail: str):
+        super().__init__(f"{code}: {detail}")
+        self.code = code
+        self.detail = detail
+
+
+def _raise(code: str, detail: str):
+    raise PagedKVError(code, detail)
+
+
+def _check(status: int):
+    if status != 0:
+        lib = _capi.lib()
+        name = _capi.STATUS_NAMES[status] if status < len(_capi.STATUS_NAMES) else str(status)
+        _raise(name, lib.pkv_last_error_detail().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def pool_desc(k_cache: torch.Tensor, layout: str = "HND") -> _capi.PoolDesc:
+    """Descriptor of a pool tensor: HND ``[NB+1, Hkv, BS, D]`` or NHD ``[NB+1, BS, Hkv, D]``."""
+    if layout not in _capi.LAYOUT_CODES:
+        _raise("SHAPE", f"unknown layout {layout!r}")
+    if k_cache.dtype not in _DTYPES:
+        _raise("DTYPE", f"pool dtype {k_cache.dtype} is not float32 or bfloat16")
+    if k_cache.dim() != 4:
+        _raise("SHAPE", "pool must be 4-D")
+    nb1 = k_cache.shape[0]
+    if layout == "HND":
+        hkv, bs = k_cache.shape[1], k_cache.shape[2]
+    else:
+        bs, hkv = k_cache.shape[1], k_cache.shape[2]
+    return _capi.PoolDesc(nb1 - 1, bs, hkv, k_cache.shape[3], _DTYPES[k_cache.dtype],
+                          _capi.LAYOUT_CODES[layout])
+
+
+def _pool_pair(k_cache, v_cache, layout):
+    desc = pool_desc(k_cache, layout)
+    if v_cache.dtype != k_cache.dtype:
+        _raise("DTYPE", "K and V pools differ in dtype")
+    if v_cache.shape != k_cache.shape:
+        _raise("SHAPE", "K and V pools differ in shape")
+    for t in (k_cache, v_cache):
+        if not t.is_cuda or not t.is_contiguous():
+            _raise("SHAPE", "pools must be contiguous device tensors")
+    return desc
+
+
+def _device_tensor(t, name, dtype, device):
+    if t.dtype != dtype:
+        _raise("DTYPE", f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        _raise("SHAPE", f"{name} must be a contiguous tensor on {device}")
+
+
+def sink_slot(k_cache: torch.Tensor, layout: str = "HND") -> int:
+    """The sink slot of a pool (num_blocks * block_size)."""
+    desc = pool_desc(k_cache, layout)
+    s = _capi.lib().pkv_sink_slot(ctypes.byref(desc))
+    if s < 0:
+        _check(_capi.lib().pkv_check_pool(ctypes.byref(desc)))
+    return int(s)
+
+
+def kv_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+             k_cache: torch.Tensor, v_cache: torch.Tensor, *, layout: str = "HND",
+             validate: bool = True) -> None:
+    """Scatter token i's K/V into slot ``slot_mapping[i]`` of the pools, in place."""
+    n = int(slot_mapping.shape[0]) if slot_mapping.dim() >= 1 else 0
+    if n == 0:
+        _raise("EMPTY", "no tokens to write")
+    desc = _pool_pair(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _device_tensor(k, "k", k_cache.dtype, dev)
+    _device_tensor(v, "v", k_cache.dtype, dev)
+    _device_tensor(slot_mapping, "slot_mapping", torch.int64, dev)
+    want = (n, desc.num_kv_heads, desc.head_dim)
+    if tuple(k.shape) != want or tuple(v.shape) != want or slot_mapping.dim() != 1:
+        _raise("SHAPE", f"k, v must be {want}, slot_mapping [{n}]")
+    with torch.cuda.device(dev):
+        _check(_capi.lib().pkv_kv_write(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(k), _ptr(v), _ptr(slot_mapping), n,
+                                        int(bool(validate)), _stream(k_cache)))
+
+
+def workspace_bytes(k_cache: torch.Tensor, num_rows: int, num_heads: int, max_blocks: int,
+                    layout: str = "HND") -> int:
+    desc = pool_desc(k_cache, layout)
+    return int(_capi.lib().pkv_workspace_bytes(ctypes.byref(desc), num_rows, num_heads,
+                                               max_blocks))
+
+
+def paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, *,
+                    layout: str = "HND", out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None,
+                    validate: bool = True) -> torch.Tensor:
+    """The batched decode read; returns ``out`` ``[rows, heads, head_dim]``."""
+    rows = int(context_lens.shape[0]) if context_lens.dim() >= 1 else 0
+    if rows == 0:
+        _raise("EMPTY", "no rows")
+    desc = _pool_pair(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _device_tensor(q, "q", k_cache.dtype, dev)
+    _device_tensor(block_tables, "block_tables", torch.int32, dev)
+    _device_tensor(context_lens, "context_lens", torch.int32, dev)
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[2] != desc.head_dim:
+        _raise("SHAPE", f"q must be [{rows}, heads, {desc.head_dim}], got {tuple(q.shape)}")
+    heads = int(q.shape[1])
+    if context_lens.dim() != 1 or block_tables.dim() != 2 or block_tables.shape[0] != rows:
+        _raise("SHAPE", "block_tables must be [rows, max_blocks], context_lens [rows]")
+    max_blocks = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, dev)
+        if out.shape != q.shape:
+            _raise("SHAPE", "out must have q's shape")
+    lib = _capi.lib()
+    need = int(lib.pkv_workspace_bytes(ctypes.byref(desc), rows, heads, max_blocks))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        _raise("WORKSPACE", "workspace must be a contiguous tensor on the pool's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        _check(lib.pkv_paged_attention(ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(block_tables), max_blocks,
+                                       _ptr(context_lens), rows, heads, float(scale),
+                                       _ptr(workspace), ws_bytes, int(bool(validate)),
+                                       _stream(k_cache)))
+    return out
+
+
+def device_status(device=None, clear: bool = True) -> int:
+    """Bitwise OR of the device-side refusal bits raised since the last clear."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    flags = ctypes.c_uint32(0)
+    with torch.cuda.device(dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        _check(_capi.lib().pkv_device_status(ctypes.byref(flags), int(bool(clear)), stream))
+    return int(flags.value)
+
+
+# ---------------------------------------------------------------------------- #
+# host-side checks (no GPU needed)
+# ---------------------------------------------------------------------------- #
+def host_desc(num_blocks, block_size, kv_heads, head_dim, dtype="bf16", layout="HND"):
+    return _capi.PoolDesc(num_blocks, block_size, kv_heads, head_dim,
+                          {"f32": _capi.F32, "bf16": _capi.BF16}.get(dtype, 99),
+                          _capi.LAYOUT_CODES.get(layout, 99))
+
+
+def check_write_host(desc: _capi.PoolDesc, slot_mapping: np.ndarray) -> str:
+    """Status name the library's host validator gives a write."""
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    st = _capi.lib().pkv_check_write_host(ctypes.byref(desc),
+                                          sm.ctypes.data_as(ctypes.c_void_p), sm.shape[0])
+    return _capi.STATUS_NAMES[st]
+
+
+def check_attention_host(desc: _capi.PoolDesc, block_tables: np.ndarray,
+                         context_lens: np.ndarray, num_heads: int) -> str:
+    """Status name the library's host validator gives a read."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    m = bt.shape[1] if bt.ndim == 2 else 0
+    st = _capi.lib().pkv_check_attention_host(
+        ctypes.byref(desc), bt.ctypes.data_as(ctypes.c_void_p), m,
+        ctx.ctypes.data_as(ctypes.c_void_p), ctx.shape[0], num_heads)
+    return _capi.STATUS_NAMES[st]

@@ -1,0 +1,300 @@
+// C ABI of the decode step: argument checks, host-side refusals, workspace sizing
+// and the launches.  The kernels themselves are in kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "pagedkv.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+pkv_status ok() {
+  g_detail.clear();
+  return PKV_OK;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int n = 0;
+  while ((int64_t{1} << n) < x) ++n;
+  return n;
+}
+
+// Descriptor checks shared by every call: DTYPE, then SHAPE, then UNSUPPORTED.
+pkv_status check_pool(const pkv_pool_desc* p) {
+  if (!p) return fail(PKV_ERR_NULL, "pool descriptor is NULL");
+  if (p->dtype != PKV_F32 && p->dtype != PKV_BF16)
+    return fail(PKV_ERR_DTYPE, "unknown dtype code %d", p->dtype);
+  if (p->num_blocks < 1 || p->num_blocks > INT32_MAX)
+    return fail(PKV_ERR_SHAPE, "num_blocks %lld outside [1, 2^31)", (long long)p->num_blocks);
+  if (p->block_size < 1 || p->num_kv_heads < 1 || p->head_dim < 1)
+    return fail(PKV_ERR_SHAPE, "block_size, num_kv_heads and head_dim must be positive");
+  if (p->layout != PKV_LAYOUT_HND && p->layout != PKV_LAYOUT_NHD)
+    return fail(PKV_ERR_SHAPE, "unknown layout code %d", p->layout);
+  if (!is_pow2(p->block_size) || p->block_size < 16 || p->block_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d: built for powers of two in [16, 256]",
+                p->block_size);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: built for 64, 128 and 256", p->head_dim);
+  return PKV_OK;
+}
+
+pkv::PoolGeom geom(const pkv_pool_desc* p) {
+  pkv::PoolGeom g;
+  g.num_blocks = p->num_blocks;
+  g.block_size = p->block_size;
+  g.log2_bs = log2i(p->block_size);
+  g.kv_heads = p->num_kv_heads;
+  g.head_dim = p->head_dim;
+  g.dtype = p->dtype;
+  const int64_t bs = p->block_size, hkv = p->num_kv_heads, d = p->head_dim;
+  g.blk_stride = bs * hkv * d;
+  if (p->layout == PKV_LAYOUT_HND) {
+    g.head_stride = bs * d;
+    g.tok_stride = d;
+  } else {
+    g.head_stride = d;
+    g.tok_stride = hkv * d;
+  }
+  return g;
+}
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t ctx_limit_of(const pkv_pool_desc* p, int32_t max_blocks) {
+  const int64_t by_table = (int64_t)max_blocks * p->block_size;
+  const int64_t by_pool = p->num_blocks * p->block_size;
+  return by_table < by_pool ? by_table : by_pool;
+}
+
+// Attention shape checks that need no data: EMPTY, pool, SHAPE, UNSUPPORTED.
+pkv_status check_attention_shape(const pkv_pool_desc* pool, int32_t max_blocks,
+                                 int64_t num_rows, int32_t num_heads) {
+  if (num_rows == 0) return fail(PKV_ERR_EMPTY, "no rows");
+  pkv_status s = check_pool(pool);
+  if (s != PKV_OK) return s;
+  if (num_rows < 0) return fail(PKV_ERR_SHAPE, "num_rows %lld < 0", (long long)num_rows);
+  if (num_heads < 1 || num_heads % pool->num_kv_heads != 0)
+    return fail(PKV_ERR_SHAPE, "%d query heads is not a positive multiple of %d KV heads",
+                num_heads, pool->num_kv_heads);
+  if (max_blocks < 1) return fail(PKV_ERR_SHAPE, "max_blocks_per_row %d < 1", max_blocks);
+  if (num_rows > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "num_rows %lld: built for at most 65535 rows",
+                (long long)num_rows);
+  if ((int64_t)max_blocks * pool->block_size > (int64_t{1} << 24))
+    return fail(PKV_ERR_UNSUPPORTED, "table width %lld tokens: built for at most 2^24",
+                (long long)max_blocks * pool->block_size);
+  return PKV_OK;
+}
+
+pkv_status check_attention_data(const pkv_pool_desc* pool, const int32_t* bt,
+                                int32_t max_blocks, const int32_t* ctx, int64_t num_rows) {
+  const int64_t limit = ctx_limit_of(pool, max_blocks);
+  for (int64_t r = 0; r < num_rows; ++r) {
+    if (ctx[r] < 0 || ctx[r] > limit)
+      return fail(PKV_ERR_CONTEXT_BOUNDS, "context_lens[%lld] = %d outside [0, %lld]",
+                  (long long)r, ctx[r], (long long)limit);
+  }
+  for (int64_t r = 0; r < num_rows; ++r) {
+    const int64_t live = (ctx[r] + (int64_t)pool->block_size - 1) / pool->block_size;
+    for (int64_t j = 0; j < live; ++j) {
+      const int32_t id = bt[r * max_blocks + j];
+      if (id < 0 || id >= pool->num_blocks)
+        return fail(PKV_ERR_BLOCK_ID, "block_tables[%lld, %lld] = %d outside [0, %lld)",
+                    (long long)r, (long long)j, id, (long long)pool->num_blocks);
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status check_write_data(const pkv_pool_desc* pool, const int64_t* slots, int64_t n) {
+  const int64_t sink = pool->num_blocks * pool->block_size;
+  for (int64_t i = 0; i < n; ++i)
+    if (slots[i] < 0 || slots[i] > sink)
+      return fail(PKV_ERR_SLOT, "slot_mapping[%lld] = %lld outside [0, %lld]", (long long)i,
+                  (long long)slots[i], (long long)sink);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_str(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "OK";
+    case PKV_ERR_EMPTY: return "EMPTY";
+    case PKV_ERR_DTYPE: return "DTYPE";
+    case PKV_ERR_SHAPE: return "SHAPE";
+    case PKV_ERR_CONTEXT_BOUNDS: return "CONTEXT_BOUNDS";
+    case PKV_ERR_BLOCK_ID: return "BLOCK_ID";
+    case PKV_ERR_SLOT: return "SLOT";
+    case PKV_ERR_UNSUPPORTED: return "UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "WORKSPACE";
+    case PKV_ERR_NULL: return "NULL";
+    case PKV_ERR_HIP: return "HIP";
+  }
+  return "UNKNOWN";
+}
+
+const char* pkv_last_error_detail(void) { return g_detail.c_str(); }
+
+int64_t pkv_sink_slot(const pkv_pool_desc* pool) {
+  if (check_pool(pool) != PKV_OK) return -1;
+  return pool->num_blocks * pool->block_size;
+}
+
+int64_t pkv_pool_elements(const pkv_pool_desc* pool) {
+  if (check_pool(pool) != PKV_OK) return -1;
+  return (pool->num_blocks + 1) * pool->block_size * (int64_t)pool->num_kv_heads *
+         pool->head_dim;
+}
+
+pkv_status pkv_check_pool(const pkv_pool_desc* pool) {
+  pkv_status s = check_pool(pool);
+  return s == PKV_OK ? ok() : s;
+}
+
+pkv_status pkv_check_write_host(const pkv_pool_desc* pool, const int64_t* slot_mapping,
+                                int64_t num_tokens) {
+  if (num_tokens == 0) return fail(PKV_ERR_EMPTY, "no tokens to write");
+  pkv_status s = check_pool(pool);
+  if (s != PKV_OK) return s;
+  if (num_tokens < 0) return fail(PKV_ERR_SHAPE, "num_tokens %lld < 0", (long long)num_tokens);
+  if (!slot_mapping) return fail(PKV_ERR_NULL, "slot_mapping is NULL");
+  s = check_write_data(pool, slot_mapping, num_tokens);
+  return s == PKV_OK ? ok() : s;
+}
+
+pkv_status pkv_check_attention_host(const pkv_pool_desc* pool, const int32_t* block_tables,
+                                    int32_t max_blocks_per_row, const int32_t* context_lens,
+                                    int64_t num_rows, int32_t num_heads) {
+  pkv_status s = check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  if (!block_tables || !context_lens) return fail(PKV_ERR_NULL, "table or lengths NULL");
+  s = check_attention_data(pool, block_tables, max_blocks_per_row, context_lens, num_rows);
+  return s == PKV_OK ? ok() : s;
+}
+
+pkv_status pkv_kv_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
+                        const void* k, const void* v, const int64_t* slot_mapping,
+                        int64_t num_tokens, int32_t validate, void* stream) {
+  if (num_tokens == 0) return fail(PKV_ERR_EMPTY, "no tokens to write");
+  pkv_status s = check_pool(pool);
+  if (s != PKV_OK) return s;
+  if (num_tokens < 0) return fail(PKV_ERR_SHAPE, "num_tokens %lld < 0", (long long)num_tokens);
+  if (!k_cache || !v_cache || !k || !v || !slot_mapping)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (validate) {
+    std::vector<int64_t> host((size_t)num_tokens);
+    hipError_t e = hipMemcpyAsync(host.data(), slot_mapping, host.size() * sizeof(int64_t),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "copying slot_mapping to the host");
+    s = check_write_data(pool, host.data(), num_tokens);
+    if (s != PKV_OK) return s;
+  }
+  pkv::WriteArgs a;
+  a.g = geom(pool);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k = k;
+  a.v = v;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  hipError_t e = pkv::launch_kv_write(a, st);
+  if (e != hipSuccess) return hip_fail(e, "launching kv_write");
+  return ok();
+}
+
+size_t pkv_workspace_bytes(const pkv_pool_desc* pool, int64_t num_rows, int32_t num_heads,
+                           int32_t max_blocks_per_row) {
+  if (check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads) != PKV_OK) return 0;
+  return pkv::workspace_bytes(num_rows, num_heads, pool->head_dim, max_blocks_per_row,
+                              pool->block_size);
+}
+
+pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, int32_t max_blocks_per_row,
+                               const int32_t* context_lens, int64_t num_rows,
+                               int32_t num_heads, float scale, void* workspace,
+                               size_t workspace_bytes, int32_t validate, void* stream) {
+  pkv_status s = check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  const size_t need = pkv::workspace_bytes(num_rows, num_heads, pool->head_dim,
+                                           max_blocks_per_row, pool->block_size);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  const int64_t most_items = num_rows * ((int64_t)max_blocks_per_row * pool->block_size /
+                                         pkv::kChunkTokens + 1) * num_heads;
+  if (most_items > (int64_t{1} << 30))
+    return fail(PKV_ERR_UNSUPPORTED, "rows x heads x chunks too large for one call");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (validate) {
+    std::vector<int32_t> ctx((size_t)num_rows);
+    std::vector<int32_t> bt((size_t)(num_rows * max_blocks_per_row));
+    hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(bt.data(), block_tables, bt.size() * sizeof(int32_t),
+                         hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "copying lengths and tables to the host");
+    s = check_attention_data(pool, bt.data(), max_blocks_per_row, ctx.data(), num_rows);
+    if (s != PKV_OK) return s;
+  }
+  pkv::AttnArgs a;
+  a.g = geom(pool);
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_rows = num_rows;
+  a.num_heads = num_heads;
+  a.max_blocks = max_blocks_per_row;
+  a.ctx_limit = (int32_t)ctx_limit_of(pool, max_blocks_per_row);
+  a.scale = scale;
+  const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads,
+                                                 pool->head_dim, max_blocks_per_row,
+                                                 pool->block_size);
+  hipError_t e = pkv::launch_paged_attention(a, ws, st);
+  if (e != hipSuccess) return hip_fail(e, "launching paged_attention");
+  return ok();
+}
+
+pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
+  if (!flags) return fail(PKV_ERR_NULL, "flags is NULL");
+  hipError_t e = pkv::read_device_status(flags, clear, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reading the device status word");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+"""The C-ABI library loads without a GPU, exports every declared symbol, and its host
+validator refuses exactly what the oracle refuses (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_attention_decode_kv_amd import _capi, binding
+from paged_attention_decode_kv_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_capi.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _capi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_capi.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_and_status_strings(lib):
+    assert lib.pkv_abi_version() == 1
+    for code, name in enumerate(_capi.STATUS_NAMES):
+        assert lib.pkv_status_str(code).decode() == name
+
+
+def test_descriptor_arithmetic(lib):
+    d = binding.host_desc(131072, 16, 32, 128)
+    assert lib.pkv_sink_slot(ctypes.byref(d)) == 131072 * 16
+    assert lib.pkv_pool_elements(ctypes.byref(d)) == 131073 * 16 * 32 * 128
+    assert lib.pkv_check_pool(ctypes.byref(d)) == 0
+    for bad, code in ((binding.host_desc(8, 16, 4, 64, dtype="f16"), "DTYPE"),
+                      (binding.host_desc(0, 16, 4, 64), "SHAPE"),
+                      (binding.host_desc(8, 16, 4, 64, layout="XYZ"), "SHAPE"),
+                      (binding.host_desc(8, 12, 4, 64), "UNSUPPORTED"),
+                      (binding.host_desc(8, 16, 4, 96), "UNSUPPORTED")):
+        assert _capi.STATUS_NAMES[lib.pkv_check_pool(ctypes.byref(bad))] == code
+        assert lib.pkv_sink_slot(ctypes.byref(bad)) == -1
+
+
+def test_workspace_size_depends_on_shape_only(lib):
+    d = binding.host_desc(131072, 16, 32, 128)
+    small = lib.pkv_workspace_bytes(ctypes.byref(d), 8, 32, 128)
+    big = lib.pkv_workspace_bytes(ctypes.byref(d), 256, 32, 512)
+    assert 0 < small < big
+    assert lib.pkv_workspace_bytes(ctypes.byref(d), 0, 32, 128) == 0
+
+
+def _oracle_code(fn):
+    try:
+        fn()
+    except oracle.Refusal as e:
+        return e.code
+    return "OK"
+
+
+def _attention_cases():
+    w = wl.make_custom([16, 40, 0, 7], heads=4, kv_heads=2, head_dim=64, num_blocks=12,
+                       max_blocks=4, seed=5)
+    cases = [("legal", w.block_tables, w.context_lens)]
+    ctx = w.context_lens.copy(); ctx[1] = -3
+    cases.append(("negative length", w.block_tables, ctx))
+    ctx = w.context_lens.copy(); ctx[3] = 4 * 16 + 1
+    cases.append(("past the table", w.block_tables, ctx))
+    bt = w.block_tables.copy(); bt[1, 2] = -1
+    cases.append(("-1 inside the live prefix", bt, w.context_lens))
+    bt = w.block_tables.copy(); bt[3, 0] = w.num_blocks
+    cases.append(("sink block named", bt, w.context_lens))
+    bt = w.block_tables.copy(); bt[0, 1:] = -1; bt[2, :] = 99
+    cases.append(("junk past the live prefix", bt, w.context_lens))
+    ctx = np.zeros_like(w.context_lens)
+    cases.append(("all padding", np.full_like(w.block_tables, -1), ctx))
+    ctx = w.context_lens.copy(); ctx[0] = 64
+    bt = w.block_tables.copy(); bt[0] = [0, 1, 2, 3]
+    cases.append(("length fills the table", bt, ctx))
+    return w, cases
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_attention_refusals_match_the_oracle(lib, idx):
+    w, cases = _attention_cases()
+    name, bt, ctx = cases[idx]
+    k, v = wl.history_host(w)
+    want = _oracle_code(lambda: oracle.validate_attention(
+        w.q, k, v, bt, ctx, num_blocks=w.num_blocks, block_size=w.block_size,
+        layout=w.layout, dtype=w.dtype))
+    d = binding.host_desc(w.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype,
+                          w.layout)
+    assert binding.check_attention_host(d, bt, ctx, w.heads) == want, name
+
+
+def test_empty_and_shape_refusals_match_the_oracle(lib):
+    w, _ = _attention_cases()
+    d = binding.host_desc(w.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype,
+                          w.layout)
+    k, v = wl.history_host(w)
+    want = _oracle_code(lambda: oracle.validate_attention(
+        w.q[:0], k, v, w.block_tables[:0], w.context_lens[:0], num_blocks=w.num_blocks,
+        block_size=w.block_size, layout=w.layout, dtype=w.dtype))
+    assert binding.check_attention_host(d, w.block_tables[:0], w.context_lens[:0],
+                                        w.heads) == want == "EMPTY"
+    want = _oracle_code(lambda: oracle.validate_attention(
+        w.q[:, :3], k, v, w.block_tables, w.context_lens, num_blocks=w.num_blocks,
+        block_size=w.block_size, layout=w.layout, dtype=w.dtype))
+    assert binding.check_attention_host(d, w.block_tables, w.context_lens, 3) == want == "SHAPE"
+
+
+@pytest.mark.parametrize("slots", [[0, 5, 8 * 16], [8 * 16, 8 * 16], [8 * 16 + 1, 3],
+                                   [2, -1], [127, 128, 129]])
+def test_write_refusals_match_the_oracle(lib, slots):
+    w = wl.make_custom([3] * len(slots), heads=2, head_dim=64, num_blocks=8, seed=1)
+    k, v = wl.history_host(w)
+    sm = np.array(slots, dtype=np.int64)
+    want = _oracle_code(lambda: oracle.validate_write(
+        k, v, w.k_new, w.v_new, sm, num_blocks=8, block_size=16, layout="HND", dtype="f32"))
+    d = binding.host_desc(8, 16, w.kv_heads, w.head_dim, "f32", "HND")
+    assert binding.check_write_host(d, sm) == want
+
+
+def test_empty_write_is_refused(lib):
+    d = binding.host_desc(8, 16, 2, 64, "f32", "HND")
+    assert binding.check_write_host(d, np.zeros(0, dtype=np.int64)) == "EMPTY"

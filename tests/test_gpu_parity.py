@@ -1,0 +1,373 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (written here, derived from the arithmetic):
+* float32 pools: max |gpu - oracle| <= 2e-6;
+* bfloat16 pools: max |gpu - oracle| <= 2e-2, and the tighter per-element bound
+  |gpu - oracle| <= 2^-8 |oracle| + 2e-5: the kernel accumulates in float32 (relative
+  error ~1e-6 on these sizes) and rounds once to bfloat16 (half an ulp, 2^-9 relative);
+* the slot scatter: bit-exact.
+Small cases compare every output; the large configurations (pools of 2-34 GB) compare
+sampled rows, each recomputed by the oracle from a host copy of just the blocks those
+rows name (block relabelling leaves the oracle's result unchanged, a pinned invariant).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_attention_decode_kv_amd import binding
+from paged_attention_decode_kv_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+# --------------------------------------------------------------------------- #
+# helpers
+# --------------------------------------------------------------------------- #
+def say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def to_dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_host(t, dtype):
+    t = t.detach().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bits(t):
+    """Integer view of a tensor, for bit-exact comparison."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def assert_close(got_storage, ref, dtype, where=""):
+    got = oracle.decode_storage(got_storage, dtype)
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got)), f"non-finite output {where}"
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max() <= 2e-6, f"max err {err.max():.3e} {where}"
+    else:
+        assert err.max() <= 2e-2, f"max err {err.max():.3e} {where}"
+        bound = 2.0 ** -8 * np.abs(ref) + 2e-5
+        worst = np.argmax(err - bound)
+        assert np.all(err <= bound), (f"err {err.flat[worst]:.3e} > bound "
+                                      f"{bound.flat[worst]:.3e} at {worst} {where}")
+    return float(err.max())
+
+
+class Step:
+    """Device tensors of one workload, before and after a decode step."""
+
+    def __init__(self, w, *, host_history=None):
+        self.w = w
+        host_history = w.history_on_host() if host_history is None else host_history
+        self.k_host = self.v_host = None
+        if host_history:
+            self.k_host, self.v_host = wl.history_host(w)
+            self.k_cache = to_dev(self.k_host, w.dtype)
+            self.v_cache = to_dev(self.v_host, w.dtype)
+        else:
+            self.k_cache = torch.empty(w.pool_shape, dtype=TORCH_DT[w.dtype], device=DEV)
+            self.v_cache = torch.empty_like(self.k_cache)
+            wl.history_device(w, self.k_cache, self.v_cache)
+        self.q = to_dev(w.q, w.dtype)
+        self.k_new = to_dev(w.k_new, w.dtype)
+        self.v_new = to_dev(w.v_new, w.dtype)
+        self.slots = to_dev(w.slot_mapping)
+        self.tables = to_dev(w.block_tables)
+        self.lens = to_dev(w.context_lens)
+
+    def run(self, validate=True, out=None):
+        w = self.w
+        binding.kv_write(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache,
+                         layout=w.layout, validate=validate)
+        out = binding.paged_attention(self.q, self.k_cache, self.v_cache, self.tables,
+                                      self.lens, w.scale, layout=w.layout, out=out,
+                                      validate=validate)
+        torch.cuda.synchronize()
+        return out
+
+    def host_pools_for(self, rows):
+        """Host copies of the pre-step blocks the given rows name, relabelled 0..n-1,
+        with the tables and write slots of those rows remapped to match."""
+        w = self.w
+        blocks = wl.live_blocks(w, rows)
+        remap = {int(b): i for i, b in enumerate(blocks)}
+        n = len(blocks)
+        idx = torch.from_numpy(np.append(blocks, w.num_blocks).astype(np.int64)).to(DEV)
+        k = to_host(self.k_cache.index_select(0, idx), w.dtype)
+        v = to_host(self.v_cache.index_select(0, idx), w.dtype)
+        bt = np.full((len(rows), w.max_blocks), -1, dtype=np.int32)
+        sm = np.empty(len(rows), dtype=np.int64)
+        for i, r in enumerate(rows):
+            live = wl.cdiv(w.context_lens[r], w.block_size)
+            bt[i, :live] = [remap[int(b)] for b in w.block_tables[r, :live]]
+            s = int(w.slot_mapping[r])
+            if w.context_lens[r] == 0:
+                sm[i] = n * w.block_size
+            else:
+                sm[i] = remap[s // w.block_size] * w.block_size + s % w.block_size
+        return k, v, bt, sm, n
+
+
+def oracle_full(w, k_host, v_host):
+    kw, vw = k_host.copy(), v_host.copy()
+    oracle.kv_write(kw, vw, w.k_new, w.v_new, w.slot_mapping, num_blocks=w.num_blocks,
+                    block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+    out = oracle.paged_attention(w.q, kw, vw, w.block_tables, w.context_lens, w.scale,
+                                 num_blocks=w.num_blocks, block_size=w.block_size,
+                                 layout=w.layout, dtype=w.dtype)
+    return out, kw, vw
+
+
+def oracle_rows(step, rows, chunk=4):
+    """Oracle outputs of the given rows, a few rows per oracle call."""
+    w = step.w
+    out = np.zeros((len(rows), w.heads, w.head_dim))
+    for at in range(0, len(rows), chunk):
+        part = rows[at:at + chunk]
+        k, v, bt, sm, n = step.host_pools_for(part)
+        oracle.kv_write(k, v, w.k_new[part], w.v_new[part], sm, num_blocks=n,
+                        block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+        out[at:at + len(part)] = oracle.paged_attention(
+            w.q[part], k, v, bt, w.context_lens[part], w.scale, num_blocks=n,
+            block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+    return out
+
+
+def check_full(w):
+    say(f"{w.name}: rows={w.rows} heads={w.heads}/{w.kv_heads} d={w.head_dim} "
+        f"bs={w.block_size} {w.dtype} {w.layout} lens={w.context_lens.tolist()[:8]}")
+    st = Step(w, host_history=True)
+    out = st.run()
+    ref, kw, vw = oracle_full(w, st.k_host, st.v_host)
+    err = assert_close(to_host(out, w.dtype), ref, w.dtype, w.name)
+    # the scatter: bit-exact everywhere but the sink, whose value is one pad row's
+    sink_b = w.num_blocks
+    gk, gv = to_host(st.k_cache, w.dtype), to_host(st.v_cache, w.dtype)
+    ints = np.uint16 if w.dtype == "bf16" else np.uint32
+    for got, want in ((gk, kw), (gv, vw)):
+        assert np.array_equal(got[:sink_b].view(ints), want[:sink_b].view(ints))
+    return err
+
+
+# --------------------------------------------------------------------------- #
+# the named configurations
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_config1_tiny_fp32(layout):
+    err = check_full(wl.make_config(1, layout=layout))
+    say(f"tiny fp32 {layout}: max err {err:.3e}")
+
+
+def test_config2_uniform_bf16():
+    err = check_full(wl.make_config(2))
+    say(f"uniform bf16: max err {err:.3e}")
+
+
+def _sampled(idx, rows_pick):
+    w = wl.make_config(idx)
+    say(f"{w.name}: building {w.pool_bytes / 1e9:.1f} GB of pools on the device")
+    st = Step(w, host_history=False)
+    k_before = st.k_cache.clone()
+    v_before = st.v_cache.clone()
+    out = st.run()
+    rows = rows_pick(w)
+    say(f"{w.name}: oracle on rows {rows}")
+    ref = oracle_rows(st, rows)
+    got = to_host(out, w.dtype)[rows]
+    err = assert_close(got, ref, w.dtype, w.name)
+    # scatter: every live row's slot holds its new K/V bit-exactly, nothing else moved
+    live = w.live_rows
+    slots = torch.from_numpy(w.slot_mapping[live]).to(DEV)
+    blk, off = slots // w.block_size, slots % w.block_size
+    rows_dev = torch.from_numpy(live).to(DEV)
+    sink_b = w.num_blocks
+    for pool, before, new in ((st.k_cache, k_before, st.k_new),
+                              (st.v_cache, v_before, st.v_new)):
+        if w.layout == "HND":
+            assert torch.equal(bits(pool[blk, :, off, :]), bits(new[rows_dev]))
+            before[blk, :, off, :] = new[rows_dev]
+            before[sink_b, :, 0, :] = pool[sink_b, :, 0, :]
+        else:
+            assert torch.equal(bits(pool[blk, off]), bits(new[rows_dev]))
+            before[blk, off] = new[rows_dev]
+            before[sink_b, 0] = pool[sink_b, 0]
+        assert torch.equal(bits(before), bits(pool)), "the scatter touched another slot"
+    # padding rows: zero output
+    pads = w.pad_rows
+    if len(pads):
+        assert torch.count_nonzero(out[torch.from_numpy(pads).to(DEV)]).item() == 0
+    say(f"{w.name}: sampled max err {err:.3e}")
+    del k_before, v_before, st
+    torch.cuda.empty_cache()
+
+
+def test_config3_ragged_sampled():
+    def pick(w):
+        lens = w.context_lens
+        return sorted({int(np.argmax(lens)), int(np.argmin(np.where(lens > 0, lens, 10**9))),
+                       *w.pad_rows.tolist(), 5, 17})
+    _sampled(3, pick)
+
+
+def test_config4_long_tail_sampled():
+    def pick(w):
+        lens = w.context_lens
+        return sorted({w.meta["forced_row"], int(np.argmin(lens)), 0, 100, 200, 255,
+                       int(np.argsort(lens)[128])})
+    _sampled(4, pick)
+
+
+def test_config5_full_width_sampled():
+    def pick(w):
+        lens = w.context_lens
+        full = np.nonzero(lens == 8192)[0]
+        mid = np.nonzero((lens > 256) & (lens < 8192))[0]
+        short = np.nonzero((lens > 0) & (lens <= 256))[0]
+        return sorted({int(full[0]), int(full[-1]), int(mid[0]), int(mid[len(mid) // 2]),
+                       int(short[0]), int(w.pad_rows[0]), int(w.pad_rows[-1])})
+    _sampled(5, pick)
+
+
+# --------------------------------------------------------------------------- #
+# shapes, ragged tails and edges at sizes the oracle finishes quickly
+# --------------------------------------------------------------------------- #
+SWEEP = [
+    # lens, heads, kv_heads, head_dim, block_size, dtype, layout
+    ([1, 15, 16, 17, 255, 256, 257, 700], 8, 8, 128, 16, "bf16", "HND"),
+    ([1, 15, 16, 17, 255, 256, 257, 700], 8, 8, 128, 16, "f32", "HND"),
+    ([513, 0, 33, 1024, 5], 8, 2, 128, 16, "bf16", "NHD"),
+    ([513, 0, 33, 1024, 5], 8, 2, 128, 16, "f32", "NHD"),
+    ([300, 64, 1, 0, 97], 4, 4, 64, 16, "bf16", "HND"),
+    ([300, 64, 1, 0, 97], 4, 1, 64, 32, "f32", "NHD"),
+    ([130, 257, 2], 4, 2, 256, 16, "bf16", "HND"),
+    ([130, 257, 2], 4, 4, 256, 64, "f32", "HND"),
+    ([777, 512, 31], 16, 4, 128, 32, "bf16", "NHD"),
+    ([1000, 3], 4, 4, 64, 128, "bf16", "HND"),
+    ([2049, 40], 4, 4, 128, 256, "f32", "NHD"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=lambda c: f"{c[5]}-{c[6]}-d{c[3]}-bs{c[4]}-h{c[1]}/{c[2]}")
+def test_shape_sweep(case):
+    lens, h, hkv, d, bs, dtype, layout = case
+    w = wl.make_custom(lens, heads=h, kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype,
+                       layout=layout, seed=sum(lens) + d + bs)
+    check_full(w)
+
+
+def test_all_padding_batch():
+    w = wl.make_custom([0, 0, 0], heads=4, head_dim=128, dtype="bf16", seed=2)
+    st = Step(w, host_history=True)
+    out = st.run()
+    assert torch.count_nonzero(out).item() == 0
+    gk = to_host(st.k_cache, w.dtype)
+    assert np.array_equal(gk[:w.num_blocks], st.k_host[:w.num_blocks])
+
+
+def test_full_table_single_row():
+    w = wl.make_custom([4096], heads=4, kv_heads=4, head_dim=128, block_size=16,
+                       dtype="f32", max_blocks=256, num_blocks=256, seed=4)
+    check_full(w)
+
+
+def test_poisoned_pad_slots_are_never_read():
+    """NaN in every slot no live position names (stale tails and unnamed blocks) and -1
+    past each live table prefix leave the output equal to the unpoisoned oracle's."""
+    w = wl.make_custom([37, 5, 0, 16, 300, 1], heads=4, head_dim=128, dtype="bf16",
+                       num_blocks=64, max_blocks=24, seed=6)
+    k_host, v_host = wl.history_host(w)
+    ref, _, _ = oracle_full(w, k_host, v_host)
+    live = {}
+    for r in range(w.rows):
+        for t in range(int(w.context_lens[r])):
+            live.setdefault(int(w.block_tables[r, t // 16]), set()).add(t % 16)
+    kp, vp = k_host.copy(), v_host.copy()
+    for b in range(w.num_blocks + 1):
+        for o in range(16):
+            if o not in live.get(b, ()):
+                kp[b, :, o, :] = wl.BF16_NAN
+                vp[b, :, o, :] = wl.BF16_NAN
+    st = Step(w, host_history=True)
+    st.k_cache.copy_(to_dev(kp, "bf16"))
+    st.v_cache.copy_(to_dev(vp, "bf16"))
+    # the written slots receive finite new K/V; the sink keeps NaN
+    out = st.run()
+    assert_close(to_host(out, w.dtype), ref, w.dtype, "poisoned")
+
+
+def test_block_placement_is_bit_invisible():
+    w = wl.make_custom([300, 45, 513, 0, 16], heads=8, kv_heads=4, head_dim=128,
+                       dtype="bf16", num_blocks=96, max_blocks=40, seed=8)
+    st = Step(w, host_history=True)
+    base = to_host(st.run(), w.dtype)
+    pi = np.random.default_rng(3).permutation(w.num_blocks)
+    k2, v2 = st.k_host.copy(), st.v_host.copy()
+    k2[pi] = st.k_host[:w.num_blocks]
+    v2[pi] = st.v_host[:w.num_blocks]
+    w2 = wl.make_custom([300, 45, 513, 0, 16], heads=8, kv_heads=4, head_dim=128,
+                        dtype="bf16", num_blocks=96, max_blocks=40, seed=8)
+    bt = w2.block_tables.copy()
+    bt[bt >= 0] = pi[bt[bt >= 0]]
+    w2.block_tables = bt
+    sm = w2.slot_mapping.copy()
+    livem = w2.context_lens > 0
+    sm[livem] = pi[sm[livem] // 16] * 16 + sm[livem] % 16
+    w2.slot_mapping = sm
+    st2 = Step(w2, host_history=True)
+    st2.k_cache.copy_(to_dev(k2, "bf16"))
+    st2.v_cache.copy_(to_dev(v2, "bf16"))
+    moved = to_host(st2.run(), w2.dtype)
+    assert np.array_equal(base, moved)
+
+
+def test_runs_are_bit_deterministic():
+    w = wl.make_config(4)
+    st = Step(w, host_history=False)
+    a = to_host(st.run(validate=False), w.dtype)
+    b = to_host(st.run(validate=False), w.dtype)
+    assert np.array_equal(a, b)
+
+
+def test_refusals_touch_nothing():
+    w = wl.make_custom([37, 5, 16], heads=4, head_dim=128, dtype="bf16", seed=9)
+    st = Step(w, host_history=True)
+    out = torch.full_like(st.q, 7.0)
+    bad = st.tables.clone()
+    bad[1, 0] = w.num_blocks                       # the sink block named in a live prefix
+    with pytest.raises(binding.PagedKVError) as e:
+        binding.paged_attention(st.q, st.k_cache, st.v_cache, bad, st.lens, w.scale,
+                                out=out)
+    assert e.value.code == "BLOCK_ID"
+    lens = st.lens.clone()
+    lens[2] = w.max_blocks * w.block_size + 1
+    with pytest.raises(binding.PagedKVError) as e:
+        binding.paged_attention(st.q, st.k_cache, st.v_cache, st.tables, lens, w.scale,
+                                out=out)
+    assert e.value.code == "CONTEXT_BOUNDS"
+    slots = st.slots.clone()
+    slots[0] = w.sink + 1
+    with pytest.raises(binding.PagedKVError) as e:
+        binding.kv_write(st.k_new, st.v_new, slots, st.k_cache, st.v_cache)
+    assert e.value.code == "SLOT"
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    assert np.array_equal(to_host(st.k_cache, "bf16"), st.k_host)
+    assert np.array_equal(to_host(st.v_cache, "bf16"), st.v_host)
+    with pytest.raises(binding.PagedKVError) as e:
+        binding.paged_attention(st.q[:0], st.k_cache, st.v_cache, st.tables[:0],
+                                st.lens[:0], w.scale)
+    assert e.value.code == "EMPTY"
