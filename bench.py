@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of one batched paged-attention decode step on one MI355X.
+
+A step is the whole hot path over one batch: the slot scatter of every row's new K/V
+(pad rows into the sink) followed by the paged attention read of every (row, head).
+The default workload is the full-width decode batch: 256 rows (16 of them padding),
+32 query heads = 32 KV heads, head_dim 128, block_size 16, bf16 K/V, table width 8192
+tokens, lengths long-tail lognormal (median 1024, sigma 1.2) with 8 rows at 8192, and
+a 131072-block pool (~34 GB of K+V).  Every input is resident in HBM before timing.
+
+Prints one JSON line on stdout.  ``value`` is KV GB/s: the bytes of K and V the read
+must stream (every live (row, KV head, position) once) divided by the wall-clock time
+per step.  ``roofline`` reports the decode kernel alone, timed with HIP events on its
+launch stream over the same timed steps, against MI355X's 8 TB/s HBM peak.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode paged-attn KV GB/s and % HBM peak; (row,head)/s at 256 rows × 8192"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_attention_decode_kv_amd", "csrc", "kernels.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5)")
+    ap.add_argument("--layout", default="HND", choices=["HND", "NHD"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--chunk-tokens", type=int, default=0,
+                    help="decode work-item length in tokens (0: library default)")
+    ap.add_argument("--decode-waves", type=int, default=0,
+                    help="waves per decode work item (0: library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_per_launch(config_name, layout):
+    """HBM bytes per decode launch from committed counter runs, if they were taken on
+    the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if rec.get("workload") != config_name or rec.get("layout") != layout:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def _host(t, dtype):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def cpu_baseline(w, k_cache, v_cache, budget_s):
+    """The oracle (kv_write + masked-rectangle read) on rows of the batch, four rows per
+    oracle call, in a seeded order, until the wall-clock budget is spent.  Host copies
+    of the rows' blocks are made before each call and are not timed."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_attention_decode_kv_amd import workloads as wl
+
+    order = np.random.default_rng(1234).permutation(w.rows)
+    spent, kv_bytes, rows_done, row_heads, tokens = 0.0, 0, 0, 0, 0
+    for at in range(0, w.rows, 4):
+        part = order[at:at + 4]
+        blocks = wl.live_blocks(w, part)
+        remap = {int(b): i for i, b in enumerate(blocks)}
+        n = len(blocks)
+        idx = torch.from_numpy(np.append(blocks, w.num_blocks).astype(np.int64)).to(k_cache.device)
+        kh = _host(k_cache.index_select(0, idx), w.dtype)
+        vh = _host(v_cache.index_select(0, idx), w.dtype)
+        bt = np.full((len(part), w.max_blocks), -1, dtype=np.int32)
+        sm = np.empty(len(part), dtype=np.int64)
+        for i, r in enumerate(part):
+            live = wl.cdiv(w.context_lens[r], w.block_size)
+            bt[i, :live] = [remap[int(b)] for b in w.block_tables[r, :live]]
+            s = int(w.slot_mapping[r])
+            sm[i] = (n * w.block_size if w.context_lens[r] == 0 else
+                     remap[s // w.block_size] * w.block_size + s % w.block_size)
+        t0 = time.perf_counter()
+        oracle.kv_write(kh, vh, w.k_new[part], w.v_new[part], sm, num_blocks=n,
+                        block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+        oracle.paged_attention(w.q[part], kh, vh, bt, w.context_lens[part], w.scale,
+                               num_blocks=n, block_size=w.block_size, layout=w.layout,
+                               dtype=w.dtype)
+        spent += time.perf_counter() - t0
+        lens = w.context_lens[part]
+        kv_bytes += int(lens.sum()) * w.kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
+        tokens += int(lens.sum())
+        rows_done += len(part)
+        row_heads += int(np.count_nonzero(lens)) * w.heads
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(kv_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{rows_done} of {w.rows} rows of the same batch ({tokens} tokens, "
+                   f"{row_heads} live (row, head) pairs), 4 rows per oracle call, float64 "
+                   f"numpy; {spent:.1f} s; {row_heads / spent:.1f} (row, head)/s"),
+        "seconds": round(spent, 3),
+        "row_heads_per_s": round(row_heads / spent, 3),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode step is built and timed on a "
+              "single MI355X (see DESIGN.md for how it would shard); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_attention_decode_kv_amd import accounting as acc
+    from paged_attention_decode_kv_amd import binding
+    from paged_attention_decode_kv_amd import workloads as wl
+    from paged_attention_decode_kv_amd import _capi
+
+    if not os.path.exists(_capi.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    binding.set_tuning(args.chunk_tokens, args.decode_waves)
+    chunk_tokens, decode_waves = binding.get_tuning()
+    w = wl.make_config(args.config, layout=args.layout)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    log(f"workload {w.name}: rows={w.rows} heads={w.heads} d={w.head_dim} bs={w.block_size} "
+        f"{w.dtype} {w.layout}; pool {w.pool_bytes / 1e9:.2f} GB; "
+        f"tokens {int(w.context_lens.sum())}")
+
+    def dev_array(a, dtype=None):
+        a = np.ascontiguousarray(a)
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    k_cache = torch.empty(w.pool_shape, dtype=tdt, device=dev)
+    v_cache = torch.empty_like(k_cache)
+    wl.history_device(w, k_cache, v_cache)
+    q = dev_array(w.q, w.dtype)
+    k_new = dev_array(w.k_new, w.dtype)
+    v_new = dev_array(w.v_new, w.dtype)
+    slots = dev_array(w.slot_mapping)
+    tables = dev_array(w.block_tables)
+    lens = dev_array(w.context_lens)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(1, binding.workspace_bytes(k_cache, w.rows, w.heads, w.max_blocks,
+                                                    w.layout)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(validate=False):
+        binding.kv_write(k_new, v_new, slots, k_cache, v_cache, layout=w.layout,
+                         validate=validate)
+        binding.paged_attention(q, k_cache, v_cache, tables, lens, w.scale, layout=w.layout,
+                                out=out, workspace=ws, validate=validate)
+
+    # one validated step: the library checks every length, block id and slot on the host
+    step(validate=True)
+    binding.device_status(dev, clear=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    binding.timing_enable(True)
+    for ph in _capi.PHASES:
+        binding.timing_read(ph, reset=True)
+    torch.cuda.synchronize()            # barrier: one process, one GPU
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    phases = {ph: binding.timing_read(ph, reset=True) for ph in _capi.PHASES}
+    binding.timing_enable(False)
+    flags = binding.device_status(dev, clear=True)
+    if flags:
+        raise SystemExit(f"kernels clamped or skipped inputs (status bits {flags}); "
+                         "the measurement is invalid")
+
+    if args.copy_calibration:
+        # an elementwise kernel that reads 1 GiB and writes 1 GiB (torch's vectorized
+        # multiply): the known-size reference for the HBM byte counters
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        log("ran 3 elementwise multiplies over 1 GiB (1073741824 B read + written each)")
+        del a, b
+
+    step_s = (t1 - t0) / args.steps
+    elem = 2 if w.dtype == "bf16" else 4
+    b = acc.algorithmic_bytes(w.context_lens, heads=w.heads, kv_heads=w.kv_heads,
+                              head_dim=w.head_dim, block_size=w.block_size, elem=elem,
+                              write_tokens=w.rows)
+    rh = acc.row_heads(w.context_lens, w.heads)
+    avg = {ph: (ms / n if n else None) for ph, (ms, n) in phases.items()}
+    for ph, (ms, n) in phases.items():
+        if n:
+            log(f"  {ph:9s} {n:5d} launches, avg {ms / n * 1e3:9.2f} us")
+    dec_s = avg["decode"] * 1e-3
+    achieved = b["attention"] / dec_s / 1e9
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic_per_launch(w.name, w.layout),
+        "kernel": "decode_kernel",
+        "kernel_avg_us": round(dec_s * 1e6, 2),
+        "bytes_per_launch": b["attention"],
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(b["kv"] / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name} decode step: {w.rows} rows ({len(w.pad_rows)} padding) x "
+                         f"{w.heads} heads x head_dim {w.head_dim}, {w.dtype} KV, block "
+                         f"{w.block_size}, table width {w.max_blocks * w.block_size}, "
+                         f"{int(w.context_lens.sum())} live tokens; kv_write + "
+                         f"paged_attention"),
+            "rows": w.rows,
+            "heads": w.heads,
+            "kv_heads": w.kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "width": w.max_blocks * w.block_size,
+            "layout": w.layout,
+            "chunk_tokens": chunk_tokens,
+            "decode_waves": decode_waves,
+            "parallelism": "single GPU",
+        },
+        "hbm_frac": round(b["total"] / step_s / 1e9 / HBM_PEAK_GBPS, 4),
+        "total_algorithmic_GBps": round(b["total"] / step_s / 1e9, 2),
+        "row_heads_per_s": round(rh / step_s, 1),
+        "phase_avg_us": {ph: (round(v * 1e3, 2) if v is not None else None)
+                         for ph, v in avg.items()},
+        "algorithmic_bytes": b,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on a sample, budget {args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(w, k_cache, v_cache, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

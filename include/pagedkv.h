@@ -165,6 +165,32 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
  * bitwise OR of PKV_DEVERR_* raised since the last clear.  Synchronises `stream`. */
 pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
 
+/* Work split of the decode read (process-wide).  A row's history is cut into chunks of
+ * chunk_tokens positions (a power of two in [32, 1024]; default 256); each (chunk, query
+ * head) is one work item of the persistent decode kernel, and rows longer than one chunk
+ * are merged afterwards in chunk order.  decode_waves (1, 2, 4 or 8; default 4) is the
+ * number of 64-lane waves that share one work item.  0 leaves a value unchanged.
+ * Changing chunk_tokens changes pkv_workspace_bytes; set it before sizing workspaces.
+ * Results do not depend on either value beyond float32 rounding order.
+ * Returns UNSUPPORTED for other values. */
+pkv_status pkv_set_tuning(int32_t chunk_tokens, int32_t decode_waves);
+pkv_status pkv_get_tuning(int32_t* chunk_tokens, int32_t* decode_waves);
+
+/* Kernel timing, for benchmarks and profiling.  While enabled, every launch of the
+ * phases below is bracketed by a pair of HIP events recorded on the launch stream;
+ * pkv_timing_read synchronises on the recorded events and returns the summed elapsed
+ * milliseconds and the number of launches of one phase.  Disabled by default; costs
+ * two event records per launch when on.  Not thread-safe against concurrent calls. */
+typedef enum pkv_phase {
+  PKV_PHASE_KV_WRITE = 0,  /* the slot scatter kernel */
+  PKV_PHASE_PLAN = 1,      /* the work-list kernel of pkv_paged_attention */
+  PKV_PHASE_DECODE = 2,    /* the streaming online-softmax kernel */
+  PKV_PHASE_COMBINE = 3    /* the merge of split rows */
+} pkv_phase;
+
+pkv_status pkv_timing_enable(int32_t on);
+pkv_status pkv_timing_read(int32_t phase, double* total_ms, int64_t* launches, int32_t reset);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,10 @@ from .binding import (  # noqa: F401
     kv_write,
     paged_attention,
     pool_desc,
+    get_tuning,
+    set_tuning,
     sink_slot,
+    timing_enable,
+    timing_read,
     workspace_bytes,
 )

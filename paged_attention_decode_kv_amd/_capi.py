@@ -39,7 +39,13 @@ SIGNATURES = {
     "pkv_paged_attention": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32, _f, _p,
                                    _sz, _i32, _p]),
     "pkv_device_status": (_i32, [ctypes.POINTER(ctypes.c_uint32), _i32, _p]),
+    "pkv_set_tuning": (_i32, [_i32, _i32]),
+    "pkv_get_tuning": (_i32, [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
+    "pkv_timing_enable": (_i32, [_i32]),
+    "pkv_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double),
+                               ctypes.POINTER(ctypes.c_int64), _i32]),
 }
+PHASES = {"kv_write": 0, "plan": 1, "decode": 2, "combine": 3}
 
 _lib = None
 

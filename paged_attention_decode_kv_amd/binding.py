@@ -171,6 +171,31 @@ def device_status(device=None, clear: bool = True) -> int:
     return int(flags.value)
 
 
+def set_tuning(chunk_tokens: int = 0, decode_waves: int = 0) -> None:
+    """Set the decode work split (0 keeps a value); see pkv_set_tuning."""
+    _check(_capi.lib().pkv_set_tuning(int(chunk_tokens), int(decode_waves)))
+
+
+def get_tuning() -> tuple[int, int]:
+    c, w = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(_capi.lib().pkv_get_tuning(ctypes.byref(c), ctypes.byref(w)))
+    return int(c.value), int(w.value)
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start (or stop) bracketing every kernel launch with HIP events."""
+    _check(_capi.lib().pkv_timing_enable(int(bool(on))))
+
+
+def timing_read(phase: str, reset: bool = True) -> tuple[float, int]:
+    """(summed milliseconds, launches) of one phase: kv_write, plan, decode, combine."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(_capi.lib().pkv_timing_read(_capi.PHASES[phase], ctypes.byref(ms), ctypes.byref(n),
+                                       int(bool(reset))))
+    return float(ms.value), int(n.value)
+
+
 # ---------------------------------------------------------------------------- #
 # host-side checks (no GPU needed)
 # ---------------------------------------------------------------------------- #

@@ -251,8 +251,9 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
                                            max_blocks_per_row, pool->block_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  const int32_t chunk = pkv::tuning_chunk_tokens();
   const int64_t most_items = num_rows * ((int64_t)max_blocks_per_row * pool->block_size /
-                                         pkv::kChunkTokens + 1) * num_heads;
+                                         chunk + 1) * num_heads;
   if (most_items > (int64_t{1} << 30))
     return fail(PKV_ERR_UNSUPPORTED, "rows x heads x chunks too large for one call");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -281,6 +282,8 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
   a.num_heads = num_heads;
   a.max_blocks = max_blocks_per_row;
   a.ctx_limit = (int32_t)ctx_limit_of(pool, max_blocks_per_row);
+  a.chunk_tokens = chunk;
+  a.log2_chunk = log2i(chunk);
   a.scale = scale;
   const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads,
                                                  pool->head_dim, max_blocks_per_row,
@@ -294,6 +297,35 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
   if (!flags) return fail(PKV_ERR_NULL, "flags is NULL");
   hipError_t e = pkv::read_device_status(flags, clear, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "reading the device status word");
+  return ok();
+}
+
+pkv_status pkv_set_tuning(int32_t chunk_tokens, int32_t decode_waves) {
+  if (!pkv::set_tuning(chunk_tokens, decode_waves))
+    return fail(PKV_ERR_UNSUPPORTED, "chunk_tokens %d / decode_waves %d not supported",
+                chunk_tokens, decode_waves);
+  return ok();
+}
+
+pkv_status pkv_get_tuning(int32_t* chunk_tokens, int32_t* decode_waves) {
+  if (!chunk_tokens || !decode_waves) return fail(PKV_ERR_NULL, "output pointer is NULL");
+  *chunk_tokens = pkv::tuning_chunk_tokens();
+  *decode_waves = pkv::tuning_decode_waves();
+  return ok();
+}
+
+pkv_status pkv_timing_enable(int32_t on) {
+  pkv::timing_enable(on != 0);
+  return ok();
+}
+
+pkv_status pkv_timing_read(int32_t phase, double* total_ms, int64_t* launches,
+                           int32_t reset) {
+  if (!total_ms || !launches) return fail(PKV_ERR_NULL, "output pointer is NULL");
+  if (phase < PKV_PHASE_KV_WRITE || phase > PKV_PHASE_COMBINE)
+    return fail(PKV_ERR_SHAPE, "unknown phase %d", phase);
+  hipError_t e = pkv::timing_read(phase, total_ms, launches, reset != 0);
+  if (e != hipSuccess) return hip_fail(e, "reading kernel timing events");
   return ok();
 }
 

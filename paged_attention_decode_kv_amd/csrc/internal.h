@@ -8,10 +8,19 @@
 
 namespace pkv {
 
-// Tokens one decode work item covers for one (row, head).  A row of context_len
-// tokens is split into cdiv(context_len, kChunkTokens) chunks; rows with more than
-// one chunk are merged by the combine kernel.
-constexpr int kChunkTokens = 256;
+// Tokens one decode work item covers for one (row, head): a power of two in
+// [kMinChunkTokens, kMaxChunkTokens], kDefaultChunkTokens unless retuned with
+// pkv_set_tuning.  A row of context_len tokens is split into
+// cdiv(context_len, chunk_tokens) chunks; rows with more than one chunk are merged
+// by the combine kernel.
+constexpr int kMinChunkTokens = 32;
+constexpr int kMaxChunkTokens = 1024;
+constexpr int kDefaultChunkTokens = 256;
+constexpr int kDefaultDecodeWaves = 4;
+
+int tuning_chunk_tokens();
+int tuning_decode_waves();
+bool set_tuning(int chunk_tokens, int decode_waves);
 
 // Pool geometry in elements, derived from the descriptor.
 struct PoolGeom {
@@ -57,6 +66,8 @@ struct AttnArgs {
   int32_t num_heads;
   int32_t max_blocks;
   int32_t ctx_limit;    // min(max_blocks * block_size, num_blocks * block_size)
+  int32_t chunk_tokens; // tokens per work item
+  int32_t log2_chunk;
   float scale;
 };
 
@@ -68,5 +79,11 @@ Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads,
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream);
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream);
+
+// Event-pair timing of kernel phases (pkv_timing_*).  begin/end bracket one launch.
+void timing_begin(int phase, hipStream_t stream);
+void timing_end(int phase, hipStream_t stream);
+void timing_enable(bool on);
+hipError_t timing_read(int phase, double* total_ms, int64_t* launches, bool reset);
 
 }  // namespace pkv

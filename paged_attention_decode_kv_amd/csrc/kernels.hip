@@ -163,22 +163,34 @@ __global__ void __launch_bounds__(256) kv_write_kernel(WriteArgs a, int64_t sink
 // ------------------------------------------------------------------------- //
 constexpr int kPlanThreads = 1024;
 
-// exclusive prefix sum of one value per thread over the workgroup; returns the
-// thread's prefix and writes the total to *total
-__device__ int block_exclusive_scan(int x, int* s_tmp, int* total) {
-  const int t = threadIdx.x;
-  s_tmp[t] = x;
-  __syncthreads();
-  for (int d = 1; d < kPlanThreads; d <<= 1) {
-    const int y = t >= d ? s_tmp[t - d] : 0;
-    __syncthreads();
-    s_tmp[t] += y;
-    __syncthreads();
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  const int incl = s_tmp[t];
-  *total = s_tmp[kPlanThreads - 1];
+  return x;
+}
+
+// exclusive prefix sum of one value per thread over the workgroup (kPlanThreads
+// threads); returns the thread's prefix and writes the total to *total
+__device__ int block_exclusive_scan(int x, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kPlanThreads / 64;
+  const int incl = wave_inclusive_scan(x);
+  if (lane == 63) s_wave[wave] = incl;
   __syncthreads();
-  return incl - x;
+  if (wave == 0) {
+    const int t = lane < kWaves ? s_wave[lane] : 0;
+    const int ti = wave_inclusive_scan(t);
+    if (lane < kWaves) s_wave[lane] = ti;
+  }
+  __syncthreads();
+  const int prefix = (wave > 0 ? s_wave[wave - 1] : 0) + incl - x;
+  *total = s_wave[kWaves - 1];
+  __syncthreads();
+  return prefix;
 }
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int limit) {
@@ -190,16 +202,18 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int limit) {
 }
 
 // Entries are ordered longest first so that the queue's tail is short work:
-//   A. every full chunk (kChunkTokens tokens) of every row, rows in order;
+//   A. every full chunk (chunk_tokens tokens) of every row, rows in order;
 //   B. every row's trailing partial chunk, by length, longest first;
 //   C. one zero-output entry per padding row.
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspace ws) {
-  constexpr int P = kChunkTokens;
-  __shared__ int s_tmp[kPlanThreads];
-  __shared__ int s_bin_start[P];   // first B position of each remainder length
-  __shared__ int s_bin_fill[P];
+  constexpr int kMaxChunk = kMaxChunkTokens;
+  __shared__ int s_wave[kPlanThreads / 64];
+  __shared__ int s_bin_start[kMaxChunk];   // first B position of each remainder length
+  __shared__ int s_bin_fill[kMaxChunk];
   __shared__ int s_pad_fill;
   const int t = threadIdx.x;
+  const int P = a.chunk_tokens;
+  const int lp = a.log2_chunk;
   for (int q = t; q < P; q += kPlanThreads) s_bin_fill[q] = 0;
   if (t == 0) s_pad_fill = 0;
   __syncthreads();
@@ -210,36 +224,35 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
     const int64_t r = base + t;
     int ctx = 0;
     if (r < a.num_rows) ctx = clamp_ctx(a.context_lens[r], a.ctx_limit);
-    const int full = ctx / P;
-    const int nch = (ctx + P - 1) / P;
+    const int full = ctx >> lp;
+    const int nch = (ctx + P - 1) >> lp;
     int tile_a, tile_pad;
-    const int at = total_a + block_exclusive_scan(full, s_tmp, &tile_a);
-    block_exclusive_scan(r < a.num_rows && ctx == 0 ? 1 : 0, s_tmp, &tile_pad);
+    const int at = total_a + block_exclusive_scan(full, s_wave, &tile_a);
+    block_exclusive_scan(r < a.num_rows && ctx == 0 ? 1 : 0, s_wave, &tile_pad);
     for (int k = 0; k < full; ++k) ws.entries[at + k] = make_int4((int)r, k, nch, ctx);
-    if (r < a.num_rows && (ctx % P) != 0) atomicAdd(&s_bin_fill[ctx % P], 1);
+    if (r < a.num_rows && (ctx & (P - 1)) != 0) atomicAdd(&s_bin_fill[ctx & (P - 1)], 1);
     total_a += tile_a;
     n_pad += tile_pad;
   }
   __syncthreads();
-  // bins of section B in descending remainder order
+  // bins of section B in descending remainder order (P <= kPlanThreads)
   int total_b = 0;
   {
-    // P <= kPlanThreads: thread q owns remainder P-1-q
-    const int q = t;
-    const int cnt = q < P ? s_bin_fill[P - 1 - q] : 0;
-    const int start = block_exclusive_scan(cnt, s_tmp, &total_b);
-    if (q < P) s_bin_start[P - 1 - q] = start;
+    const int cnt = t < P ? s_bin_fill[P - 1 - t] : 0;
+    const int start = block_exclusive_scan(cnt, s_wave, &total_b);
+    if (t < P) s_bin_start[P - 1 - t] = start;
   }
   for (int q = t; q < P; q += kPlanThreads) s_bin_fill[q] = 0;
   __syncthreads();
   // pass 2: place sections B and C
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
-    const int ctx = clamp_ctx(a.context_lens[r], a.ctx_limit);
-    const int rem = ctx % P;
-    const int nch = (ctx + P - 1) / P;
+    int ctx = a.context_lens[r];
+    ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
+    const int rem = ctx & (P - 1);
+    const int nch = (ctx + P - 1) >> lp;
     if (rem != 0) {
       const int pos = total_a + s_bin_start[rem] + atomicAdd(&s_bin_fill[rem], 1);
-      ws.entries[pos] = make_int4((int)r, ctx / P, nch, ctx);
+      ws.entries[pos] = make_int4((int)r, ctx >> lp, nch, ctx);
     } else if (ctx == 0) {
       const int pos = total_a + total_b + atomicAdd(&s_pad_fill, 1);
       ws.entries[pos] = make_int4((int)r, -1, 0, 0);
@@ -254,6 +267,15 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
 // ------------------------------------------------------------------------- //
 // decode
 // ------------------------------------------------------------------------- //
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// K/V are read once per step: non-temporal loads keep them from displacing
+// anything in the caches and measurably raise the achieved HBM read rate.
+__device__ __forceinline__ uint4 load16_stream(const char* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T, int D>
 struct Shape {
   static constexpr int E = Elem<T>::kPerLane;       // elements per lane load
@@ -262,7 +284,7 @@ struct Shape {
   static constexpr int U = (16 / TPS) < 8 ? (16 / TPS) : 8;   // loads per sub-chunk
   static constexpr int CH = TPS * U;                // tokens per sub-chunk
   static_assert(LPT >= 8 && LPT <= 64, "unsupported head_dim/dtype");
-  static_assert(kChunkTokens % CH == 0, "chunk must hold whole sub-chunks");
+  static_assert(kMinChunkTokens % CH == 0, "a chunk must hold whole sub-chunks");
 };
 
 template <typename T, int D, int WAVES>
@@ -271,8 +293,9 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using S = Shape<T, D>;
   using El = Elem<T>;
   constexpr int E = S::E, LPT = S::LPT, TPS = S::TPS, U = S::U, CH = S::CH;
+  constexpr int ES = sizeof(T);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane / LPT;       // which token of a wave load this lane holds
   const int sub = lane % LPT;     // which 16-byte piece of the token's head vector
 
@@ -283,18 +306,28 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int heads = a.num_heads;
   const int group = heads / a.g.kv_heads;
   const int n_items = ws.counters[0] * heads;
+  const int P = a.chunk_tokens;
+  const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
+  const int64_t tok_bytes = a.g.tok_stride * ES;
+  const int64_t blk_bytes = a.g.blk_stride * ES;
+  // byte offset of this lane's 16 bytes inside one wave load, and of one wave load
+  const uint32_t lane_off = (uint32_t)(g * tok_bytes + sub * E * ES);
+  const int64_t step_bytes = TPS * tok_bytes;
 
   for (;;) {
     if (threadIdx.x == 0) s_ticket = atomicAdd(&ws.counters[1], 1);
     __syncthreads();
-    const int item = s_ticket;
+    const int item = __builtin_amdgcn_readfirstlane(s_ticket);
     __syncthreads();
     if (item >= n_items) break;
     const int e = item / heads;
     const int h = item - e * heads;
     const int4 ent = ws.entries[e];
-    const int r = ent.x, chunk = ent.y, nch = ent.z, ctx = ent.w;
+    const int r = __builtin_amdgcn_readfirstlane(ent.x);
+    const int chunk = __builtin_amdgcn_readfirstlane(ent.y);
+    const int nch = __builtin_amdgcn_readfirstlane(ent.z);
+    const int ctx = __builtin_amdgcn_readfirstlane(ent.w);
     const int64_t rh = (int64_t)r * heads + h;
     T* outp = static_cast<T*>(a.out) + rh * D + sub * E;
 
@@ -302,13 +335,17 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       if (wave == 0 && g == 0) store16(outp, make_uint4(0, 0, 0, 0));
       continue;
     }
-    const int t_begin = chunk * kChunkTokens;
-    const int t_end = min(ctx, t_begin + kChunkTokens);
+    const int t_begin = chunk * P;
+    const int t_end = min(ctx, t_begin + P);
     const int hkv = h / group;
     const uint4 qv = load16(static_cast<const T*>(a.q) + rh * D + sub * E);
-    const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks;
-    const T* kb = static_cast<const T*>(a.k_cache) + hkv * a.g.head_stride + sub * E;
-    const T* vb = static_cast<const T*>(a.v_cache) + hkv * a.g.head_stride + sub * E;
+    // the chunk's block ids, one per lane (a chunk spans at most 64 blocks)
+    const int j0 = t_begin >> log2_bs;
+    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
+    const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks + j0;
+    const int my_blk = lane < nblk ? bt[lane] : 0;
+    const char* kh = static_cast<const char*>(a.k_cache) + hkv * a.g.head_stride * ES;
+    const char* vh = static_cast<const char*>(a.v_cache) + hkv * a.g.head_stride * ES;
 
     float m = -INFINITY, l = 0.f;
     float acc[E];
@@ -318,23 +355,33 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
     for (int s = wave; s < n_sub; s += WAVES) {
       const int t0 = t_begin + s * CH;
-      int blk = bt[t0 >> a.g.log2_bs];
+      int blk = __builtin_amdgcn_readlane(my_blk, (t0 >> log2_bs) - j0);
       const bool blk_ok = blk >= 0 && blk < a.g.num_blocks;
       if (!blk_ok) {
         if (lane == 0) atomicOr(&g_status, PKV_DEVERR_BLOCK_ID);
         blk = 0;
       }
-      const int64_t boff = (int64_t)blk * a.g.blk_stride +
-                           (int64_t)((t0 & bs_mask) + g) * a.g.tok_stride;
+      const int64_t off = (int64_t)blk * blk_bytes + (int64_t)(t0 & bs_mask) * tok_bytes;
+      const char* kp = kh + off;
+      const char* vp = vh + off;
+      // tokens of this sub-chunk that exist; masked tokens are never loaded
+      const int nvalid = blk_ok ? min(CH, t_end - t0) : 0;
       uint4 kr[U], vr[U];
+      if (nvalid == CH) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-        if (blk_ok && t0 + u * TPS + g < t_end) {   // masked tokens are never loaded
-          const int64_t off = boff + (int64_t)(u * TPS) * a.g.tok_stride;
-          kr[u] = load16(kb + off);
-          vr[u] = load16(vb + off);
+        for (int u = 0; u < U; ++u) {
+          kr[u] = load16_stream(kp + u * step_bytes + lane_off);
+          vr[u] = load16_stream(vp + u * step_bytes + lane_off);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          kr[u] = make_uint4(0, 0, 0, 0);
+          vr[u] = make_uint4(0, 0, 0, 0);
+          if (u * TPS + g < nvalid) {
+            kr[u] = load16_stream(kp + u * step_bytes + lane_off);
+            vr[u] = load16_stream(vp + u * step_bytes + lane_off);
+          }
         }
       }
       float sc[U];
@@ -342,7 +389,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float d = group_sum<LPT>(El::dot(qv, kr[u], 0.f));
-        sc[u] = (blk_ok && t0 + u * TPS + g < t_end) ? d * scale_log2 : -INFINITY;
+        sc[u] = u * TPS + g < nvalid ? d * scale_log2 : -INFINITY;
         smax = fmaxf(smax, sc[u]);
       }
       const float m_new = fmaxf(m, smax);
@@ -426,40 +473,89 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 // ------------------------------------------------------------------------- //
 // combine
 // ------------------------------------------------------------------------- //
+constexpr int kCombineThreads = 256;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = fmaxf(x, __shfl_xor(x, d));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
+// One workgroup per (head, row) of a row split into several chunks.  Chunk c of the
+// row carries (m_c, l_c, acc_c); the result is sum_c 2^(m_c - M) acc_c divided by
+// sum_c 2^(m_c - M) l_c with M = max_c m_c.  Each wave sums a fixed subset of the
+// chunks (c = wave mod 4) and the four partial sums are added in wave order, so the
+// result does not depend on scheduling.
 template <typename T, int D>
-__global__ void __launch_bounds__(64) combine_kernel(AttnArgs a, Workspace ws) {
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Workspace ws) {
   constexpr int PER = D / 64;     // dims per lane
+  constexpr int W = kCombineThreads / 64;
+  __shared__ float s_red[W];
+  __shared__ float s_acc[W][D];
   const int h = blockIdx.x;
   const int64_t r = blockIdx.y;
   int ctx = a.context_lens[r];
   ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
-  const int nch = (ctx + kChunkTokens - 1) / kChunkTokens;
+  const int nch = (ctx + a.chunk_tokens - 1) >> a.log2_chunk;
   if (nch <= 1) return;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t rh = r * a.num_heads + h;
   const float* rec = ws.partials + rh * ws.max_chunks * (D + 4);
+
   float mx = -INFINITY;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, rec[c * (D + 4)]);
+  for (int c = threadIdx.x; c < nch; c += kCombineThreads) mx = fmaxf(mx, rec[c * (D + 4)]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  mx = s_red[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) mx = fmaxf(mx, s_red[w]);
+  __syncthreads();
+
   float l = 0.f, acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int c = 0; c < nch; ++c) {
+  for (int c = threadIdx.x; c < nch; c += kCombineThreads)
+    l += rec[c * (D + 4) + 1] * __builtin_amdgcn_exp2f(rec[c * (D + 4)] - mx);
+  for (int c = wave; c < nch; c += W) {
     const float* p = rec + c * (D + 4);
     const float f = __builtin_amdgcn_exp2f(p[0] - mx);
-    l += p[1] * f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] += p[4 + lane * PER + i] * f;
   }
-  const float inv = 1.0f / l;
+  l = wave_sum(l);
+  if (lane == 0) s_red[wave] = l;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s_acc[wave][lane * PER + i] = acc[i];
+  __syncthreads();
+  if (wave != 0) return;
+  float lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) lt += s_red[w];
+  const float inv = 1.0f / lt;
   T* outp = static_cast<T*>(a.out) + rh * D + lane * PER;
+  float y[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const float y = acc[i] * inv;
-    if constexpr (sizeof(T) == 4) {
-      outp[i] = y;
-    } else {
-      outp[i] = (uint16_t)(Elem<uint16_t>::cvt2(y, 0.f) & 0xffffu);
-    }
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) s += s_acc[w][lane * PER + i];
+    y[i] = s * inv;
+  }
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) outp[i] = y[i];
+  } else if constexpr (PER == 1) {
+    outp[0] = (uint16_t)(Elem<uint16_t>::cvt2(y[0], 0.f) & 0xffffu);
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; i += 2)
+      *reinterpret_cast<uint32_t*>(outp + i) = Elem<uint16_t>::cvt2(y[i], y[i + 1]);
   }
 }
 
@@ -468,14 +564,14 @@ __global__ void __launch_bounds__(64) combine_kernel(AttnArgs a, Workspace ws) {
 // ------------------------------------------------------------------------- //
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-static int max_chunks_for(int32_t max_blocks, int32_t block_size) {
+static int max_chunks_for(int32_t max_blocks, int32_t block_size, int32_t chunk) {
   const int64_t width = (int64_t)max_blocks * block_size;
-  return (int)((width + kChunkTokens - 1) / kChunkTokens);
+  return (int)((width + chunk - 1) / chunk);
 }
 
 size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
                        int32_t max_blocks, int32_t block_size) {
-  const int64_t mc = max_chunks_for(max_blocks, block_size);
+  const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_tokens());
   const int64_t entries = num_rows * (mc > 1 ? mc : 1);
   int64_t bytes = align_up(entries * (int64_t)sizeof(int4), 256);
   bytes += 256;   // counters
@@ -486,7 +582,7 @@ size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
 Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads, int32_t head_dim,
                           int32_t max_blocks, int32_t block_size) {
   Workspace w;
-  const int64_t mc = max_chunks_for(max_blocks, block_size);
+  const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_tokens());
   w.max_chunks = (int32_t)mc;
   w.max_entries = num_rows * (mc > 1 ? mc : 1);
   char* p = static_cast<char*>(base);
@@ -506,21 +602,20 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
   const int threads = 256;
   const int64_t blocks = (pieces + threads - 1) / threads;
   const int64_t sink = a.g.num_blocks * a.g.block_size;
+  timing_begin(PKV_PHASE_KV_WRITE, stream);
   if (a.g.dtype == PKV_F32)
     hipLaunchKernelGGL(kv_write_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0,
                        stream, a, sink);
   else
     hipLaunchKernelGGL(kv_write_kernel<uint16_t>, dim3((unsigned)blocks), dim3(threads), 0,
                        stream, a, sink);
+  timing_end(PKV_PHASE_KV_WRITE, stream);
   return hipGetLastError();
 }
 
-constexpr int kDecodeWaves = 4;
-
-template <typename T, int D>
-static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws,
-                                  hipStream_t stream) {
-  auto kern = decode_kernel<T, D, kDecodeWaves>;
+template <typename T, int D, int WAVES>
+static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
+  auto kern = decode_kernel<T, D, WAVES>;
   static int per_cu[64] = {0};   // occupancy per device, computed once
   static int num_cu[64] = {0};
   int dev = 0;
@@ -529,7 +624,7 @@ static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws,
   if (dev >= 64) return hipErrorInvalidDevice;
   if (per_cu[dev] == 0) {
     int n = 0;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kDecodeWaves * 64, 0);
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WAVES * 64, 0);
     if (err != hipSuccess) return err;
     int cus = 0;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -538,16 +633,34 @@ static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws,
     per_cu[dev] = n > 0 ? n : 1;
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
+  timing_begin(PKV_PHASE_PLAN, stream);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, ws);
+  timing_end(PKV_PHASE_PLAN, stream);
   int64_t grid = (int64_t)num_cu[dev] * per_cu[dev];
   const int64_t most = ws.max_entries * a.num_heads;
   if (grid > most) grid = most;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDecodeWaves * 64), 0, stream, a, ws,
+  timing_begin(PKV_PHASE_DECODE, stream);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a, ws,
                      scale_log2);
-  if (ws.max_chunks > 1)
+  timing_end(PKV_PHASE_DECODE, stream);
+  if (ws.max_chunks > 1) {
+    timing_begin(PKV_PHASE_COMBINE, stream);
     hipLaunchKernelGGL((combine_kernel<T, D>), dim3(a.num_heads, (unsigned)a.num_rows),
-                       dim3(64), 0, stream, a, ws);
+                       dim3(kCombineThreads), 0, stream, a, ws);
+    timing_end(PKV_PHASE_COMBINE, stream);
+  }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws,
+                                  hipStream_t stream) {
+  switch (tuning_decode_waves()) {
+    case 1: return launch_decode_w<T, D, 1>(a, ws, stream);
+    case 2: return launch_decode_w<T, D, 2>(a, ws, stream);
+    case 8: return launch_decode_w<T, D, 8>(a, ws, stream);
+    default: return launch_decode_w<T, D, 4>(a, ws, stream);
+  }
 }
 
 hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws,

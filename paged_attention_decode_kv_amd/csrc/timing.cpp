@@ -1,0 +1,112 @@
+// Event-pair timing of the library's kernel phases (pkv_timing_enable / _read).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kPhases = 4;
+
+struct PhaseLog {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;  // recorded, not yet read
+  std::vector<hipEvent_t> spare;                           // reusable events
+  hipEvent_t open = nullptr;                               // start of the current launch
+  double total_ms = 0.0;
+  int64_t launches = 0;
+};
+
+std::mutex g_mu;
+bool g_on = false;
+PhaseLog g_log[kPhases];
+
+hipEvent_t take(PhaseLog& p) {
+  if (!p.spare.empty()) {
+    hipEvent_t e = p.spare.back();
+    p.spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+void timing_enable(bool on) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_on = on;
+}
+
+void timing_begin(int phase, hipStream_t stream) {
+  if (!g_on) return;
+  std::lock_guard<std::mutex> lock(g_mu);
+  PhaseLog& p = g_log[phase];
+  p.open = take(p);
+  if (p.open && hipEventRecord(p.open, stream) != hipSuccess) p.open = nullptr;
+}
+
+void timing_end(int phase, hipStream_t stream) {
+  if (!g_on) return;
+  std::lock_guard<std::mutex> lock(g_mu);
+  PhaseLog& p = g_log[phase];
+  if (!p.open) return;
+  hipEvent_t stop = take(p);
+  if (!stop) return;
+  if (hipEventRecord(stop, stream) != hipSuccess) { p.spare.push_back(p.open); p.spare.push_back(stop); p.open = nullptr; return; }
+  p.pending.emplace_back(p.open, stop);
+  p.open = nullptr;
+}
+
+hipError_t timing_read(int phase, double* total_ms, int64_t* launches, bool reset) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  PhaseLog& p = g_log[phase];
+  for (auto& pr : p.pending) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e != hipSuccess) return e;
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return e;
+    p.total_ms += ms;
+    p.launches += 1;
+    p.spare.push_back(pr.first);
+    p.spare.push_back(pr.second);
+  }
+  p.pending.clear();
+  *total_ms = p.total_ms;
+  *launches = p.launches;
+  if (reset) {
+    p.total_ms = 0.0;
+    p.launches = 0;
+  }
+  return hipSuccess;
+}
+
+namespace {
+std::atomic<int> g_chunk_tokens{kDefaultChunkTokens};
+std::atomic<int> g_decode_waves{kDefaultDecodeWaves};
+}  // namespace
+
+int tuning_chunk_tokens() { return g_chunk_tokens.load(std::memory_order_relaxed); }
+int tuning_decode_waves() { return g_decode_waves.load(std::memory_order_relaxed); }
+
+bool set_tuning(int chunk_tokens, int decode_waves) {
+  if (chunk_tokens != 0) {
+    if (chunk_tokens < kMinChunkTokens || chunk_tokens > kMaxChunkTokens ||
+        (chunk_tokens & (chunk_tokens - 1)) != 0)
+      return false;
+  }
+  if (decode_waves != 0 && decode_waves != 1 && decode_waves != 2 && decode_waves != 4 &&
+      decode_waves != 8)
+    return false;
+  if (chunk_tokens != 0) g_chunk_tokens.store(chunk_tokens);
+  if (decode_waves != 0) g_decode_waves.store(decode_waves);
+  return true;
+}
+
+}  // namespace pkv
