@@ -46,10 +46,16 @@ def parse():
     ap.add_argument("--layout", default="HND", choices=["HND", "NHD"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample")
-    ap.add_argument("--chunk-tokens", type=int, default=0,
-                    help="decode work-item length in tokens (0: library default)")
+    ap.add_argument("--chunk-min", type=int, default=0,
+                    help="shortest decode work-item length in tokens (0: library default)")
+    ap.add_argument("--chunk-max", type=int, default=0,
+                    help="longest decode work-item length in tokens (0: library default)")
     ap.add_argument("--decode-waves", type=int, default=0,
                     help="waves per decode work item (0: library default)")
+    ap.add_argument("--items-per-group", type=int, default=0,
+                    help="work items per decode workgroup the plan aims for (0: default)")
+    ap.add_argument("--deal", type=int, default=0,
+                    help="1: deal full-chunk rounds statically, 2: queue every item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
@@ -93,10 +99,12 @@ def _host(t, dtype):
     return t.cpu().numpy()
 
 
-def cpu_baseline(w, k_cache, v_cache, budget_s):
+def cpu_baseline(w, k_cache, v_cache, budget_s, min_rows=0):
     """The oracle (kv_write + masked-rectangle read) on rows of the batch, four rows per
-    oracle call, in a seeded order, until the wall-clock budget is spent.  Host copies
-    of the rows' blocks are made before each call and are not timed."""
+    oracle call, in a seeded order, until the wall-clock budget is spent (and at least
+    ``min_rows`` rows are done).  Runs on the pool before any GPU step touches it; host
+    copies of the rows' blocks are made before each call and are not timed.  Returns
+    the timing record and the oracle outputs of the rows it covered."""
     import numpy as np
     import torch
 
@@ -104,7 +112,9 @@ def cpu_baseline(w, k_cache, v_cache, budget_s):
     from paged_attention_decode_kv_amd import workloads as wl
 
     order = np.random.default_rng(1234).permutation(w.rows)
-    spent, kv_bytes, rows_done, row_heads, tokens = 0.0, 0, 0, 0, 0
+    spent, kv_bytes, row_heads, tokens = 0.0, 0, 0, 0
+    rows_done, outputs = [], []
+    elem = 2 if w.dtype == "bf16" else 4
     for at in range(0, w.rows, 4):
         part = order[at:at + 4]
         blocks = wl.live_blocks(w, part)
@@ -124,28 +134,45 @@ def cpu_baseline(w, k_cache, v_cache, budget_s):
         t0 = time.perf_counter()
         oracle.kv_write(kh, vh, w.k_new[part], w.v_new[part], sm, num_blocks=n,
                         block_size=w.block_size, layout=w.layout, dtype=w.dtype)
-        oracle.paged_attention(w.q[part], kh, vh, bt, w.context_lens[part], w.scale,
-                               num_blocks=n, block_size=w.block_size, layout=w.layout,
-                               dtype=w.dtype)
+        out = oracle.paged_attention(w.q[part], kh, vh, bt, w.context_lens[part], w.scale,
+                                     num_blocks=n, block_size=w.block_size, layout=w.layout,
+                                     dtype=w.dtype)
         spent += time.perf_counter() - t0
+        outputs.append(out)
         lens = w.context_lens[part]
-        kv_bytes += int(lens.sum()) * w.kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
+        kv_bytes += int(lens.sum()) * w.kv_heads * w.head_dim * 2 * elem
         tokens += int(lens.sum())
-        rows_done += len(part)
+        rows_done.extend(int(r) for r in part)
         row_heads += int(np.count_nonzero(lens)) * w.heads
-        if spent >= budget_s:
+        if spent >= budget_s and len(rows_done) >= min_rows:
             break
-    return {
+    rec = {
         "value": round(kv_bytes / spent / 1e9, 4),
         "unit": "GB/s",
         "cores": blas_threads(),
         "kind": "oracle",
-        "sample": (f"{rows_done} of {w.rows} rows of the same batch ({tokens} tokens, "
+        "sample": (f"{len(rows_done)} of {w.rows} rows of the same batch ({tokens} tokens, "
                    f"{row_heads} live (row, head) pairs), 4 rows per oracle call, float64 "
                    f"numpy; {spent:.1f} s; {row_heads / spent:.1f} (row, head)/s"),
         "seconds": round(spent, 3),
         "row_heads_per_s": round(row_heads / spent, 3),
     }
+    return rec, np.array(rows_done), np.concatenate(outputs)
+
+
+def check_outputs(out, rows, ref, dtype):
+    """GPU outputs of the sampled rows against the oracle's (same tolerances as the
+    parity tests: 2e-6 for float32, 2e-2 and 2^-8 relative + 2e-5 for bfloat16)."""
+    import numpy as np
+    import torch
+
+    got = out[torch.from_numpy(rows).to(out.device)].float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        ok = bool(err.max() <= 2e-6)
+    else:
+        ok = bool(err.max() <= 2e-2 and np.all(err <= 2.0 ** -8 * np.abs(ref) + 2e-5))
+    return {"rows": int(len(rows)), "max_abs_err": float(err.max()), "ok": ok}
 
 
 def main():
@@ -170,8 +197,9 @@ def main():
         __graft_entry__.build()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    binding.set_tuning(args.chunk_tokens, args.decode_waves)
-    chunk_tokens, decode_waves = binding.get_tuning()
+    binding.set_tuning(args.chunk_min, args.chunk_max, args.decode_waves,
+                       args.items_per_group, args.deal)
+    tuning = binding.get_tuning()
     w = wl.make_config(args.config, layout=args.layout)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
     log(f"workload {w.name}: rows={w.rows} heads={w.heads} d={w.head_dim} bs={w.block_size} "
@@ -197,6 +225,12 @@ def main():
     ws = torch.empty(max(1, binding.workspace_bytes(k_cache, w.rows, w.heads, w.max_blocks,
                                                     w.layout)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+
+    # the CPU oracle runs first, on the untouched pool: its timing is the baseline and
+    # its outputs check the GPU step's outputs afterwards
+    budget = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    log(f"cpu oracle on a sample of rows (budget {budget:.0f} s)")
+    base_rec, check_rows, check_ref = cpu_baseline(w, k_cache, v_cache, budget, min_rows=4)
 
     def step(validate=False):
         binding.kv_write(k_new, v_new, slots, k_cache, v_cache, layout=w.layout,
@@ -287,8 +321,7 @@ def main():
             "block_size": w.block_size,
             "width": w.max_blocks * w.block_size,
             "layout": w.layout,
-            "chunk_tokens": chunk_tokens,
-            "decode_waves": decode_waves,
+            "tuning": tuning,
             "parallelism": "single GPU",
         },
         "hbm_frac": round(b["total"] / step_s / 1e9 / HBM_PEAK_GBPS, 4),
@@ -299,12 +332,11 @@ def main():
         "algorithmic_bytes": b,
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on a sample, budget {args.cpu_seconds:.0f} s")
-        result["cpu_baseline"] = cpu_baseline(w, k_cache, v_cache, args.cpu_seconds)
-    else:
-        result["cpu_baseline"] = None
+    result["cpu_baseline"] = None if args.no_cpu_baseline else base_rec
+    result["check"] = check_outputs(out, check_rows, check_ref, w.dtype)
     print(json.dumps(result), flush=True)
+    if not result["check"]["ok"]:
+        raise SystemExit(f"GPU outputs disagree with the oracle: {result['check']}")
 
 
 if __name__ == "__main__":

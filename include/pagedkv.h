@@ -165,16 +165,32 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
  * bitwise OR of PKV_DEVERR_* raised since the last clear.  Synchronises `stream`. */
 pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
 
-/* Work split of the decode read (process-wide).  A row's history is cut into chunks of
- * chunk_tokens positions (a power of two in [32, 1024]; default 256); each (chunk, query
- * head) is one work item of the persistent decode kernel, and rows longer than one chunk
- * are merged afterwards in chunk order.  decode_waves (1, 2, 4 or 8; default 4) is the
- * number of 64-lane waves that share one work item.  0 leaves a value unchanged.
- * Changing chunk_tokens changes pkv_workspace_bytes; set it before sizing workspaces.
- * Results do not depend on either value beyond float32 rounding order.
- * Returns UNSUPPORTED for other values. */
-pkv_status pkv_set_tuning(int32_t chunk_tokens, int32_t decode_waves);
-pkv_status pkv_get_tuning(int32_t* chunk_tokens, int32_t* decode_waves);
+/* Work split of the decode read (process-wide).  Each call cuts every row's history
+ * into chunks; one (chunk, query head) is a work item of the persistent decode kernel,
+ * shared by the waves of one workgroup, and rows longer than one chunk are merged
+ * afterwards in chunk order.  The chunk length is chosen on the device per call: the
+ * largest power of two in [chunk_min, chunk_max] that still yields items_per_group
+ * items per decode workgroup (else chunk_min).  Setting chunk_min == chunk_max pins it.
+ *   chunk_min, chunk_max  powers of two in [32, 2048], chunk_max/chunk_min <= 32
+ *                         (defaults 128, 2048)
+ *   decode_waves          64-lane waves per workgroup: 1, 2, 4 or 8 (default 8)
+ *   items_per_group       default 16
+ *   deal                  1: whole rounds of full-length chunks are dealt to workgroups
+ *                         round robin and only the rest goes through the shared work
+ *                         queue; 2: every item goes through the queue (default 1)
+ * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it
+ * before sizing workspaces.  Results do not depend on these values beyond float32
+ * rounding order.  Returns UNSUPPORTED for other values. */
+typedef struct pkv_tuning {
+  int32_t chunk_min;
+  int32_t chunk_max;
+  int32_t decode_waves;
+  int32_t items_per_group;
+  int32_t deal;
+} pkv_tuning;
+
+pkv_status pkv_set_tuning(const pkv_tuning* tuning);
+pkv_status pkv_get_tuning(pkv_tuning* tuning);
 
 /* Kernel timing, for benchmarks and profiling.  While enabled, every launch of the
  * phases below is bracketed by a pair of HIP events recorded on the launch stream;

@@ -24,6 +24,12 @@ class PoolDesc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
+class Tuning(ctypes.Structure):
+    _fields_ = [("chunk_min", ctypes.c_int32), ("chunk_max", ctypes.c_int32),
+                ("decode_waves", ctypes.c_int32), ("items_per_group", ctypes.c_int32),
+                ("deal", ctypes.c_int32)]
+
+
 _PD = ctypes.POINTER(PoolDesc)
 SIGNATURES = {
     "pkv_abi_version": (_i32, []),
@@ -39,8 +45,8 @@ SIGNATURES = {
     "pkv_paged_attention": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32, _f, _p,
                                    _sz, _i32, _p]),
     "pkv_device_status": (_i32, [ctypes.POINTER(ctypes.c_uint32), _i32, _p]),
-    "pkv_set_tuning": (_i32, [_i32, _i32]),
-    "pkv_get_tuning": (_i32, [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
+    "pkv_set_tuning": (_i32, [ctypes.POINTER(Tuning)]),
+    "pkv_get_tuning": (_i32, [ctypes.POINTER(Tuning)]),
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double),
                                ctypes.POINTER(ctypes.c_int64), _i32]),

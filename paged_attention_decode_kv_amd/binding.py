@@ -171,15 +171,17 @@ def device_status(device=None, clear: bool = True) -> int:
     return int(flags.value)
 
 
-def set_tuning(chunk_tokens: int = 0, decode_waves: int = 0) -> None:
+def set_tuning(chunk_min: int = 0, chunk_max: int = 0, decode_waves: int = 0,
+               items_per_group: int = 0, deal: int = 0) -> None:
     """Set the decode work split (0 keeps a value); see pkv_set_tuning."""
-    _check(_capi.lib().pkv_set_tuning(int(chunk_tokens), int(decode_waves)))
+    t = _capi.Tuning(chunk_min, chunk_max, decode_waves, items_per_group, deal)
+    _check(_capi.lib().pkv_set_tuning(ctypes.byref(t)))
 
 
-def get_tuning() -> tuple[int, int]:
-    c, w = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(_capi.lib().pkv_get_tuning(ctypes.byref(c), ctypes.byref(w)))
-    return int(c.value), int(w.value)
+def get_tuning() -> dict:
+    t = _capi.Tuning()
+    _check(_capi.lib().pkv_get_tuning(ctypes.byref(t)))
+    return {f: int(getattr(t, f)) for f, _ in _capi.Tuning._fields_}
 
 
 def timing_enable(on: bool = True) -> None:

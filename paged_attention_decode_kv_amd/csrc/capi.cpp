@@ -251,7 +251,7 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
                                            max_blocks_per_row, pool->block_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  const int32_t chunk = pkv::tuning_chunk_tokens();
+  const int32_t chunk = pkv::tuning_chunk_min();
   const int64_t most_items = num_rows * ((int64_t)max_blocks_per_row * pool->block_size /
                                          chunk + 1) * num_heads;
   if (most_items > (int64_t{1} << 30))
@@ -282,8 +282,10 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
   a.num_heads = num_heads;
   a.max_blocks = max_blocks_per_row;
   a.ctx_limit = (int32_t)ctx_limit_of(pool, max_blocks_per_row);
-  a.chunk_tokens = chunk;
-  a.log2_chunk = log2i(chunk);
+  a.log2_chunk_min = log2i(chunk);
+  a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
+  a.target_items = 0;
+  a.deal_static = 1;
   a.scale = scale;
   const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads,
                                                  pool->head_dim, max_blocks_per_row,
@@ -300,17 +302,23 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
   return ok();
 }
 
-pkv_status pkv_set_tuning(int32_t chunk_tokens, int32_t decode_waves) {
-  if (!pkv::set_tuning(chunk_tokens, decode_waves))
-    return fail(PKV_ERR_UNSUPPORTED, "chunk_tokens %d / decode_waves %d not supported",
-                chunk_tokens, decode_waves);
+pkv_status pkv_set_tuning(const pkv_tuning* t) {
+  if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
+  if (!pkv::set_tuning(t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group,
+                       t->deal))
+    return fail(PKV_ERR_UNSUPPORTED, "tuning chunk [%d, %d], waves %d, items/group %d, "
+                "deal %d not supported", t->chunk_min, t->chunk_max, t->decode_waves,
+                t->items_per_group, t->deal);
   return ok();
 }
 
-pkv_status pkv_get_tuning(int32_t* chunk_tokens, int32_t* decode_waves) {
-  if (!chunk_tokens || !decode_waves) return fail(PKV_ERR_NULL, "output pointer is NULL");
-  *chunk_tokens = pkv::tuning_chunk_tokens();
-  *decode_waves = pkv::tuning_decode_waves();
+pkv_status pkv_get_tuning(pkv_tuning* t) {
+  if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
+  t->chunk_min = pkv::tuning_chunk_min();
+  t->chunk_max = pkv::tuning_chunk_max();
+  t->decode_waves = pkv::tuning_decode_waves();
+  t->items_per_group = pkv::tuning_items_per_group();
+  t->deal = pkv::tuning_deal_static() ? 1 : 2;
   return ok();
 }
 

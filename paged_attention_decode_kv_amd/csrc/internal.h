@@ -8,19 +8,26 @@
 
 namespace pkv {
 
-// Tokens one decode work item covers for one (row, head): a power of two in
-// [kMinChunkTokens, kMaxChunkTokens], kDefaultChunkTokens unless retuned with
-// pkv_set_tuning.  A row of context_len tokens is split into
-// cdiv(context_len, chunk_tokens) chunks; rows with more than one chunk are merged
-// by the combine kernel.
+// Tokens one decode work item covers for one (row, head).  The plan kernel picks a
+// power of two in [chunk_min, chunk_max] per call: the largest whose item count
+// reaches items_per_group items per decode workgroup.  A row of context_len tokens
+// is split into cdiv(context_len, chunk) chunks; rows with more than one chunk are
+// merged by the combine kernel.  pkv_set_tuning can pin the chunk length.
 constexpr int kMinChunkTokens = 32;
-constexpr int kMaxChunkTokens = 1024;
-constexpr int kDefaultChunkTokens = 256;
-constexpr int kDefaultDecodeWaves = 4;
+constexpr int kMaxChunkTokens = 2048;
+constexpr int kDefaultChunkMin = 128;
+constexpr int kDefaultChunkMax = 2048;
+constexpr int kDefaultDecodeWaves = 8;
+constexpr int kDefaultItemsPerGroup = 16;
+constexpr int kDefaultDealStatic = 1;
 
-int tuning_chunk_tokens();
+int tuning_chunk_min();
+int tuning_chunk_max();
 int tuning_decode_waves();
-bool set_tuning(int chunk_tokens, int decode_waves);
+int tuning_items_per_group();
+int tuning_deal_static();
+bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
+                int deal);
 
 // Pool geometry in elements, derived from the descriptor.
 struct PoolGeom {
@@ -48,7 +55,8 @@ struct WriteArgs {
 // Workspace carve-up of one pkv_paged_attention call.
 struct Workspace {
   int4* entries;        // [max_entries]: {row, chunk (-1: pad row), chunks in row, context_len}
-  int32_t* counters;    // [0] entries written by the plan, [1] queue ticket
+  int32_t* counters;    // [0] entries, [1] queue ticket, [2] chunk length, [3] its log2,
+                        // [4] section-A entries, [5] section-A+B entries
   float* partials;      // [rows][heads][max_chunks][head_dim + 2]: m (log2 units), l, acc
   int64_t max_entries;
   int32_t max_chunks;
@@ -66,8 +74,10 @@ struct AttnArgs {
   int32_t num_heads;
   int32_t max_blocks;
   int32_t ctx_limit;    // min(max_blocks * block_size, num_blocks * block_size)
-  int32_t chunk_tokens; // tokens per work item
-  int32_t log2_chunk;
+  int32_t log2_chunk_min;  // the plan's chunk length range (powers of two)
+  int32_t log2_chunk_max;
+  int32_t target_items;    // items the plan aims for (set by the launcher)
+  int32_t deal_static;     // 1: whole rounds of full chunks are dealt without the queue
   float scale;
 };
 

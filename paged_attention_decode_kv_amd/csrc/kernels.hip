@@ -201,21 +201,57 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int limit) {
   return ctx;
 }
 
-// Entries are ordered longest first so that the queue's tail is short work:
-//   A. every full chunk (chunk_tokens tokens) of every row, rows in order;
+// Chooses the chunk length and writes the work list.
+//
+// The chunk length P is the largest power of two in [chunk_min, chunk_max] whose
+// (chunk, head) item count reaches target_items (enough items per decode workgroup
+// for the queue to balance), else chunk_min.  Entries are ordered longest first so
+// that the queue's tail is short work:
+//   A. every full chunk (P tokens) of every row, rows in order;
 //   B. every row's trailing partial chunk, by length, longest first;
 //   C. one zero-output entry per padding row.
+// counters[0] = entries, [1] = queue ticket (reset to 0), [2] = P, [3] = log2 P,
+// [4] = entries in section A, [5] = entries in sections A and B.
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspace ws) {
   constexpr int kMaxChunk = kMaxChunkTokens;
+  constexpr int kCand = 6;                 // chunk_max / chunk_min <= 32
   __shared__ int s_wave[kPlanThreads / 64];
   __shared__ int s_bin_start[kMaxChunk];   // first B position of each remainder length
   __shared__ int s_bin_fill[kMaxChunk];
   __shared__ int s_pad_fill;
+  __shared__ int s_cand[kCand];
   const int t = threadIdx.x;
-  const int P = a.chunk_tokens;
-  const int lp = a.log2_chunk;
-  for (int q = t; q < P; q += kPlanThreads) s_bin_fill[q] = 0;
+  const int lane = t & 63;
+  if (t < kCand) s_cand[t] = 0;
   if (t == 0) s_pad_fill = 0;
+  __syncthreads();
+
+  // pass 0: chunk count of every candidate length
+  const int lmin = a.log2_chunk_min;
+  const int ncand = a.log2_chunk_max - lmin + 1;
+  int cnt[kCand] = {0, 0, 0, 0, 0, 0};
+  for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
+    const int ctx = clamp_ctx(a.context_lens[r], a.ctx_limit);
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) cnt[k] += (ctx + (1 << (lmin + k)) - 1) >> (lmin + k);
+  }
+#pragma unroll
+  for (int k = 0; k < kCand; ++k) {
+    int v = cnt[k];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    if (lane == 0 && k < ncand) atomicAdd(&s_cand[k], v);
+  }
+  __syncthreads();
+  int lp = lmin;
+  for (int k = ncand - 1; k >= 0; --k) {
+    if ((int64_t)s_cand[k] * a.num_heads >= a.target_items) {
+      lp = lmin + k;
+      break;
+    }
+  }
+  const int P = 1 << lp;
+  for (int q = t; q < P; q += kPlanThreads) s_bin_fill[q] = 0;
   __syncthreads();
 
   // pass 1: section A, remainder histogram, pad count
@@ -223,7 +259,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
   for (int64_t base = 0; base < a.num_rows; base += kPlanThreads) {
     const int64_t r = base + t;
     int ctx = 0;
-    if (r < a.num_rows) ctx = clamp_ctx(a.context_lens[r], a.ctx_limit);
+    if (r < a.num_rows) {
+      ctx = a.context_lens[r];
+      ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
+    }
     const int full = ctx >> lp;
     const int nch = (ctx + P - 1) >> lp;
     int tile_a, tile_pad;
@@ -235,13 +274,27 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
     n_pad += tile_pad;
   }
   __syncthreads();
-  // bins of section B in descending remainder order (P <= kPlanThreads)
+  // bins of section B in descending remainder order; thread t owns PER consecutive bins
   int total_b = 0;
   {
-    const int cnt = t < P ? s_bin_fill[P - 1 - t] : 0;
-    const int start = block_exclusive_scan(cnt, s_wave, &total_b);
-    if (t < P) s_bin_start[P - 1 - t] = start;
+    constexpr int PER = kMaxChunk / kPlanThreads;
+    int local[PER];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = t * PER + i;               // q-th bin in descending order
+      local[i] = q < P ? s_bin_fill[P - 1 - q] : 0;
+      sum += local[i];
+    }
+    int start = block_exclusive_scan(sum, s_wave, &total_b);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = t * PER + i;
+      if (q < P) s_bin_start[P - 1 - q] = start;
+      start += local[i];
+    }
   }
+  __syncthreads();
   for (int q = t; q < P; q += kPlanThreads) s_bin_fill[q] = 0;
   __syncthreads();
   // pass 2: place sections B and C
@@ -261,6 +314,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
   if (t == 0) {
     ws.counters[0] = total_a + total_b + n_pad;
     ws.counters[1] = 0;
+    ws.counters[2] = P;
+    ws.counters[3] = lp;
+    ws.counters[4] = total_a;
+    ws.counters[5] = total_a + total_b;
   }
 }
 
@@ -281,12 +338,80 @@ struct Shape {
   static constexpr int E = Elem<T>::kPerLane;       // elements per lane load
   static constexpr int LPT = D / E;                 // lanes per token vector
   static constexpr int TPS = 64 / LPT;              // tokens per wave load
-  static constexpr int U = (16 / TPS) < 8 ? (16 / TPS) : 8;   // loads per sub-chunk
-  static constexpr int CH = TPS * U;                // tokens per sub-chunk
+  static constexpr int U = (16 / TPS) < 4 ? (16 / TPS) : 4;   // wave loads per sub-chunk
+  static constexpr int CH = TPS * U;                // tokens per sub-chunk (<= 16)
   static_assert(LPT >= 8 && LPT <= 64, "unsupported head_dim/dtype");
-  static_assert(kMinChunkTokens % CH == 0, "a chunk must hold whole sub-chunks");
+  static_assert(kMinChunkTokens % CH == 0 && 16 % CH == 0, "sub-chunks tile chunks and blocks");
+  static_assert(kMaxChunkTokens / 16 <= 128, "block ids of a chunk: two per lane");
 };
 
+// Everything a work item needs before its first K/V load.
+struct ItemMeta {
+  int r, h, chunk, nch, ctx;
+  uint4 q;       // this lane's 16 bytes of the query
+  int blk;       // lane i: block id of the chunk's i-th block
+  int blk_hi;    // lane i: block id of the chunk's (64 + i)-th block
+};
+
+// First half of fetching an item's metadata: the work-list entry load is issued and
+// its value is not consumed, so no wait is inserted here.
+__device__ __forceinline__ int4 issue_entry(const Workspace& ws, int item, int heads) {
+  return ws.entries[item / heads];
+}
+
+// Second half: the entry becomes wave-uniform and the query and block-id loads are
+// issued (they complete while the current item finishes).
+template <typename T, int D>
+__device__ __forceinline__ ItemMeta finish_meta(const AttnArgs& a, int4 ent, int item,
+                                                int lp, int log2_bs, int lane, int sub) {
+  constexpr int E = Elem<T>::kPerLane;
+  ItemMeta m;
+  const int e = item / a.num_heads;
+  m.h = item - e * a.num_heads;
+  m.r = __builtin_amdgcn_readfirstlane(ent.x);
+  m.chunk = __builtin_amdgcn_readfirstlane(ent.y);
+  m.nch = __builtin_amdgcn_readfirstlane(ent.z);
+  m.ctx = __builtin_amdgcn_readfirstlane(ent.w);
+  m.q = make_uint4(0, 0, 0, 0);
+  m.blk = 0;
+  m.blk_hi = 0;
+  if (m.chunk >= 0) {
+    const int64_t rh = (int64_t)m.r * a.num_heads + m.h;
+    m.q = load16(static_cast<const T*>(a.q) + rh * D + sub * E);
+    const int t_begin = m.chunk << lp;
+    const int t_end = min(m.ctx, t_begin + (1 << lp));
+    const int j0 = t_begin >> log2_bs;
+    // a chunk spans at most kMaxChunkTokens / 16 = 128 blocks
+    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
+    const int32_t* bt = a.block_tables + (int64_t)m.r * a.max_blocks + j0;
+    if (lane < nblk) m.blk = bt[lane];
+    if (lane + 64 < nblk) m.blk_hi = bt[lane + 64];
+  }
+  return m;
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;   // raw 32-bit buffer (gfx9 word 3)
+constexpr int kLoadNonTemporal = 2;        // cache policy: nt
+
+// 16 bytes at byte `voff` of a buffer.  Offsets at or past the descriptor's record
+// count read as zero without a memory access: that is how masked tokens are skipped.
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, kLoadNonTemporal);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The decode read.  Persistent workgroups process work items; an item is (chunk of a
+// row's history, query head), and the waves of a workgroup share it, wave w folding
+// sub-chunks w, w + WAVES, ... into its own online-softmax state before the waves are
+// merged through LDS.
+//
+// Schedule: whole rounds of the full chunks (section A, all the same length) are
+// dealt round robin, workgroup g taking items g, g + G, g + 2G, ...; the rest of A and
+// the trailing partial chunks (section B, longest first) come from one shared ticket
+// counter, so the uneven tail is balanced dynamically with few atomics; padding rows
+// (section C) are zeroed round robin at the end.  The next item's metadata and the
+// ticket after it are fetched while the current item streams.
 template <typename T, int D, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
@@ -299,53 +424,79 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int g = lane / LPT;       // which token of a wave load this lane holds
   const int sub = lane % LPT;     // which 16-byte piece of the token's head vector
 
-  __shared__ int s_ticket;
-  __shared__ float s_m[WAVES], s_l[WAVES];
-  __shared__ float s_acc[WAVES][D];
+  __shared__ int s_ticket[2];
+  __shared__ float s_m[2][WAVES], s_l[2][WAVES];
+  __shared__ float s_acc[2][WAVES][D];
 
   const int heads = a.num_heads;
   const int group = heads / a.g.kv_heads;
+  const int lp = ws.counters[3];
+  const int P = 1 << lp;
+  const int n_static = ws.counters[4] * heads;    // section A items
+  const int n_data = ws.counters[5] * heads;      // sections A and B
   const int n_items = ws.counters[0] * heads;
-  const int P = a.chunk_tokens;
+  const int G = gridDim.x;
+  const int n_dealt = a.deal_static ? n_static / G * G : 0;
   const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
   const int64_t tok_bytes = a.g.tok_stride * ES;
   const int64_t blk_bytes = a.g.blk_stride * ES;
-  // byte offset of this lane's 16 bytes inside one wave load, and of one wave load
-  const uint32_t lane_off = (uint32_t)(g * tok_bytes + sub * E * ES);
-  const int64_t step_bytes = TPS * tok_bytes;
+  const int64_t head_bytes = a.g.head_stride * ES;
+  // byte offset of this lane's 16 bytes in the u-th wave load of a sub-chunk
+  uint32_t voff[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    voff[u] = (uint32_t)((u * TPS + g) * tok_bytes + sub * E * ES);
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
 
-  for (;;) {
-    if (threadIdx.x == 0) s_ticket = atomicAdd(&ws.counters[1], 1);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_ticket);
-    __syncthreads();
-    if (item >= n_items) break;
-    const int e = item / heads;
-    const int h = item - e * heads;
-    const int4 ent = ws.entries[e];
-    const int r = __builtin_amdgcn_readfirstlane(ent.x);
-    const int chunk = __builtin_amdgcn_readfirstlane(ent.y);
-    const int nch = __builtin_amdgcn_readfirstlane(ent.z);
-    const int ctx = __builtin_amdgcn_readfirstlane(ent.w);
-    const int64_t rh = (int64_t)r * heads + h;
-    T* outp = static_cast<T*>(a.out) + rh * D + sub * E;
-
-    if (chunk < 0) {   // padding row: zero output, nothing read
-      if (wave == 0 && g == 0) store16(outp, make_uint4(0, 0, 0, 0));
-      continue;
+  // Item indices: static ones from the deal, dynamic ones from the ticket counter
+  // (n_dealt + ticket; anything at or past n_data ends the stream).
+  int static_next = blockIdx.x;
+  auto take = [&](int& out) -> bool {        // true: a static item was taken
+    if (static_next < n_dealt) {
+      out = static_next;
+      static_next += G;
+      return true;
     }
+    return false;
+  };
+  int item, next;
+  {
+    const bool st0 = take(item);
+    const bool st1 = take(next);
+    if (!st0 || !st1) {
+      if (threadIdx.x == 0) {
+        s_ticket[0] = st0 ? 0 : atomicAdd(&ws.counters[1], 1);
+        s_ticket[1] = st1 ? 0 : atomicAdd(&ws.counters[1], 1);
+      }
+      __syncthreads();
+      if (!st0) item = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[0]);
+      if (!st1) next = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[1]);
+      __syncthreads();
+    }
+  }
+  int buf = 0;
+  bool bad_block = false;   // a live block id outside [0, num_blocks) was skipped
+  ItemMeta cur;
+  if (item < n_data)
+    cur = finish_meta<T, D>(a, issue_entry(ws, item, heads), item, lp, log2_bs, lane, sub);
+
+  while (item < n_data) {
+    // the item after next: static, or a ticket whose value is needed only at the end
+    int after = 0;
+    const bool after_static = take(after);
+    if (!after_static && threadIdx.x == 0) after = atomicAdd(&ws.counters[1], 1);
+    int4 next_ent = make_int4(0, -1, 0, 0);
+    if (next < n_data) next_ent = issue_entry(ws, next, heads);
+
+    // (the item's fields are wave-uniform; saying so keeps the load descriptors scalar)
+    const int chunk = __builtin_amdgcn_readfirstlane(cur.chunk);
     const int t_begin = chunk * P;
-    const int t_end = min(ctx, t_begin + P);
-    const int hkv = h / group;
-    const uint4 qv = load16(static_cast<const T*>(a.q) + rh * D + sub * E);
-    // the chunk's block ids, one per lane (a chunk spans at most 64 blocks)
+    const int t_end = min(__builtin_amdgcn_readfirstlane(cur.ctx), t_begin + P);
     const int j0 = t_begin >> log2_bs;
-    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
-    const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks + j0;
-    const int my_blk = lane < nblk ? bt[lane] : 0;
-    const char* kh = static_cast<const char*>(a.k_cache) + hkv * a.g.head_stride * ES;
-    const char* vh = static_cast<const char*>(a.v_cache) + hkv * a.g.head_stride * ES;
+    const int64_t head_off =
+        (int64_t)(__builtin_amdgcn_readfirstlane(cur.h) / group) * head_bytes;
 
     float m = -INFINITY, l = 0.f;
     float acc[E];
@@ -355,40 +506,32 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
     for (int s = wave; s < n_sub; s += WAVES) {
       const int t0 = t_begin + s * CH;
-      int blk = __builtin_amdgcn_readlane(my_blk, (t0 >> log2_bs) - j0);
-      const bool blk_ok = blk >= 0 && blk < a.g.num_blocks;
-      if (!blk_ok) {
-        if (lane == 0) atomicOr(&g_status, PKV_DEVERR_BLOCK_ID);
-        blk = 0;
-      }
-      const int64_t off = (int64_t)blk * blk_bytes + (int64_t)(t0 & bs_mask) * tok_bytes;
-      const char* kp = kh + off;
-      const char* vp = vh + off;
-      // tokens of this sub-chunk that exist; masked tokens are never loaded
+      const int jb = (t0 >> log2_bs) - j0;   // block of this sub-chunk within the chunk
+      const int raw = jb < 64 ? __builtin_amdgcn_readlane(cur.blk, jb)
+                              : __builtin_amdgcn_readlane(cur.blk_hi, jb - 64);
+      const bool blk_ok = raw >= 0 && raw < a.g.num_blocks;
+      bad_block |= !blk_ok;
+      const int blk = blk_ok ? raw : 0;
+      const int64_t off = head_off + (int64_t)blk * blk_bytes + (int64_t)(t0 & bs_mask) * tok_bytes;
+      // tokens of this sub-chunk that exist; the descriptors end after them, so the
+      // loads of masked tokens never reach memory
       const int nvalid = blk_ok ? min(CH, t_end - t0) : 0;
+      const int bytes = (int)(nvalid * tok_bytes);
+      const __amdgpu_buffer_rsrc_t kr_src =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), 0, bytes, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vr_src =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), 0, bytes, kBufferFlags);
       uint4 kr[U], vr[U];
-      if (nvalid == CH) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          kr[u] = load16_stream(kp + u * step_bytes + lane_off);
-          vr[u] = load16_stream(vp + u * step_bytes + lane_off);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          kr[u] = make_uint4(0, 0, 0, 0);
-          vr[u] = make_uint4(0, 0, 0, 0);
-          if (u * TPS + g < nvalid) {
-            kr[u] = load16_stream(kp + u * step_bytes + lane_off);
-            vr[u] = load16_stream(vp + u * step_bytes + lane_off);
-          }
-        }
+      for (int u = 0; u < U; ++u) {
+        kr[u] = buffer_load16(kr_src, voff[u]);
+        vr[u] = buffer_load16(vr_src, voff[u]);
       }
       float sc[U];
       float smax = -INFINITY;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float d = group_sum<LPT>(El::dot(qv, kr[u], 0.f));
+        const float d = group_sum<LPT>(El::dot(cur.q, kr[u], 0.f));
         sc[u] = u * TPS + g < nvalid ? d * scale_log2 : -INFINITY;
         smax = fmaxf(smax, sc[u]);
       }
@@ -407,6 +550,9 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       m = m_new;
     }
 
+    // the next item's query and block ids load while this item's state is merged
+    const ItemMeta nxt = finish_meta<T, D>(a, next_ent, next, lp, log2_bs, lane, sub);
+
     // merge the lane groups of this wave
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
@@ -421,52 +567,74 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       for (int i = 0; i < E; ++i) acc[i] = acc[i] * fa + __shfl_xor(acc[i], off) * fb;
       m = mx;
     }
-    // merge the waves of the workgroup
+    // merge the waves into wave 0 (LDS double-buffered by item parity: one barrier)
+    const bool writer = wave == 0 && g == 0;
     if constexpr (WAVES > 1) {
       if (g == 0) {
 #pragma unroll
-        for (int i = 0; i < E; ++i) s_acc[wave][sub * E + i] = acc[i];
+        for (int i = 0; i < E; ++i) s_acc[buf][wave][sub * E + i] = acc[i];
         if (sub == 0) {
-          s_m[wave] = m;
-          s_l[wave] = l;
+          s_m[buf][wave] = m;
+          s_l[buf][wave] = l;
         }
       }
-      __syncthreads();
-      if (wave != 0) continue;
-      float mx = s_m[0];
-#pragma unroll
-      for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[w]);
-      l = 0.f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        const float f = __builtin_amdgcn_exp2f(s_m[w] - mx);   // mx is finite here
-        l += s_l[w] * f;
-#pragma unroll
-        for (int i = 0; i < E; ++i) acc[i] += s_acc[w][sub * E + i] * f;
-      }
-      m = mx;
     }
-    if (g != 0) continue;
-    if (nch == 1) {
-      const float inv = 1.0f / l;
+    if (!after_static && threadIdx.x == 0) s_ticket[buf] = after;
+    __syncthreads();
+    if (!after_static) after = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[buf]);
+    if constexpr (WAVES > 1) {
+      if (writer) {
+        float mx = s_m[buf][0];
 #pragma unroll
-      for (int i = 0; i < E; ++i) acc[i] *= inv;
-      store16(outp, El::pack(acc));
-    } else {
-      float* rec = ws.partials + (rh * ws.max_chunks + chunk) * (D + 4);
-      if (sub == 0) {
-        rec[0] = m;
-        rec[1] = l;
+        for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[buf][w]);
+        l = 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+          const float f = __builtin_amdgcn_exp2f(s_m[buf][w] - mx);   // mx is finite here
+          l += s_l[buf][w] * f;
+#pragma unroll
+          for (int i = 0; i < E; ++i) acc[i] += s_acc[buf][w][sub * E + i] * f;
+        }
+        m = mx;
       }
-#pragma unroll
-      for (int i = 0; i < E; i += 4)
-        store16(rec + 4 + sub * E + i, make_uint4(__float_as_uint(acc[i]),
-                                                  __float_as_uint(acc[i + 1]),
-                                                  __float_as_uint(acc[i + 2]),
-                                                  __float_as_uint(acc[i + 3])));
     }
+    if (writer) {
+      const int64_t rh = (int64_t)cur.r * heads + cur.h;
+      if (cur.nch == 1) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] *= inv;
+        store16(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(acc));
+      } else {
+        float* rec = ws.partials + (rh * ws.max_chunks + chunk) * (D + 4);
+        if (sub == 0) {
+          rec[0] = m;
+          rec[1] = l;
+        }
+#pragma unroll
+        for (int i = 0; i < E; i += 4)
+          store16(rec + 4 + sub * E + i, make_uint4(__float_as_uint(acc[i]),
+                                                    __float_as_uint(acc[i + 1]),
+                                                    __float_as_uint(acc[i + 2]),
+                                                    __float_as_uint(acc[i + 3])));
+      }
+    }
+    buf ^= 1;
+    item = next;
+    cur = nxt;
+    next = after;
+  }
+  if (bad_block && lane == 0) atomicOr(&g_status, PKV_DEVERR_BLOCK_ID);
+  // padding rows: zero output, nothing read
+  for (int it = n_data + (int)blockIdx.x; it < n_items; it += G) {
+    const int e = it / heads;
+    const int h = it - e * heads;
+    const int r = ws.entries[e].x;
+    if (wave == 0 && g == 0)
+      store16(static_cast<T*>(a.out) + ((int64_t)r * heads + h) * D + sub * E,
+              make_uint4(0, 0, 0, 0));
   }
 }
 
@@ -501,7 +669,8 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
   const int64_t r = blockIdx.y;
   int ctx = a.context_lens[r];
   ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
-  const int nch = (ctx + a.chunk_tokens - 1) >> a.log2_chunk;
+  const int lp = ws.counters[3];
+  const int nch = (ctx + (1 << lp) - 1) >> lp;
   if (nch <= 1) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t rh = r * a.num_heads + h;
@@ -571,7 +740,7 @@ static int max_chunks_for(int32_t max_blocks, int32_t block_size, int32_t chunk)
 
 size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
                        int32_t max_blocks, int32_t block_size) {
-  const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_tokens());
+  const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_min());
   const int64_t entries = num_rows * (mc > 1 ? mc : 1);
   int64_t bytes = align_up(entries * (int64_t)sizeof(int4), 256);
   bytes += 256;   // counters
@@ -582,7 +751,7 @@ size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
 Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads, int32_t head_dim,
                           int32_t max_blocks, int32_t block_size) {
   Workspace w;
-  const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_tokens());
+  const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_min());
   w.max_chunks = (int32_t)mc;
   w.max_entries = num_rows * (mc > 1 ? mc : 1);
   char* p = static_cast<char*>(base);
@@ -633,14 +802,17 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
     per_cu[dev] = n > 0 ? n : 1;
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  timing_begin(PKV_PHASE_PLAN, stream);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, ws);
-  timing_end(PKV_PHASE_PLAN, stream);
   int64_t grid = (int64_t)num_cu[dev] * per_cu[dev];
   const int64_t most = ws.max_entries * a.num_heads;
   if (grid > most) grid = most;
+  AttnArgs pa = a;
+  pa.target_items = (int32_t)(grid * tuning_items_per_group());
+  pa.deal_static = tuning_deal_static();
+  timing_begin(PKV_PHASE_PLAN, stream);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa, ws);
+  timing_end(PKV_PHASE_PLAN, stream);
   timing_begin(PKV_PHASE_DECODE, stream);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a, ws,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, pa, ws,
                      scale_log2);
   timing_end(PKV_PHASE_DECODE, stream);
   if (ws.max_chunks > 1) {

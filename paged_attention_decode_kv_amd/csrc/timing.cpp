@@ -88,24 +88,38 @@ hipError_t timing_read(int phase, double* total_ms, int64_t* launches, bool rese
 }
 
 namespace {
-std::atomic<int> g_chunk_tokens{kDefaultChunkTokens};
+std::atomic<int> g_chunk_min{kDefaultChunkMin};
+std::atomic<int> g_chunk_max{kDefaultChunkMax};
 std::atomic<int> g_decode_waves{kDefaultDecodeWaves};
+std::atomic<int> g_items_per_group{kDefaultItemsPerGroup};
+std::atomic<int> g_deal_static{kDefaultDealStatic};
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 }  // namespace
 
-int tuning_chunk_tokens() { return g_chunk_tokens.load(std::memory_order_relaxed); }
+int tuning_chunk_min() { return g_chunk_min.load(std::memory_order_relaxed); }
+int tuning_chunk_max() { return g_chunk_max.load(std::memory_order_relaxed); }
 int tuning_decode_waves() { return g_decode_waves.load(std::memory_order_relaxed); }
+int tuning_items_per_group() { return g_items_per_group.load(std::memory_order_relaxed); }
+int tuning_deal_static() { return g_deal_static.load(std::memory_order_relaxed); }
 
-bool set_tuning(int chunk_tokens, int decode_waves) {
-  if (chunk_tokens != 0) {
-    if (chunk_tokens < kMinChunkTokens || chunk_tokens > kMaxChunkTokens ||
-        (chunk_tokens & (chunk_tokens - 1)) != 0)
-      return false;
-  }
+bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
+                int deal) {
+  const int lo = chunk_min ? chunk_min : tuning_chunk_min();
+  const int hi = chunk_max ? chunk_max : tuning_chunk_max();
+  if (!pow2_in(lo, kMinChunkTokens, kMaxChunkTokens) ||
+      !pow2_in(hi, kMinChunkTokens, kMaxChunkTokens) || lo > hi || hi / lo > 32)
+    return false;
   if (decode_waves != 0 && decode_waves != 1 && decode_waves != 2 && decode_waves != 4 &&
       decode_waves != 8)
     return false;
-  if (chunk_tokens != 0) g_chunk_tokens.store(chunk_tokens);
+  if (items_per_group < 0 || items_per_group > 1024) return false;
+  if (deal < 0 || deal > 2) return false;
+  if (deal != 0) g_deal_static.store(deal == 1 ? 1 : 0);
+  g_chunk_min.store(lo);
+  g_chunk_max.store(hi);
   if (decode_waves != 0) g_decode_waves.store(decode_waves);
+  if (items_per_group != 0) g_items_per_group.store(items_per_group);
   return true;
 }
 

@@ -371,3 +371,28 @@ def test_refusals_touch_nothing():
         binding.paged_attention(st.q[:0], st.k_cache, st.v_cache, st.tables[:0],
                                 st.lens[:0], w.scale)
     assert e.value.code == "EMPTY"
+
+
+TUNINGS = [
+    dict(chunk_min=128, chunk_max=1024, decode_waves=8, items_per_group=8, deal=2),
+    dict(chunk_min=32, chunk_max=32, decode_waves=1, items_per_group=1),
+    dict(chunk_min=2048, chunk_max=2048, decode_waves=4, items_per_group=1),
+    dict(chunk_min=64, chunk_max=2048, decode_waves=2, items_per_group=64),
+    dict(chunk_min=256, chunk_max=256, decode_waves=8, items_per_group=1, deal=1),
+]
+
+
+@pytest.mark.parametrize("tuning", TUNINGS, ids=lambda t: "-".join(f"{k}{v}" for k, v in t.items()))
+def test_work_split_variants(tuning):
+    """Every work split (chunk range, waves per workgroup, items per wave) gives oracle
+    parity."""
+    before = binding.get_tuning()
+    binding.set_tuning(**tuning)
+    try:
+        for dtype in ("bf16", "f32"):
+            w = wl.make_custom([4100, 0, 1, 255, 256, 257, 2049, 31, 700], heads=8, kv_heads=2,
+                               head_dim=128, block_size=16, dtype=dtype, layout="HND",
+                               seed=77)
+            check_full(w)
+    finally:
+        binding.set_tuning(**{k: v for k, v in before.items()})
