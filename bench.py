@@ -56,6 +56,8 @@ def parse():
                     help="work items per decode workgroup the plan aims for (0: default)")
     ap.add_argument("--deal", type=int, default=0,
                     help="1: deal full-chunk rounds statically, 2: queue every item")
+    ap.add_argument("--staging", type=int, default=0,
+                    help="1: K/V straight to registers, 2: through an LDS stage")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
@@ -198,7 +200,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     binding.set_tuning(args.chunk_min, args.chunk_max, args.decode_waves,
-                       args.items_per_group, args.deal)
+                       args.items_per_group, args.deal, args.staging)
     tuning = binding.get_tuning()
     w = wl.make_config(args.config, layout=args.layout)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]

@@ -178,6 +178,10 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *   deal                  1: whole rounds of full-length chunks are dealt to workgroups
  *                         round robin and only the rest goes through the shared work
  *                         queue; 2: every item goes through the queue (default 1)
+ *   staging               1: each wave loads a sub-chunk's K/V straight into registers;
+ *                         2: each wave streams its next sub-chunk into an LDS stage by
+ *                         direct buffer-to-LDS loads while folding the current one
+ *                         (default 2)
  * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it
  * before sizing workspaces.  Results do not depend on these values beyond float32
  * rounding order.  Returns UNSUPPORTED for other values. */
@@ -187,6 +191,7 @@ typedef struct pkv_tuning {
   int32_t decode_waves;
   int32_t items_per_group;
   int32_t deal;
+  int32_t staging;
 } pkv_tuning;
 
 pkv_status pkv_set_tuning(const pkv_tuning* tuning);

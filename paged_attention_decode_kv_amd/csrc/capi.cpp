@@ -305,10 +305,10 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
 pkv_status pkv_set_tuning(const pkv_tuning* t) {
   if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
   if (!pkv::set_tuning(t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group,
-                       t->deal))
+                       t->deal, t->staging))
     return fail(PKV_ERR_UNSUPPORTED, "tuning chunk [%d, %d], waves %d, items/group %d, "
-                "deal %d not supported", t->chunk_min, t->chunk_max, t->decode_waves,
-                t->items_per_group, t->deal);
+                "deal %d, staging %d not supported", t->chunk_min, t->chunk_max,
+                t->decode_waves, t->items_per_group, t->deal, t->staging);
   return ok();
 }
 
@@ -319,6 +319,7 @@ pkv_status pkv_get_tuning(pkv_tuning* t) {
   t->decode_waves = pkv::tuning_decode_waves();
   t->items_per_group = pkv::tuning_items_per_group();
   t->deal = pkv::tuning_deal_static() ? 1 : 2;
+  t->staging = pkv::tuning_lds_stage() ? 2 : 1;
   return ok();
 }
 

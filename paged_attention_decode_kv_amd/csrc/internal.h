@@ -20,14 +20,16 @@ constexpr int kDefaultChunkMax = 2048;
 constexpr int kDefaultDecodeWaves = 8;
 constexpr int kDefaultItemsPerGroup = 16;
 constexpr int kDefaultDealStatic = 1;
+constexpr int kDefaultLdsStage = 1;
 
 int tuning_chunk_min();
 int tuning_chunk_max();
 int tuning_decode_waves();
 int tuning_items_per_group();
 int tuning_deal_static();
+int tuning_lds_stage();
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal);
+                int deal, int staging);
 
 // Pool geometry in elements, derived from the descriptor.
 struct PoolGeom {

@@ -393,6 +393,17 @@ __device__ __forceinline__ ItemMeta finish_meta(const AttnArgs& a, int4 ent, int
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferFlags = 0x00020000;   // raw 32-bit buffer (gfx9 word 3)
 constexpr int kLoadNonTemporal = 2;        // cache policy: nt
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0,15:14], expcnt[6:4], lgkmcnt[11:8])
+constexpr int kWaitVm0 = 0x0F70;           // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;         // lgkmcnt(0)
+
+// 16 bytes at byte `voff` of a buffer into LDS: lane i's bytes land at dst + 16 i.
+// Out-of-range offsets write zeros and read no memory.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                                  uint4* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, kLoadNonTemporal);
+}
 
 // 16 bytes at byte `voff` of a buffer.  Offsets at or past the descriptor's record
 // count read as zero without a memory access: that is how masked tokens are skipped.
@@ -412,7 +423,7 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
 // counter, so the uneven tail is balanced dynamically with few atomics; padding rows
 // (section C) are zeroed round robin at the end.  The next item's metadata and the
 // ticket after it are fetched while the current item streams.
-template <typename T, int D, int WAVES>
+template <typename T, int D, int WAVES, bool LDS_STAGE>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using S = Shape<T, D>;
@@ -424,6 +435,12 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int g = lane / LPT;       // which token of a wave load this lane holds
   const int sub = lane % LPT;     // which 16-byte piece of the token's head vector
 
+  // LDS staging: each wave owns one sub-chunk stage (its U K loads, then its U V loads,
+  // 64 lanes x 16 bytes each); the next sub-chunk streams into it by direct
+  // buffer-to-LDS loads while the current one is folded from registers.
+  constexpr int kStageWaves = LDS_STAGE ? WAVES : 1;
+  constexpr int kStageLoads = LDS_STAGE ? 2 * U : 1;
+  __shared__ __attribute__((aligned(16))) uint4 s_stage[kStageWaves][kStageLoads][64];
   __shared__ int s_ticket[2];
   __shared__ float s_m[2][WAVES], s_l[2][WAVES];
   __shared__ float s_acc[2][WAVES][D];
@@ -504,7 +521,9 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     for (int i = 0; i < E; ++i) acc[i] = 0.f;
 
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
-    for (int s = wave; s < n_sub; s += WAVES) {
+    // Descriptors of sub-chunk s's K and V: they end after its valid tokens, so the
+    // loads of masked tokens never reach memory.  Returns the valid-token count.
+    auto describe = [&](int s, __amdgpu_buffer_rsrc_t& ksrc, __amdgpu_buffer_rsrc_t& vsrc) {
       const int t0 = t_begin + s * CH;
       const int jb = (t0 >> log2_bs) - j0;   // block of this sub-chunk within the chunk
       const int raw = jb < 64 ? __builtin_amdgcn_readlane(cur.blk, jb)
@@ -513,19 +532,48 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       bad_block |= !blk_ok;
       const int blk = blk_ok ? raw : 0;
       const int64_t off = head_off + (int64_t)blk * blk_bytes + (int64_t)(t0 & bs_mask) * tok_bytes;
-      // tokens of this sub-chunk that exist; the descriptors end after them, so the
-      // loads of masked tokens never reach memory
       const int nvalid = blk_ok ? min(CH, t_end - t0) : 0;
       const int bytes = (int)(nvalid * tok_bytes);
-      const __amdgpu_buffer_rsrc_t kr_src =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), 0, bytes, kBufferFlags);
-      const __amdgpu_buffer_rsrc_t vr_src =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), 0, bytes, kBufferFlags);
-      uint4 kr[U], vr[U];
+      ksrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), 0, bytes,
+                                               kBufferFlags);
+      vsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), 0, bytes,
+                                               kBufferFlags);
+      return nvalid;
+    };
+    auto stage_in = [&](int s) {   // sub-chunk s -> this wave's LDS stage
+      __amdgpu_buffer_rsrc_t ksrc, vsrc;
+      describe(s, ksrc, vsrc);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        kr[u] = buffer_load16(kr_src, voff[u]);
-        vr[u] = buffer_load16(vr_src, voff[u]);
+        buffer_load16_lds(ksrc, voff[u], &s_stage[wave][u][0]);
+        buffer_load16_lds(vsrc, voff[u], &s_stage[wave][U + u][0]);
+      }
+    };
+    if constexpr (LDS_STAGE) {
+      if (wave < n_sub) stage_in(wave);
+    }
+    for (int s = wave; s < n_sub; s += WAVES) {
+      uint4 kr[U], vr[U];
+      int nvalid;
+      if constexpr (LDS_STAGE) {
+        __amdgpu_buffer_rsrc_t ksrc, vsrc;
+        nvalid = describe(s, ksrc, vsrc);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this wave's stage has landed
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          kr[u] = s_stage[wave][u][lane];
+          vr[u] = s_stage[wave][U + u][lane];
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // stage read before it is refilled
+        if (s + WAVES < n_sub) stage_in(s + WAVES);
+      } else {
+        __amdgpu_buffer_rsrc_t ksrc, vsrc;
+        nvalid = describe(s, ksrc, vsrc);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          kr[u] = buffer_load16(ksrc, voff[u]);
+          vr[u] = buffer_load16(vsrc, voff[u]);
+        }
       }
       float sc[U];
       float smax = -INFINITY;
@@ -782,9 +830,9 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int WAVES>
+template <typename T, int D, int WAVES, bool LDS_STAGE>
 static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
-  auto kern = decode_kernel<T, D, WAVES>;
+  auto kern = decode_kernel<T, D, WAVES, LDS_STAGE>;
   static int per_cu[64] = {0};   // occupancy per device, computed once
   static int num_cu[64] = {0};
   int dev = 0;
@@ -827,11 +875,19 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
 template <typename T, int D>
 static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws,
                                   hipStream_t stream) {
+  if (tuning_lds_stage()) {
+    switch (tuning_decode_waves()) {
+      case 1: return launch_decode_w<T, D, 1, true>(a, ws, stream);
+      case 2: return launch_decode_w<T, D, 2, true>(a, ws, stream);
+      case 8: return launch_decode_w<T, D, 8, true>(a, ws, stream);
+      default: return launch_decode_w<T, D, 4, true>(a, ws, stream);
+    }
+  }
   switch (tuning_decode_waves()) {
-    case 1: return launch_decode_w<T, D, 1>(a, ws, stream);
-    case 2: return launch_decode_w<T, D, 2>(a, ws, stream);
-    case 8: return launch_decode_w<T, D, 8>(a, ws, stream);
-    default: return launch_decode_w<T, D, 4>(a, ws, stream);
+    case 1: return launch_decode_w<T, D, 1, false>(a, ws, stream);
+    case 2: return launch_decode_w<T, D, 2, false>(a, ws, stream);
+    case 8: return launch_decode_w<T, D, 8, false>(a, ws, stream);
+    default: return launch_decode_w<T, D, 4, false>(a, ws, stream);
   }
 }
 

@@ -93,6 +93,7 @@ std::atomic<int> g_chunk_max{kDefaultChunkMax};
 std::atomic<int> g_decode_waves{kDefaultDecodeWaves};
 std::atomic<int> g_items_per_group{kDefaultItemsPerGroup};
 std::atomic<int> g_deal_static{kDefaultDealStatic};
+std::atomic<int> g_lds_stage{kDefaultLdsStage};
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 }  // namespace
@@ -102,9 +103,10 @@ int tuning_chunk_max() { return g_chunk_max.load(std::memory_order_relaxed); }
 int tuning_decode_waves() { return g_decode_waves.load(std::memory_order_relaxed); }
 int tuning_items_per_group() { return g_items_per_group.load(std::memory_order_relaxed); }
 int tuning_deal_static() { return g_deal_static.load(std::memory_order_relaxed); }
+int tuning_lds_stage() { return g_lds_stage.load(std::memory_order_relaxed); }
 
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal) {
+                int deal, int staging) {
   const int lo = chunk_min ? chunk_min : tuning_chunk_min();
   const int hi = chunk_max ? chunk_max : tuning_chunk_max();
   if (!pow2_in(lo, kMinChunkTokens, kMaxChunkTokens) ||
@@ -115,6 +117,8 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
     return false;
   if (items_per_group < 0 || items_per_group > 1024) return false;
   if (deal < 0 || deal > 2) return false;
+  if (staging < 0 || staging > 2) return false;
+  if (staging != 0) g_lds_stage.store(staging == 2 ? 1 : 0);
   if (deal != 0) g_deal_static.store(deal == 1 ? 1 : 0);
   g_chunk_min.store(lo);
   g_chunk_max.store(hi);

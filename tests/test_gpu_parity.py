@@ -375,9 +375,10 @@ def test_refusals_touch_nothing():
 
 TUNINGS = [
     dict(chunk_min=128, chunk_max=1024, decode_waves=8, items_per_group=8, deal=2),
-    dict(chunk_min=32, chunk_max=32, decode_waves=1, items_per_group=1),
+    dict(chunk_min=32, chunk_max=32, decode_waves=1, items_per_group=1, staging=2),
     dict(chunk_min=2048, chunk_max=2048, decode_waves=4, items_per_group=1),
-    dict(chunk_min=64, chunk_max=2048, decode_waves=2, items_per_group=64),
+    dict(chunk_min=64, chunk_max=2048, decode_waves=2, items_per_group=64, staging=2),
+    dict(chunk_min=128, chunk_max=2048, decode_waves=8, items_per_group=16, staging=2),
     dict(chunk_min=256, chunk_max=256, decode_waves=8, items_per_group=1, deal=1),
 ]
 
