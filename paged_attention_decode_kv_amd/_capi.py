@@ -5,7 +5,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PAGEDKV_LIB names another build of the same library (for side-by-side comparisons)
+LIB_PATH = os.environ.get("PAGEDKV_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 F32, BF16 = 0, 1
 LAYOUT_CODES = {"HND": 0, "NHD": 1}
