@@ -58,6 +58,10 @@ def parse():
                     help="1: deal full-chunk rounds statically, 2: queue every item")
     ap.add_argument("--staging", type=int, default=0,
                     help="1: K/V straight to registers, 2: through an LDS stage")
+    ap.add_argument("--max-query-group", type=int, default=0,
+                    help="query heads sharing one K/V load under GQA (0: default)")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="override the workload's KV heads (grouped-query variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
@@ -200,9 +204,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     binding.set_tuning(args.chunk_min, args.chunk_max, args.decode_waves,
-                       args.items_per_group, args.deal, args.staging)
+                       args.items_per_group, args.deal, args.staging, args.max_query_group)
     tuning = binding.get_tuning()
-    w = wl.make_config(args.config, layout=args.layout)
+    w = wl.make_config(args.config, layout=args.layout, kv_heads=args.kv_heads or None)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
     log(f"workload {w.name}: rows={w.rows} heads={w.heads} d={w.head_dim} bs={w.block_size} "
         f"{w.dtype} {w.layout}; pool {w.pool_bytes / 1e9:.2f} GB; "

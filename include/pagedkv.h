@@ -182,6 +182,12 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *                         2: each wave streams its next sub-chunk into an LDS stage by
  *                         direct buffer-to-LDS loads while folding the current one
  *                         (default 2)
+ *   max_query_group       1, 2, 4 or 8 (default 8).  With grouped-query attention
+ *                         (num_heads > num_kv_heads) one work item covers QG query heads
+ *                         that share a KV head, QG the largest of 8, 4, 2, 1 that divides
+ *                         num_heads / num_kv_heads and is at most max_query_group, so
+ *                         each K/V sub-chunk is read once for QG heads; 1 reads it once
+ *                         per query head
  * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it
  * before sizing workspaces.  Results do not depend on these values beyond float32
  * rounding order.  Returns UNSUPPORTED for other values. */
@@ -192,6 +198,7 @@ typedef struct pkv_tuning {
   int32_t items_per_group;
   int32_t deal;
   int32_t staging;
+  int32_t max_query_group;
 } pkv_tuning;
 
 pkv_status pkv_set_tuning(const pkv_tuning* tuning);

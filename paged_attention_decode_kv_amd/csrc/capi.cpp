@@ -286,6 +286,7 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
   a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
   a.target_items = 0;
   a.deal_static = 1;
+  a.query_group = 1;
   a.scale = scale;
   const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads,
                                                  pool->head_dim, max_blocks_per_row,
@@ -305,10 +306,11 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
 pkv_status pkv_set_tuning(const pkv_tuning* t) {
   if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
   if (!pkv::set_tuning(t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group,
-                       t->deal, t->staging))
+                       t->deal, t->staging, t->max_query_group))
     return fail(PKV_ERR_UNSUPPORTED, "tuning chunk [%d, %d], waves %d, items/group %d, "
-                "deal %d, staging %d not supported", t->chunk_min, t->chunk_max,
-                t->decode_waves, t->items_per_group, t->deal, t->staging);
+                "deal %d, staging %d, query group %d not supported", t->chunk_min,
+                t->chunk_max, t->decode_waves, t->items_per_group, t->deal, t->staging,
+                t->max_query_group);
   return ok();
 }
 
@@ -320,6 +322,7 @@ pkv_status pkv_get_tuning(pkv_tuning* t) {
   t->items_per_group = pkv::tuning_items_per_group();
   t->deal = pkv::tuning_deal_static() ? 1 : 2;
   t->staging = pkv::tuning_lds_stage() ? 2 : 1;
+  t->max_query_group = pkv::tuning_max_query_group();
   return ok();
 }
 

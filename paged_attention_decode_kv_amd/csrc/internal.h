@@ -21,6 +21,7 @@ constexpr int kDefaultDecodeWaves = 8;
 constexpr int kDefaultItemsPerGroup = 16;
 constexpr int kDefaultDealStatic = 1;
 constexpr int kDefaultLdsStage = 1;
+constexpr int kDefaultMaxQueryGroup = 8;
 
 int tuning_chunk_min();
 int tuning_chunk_max();
@@ -28,8 +29,9 @@ int tuning_decode_waves();
 int tuning_items_per_group();
 int tuning_deal_static();
 int tuning_lds_stage();
+int tuning_max_query_group();
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal, int staging);
+                int deal, int staging, int max_query_group);
 
 // Pool geometry in elements, derived from the descriptor.
 struct PoolGeom {
@@ -80,6 +82,7 @@ struct AttnArgs {
   int32_t log2_chunk_max;
   int32_t target_items;    // items the plan aims for (set by the launcher)
   int32_t deal_static;     // 1: whole rounds of full chunks are dealt without the queue
+  int32_t query_group;     // query heads per work item (they share one KV head)
   float scale;
 };
 

@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
   __syncthreads();
   int lp = lmin;
   for (int k = ncand - 1; k >= 0; --k) {
-    if ((int64_t)s_cand[k] * a.num_heads >= a.target_items) {
+    if ((int64_t)s_cand[k] * (a.num_heads / a.query_group) >= a.target_items) {
       lp = lmin + k;
       break;
     }
@@ -345,39 +345,45 @@ struct Shape {
   static_assert(kMaxChunkTokens / 16 <= 128, "block ids of a chunk: two per lane");
 };
 
-// Everything a work item needs before its first K/V load.
+// Everything a work item needs before its first K/V load.  An item is (row, chunk of
+// the row's history, group of QG query heads that share one KV head).
+template <int QG>
 struct ItemMeta {
-  int r, h, chunk, nch, ctx;
-  uint4 q;       // this lane's 16 bytes of the query
+  int r, hg, chunk, nch, ctx;   // hg: query-head group; heads hg*QG .. hg*QG + QG - 1
+  uint4 q[QG];   // this lane's 16 bytes of each head's query
   int blk;       // lane i: block id of the chunk's i-th block
   int blk_hi;    // lane i: block id of the chunk's (64 + i)-th block
 };
 
 // First half of fetching an item's metadata: the work-list entry load is issued and
 // its value is not consumed, so no wait is inserted here.
-__device__ __forceinline__ int4 issue_entry(const Workspace& ws, int item, int heads) {
-  return ws.entries[item / heads];
+__device__ __forceinline__ int4 issue_entry(const Workspace& ws, int item, int groups) {
+  return ws.entries[item / groups];
 }
 
 // Second half: the entry becomes wave-uniform and the query and block-id loads are
 // issued (they complete while the current item finishes).
-template <typename T, int D>
-__device__ __forceinline__ ItemMeta finish_meta(const AttnArgs& a, int4 ent, int item,
-                                                int lp, int log2_bs, int lane, int sub) {
+template <typename T, int D, int QG>
+__device__ __forceinline__ ItemMeta<QG> finish_meta(const AttnArgs& a, int4 ent, int item,
+                                                    int lp, int log2_bs, int lane, int sub) {
   constexpr int E = Elem<T>::kPerLane;
-  ItemMeta m;
-  const int e = item / a.num_heads;
-  m.h = item - e * a.num_heads;
+  const int groups = a.num_heads / QG;
+  ItemMeta<QG> m;
+  const int e = item / groups;
+  m.hg = item - e * groups;
   m.r = __builtin_amdgcn_readfirstlane(ent.x);
   m.chunk = __builtin_amdgcn_readfirstlane(ent.y);
   m.nch = __builtin_amdgcn_readfirstlane(ent.z);
   m.ctx = __builtin_amdgcn_readfirstlane(ent.w);
-  m.q = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < QG; ++j) m.q[j] = make_uint4(0, 0, 0, 0);
   m.blk = 0;
   m.blk_hi = 0;
   if (m.chunk >= 0) {
-    const int64_t rh = (int64_t)m.r * a.num_heads + m.h;
-    m.q = load16(static_cast<const T*>(a.q) + rh * D + sub * E);
+    const int64_t rh = (int64_t)m.r * a.num_heads + (int64_t)m.hg * QG;
+#pragma unroll
+    for (int j = 0; j < QG; ++j)
+      m.q[j] = load16(static_cast<const T*>(a.q) + (rh + j) * D + sub * E);
     const int t_begin = m.chunk << lp;
     const int t_end = min(m.ctx, t_begin + (1 << lp));
     const int j0 = t_begin >> log2_bs;
@@ -413,9 +419,10 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
 }
 
 // The decode read.  Persistent workgroups process work items; an item is (chunk of a
-// row's history, query head), and the waves of a workgroup share it, wave w folding
-// sub-chunks w, w + WAVES, ... into its own online-softmax state before the waves are
-// merged through LDS.
+// row's history, group of QG query heads sharing one KV head), and the waves of a
+// workgroup share it, wave w folding sub-chunks w, w + WAVES, ... into its own
+// online-softmax state of every head of the group before the waves are merged through
+// LDS.  With grouped-query attention one K/V load serves QG query heads.
 //
 // Schedule: whole rounds of the full chunks (section A, all the same length) are
 // dealt round robin, workgroup g taking items g, g + G, g + 2G, ...; the rest of A and
@@ -423,11 +430,12 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
 // counter, so the uneven tail is balanced dynamically with few atomics; padding rows
 // (section C) are zeroed round robin at the end.  The next item's metadata and the
 // ticket after it are fetched while the current item streams.
-template <typename T, int D, int WAVES, bool LDS_STAGE>
+template <typename T, int D, int WAVES, bool LDS_STAGE, int QG>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using S = Shape<T, D>;
   using El = Elem<T>;
+  using Meta = ItemMeta<QG>;
   constexpr int E = S::E, LPT = S::LPT, TPS = S::TPS, U = S::U, CH = S::CH;
   constexpr int ES = sizeof(T);
   const int lane = threadIdx.x & 63;
@@ -442,16 +450,17 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   constexpr int kStageLoads = LDS_STAGE ? 2 * U : 1;
   __shared__ __attribute__((aligned(16))) uint4 s_stage[kStageWaves][kStageLoads][64];
   __shared__ int s_ticket[2];
-  __shared__ float s_m[2][WAVES], s_l[2][WAVES];
-  __shared__ float s_acc[2][WAVES][D];
+  __shared__ float s_m[2][QG][WAVES], s_l[2][QG][WAVES];
+  __shared__ float s_acc[2][QG][WAVES][D];
 
   const int heads = a.num_heads;
-  const int group = heads / a.g.kv_heads;
+  const int groups = heads / QG;              // items per work-list entry
+  const int qpkv = heads / a.g.kv_heads;      // query heads per KV head
   const int lp = ws.counters[3];
   const int P = 1 << lp;
-  const int n_static = ws.counters[4] * heads;    // section A items
-  const int n_data = ws.counters[5] * heads;      // sections A and B
-  const int n_items = ws.counters[0] * heads;
+  const int n_static = ws.counters[4] * groups;   // section A items
+  const int n_data = ws.counters[5] * groups;     // sections A and B
+  const int n_items = ws.counters[0] * groups;
   const int G = gridDim.x;
   const int n_dealt = a.deal_static ? n_static / G * G : 0;
   const int log2_bs = a.g.log2_bs;
@@ -495,9 +504,9 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   }
   int buf = 0;
   bool bad_block = false;   // a live block id outside [0, num_blocks) was skipped
-  ItemMeta cur;
+  Meta cur;
   if (item < n_data)
-    cur = finish_meta<T, D>(a, issue_entry(ws, item, heads), item, lp, log2_bs, lane, sub);
+    cur = finish_meta<T, D, QG>(a, issue_entry(ws, item, groups), item, lp, log2_bs, lane, sub);
 
   while (item < n_data) {
     // the item after next: static, or a ticket whose value is needed only at the end
@@ -505,20 +514,24 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     const bool after_static = take(after);
     if (!after_static && threadIdx.x == 0) after = atomicAdd(&ws.counters[1], 1);
     int4 next_ent = make_int4(0, -1, 0, 0);
-    if (next < n_data) next_ent = issue_entry(ws, next, heads);
+    if (next < n_data) next_ent = issue_entry(ws, next, groups);
 
     // (the item's fields are wave-uniform; saying so keeps the load descriptors scalar)
     const int chunk = __builtin_amdgcn_readfirstlane(cur.chunk);
+    const int hg = __builtin_amdgcn_readfirstlane(cur.hg);
     const int t_begin = chunk * P;
     const int t_end = min(__builtin_amdgcn_readfirstlane(cur.ctx), t_begin + P);
     const int j0 = t_begin >> log2_bs;
-    const int64_t head_off =
-        (int64_t)(__builtin_amdgcn_readfirstlane(cur.h) / group) * head_bytes;
+    const int64_t head_off = (int64_t)(hg * QG / qpkv) * head_bytes;
 
-    float m = -INFINITY, l = 0.f;
-    float acc[E];
+    float m[QG], l[QG], acc[QG][E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) acc[i] = 0.f;
+    for (int j = 0; j < QG; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[j][i] = 0.f;
+    }
 
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
     // Descriptors of sub-chunk s's K and V: they end after its valid tokens, so the
@@ -575,98 +588,113 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
           vr[u] = buffer_load16(vsrc, voff[u]);
         }
       }
-      float sc[U];
-      float smax = -INFINITY;
+      // fold the sub-chunk into every head of the group: one K/V load, QG heads
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float d = group_sum<LPT>(El::dot(cur.q, kr[u], 0.f));
-        sc[u] = u * TPS + g < nvalid ? d * scale_log2 : -INFINITY;
-        smax = fmaxf(smax, sc[u]);
+      for (int j = 0; j < QG; ++j) {
+        float sc[U];
+        float smax = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float d = group_sum<LPT>(El::dot(cur.q[j], kr[u], 0.f));
+          sc[u] = u * TPS + g < nvalid ? d * scale_log2 : -INFINITY;
+          smax = fmaxf(smax, sc[u]);
+        }
+        const float m_new = fmaxf(m[j], smax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m[j] - m_use);
+        l[j] *= alpha;
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[j][i] *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float p = __builtin_amdgcn_exp2f(sc[u] - m_use);
+          l[j] += p;
+          El::axpy(p, vr[u], acc[j]);
+        }
+        m[j] = m_new;
       }
-      const float m_new = fmaxf(m, smax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < E; ++i) acc[i] *= alpha;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float p = __builtin_amdgcn_exp2f(sc[u] - m_use);
-        l += p;
-        El::axpy(p, vr[u], acc);
-      }
-      m = m_new;
     }
 
     // the next item's query and block ids load while this item's state is merged
-    const ItemMeta nxt = finish_meta<T, D>(a, next_ent, next, lp, log2_bs, lane, sub);
+    const Meta nxt = finish_meta<T, D, QG>(a, next_ent, next, lp, log2_bs, lane, sub);
 
-    // merge the lane groups of this wave
+    // merge the lane groups of this wave, head by head
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-      const float m_o = __shfl_xor(m, off);
-      const float l_o = __shfl_xor(l, off);
-      const float mx = fmaxf(m, m_o);
-      const float mu = mx == -INFINITY ? 0.f : mx;
-      const float fa = __builtin_amdgcn_exp2f(m - mu);
-      const float fb = __builtin_amdgcn_exp2f(m_o - mu);
-      l = l * fa + l_o * fb;
+    for (int j = 0; j < QG; ++j) {
 #pragma unroll
-      for (int i = 0; i < E; ++i) acc[i] = acc[i] * fa + __shfl_xor(acc[i], off) * fb;
-      m = mx;
+      for (int off = LPT; off < 64; off <<= 1) {
+        const float m_o = __shfl_xor(m[j], off);
+        const float l_o = __shfl_xor(l[j], off);
+        const float mx = fmaxf(m[j], m_o);
+        const float mu = mx == -INFINITY ? 0.f : mx;
+        const float fa = __builtin_amdgcn_exp2f(m[j] - mu);
+        const float fb = __builtin_amdgcn_exp2f(m_o - mu);
+        l[j] = l[j] * fa + l_o * fb;
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[j][i] = acc[j][i] * fa + __shfl_xor(acc[j][i], off) * fb;
+        m[j] = mx;
+      }
     }
-    // merge the waves into wave 0 (LDS double-buffered by item parity: one barrier)
-    const bool writer = wave == 0 && g == 0;
+    // merge the waves (LDS double-buffered by item parity: one barrier); wave w merges
+    // and writes heads w, w + WAVES, ... of the group
     if constexpr (WAVES > 1) {
       if (g == 0) {
 #pragma unroll
-        for (int i = 0; i < E; ++i) s_acc[buf][wave][sub * E + i] = acc[i];
-        if (sub == 0) {
-          s_m[buf][wave] = m;
-          s_l[buf][wave] = l;
+        for (int j = 0; j < QG; ++j) {
+#pragma unroll
+          for (int i = 0; i < E; ++i) s_acc[buf][j][wave][sub * E + i] = acc[j][i];
+          if (sub == 0) {
+            s_m[buf][j][wave] = m[j];
+            s_l[buf][j][wave] = l[j];
+          }
         }
       }
     }
     if (!after_static && threadIdx.x == 0) s_ticket[buf] = after;
     __syncthreads();
     if (!after_static) after = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[buf]);
-    if constexpr (WAVES > 1) {
-      if (writer) {
-        float mx = s_m[buf][0];
+    if (g == 0) {
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[buf][w]);
-        l = 0.f;
+      for (int j = 0; j < QG; ++j) {
+        if (j % WAVES != wave) continue;
+        float mj = m[j], lj = l[j], aj[E];
 #pragma unroll
-        for (int i = 0; i < E; ++i) acc[i] = 0.f;
+        for (int i = 0; i < E; ++i) aj[i] = acc[j][i];
+        if constexpr (WAVES > 1) {
+          float mx = s_m[buf][j][0];
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-          const float f = __builtin_amdgcn_exp2f(s_m[buf][w] - mx);   // mx is finite here
-          l += s_l[buf][w] * f;
+          for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[buf][j][w]);
+          lj = 0.f;
 #pragma unroll
-          for (int i = 0; i < E; ++i) acc[i] += s_acc[buf][w][sub * E + i] * f;
+          for (int i = 0; i < E; ++i) aj[i] = 0.f;
+#pragma unroll
+          for (int w = 0; w < WAVES; ++w) {
+            const float f = __builtin_amdgcn_exp2f(s_m[buf][j][w] - mx);   // mx is finite
+            lj += s_l[buf][j][w] * f;
+#pragma unroll
+            for (int i = 0; i < E; ++i) aj[i] += s_acc[buf][j][w][sub * E + i] * f;
+          }
+          mj = mx;
         }
-        m = mx;
-      }
-    }
-    if (writer) {
-      const int64_t rh = (int64_t)cur.r * heads + cur.h;
-      if (cur.nch == 1) {
-        const float inv = 1.0f / l;
+        const int64_t rh = (int64_t)cur.r * heads + (int64_t)hg * QG + j;
+        if (cur.nch == 1) {
+          const float inv = 1.0f / lj;
 #pragma unroll
-        for (int i = 0; i < E; ++i) acc[i] *= inv;
-        store16(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(acc));
-      } else {
-        float* rec = ws.partials + (rh * ws.max_chunks + chunk) * (D + 4);
-        if (sub == 0) {
-          rec[0] = m;
-          rec[1] = l;
+          for (int i = 0; i < E; ++i) aj[i] *= inv;
+          store16(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(aj));
+        } else {
+          float* rec = ws.partials + (rh * ws.max_chunks + chunk) * (D + 4);
+          if (sub == 0) {
+            rec[0] = mj;
+            rec[1] = lj;
+          }
+#pragma unroll
+          for (int i = 0; i < E; i += 4)
+            store16(rec + 4 + sub * E + i, make_uint4(__float_as_uint(aj[i]),
+                                                      __float_as_uint(aj[i + 1]),
+                                                      __float_as_uint(aj[i + 2]),
+                                                      __float_as_uint(aj[i + 3])));
         }
-#pragma unroll
-        for (int i = 0; i < E; i += 4)
-          store16(rec + 4 + sub * E + i, make_uint4(__float_as_uint(acc[i]),
-                                                    __float_as_uint(acc[i + 1]),
-                                                    __float_as_uint(acc[i + 2]),
-                                                    __float_as_uint(acc[i + 3])));
       }
     }
     buf ^= 1;
@@ -677,12 +705,17 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   if (bad_block && lane == 0) atomicOr(&g_status, PKV_DEVERR_BLOCK_ID);
   // padding rows: zero output, nothing read
   for (int it = n_data + (int)blockIdx.x; it < n_items; it += G) {
-    const int e = it / heads;
-    const int h = it - e * heads;
+    const int e = it / groups;
+    const int hgp = it - e * groups;
     const int r = ws.entries[e].x;
-    if (wave == 0 && g == 0)
-      store16(static_cast<T*>(a.out) + ((int64_t)r * heads + h) * D + sub * E,
-              make_uint4(0, 0, 0, 0));
+    if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < QG; ++j)
+        if (j % WAVES == wave)
+          store16(static_cast<T*>(a.out) + ((int64_t)r * heads + (int64_t)hgp * QG + j) * D +
+                      sub * E,
+                  make_uint4(0, 0, 0, 0));
+    }
   }
 }
 
@@ -830,9 +863,9 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int WAVES, bool LDS_STAGE>
+template <typename T, int D, int WAVES, bool LDS_STAGE, int QG>
 static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
-  auto kern = decode_kernel<T, D, WAVES, LDS_STAGE>;
+  auto kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
   static int per_cu[64] = {0};   // occupancy per device, computed once
   static int num_cu[64] = {0};
   int dev = 0;
@@ -851,9 +884,10 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
   int64_t grid = (int64_t)num_cu[dev] * per_cu[dev];
-  const int64_t most = ws.max_entries * a.num_heads;
+  const int64_t most = ws.max_entries * (a.num_heads / QG);
   if (grid > most) grid = most;
   AttnArgs pa = a;
+  pa.query_group = QG;
   pa.target_items = (int32_t)(grid * tuning_items_per_group());
   pa.deal_static = tuning_deal_static();
   timing_begin(PKV_PHASE_PLAN, stream);
@@ -872,22 +906,42 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   return hipGetLastError();
 }
 
+// query heads per work item: the largest of 8, 4, 2, 1 that divides the number of query
+// heads per KV head and is at most the tuning cap (4 for head_dim 256, whose per-head
+// merge buffers would not fit in LDS beside the K/V stages at 8)
+static int query_group_of(const AttnArgs& a) {
+  const int qpkv = a.num_heads / a.g.kv_heads;
+  int cap = tuning_max_query_group();
+  if (a.g.head_dim >= 256 && cap > 4) cap = 4;
+  for (int qg = 8; qg > 1; qg >>= 1)
+    if (qg <= cap && qpkv % qg == 0) return qg;
+  return 1;
+}
+
 template <typename T, int D>
 static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws,
                                   hipStream_t stream) {
+  switch (query_group_of(a)) {
+    case 8:
+      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream);
+      break;
+    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, stream);
+    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, stream);
+    default: break;
+  }
   if (tuning_lds_stage()) {
     switch (tuning_decode_waves()) {
-      case 1: return launch_decode_w<T, D, 1, true>(a, ws, stream);
-      case 2: return launch_decode_w<T, D, 2, true>(a, ws, stream);
-      case 8: return launch_decode_w<T, D, 8, true>(a, ws, stream);
-      default: return launch_decode_w<T, D, 4, true>(a, ws, stream);
+      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, stream);
+      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, stream);
+      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, stream);
+      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, stream);
     }
   }
   switch (tuning_decode_waves()) {
-    case 1: return launch_decode_w<T, D, 1, false>(a, ws, stream);
-    case 2: return launch_decode_w<T, D, 2, false>(a, ws, stream);
-    case 8: return launch_decode_w<T, D, 8, false>(a, ws, stream);
-    default: return launch_decode_w<T, D, 4, false>(a, ws, stream);
+    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, stream);
+    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, stream);
+    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, stream);
+    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, stream);
   }
 }
 

@@ -94,6 +94,7 @@ std::atomic<int> g_decode_waves{kDefaultDecodeWaves};
 std::atomic<int> g_items_per_group{kDefaultItemsPerGroup};
 std::atomic<int> g_deal_static{kDefaultDealStatic};
 std::atomic<int> g_lds_stage{kDefaultLdsStage};
+std::atomic<int> g_max_query_group{kDefaultMaxQueryGroup};
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 }  // namespace
@@ -104,9 +105,10 @@ int tuning_decode_waves() { return g_decode_waves.load(std::memory_order_relaxed
 int tuning_items_per_group() { return g_items_per_group.load(std::memory_order_relaxed); }
 int tuning_deal_static() { return g_deal_static.load(std::memory_order_relaxed); }
 int tuning_lds_stage() { return g_lds_stage.load(std::memory_order_relaxed); }
+int tuning_max_query_group() { return g_max_query_group.load(std::memory_order_relaxed); }
 
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal, int staging) {
+                int deal, int staging, int max_query_group) {
   const int lo = chunk_min ? chunk_min : tuning_chunk_min();
   const int hi = chunk_max ? chunk_max : tuning_chunk_max();
   if (!pow2_in(lo, kMinChunkTokens, kMaxChunkTokens) ||
@@ -119,6 +121,10 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
   if (deal < 0 || deal > 2) return false;
   if (staging < 0 || staging > 2) return false;
   if (staging != 0) g_lds_stage.store(staging == 2 ? 1 : 0);
+  if (max_query_group != 0 && max_query_group != 1 && max_query_group != 2 &&
+      max_query_group != 4 && max_query_group != 8)
+    return false;
+  if (max_query_group != 0) g_max_query_group.store(max_query_group);
   if (deal != 0) g_deal_static.store(deal == 1 ? 1 : 0);
   g_chunk_min.store(lo);
   g_chunk_max.store(hi);

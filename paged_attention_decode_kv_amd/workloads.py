@@ -176,21 +176,34 @@ def _lognormal_lens(rng, n, median, sigma, hi):
 # --------------------------------------------------------------------------- #
 # the five named configurations
 # --------------------------------------------------------------------------- #
-def make_config(index: int, layout: str = "HND") -> Workload:
-    """Build configuration ``index`` (1..5) with seed = index."""
+def make_config(index: int, layout: str = "HND", kv_heads: int | None = None) -> Workload:
+    """Build configuration ``index`` (1..5) with seed = index.
+
+    ``kv_heads`` gives the grouped-query variant of a configuration: the same lengths,
+    placement and query heads, with fewer KV heads (query head h reads KV head
+    h // (heads // kv_heads)); the pool shrinks by heads / kv_heads.  The named
+    configurations themselves have kv_heads == heads."""
+    w = _make_config(index, layout, kv_heads)
+    if kv_heads is not None:
+        w.name = f"{w.name}-gqa{w.heads // w.kv_heads}"
+    return w
+
+
+def _make_config(index, layout, kv_heads_override):
     seed = int(index)
     rng = np.random.default_rng(seed)
     name = CONFIG_NAMES[index]
     bs = 16
     if index == 1:
         lens = [16, 40]
-        return _finish(name, seed, rng, lens, heads=4, kv_heads=4, head_dim=64,
+        return _finish(name, seed, rng, lens, heads=4, kv_heads=kv_heads_override or 4,
+                       head_dim=64,
                        block_size=bs, dtype="f32", layout=layout, num_blocks=8,
                        max_blocks=3)
     if index == 2:
         lens = [2048] * 8
         nb = sum(cdiv(c, bs) for c in lens)
-        return _finish(name, seed, rng, lens, heads=32, kv_heads=32, head_dim=128,
+        return _finish(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
                        block_size=bs, dtype="bf16", layout=layout, num_blocks=nb,
                        max_blocks=2048 // bs)
     if index == 3:
@@ -199,14 +212,14 @@ def make_config(index: int, layout: str = "HND") -> Workload:
         lens = np.zeros(34, dtype=np.int64)
         lens[np.setdiff1d(np.arange(34), pads)] = live
         nb = math.ceil(1.2 * sum(cdiv(c, bs) for c in lens))
-        return _finish(name, seed, rng, lens, heads=32, kv_heads=32, head_dim=128,
+        return _finish(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
                        block_size=bs, dtype="bf16", layout=layout, num_blocks=nb,
                        max_blocks=8192 // bs, meta={"pad_rows": pads.tolist()})
     if index == 4:
         lens = _lognormal_lens(rng, 256, 256, 1.0, 2048)
         forced = int(rng.integers(256))
         lens[forced] = 2048
-        return _finish(name, seed, rng, lens, heads=32, kv_heads=32, head_dim=128,
+        return _finish(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
                        block_size=bs, dtype="bf16", layout=layout,
                        num_blocks=256 * 2048 // bs, max_blocks=2048 // bs,
                        meta={"forced_row": forced})
@@ -214,7 +227,7 @@ def make_config(index: int, layout: str = "HND") -> Workload:
         body = _lognormal_lens(rng, 232, 1024, 1.2, 8192)
         lens = np.concatenate([body, np.full(8, 8192), np.zeros(16, dtype=np.int64)])
         lens = lens[rng.permutation(256)]
-        return _finish(name, seed, rng, lens, heads=32, kv_heads=32, head_dim=128,
+        return _finish(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
                        block_size=bs, dtype="bf16", layout=layout,
                        num_blocks=256 * 8192 // bs, max_blocks=8192 // bs)
     raise ValueError(f"no configuration {index}")

@@ -396,4 +396,49 @@ def test_work_split_variants(tuning):
                                seed=77)
             check_full(w)
     finally:
-        binding.set_tuning(**{k: v for k, v in before.items()})
+        binding.set_tuning(**before)
+
+
+GQA_CASES = [
+    # lens, heads, kv_heads, head_dim, dtype, layout: query groups 8, 4, 2 and 16 (two items)
+    ([700, 1, 0, 2049, 31], 16, 2, 128, "bf16", "HND"),
+    ([700, 1, 0, 2049, 31], 16, 2, 128, "f32", "NHD"),
+    ([513, 64, 1000], 32, 8, 64, "bf16", "HND"),
+    ([257, 5], 8, 4, 256, "f32", "HND"),
+    ([300, 90], 32, 2, 128, "bf16", "NHD"),
+    ([130, 2500], 16, 4, 256, "bf16", "HND"),
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=lambda c: f"{c[4]}-{c[5]}-d{c[3]}-h{c[1]}/{c[2]}")
+@pytest.mark.parametrize("max_group", [8, 1])
+def test_grouped_query_heads(case, max_group):
+    """Grouped-query attention: one K/V load serves up to 8 query heads (max_group 8) or
+    one (max_group 1); both match the oracle."""
+    lens, h, hkv, d, dtype, layout = case
+    before = binding.get_tuning()
+    binding.set_tuning(max_query_group=max_group)
+    try:
+        w = wl.make_custom(lens, heads=h, kv_heads=hkv, head_dim=d, dtype=dtype,
+                           layout=layout, seed=sum(lens) + h)
+        check_full(w)
+    finally:
+        binding.set_tuning(**before)
+
+
+@pytest.mark.parametrize("kv_heads", [8, 4])
+def test_config5_grouped_variant_sampled(kv_heads):
+    """The full-width batch with 32 query heads over 8 or 4 KV heads, sampled rows."""
+    w = wl.make_config(5, kv_heads=kv_heads)
+    say(f"{w.name}: building {w.pool_bytes / 1e9:.1f} GB of pools on the device")
+    st = Step(w, host_history=False)
+    out = st.run()
+    lens = w.context_lens
+    full = np.nonzero(lens == 8192)[0]
+    short = np.nonzero((lens > 0) & (lens <= 256))[0]
+    rows = sorted({int(full[0]), int(short[0]), int(w.pad_rows[0]), 3, 77})
+    ref = oracle_rows(st, rows)
+    err = assert_close(to_host(out, w.dtype)[rows], ref, w.dtype, w.name)
+    say(f"{w.name}: sampled max err {err:.3e}")
+    del st
+    torch.cuda.empty_cache()
