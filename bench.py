@@ -10,8 +10,11 @@ a 131072-block pool (~34 GB of K+V).  Every input is resident in HBM before timi
 
 Prints one JSON line on stdout.  ``value`` is KV GB/s: the bytes of K and V the read
 must stream (every live (row, KV head, position) once) divided by the wall-clock time
-per step.  ``roofline`` reports the decode kernel alone, timed with HIP events on its
-launch stream over the same timed steps, against MI355X's 8 TB/s HBM peak.
+per step.  The step is timed twice over the same tensors: as the two library calls
+per step (eager), and as replays of one HIP graph recorded from those calls (graph, the
+default ``value``; ``--launch eager`` reports the other).  ``roofline`` reports the
+decode kernel alone, timed with HIP events on its launch stream over the eager steps,
+against MI355X's 8 TB/s HBM peak.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
 """
 
@@ -62,6 +65,10 @@ def parse():
                     help="query heads sharing one K/V load under GQA (0: default)")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="override the workload's KV heads (grouped-query variant)")
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="graph (default): time the two library calls per step, then replays "
+                         "of one HIP graph recorded from them, and report the replays as "
+                         "value; eager: time and report the library calls only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
@@ -262,10 +269,30 @@ def main():
     t1 = time.perf_counter()
     phases = {ph: binding.timing_read(ph, reset=True) for ph in _capi.PHASES}
     binding.timing_enable(False)
+    eager_s = (t1 - t0) / args.steps
+
+    # the same step recorded once into a HIP graph over the same tensors, then replayed:
+    # identical kernels and arguments, without a host launch per kernel
+    graph_s = None
+    if args.launch == "graph":
+        graph = binding.capture_step(k_new, v_new, slots, q, k_cache, v_cache, tables, lens,
+                                     w.scale, out, ws, layout=w.layout)
+        for _ in range(args.warmup):
+            graph.launch()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.launch()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        graph_s = (t1 - t0) / args.steps
+        graph.destroy()
     flags = binding.device_status(dev, clear=True)
     if flags:
         raise SystemExit(f"kernels clamped or skipped inputs (status bits {flags}); "
                          "the measurement is invalid")
+    log(f"step: eager {eager_s * 1e3:.4f} ms" +
+        (f", graph replay {graph_s * 1e3:.4f} ms" if graph_s else ""))
 
     if args.copy_calibration:
         # an elementwise kernel that reads 1 GiB and writes 1 GiB (torch's vectorized
@@ -278,7 +305,7 @@ def main():
         log("ran 3 elementwise multiplies over 1 GiB (1073741824 B read + written each)")
         del a, b
 
-    step_s = (t1 - t0) / args.steps
+    step_s = graph_s if args.launch == "graph" else eager_s
     elem = 2 if w.dtype == "bf16" else 4
     b = acc.algorithmic_bytes(w.context_lens, heads=w.heads, kv_heads=w.kv_heads,
                               head_dim=w.head_dim, block_size=w.block_size, elem=elem,
@@ -328,8 +355,11 @@ def main():
             "width": w.max_blocks * w.block_size,
             "layout": w.layout,
             "tuning": tuning,
+            "launch": args.launch,
             "parallelism": "single GPU",
         },
+        "eager_ms_per_step": round(eager_s * 1e3, 4),
+        "graph_ms_per_step": round(graph_s * 1e3, 4) if graph_s else None,
         "hbm_frac": round(b["total"] / step_s / 1e9 / HBM_PEAK_GBPS, 4),
         "total_algorithmic_GBps": round(b["total"] / step_s / 1e9, 2),
         "row_heads_per_s": round(rh / step_s, 1),

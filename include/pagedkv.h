@@ -219,6 +219,38 @@ typedef enum pkv_phase {
 pkv_status pkv_timing_enable(int32_t on);
 pkv_status pkv_timing_read(int32_t phase, double* total_ms, int64_t* launches, int32_t reset);
 
+/* A captured decode step: kv_write followed by paged_attention, recorded once into a
+ * HIP graph over fixed buffers and replayed for every later step whose inputs are
+ * written into those same buffers (Day 55, "Why it matters": a recording made over an
+ * all-padding batch computes real steps because every argument it keeps is storage
+ * that each step writes through).
+ *   Arguments are those of pkv_kv_write and pkv_paged_attention for one decode step,
+ *   one new token per row: k, v [num_rows][num_kv_heads][head_dim], slot_mapping
+ *   [num_rows] int64.  Every pointer is kept by the graph and must stay valid, at the
+ *   same address, until pkv_graph_destroy; the workspace too.  Nothing is read or run
+ *   while capturing, so the buffers may hold anything then.
+ *   Each launch reads the buffers' contents at that moment, with validate = 0
+ *   semantics: no host checks; bad lengths are clamped, bad block ids and slots
+ *   skipped, and each raises its bit in the device status word.  A padding row
+ *   (context_lens 0, slot_mapping the sink) reads nothing and writes only the sink.
+ *   The tuning in force at capture time is frozen into the graph.
+ * Capture uses a private stream and needs no synchronisation of the caller's streams.
+ * pkv_graph_launch enqueues one replay on `stream`, which must belong to the device that
+ * was current at capture; replays of graphs sharing buffers must be ordered (one
+ * stream).  pkv_graph_destroy(NULL) is a no-op.  Capture fails with the same refusals
+ * as the two calls' shape checks, or HIP if the runtime refuses the capture. */
+typedef struct pkv_step_graph pkv_step_graph;
+
+pkv_status pkv_graph_capture(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
+                             const void* k, const void* v, const int64_t* slot_mapping,
+                             void* out, const void* q, const int32_t* block_tables,
+                             int32_t max_blocks_per_row, const int32_t* context_lens,
+                             int64_t num_rows, int32_t num_heads, float scale,
+                             void* workspace, size_t workspace_bytes,
+                             pkv_step_graph** graph);
+pkv_status pkv_graph_launch(const pkv_step_graph* graph, void* stream);
+pkv_status pkv_graph_destroy(pkv_step_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,10 @@ SIGNATURES = {
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double),
                                ctypes.POINTER(ctypes.c_int64), _i32]),
+    "pkv_graph_capture": (_i32, [_PD, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32,
+                                 _f, _p, _sz, ctypes.POINTER(ctypes.c_void_p)]),
+    "pkv_graph_launch": (_i32, [_p, _p]),
+    "pkv_graph_destroy": (_i32, [_p]),
 }
 PHASES = {"kv_write": 0, "plan": 1, "decode": 2, "combine": 3}
 

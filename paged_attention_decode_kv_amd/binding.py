@@ -161,6 +161,75 @@ def paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     return out
 
 
+class StepGraph:
+    """One captured decode step (pkv_graph_capture): kv_write then paged_attention over
+    the tensors it was captured with, replayed by ``launch``.  Holds references to those
+    tensors so their storage outlives the graph."""
+
+    def __init__(self, handle: ctypes.c_void_p, device: torch.device, keep: tuple):
+        self._handle = handle
+        self.device = device
+        self._keep = keep
+
+    def launch(self, stream=None) -> None:
+        if self._handle is None:
+            _raise("NULL", "graph already destroyed")
+        s = torch.cuda.current_stream(self.device) if stream is None else stream
+        with torch.cuda.device(self.device):
+            _check(_capi.lib().pkv_graph_launch(self._handle, ctypes.c_void_p(s.cuda_stream)))
+
+    def destroy(self) -> None:
+        if self._handle is not None:
+            handle, self._handle = self._handle, None
+            _check(_capi.lib().pkv_graph_destroy(handle))
+            self._keep = ()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def capture_step(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                 q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                 out: torch.Tensor, workspace: torch.Tensor, *,
+                 layout: str = "HND") -> StepGraph:
+    """Record kv_write + paged_attention over these tensors into a graph; nothing runs."""
+    rows = int(context_lens.shape[0]) if context_lens.dim() == 1 else 0
+    if rows == 0:
+        _raise("EMPTY", "no rows")
+    desc = _pool_pair(k_cache, v_cache, layout)
+    dev = k_cache.device
+    for t, name in ((k, "k"), (v, "v"), (q, "q"), (out, "out")):
+        _device_tensor(t, name, k_cache.dtype, dev)
+    _device_tensor(slot_mapping, "slot_mapping", torch.int64, dev)
+    _device_tensor(block_tables, "block_tables", torch.int32, dev)
+    _device_tensor(context_lens, "context_lens", torch.int32, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        _raise("WORKSPACE", "workspace must be a contiguous tensor on the pool's device")
+    kv_shape = (rows, desc.num_kv_heads, desc.head_dim)
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape or \
+            tuple(slot_mapping.shape) != (rows,):
+        _raise("SHAPE", f"k, v must be {kv_shape}, slot_mapping [{rows}]")
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[2] != desc.head_dim or \
+            out.shape != q.shape:
+        _raise("SHAPE", f"q and out must be [{rows}, heads, {desc.head_dim}]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != rows:
+        _raise("SHAPE", "block_tables must be [rows, max_blocks]")
+    handle = ctypes.c_void_p()
+    with torch.cuda.device(dev):
+        _check(_capi.lib().pkv_graph_capture(
+            ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k), _ptr(v),
+            _ptr(slot_mapping), _ptr(out), _ptr(q), _ptr(block_tables),
+            int(block_tables.shape[1]), _ptr(context_lens), rows, int(q.shape[1]),
+            float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            ctypes.byref(handle)))
+    return StepGraph(handle, dev, (k, v, slot_mapping, q, k_cache, v_cache, block_tables,
+                                   context_lens, out, workspace))
+
+
 def device_status(device=None, clear: bool = True) -> int:
     """Bitwise OR of the device-side refusal bits raised since the last clear."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device

@@ -136,6 +136,59 @@ pkv_status check_write_data(const pkv_pool_desc* pool, const int64_t* slots, int
   return PKV_OK;
 }
 
+
+// Work items of one call at the shortest chunk; the plan indexes them in 32 bits.
+pkv_status check_attention_items(const pkv_pool_desc* pool, int32_t max_blocks,
+                                 int64_t num_rows, int32_t num_heads) {
+  const int64_t most_items = num_rows * ((int64_t)max_blocks * pool->block_size /
+                                         pkv::tuning_chunk_min() + 1) * num_heads;
+  if (most_items > (int64_t{1} << 30))
+    return fail(PKV_ERR_UNSUPPORTED, "rows x heads x chunks too large for one call");
+  return PKV_OK;
+}
+
+hipError_t launch_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache, const void* k,
+                        const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                        hipStream_t st) {
+  pkv::WriteArgs a;
+  a.g = geom(pool);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k = k;
+  a.v = v;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  return pkv::launch_kv_write(a, st);
+}
+
+hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* context_lens, int64_t num_rows, int32_t num_heads,
+                            float scale, void* workspace, hipStream_t st) {
+  pkv::AttnArgs a;
+  a.g = geom(pool);
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_rows = num_rows;
+  a.num_heads = num_heads;
+  a.max_blocks = max_blocks;
+  a.ctx_limit = (int32_t)ctx_limit_of(pool, max_blocks);
+  a.log2_chunk_min = log2i(pkv::tuning_chunk_min());
+  a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
+  a.target_items = 0;
+  a.deal_static = 1;
+  a.query_group = 1;
+  a.scale = scale;
+  const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads,
+                                                 pool->head_dim, max_blocks, pool->block_size);
+  return pkv::launch_paged_attention(a, ws, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,15 +270,7 @@ pkv_status pkv_kv_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
     s = check_write_data(pool, host.data(), num_tokens);
     if (s != PKV_OK) return s;
   }
-  pkv::WriteArgs a;
-  a.g = geom(pool);
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.k = k;
-  a.v = v;
-  a.slot_mapping = slot_mapping;
-  a.num_tokens = num_tokens;
-  hipError_t e = pkv::launch_kv_write(a, st);
+  hipError_t e = launch_write(pool, k_cache, v_cache, k, v, slot_mapping, num_tokens, st);
   if (e != hipSuccess) return hip_fail(e, "launching kv_write");
   return ok();
 }
@@ -251,11 +296,8 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
                                            max_blocks_per_row, pool->block_size);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  const int32_t chunk = pkv::tuning_chunk_min();
-  const int64_t most_items = num_rows * ((int64_t)max_blocks_per_row * pool->block_size /
-                                         chunk + 1) * num_heads;
-  if (most_items > (int64_t{1} << 30))
-    return fail(PKV_ERR_UNSUPPORTED, "rows x heads x chunks too large for one call");
+  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads);
+  if (s != PKV_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (validate) {
     std::vector<int32_t> ctx((size_t)num_rows);
@@ -270,28 +312,9 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
     s = check_attention_data(pool, bt.data(), max_blocks_per_row, ctx.data(), num_rows);
     if (s != PKV_OK) return s;
   }
-  pkv::AttnArgs a;
-  a.g = geom(pool);
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.num_rows = num_rows;
-  a.num_heads = num_heads;
-  a.max_blocks = max_blocks_per_row;
-  a.ctx_limit = (int32_t)ctx_limit_of(pool, max_blocks_per_row);
-  a.log2_chunk_min = log2i(chunk);
-  a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
-  a.target_items = 0;
-  a.deal_static = 1;
-  a.query_group = 1;
-  a.scale = scale;
-  const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads,
-                                                 pool->head_dim, max_blocks_per_row,
-                                                 pool->block_size);
-  hipError_t e = pkv::launch_paged_attention(a, ws, st);
+  hipError_t e = launch_attention(pool, out, q, k_cache, v_cache, block_tables,
+                                  max_blocks_per_row, context_lens, num_rows, num_heads, scale,
+                                  workspace, st);
   if (e != hipSuccess) return hip_fail(e, "launching paged_attention");
   return ok();
 }
@@ -338,6 +361,75 @@ pkv_status pkv_timing_read(int32_t phase, double* total_ms, int64_t* launches,
     return fail(PKV_ERR_SHAPE, "unknown phase %d", phase);
   hipError_t e = pkv::timing_read(phase, total_ms, launches, reset != 0);
   if (e != hipSuccess) return hip_fail(e, "reading kernel timing events");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------------
+// captured steps
+// ---------------------------------------------------------------------------------
+struct pkv_step_graph {
+  hipGraphExec_t exec;
+};
+
+pkv_status pkv_graph_capture(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
+                             const void* k, const void* v, const int64_t* slot_mapping,
+                             void* out, const void* q, const int32_t* block_tables,
+                             int32_t max_blocks_per_row, const int32_t* context_lens,
+                             int64_t num_rows, int32_t num_heads, float scale,
+                             void* workspace, size_t workspace_bytes,
+                             pkv_step_graph** graph) {
+  if (!graph) return fail(PKV_ERR_NULL, "graph is NULL");
+  *graph = nullptr;
+  pkv_status s = check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  if (!k_cache || !v_cache || !k || !v || !slot_mapping || !out || !q || !block_tables ||
+      !context_lens)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  const size_t need = pkv::workspace_bytes(num_rows, num_heads, pool->head_dim,
+                                           max_blocks_per_row, pool->block_size);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+
+  // Capture on a private stream: the legacy default stream cannot be captured, and the
+  // caller's streams stay free of capture state.  Nothing runs during the capture.
+  // Relaxed mode: a launcher's first use on a device queries occupancy, which is not a
+  // stream operation but which the stricter modes may refuse.
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "creating the capture stream");
+  hipGraph_t g = nullptr;
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+  if (e == hipSuccess) {
+    hipError_t le = launch_write(pool, k_cache, v_cache, k, v, slot_mapping, num_rows, cs);
+    if (le == hipSuccess)
+      le = launch_attention(pool, out, q, k_cache, v_cache, block_tables, max_blocks_per_row,
+                            context_lens, num_rows, num_heads, scale, workspace, cs);
+    e = hipStreamEndCapture(cs, &g);   // always end, so the stream leaves capture mode
+    if (le != hipSuccess) e = le;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (e == hipSuccess) e = hipGraphInstantiateWithFlags(&exec, g, 0);
+  if (g) (void)hipGraphDestroy(g);
+  (void)hipStreamDestroy(cs);
+  if (e != hipSuccess) return hip_fail(e, "capturing the decode step");
+  *graph = new pkv_step_graph{exec};
+  return ok();
+}
+
+pkv_status pkv_graph_launch(const pkv_step_graph* graph, void* stream) {
+  if (!graph) return fail(PKV_ERR_NULL, "graph is NULL");
+  hipError_t e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching a captured step");
+  return ok();
+}
+
+pkv_status pkv_graph_destroy(pkv_step_graph* graph) {
+  if (!graph) return ok();
+  hipError_t e = hipGraphExecDestroy(graph->exec);
+  delete graph;
+  if (e != hipSuccess) return hip_fail(e, "destroying a captured step");
   return ok();
 }
 

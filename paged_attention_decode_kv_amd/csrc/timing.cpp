@@ -22,7 +22,7 @@ struct PhaseLog {
 };
 
 std::mutex g_mu;
-bool g_on = false;
+std::atomic<bool> g_on{false};
 PhaseLog g_log[kPhases];
 
 hipEvent_t take(PhaseLog& p) {
@@ -43,8 +43,15 @@ void timing_enable(bool on) {
   g_on = on;
 }
 
+// A stream under capture records nodes, not work: events there would never complete
+// on their own, so captured launches go untimed.
+static bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(stream, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
 void timing_begin(int phase, hipStream_t stream) {
-  if (!g_on) return;
+  if (!g_on || capturing(stream)) return;
   std::lock_guard<std::mutex> lock(g_mu);
   PhaseLog& p = g_log[phase];
   p.open = take(p);
@@ -52,7 +59,7 @@ void timing_begin(int phase, hipStream_t stream) {
 }
 
 void timing_end(int phase, hipStream_t stream) {
-  if (!g_on) return;
+  if (!g_on || capturing(stream)) return;
   std::lock_guard<std::mutex> lock(g_mu);
   PhaseLog& p = g_log[phase];
   if (!p.open) return;

@@ -140,3 +140,40 @@ def test_write_refusals_match_the_oracle(lib, slots):
 def test_empty_write_is_refused(lib):
     d = binding.host_desc(8, 16, 2, 64, "f32", "HND")
     assert binding.check_write_host(d, np.zeros(0, dtype=np.int64)) == "EMPTY"
+
+
+def test_graph_capture_refusals_need_no_gpu(lib):
+    """pkv_graph_capture makes the shape refusals of the two calls before touching HIP."""
+    desc = binding.host_desc(64, 16, 4, 128, "bf16", "HND")
+    handle = ctypes.c_void_p(123)
+    p = ctypes.c_void_p(16)         # never dereferenced: every case below is refused first
+
+    def cap(rows, heads, ws_bytes, max_blocks=8, d=desc, out=ctypes.byref(handle)):
+        return _capi.STATUS_NAMES[lib.pkv_graph_capture(
+            ctypes.byref(d), p, p, p, p, p, p, p, p, max_blocks, p, rows, heads, 1.0, p,
+            ws_bytes, out)]
+
+    need = lib.pkv_workspace_bytes(ctypes.byref(desc), 4, 8, 8)
+    assert cap(0, 8, need) == "EMPTY"
+    assert handle.value is None          # cleared on refusal
+    assert cap(4, 6, need) == "SHAPE"    # 6 query heads over 4 KV heads
+    assert cap(4, 8, need, max_blocks=0) == "SHAPE"
+    assert cap(4, 8, need - 1) == "WORKSPACE"
+    bad = binding.host_desc(64, 16, 4, 96, "bf16", "HND")
+    assert cap(4, 8, need, d=bad) == "UNSUPPORTED"
+    assert cap(4, 8, need, out=None) == "NULL"
+    assert _capi.STATUS_NAMES[lib.pkv_graph_launch(None, None)] == "NULL"
+    assert _capi.STATUS_NAMES[lib.pkv_graph_destroy(None)] == "OK"
+
+
+def test_row_buckets():
+    from paged_attention_decode_kv_amd.graphs import bucket_for, default_buckets
+    assert default_buckets(1) == [1]
+    assert default_buckets(256) == [1, 2, 4, 8, 16, 32, 64, 128, 256]
+    assert default_buckets(24) == [1, 2, 4, 8, 16, 24]
+    b = [4, 8, 16]
+    assert [bucket_for(b, n) for n in (1, 4, 5, 8, 9, 16)] == [4, 4, 8, 8, 16, 16]
+    with pytest.raises(binding.PagedKVError, match="SHAPE"):
+        bucket_for(b, 17)
+    with pytest.raises(binding.PagedKVError, match="EMPTY"):
+        bucket_for(b, 0)

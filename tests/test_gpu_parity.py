@@ -442,3 +442,111 @@ def test_config5_grouped_variant_sampled(kv_heads):
     say(f"{w.name}: sampled max err {err:.3e}")
     del st
     torch.cuda.empty_cache()
+
+
+
+# --------------------------------------------------------------------------- #
+# captured steps
+# --------------------------------------------------------------------------- #
+def _graph_step_workload(n, seed, num_blocks, max_blocks, heads, kv_heads, max_len):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, max_len + 1, n)
+    return wl.make_custom(lens.tolist(), heads=heads, kv_heads=kv_heads, head_dim=128,
+                          block_size=16, dtype="bf16", layout="HND", num_blocks=num_blocks,
+                          max_blocks=max_blocks, seed=seed)
+
+
+@pytest.mark.parametrize("heads,kv_heads", [(8, 8), (8, 2)])
+def test_bucketed_graphs_replay_real_steps(heads, kv_heads):
+    """Graphs recorded per row bucket over an all-padding batch replay a sequence of
+    real steps of other sizes on one evolving pool; every step matches the oracle."""
+    from paged_attention_decode_kv_amd.graphs import DecodeGraphs
+    mb, nb = 48, 16 * 48 + 8
+    first = _graph_step_workload(16, 100, nb, mb, heads, kv_heads, 700)
+    k_host, v_host = wl.history_host(first)
+    k_cache, v_cache = to_dev(k_host, "bf16"), to_dev(v_host, "bf16")
+    say(f"bucketed graphs heads={heads}/{kv_heads} pool={first.pool_shape}")
+    binding.device_status(DEV, clear=True)
+    graphs = DecodeGraphs(k_cache, v_cache, num_heads=heads, max_blocks=mb, scale=first.scale,
+                          buckets=[4, 8, 16])
+    torch.cuda.synchronize()
+    # the warm runs wrote only the sink and left zeros
+    assert torch.count_nonzero(graphs.out).item() == 0
+    assert np.array_equal(to_host(k_cache, "bf16")[:nb], k_host[:nb])
+    kh, vh = k_host.copy(), v_host.copy()
+    plan = [(16, 700, mb), (5, 700, mb), (8, 250, 16), (1, 700, mb), (13, 700, mb)]
+    for i, (n, max_len, width) in enumerate(plan):
+        w = _graph_step_workload(n, 200 + i, nb, width, heads, kv_heads, max_len)
+        say(f"  step {i}: rows {n} bucket {graphs.bucket_for(n)} width {width} "
+            f"lens {w.context_lens.tolist()}")
+        got = graphs.step(to_dev(w.q, "bf16"), to_dev(w.k_new, "bf16"),
+                          to_dev(w.v_new, "bf16"), to_dev(w.slot_mapping),
+                          to_dev(w.block_tables), to_dev(w.context_lens))
+        torch.cuda.synchronize()
+        oracle.kv_write(kh, vh, w.k_new, w.v_new, w.slot_mapping, num_blocks=nb,
+                        block_size=16, layout="HND", dtype="bf16")
+        ref = oracle.paged_attention(w.q, kh, vh, w.block_tables, w.context_lens, w.scale,
+                                     num_blocks=nb, block_size=16, layout="HND",
+                                     dtype="bf16")
+        assert_close(to_host(got, "bf16"), ref, "bf16", f"graph step {i}")
+        assert np.array_equal(to_host(k_cache, "bf16")[:nb], kh[:nb])
+        assert np.array_equal(to_host(v_cache, "bf16")[:nb], vh[:nb])
+        # rows past n in the bucket are padding: their output is zero
+        b = graphs.bucket_for(n)
+        assert torch.count_nonzero(graphs.out[n:b]).item() == 0
+    assert binding.device_status(DEV, clear=True) == 0
+    graphs.close()
+
+
+def test_caller_stream_capture_of_the_step():
+    """The two entry points with validate=0 are capturable by a caller's own stream
+    capture: recorded over padding, replayed several times on real batches written into
+    the same tensors, with eager work between replays."""
+    rows, mb = 24, 64
+    nb = rows * mb + 8
+    rng = np.random.default_rng(5)
+    batches = [_graph_step_workload(rows, 40 + i, nb, mb, 16, 4, 1024) for i in range(2)]
+    w0 = batches[0]
+    st = Step(w0, host_history=True)
+    k_host, v_host = st.k_host, st.v_host
+    out = torch.empty_like(st.q)
+    ws = torch.empty(binding.workspace_bytes(st.k_cache, rows, 16, mb), dtype=torch.uint8,
+                     device=DEV)
+    st.lens.zero_()
+    st.slots.fill_(w0.sink)
+    st.tables.fill_(-1)
+    say(f"caller capture: rows={rows} lens {[w.context_lens.tolist()[:6] for w in batches]}")
+    torch.cuda.synchronize()
+    binding.paged_attention(st.q, st.k_cache, st.v_cache, st.tables, st.lens, w0.scale,
+                            out=out, workspace=ws, validate=False)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        binding.kv_write(st.k_new, st.v_new, st.slots, st.k_cache, st.v_cache, validate=False)
+        binding.paged_attention(st.q, st.k_cache, st.v_cache, st.tables, st.lens, w0.scale,
+                                out=out, workspace=ws, validate=False)
+    st.k_cache.copy_(to_dev(k_host, "bf16"))
+    st.v_cache.copy_(to_dev(v_host, "bf16"))
+    out.fill_(7.0)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    assert np.array_equal(to_host(st.k_cache, "bf16")[:nb], k_host[:nb])
+    for w in batches:
+        st.k_cache.copy_(to_dev(k_host, "bf16"))
+        st.v_cache.copy_(to_dev(v_host, "bf16"))
+        for dst, src, dt in ((st.q, w.q, "bf16"), (st.k_new, w.k_new, "bf16"),
+                             (st.v_new, w.v_new, "bf16"), (st.slots, w.slot_mapping, None),
+                             (st.tables, w.block_tables, None), (st.lens, w.context_lens, None)):
+            dst.copy_(to_dev(src, dt))
+        torch.cuda.synchronize()
+        for rep in range(2):
+            graph.replay()
+            torch.cuda.synchronize()
+            if rep == 0:
+                ref, kw, vw = oracle_full(w, k_host, v_host)
+            assert_close(to_host(out, "bf16"), ref, "bf16", f"replay {rep} seed {w.seed}")
+            # the second replay writes the same vectors into the same slots
+            assert np.array_equal(to_host(st.k_cache, "bf16")[:nb], kw[:nb])
+            assert np.array_equal(to_host(st.v_cache, "bf16")[:nb], vw[:nb])
