@@ -18,6 +18,9 @@ pages:
   ``rebuild_mapping`` construction (Day 51, "What I added today") and the
   block-id addressing ``block_id * block_size + offset`` (Day 51, "Why it
   matters").
+* ``paged_attention_slots``: the same read addressed by a per-token slot
+  rectangle handed in directly, a window on the persistent slot table (Day 51,
+  "What I added today").
 
 Every floating-point step runs in float64.  Parity is pinned by the tests under
 ``tests/test_oracle_*.py`` (brute force, library routines, closed forms,
@@ -33,9 +36,11 @@ from .decode import (  # noqa: F401
     gather,
     kv_write,
     paged_attention,
+    paged_attention_slots,
     rebuild_mapping,
     sink_slot,
     slot_view,
     validate_attention,
+    validate_attention_slots,
     validate_write,
 )

@@ -17,7 +17,10 @@ Conventions shared with the library's C boundary (restated here, not imported):
 * ``q`` and the output are ``[rows, heads, head_dim]``; query head ``h`` reads KV
   head ``h // (heads // kv_heads)``;
 * ``block_tables`` is int32 ``[rows, max_blocks]`` and ``context_lens`` int32 ``[rows]``;
-  ``slot_mapping`` is int64 ``[tokens]``.
+  ``slot_mapping`` is int64 ``[tokens]``;
+* the read may instead be addressed by a slot rectangle, int64 ``[rows, width]``, whose
+  cell (r, t) names the slot holding position t of row r (cells at or past the row's
+  length may hold anything and are never read).
 
 Every floating-point operation is float64.
 """
@@ -196,6 +199,63 @@ def validate_attention(q, k_cache, v_cache, block_tables, context_lens, *, num_b
                                       f"outside [0, {num_blocks})")
 
 
+def validate_attention_slots(q, k_cache, v_cache, slot_rect, context_lens, *, num_blocks,
+                             block_size, layout, dtype):
+    """Refusals of the read addressed by a slot rectangle, in the order EMPTY, DTYPE,
+    SHAPE, CONTEXT_BOUNDS, SLOT.
+
+    Day 51 ("What I added today"): the decode step reads through a persistent
+    [max_batch, max_model_len] int64 slot table, handed to the read as the window
+    ``slots[:rows, :width]``, with the lengths passed beside it.
+
+    * A length may not be negative, may not exceed the rectangle's width and may not
+      exceed the pool's slot count.
+    * Every live cell (t < len) must name an allocatable slot, in [0, num_blocks *
+      block_size).  The sink holds padding writes only and is no row's token (Day 55,
+      "Why it matters").  Cells past a row's length are never read and not checked:
+      a re-tenanted row keeps its old tenant's slots there (Day 51, "What I learned").
+    """
+    ctx = np.asarray(context_lens)
+    rect = np.asarray(slot_rect)
+    r = int(ctx.shape[0]) if ctx.ndim >= 1 else 0
+    if r == 0:
+        raise Refusal("EMPTY", "no rows")
+    _check_pool(k_cache, v_cache, num_blocks, block_size, layout, dtype)
+    if q.dtype != _STORAGE[dtype]:
+        raise Refusal("DTYPE", "q storage does not match the declared dtype")
+    if ctx.dtype != np.int32 or rect.dtype != np.int64:
+        raise Refusal("DTYPE", "the slot rectangle must be int64 and context_lens int32")
+    dims = _pool_dims(k_cache, layout)
+    if dims is None:
+        raise Refusal("SHAPE", "pool must be 4-D")
+    hkv, d = dims
+    want = _pool_shape(num_blocks, block_size, hkv, d, layout)
+    if k_cache.shape != want or v_cache.shape != want:
+        raise Refusal("SHAPE", f"pool shape {k_cache.shape} != {want}")
+    if q.ndim != 3 or q.shape[0] != r or q.shape[2] != d:
+        raise Refusal("SHAPE", f"q shape {q.shape} does not match rows={r}, head_dim={d}")
+    h = q.shape[1]
+    if h == 0 or h % hkv != 0:
+        raise Refusal("SHAPE", f"{h} query heads is not a multiple of {hkv} KV heads")
+    if ctx.shape != (r,) or rect.ndim != 2 or rect.shape[0] != r or rect.shape[1] < 1:
+        raise Refusal("SHAPE", "slot rectangle must be [rows, width>=1], context_lens [rows]")
+    width = int(rect.shape[1])
+    slots = num_blocks * block_size
+    limit = min(width, slots)
+    bad = np.nonzero((ctx < 0) | (ctx > limit))[0]
+    if bad.size:
+        i = int(bad[0])
+        raise Refusal("CONTEXT_BOUNDS",
+                      f"context_lens[{i}] = {int(ctx[i])} outside [0, {limit}]")
+    for row in range(r):
+        cells = rect[row, :int(ctx[row])]
+        wrong = np.nonzero((cells < 0) | (cells >= slots))[0]
+        if wrong.size:
+            t = int(wrong[0])
+            raise Refusal("SLOT", f"slot rectangle [{row}, {t}] = {int(cells[t])} "
+                                  f"outside [0, {slots})")
+
+
 # --------------------------------------------------------------------------- #
 # O1: the slot scatter
 # --------------------------------------------------------------------------- #
@@ -269,12 +329,40 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale, *,
     validate_attention(q, k_cache, v_cache, block_tables, context_lens,
                        num_blocks=num_blocks, block_size=block_size, layout=layout,
                        dtype=dtype)
+    mapping, live = rebuild_mapping(block_tables, context_lens, block_size)
+    return _attend(q, k_cache, v_cache, mapping, live, context_lens, scale, layout, dtype)
+
+
+def paged_attention_slots(q, k_cache, v_cache, slot_rect, context_lens, scale, *,
+                          num_blocks, block_size, layout, dtype):
+    """The same read with the rectangle handed in rather than rebuilt from block
+    tables, float64 ``[rows, heads, head_dim]``.
+
+    Day 51 ("What I added today"): the read is given the window of the slot table and
+    the lengths.  The mapping is the window's first max(len) columns, with the cells
+    past each row's length replaced by slot 0, a legal index the mask then discards
+    (Day 51, "What I learned": the reference gathers before it masks).
+    """
+    validate_attention_slots(q, k_cache, v_cache, slot_rect, context_lens,
+                             num_blocks=num_blocks, block_size=block_size, layout=layout,
+                             dtype=dtype)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    width = int(ctx.max())
+    t = np.arange(width, dtype=np.int64)
+    live = t[None, :] < ctx[:, None]
+    mapping = np.where(live, np.asarray(slot_rect)[:, :width], 0)
+    return _attend(q, k_cache, v_cache, mapping, live, context_lens, scale, layout, dtype)
+
+
+def _attend(q, k_cache, v_cache, mapping, live, context_lens, scale, layout, dtype):
+    """Gather, score, mask, softmax and weight V over a [rows, width] slot mapping
+    whose cells outside ``live`` are legal but meaningless (Day 59, "What I added
+    today")."""
     rows, heads, head_dim = q.shape
     kv_heads = k_cache.shape[1] if layout == "HND" else k_cache.shape[2]
     group = heads // kv_heads
     kv_of_head = np.arange(heads) // group                     # query head -> KV head
 
-    mapping, live = rebuild_mapping(block_tables, context_lens, block_size)
     width = mapping.shape[1]
     out = np.zeros((rows, heads, head_dim), dtype=np.float64)
     if width == 0:
