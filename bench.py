@@ -69,6 +69,9 @@ def parse():
                     help="graph (default): time the two library calls per step, then replays "
                          "of one HIP graph recorded from them, and report the replays as "
                          "value; eager: time and report the library calls only")
+    ap.add_argument("--address", default="blocks", choices=["blocks", "slots"],
+                    help="how the read is addressed: block tables (default), or the "
+                         "per-token int64 slot window of a wider slot table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
@@ -235,8 +238,23 @@ def main():
     tables = dev_array(w.block_tables)
     lens = dev_array(w.context_lens)
     out = torch.empty_like(q)
-    ws = torch.empty(max(1, binding.workspace_bytes(k_cache, w.rows, w.heads, w.max_blocks,
-                                                    w.layout)), dtype=torch.uint8, device=dev)
+    width = w.max_blocks * w.block_size
+    slot_win = None
+    if args.address == "slots":
+        # the slot table a serving loop keeps: [rows, width + 64] int64, each row's live
+        # positions holding block id * block size + offset of the same placement, junk
+        # (-1) elsewhere; the read gets its first `width` columns as a window
+        t = torch.arange(width, device=dev)
+        cells = tables.long().clamp_min(0)[:, t // w.block_size] * w.block_size + \
+            t % w.block_size
+        slot_table = torch.full((w.rows, width + 64), -1, dtype=torch.int64, device=dev)
+        slot_table[:, :width] = torch.where(t[None, :] < lens[:, None].long(), cells, -1)
+        slot_win = slot_table[:, :width]
+        del t, cells
+        ws_bytes = binding.workspace_bytes_slots(k_cache, w.rows, w.heads, width, w.layout)
+    else:
+        ws_bytes = binding.workspace_bytes(k_cache, w.rows, w.heads, w.max_blocks, w.layout)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     # the CPU oracle runs first, on the untouched pool: its timing is the baseline and
@@ -248,8 +266,14 @@ def main():
     def step(validate=False):
         binding.kv_write(k_new, v_new, slots, k_cache, v_cache, layout=w.layout,
                          validate=validate)
-        binding.paged_attention(q, k_cache, v_cache, tables, lens, w.scale, layout=w.layout,
-                                out=out, workspace=ws, validate=validate)
+        if slot_win is not None:
+            binding.paged_attention_slots(q, k_cache, v_cache, slot_win, lens, w.scale,
+                                          layout=w.layout, out=out, workspace=ws,
+                                          validate=validate)
+        else:
+            binding.paged_attention(q, k_cache, v_cache, tables, lens, w.scale,
+                                    layout=w.layout, out=out, workspace=ws,
+                                    validate=validate)
 
     # one validated step: the library checks every length, block id and slot on the host
     step(validate=True)
@@ -275,8 +299,13 @@ def main():
     # identical kernels and arguments, without a host launch per kernel
     graph_s = None
     if args.launch == "graph":
-        graph = binding.capture_step(k_new, v_new, slots, q, k_cache, v_cache, tables, lens,
-                                     w.scale, out, ws, layout=w.layout)
+        if slot_win is not None:
+            graph = binding.capture_step_slots(k_new, v_new, slots, q, k_cache, v_cache,
+                                               slot_win, lens, w.scale, out, ws,
+                                               layout=w.layout)
+        else:
+            graph = binding.capture_step(k_new, v_new, slots, q, k_cache, v_cache, tables,
+                                         lens, w.scale, out, ws, layout=w.layout)
         for _ in range(args.warmup):
             graph.launch()
         torch.cuda.synchronize()
@@ -307,16 +336,19 @@ def main():
 
     step_s = graph_s if args.launch == "graph" else eager_s
     elem = 2 if w.dtype == "bf16" else 4
-    b = acc.algorithmic_bytes(w.context_lens, heads=w.heads, kv_heads=w.kv_heads,
-                              head_dim=w.head_dim, block_size=w.block_size, elem=elem,
-                              write_tokens=w.rows)
+    shape = dict(heads=w.heads, kv_heads=w.kv_heads, head_dim=w.head_dim,
+                 block_size=w.block_size, elem=elem, write_tokens=w.rows)
+    b = acc.algorithmic_bytes(w.context_lens, address=args.address, **shape)
+    # the decode kernel reads block ids in both modes (with slots, the table the
+    # translation pass derived from the window)
+    dec_bytes = acc.algorithmic_bytes(w.context_lens, **shape)["attention"]
     rh = acc.row_heads(w.context_lens, w.heads)
     avg = {ph: (ms / n if n else None) for ph, (ms, n) in phases.items()}
     for ph, (ms, n) in phases.items():
         if n:
             log(f"  {ph:9s} {n:5d} launches, avg {ms / n * 1e3:9.2f} us")
     dec_s = avg["decode"] * 1e-3
-    achieved = b["attention"] / dec_s / 1e9
+    achieved = dec_bytes / dec_s / 1e9
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 2),
@@ -326,7 +358,7 @@ def main():
         "traffic": traffic_per_launch(w.name, w.layout),
         "kernel": "decode_kernel",
         "kernel_avg_us": round(dec_s * 1e6, 2),
-        "bytes_per_launch": b["attention"],
+        "bytes_per_launch": dec_bytes,
     }
     result = {
         "metric": METRIC,
@@ -346,7 +378,10 @@ def main():
                          f"{w.heads} heads x head_dim {w.head_dim}, {w.dtype} KV, block "
                          f"{w.block_size}, table width {w.max_blocks * w.block_size}, "
                          f"{int(w.context_lens.sum())} live tokens; kv_write + "
-                         f"paged_attention"),
+                         + ("paged_attention" if args.address == "blocks" else
+                            "paged_attention_slots through a [rows, width] int64 slot "
+                            "window")),
+            "address": args.address,
             "rows": w.rows,
             "heads": w.heads,
             "kv_heads": w.kv_heads,

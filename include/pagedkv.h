@@ -91,7 +91,8 @@ typedef struct pkv_pool_desc {
 } pkv_pool_desc;
 
 /* Device status bits raised by kernels run with validate == 0 on bad inputs. */
-#define PKV_DEVERR_SLOT 1u            /* a write slot outside [0, sink] was skipped */
+#define PKV_DEVERR_SLOT 1u            /* a write slot outside [0, sink], or a live read
+                                         slot outside [0, sink), was skipped */
 #define PKV_DEVERR_CONTEXT_BOUNDS 2u  /* a context_len was clamped */
 #define PKV_DEVERR_BLOCK_ID 4u        /* a live block id outside [0, num_blocks) was skipped */
 
@@ -161,6 +162,43 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
                                int32_t num_heads, float scale, void* workspace,
                                size_t workspace_bytes, int32_t validate, void* stream);
 
+/* The decode read addressed by a per-token slot rectangle instead of block tables
+ * (Day 51, "What I added today": the step reads through a persistent
+ * [max_batch, max_model_len] int64 slot table, handed over as the window
+ * slots[:rows, :width] with the lengths beside it).
+ *   slot_table     int64; cell (r, t) at slot_table[r * row_stride + t] is the slot
+ *                  holding position t of row r.  row_stride >= width, so a window on a
+ *                  wider table is passed as its first cell's address and the table's
+ *                  row length.  Cells at or past context_lens[r] may hold anything
+ *                  (a re-tenanted row keeps its old slots there) and are never read.
+ *   context_lens   [num_rows] int32, each in [0, min(width, num_blocks * block_size)]
+ *   q, out, k_cache, v_cache, scale, workspace, validate, stream: as in
+ *                  pkv_paged_attention; the workspace is pkv_workspace_bytes_slots(...)
+ * Refusals, in order: EMPTY, DTYPE, SHAPE (row_stride < width, width < 1, heads),
+ * CONTEXT_BOUNDS, SLOT (a live cell outside [0, num_blocks * block_size): the sink is
+ * no row's token), UNSUPPORTED (width > 2^24, rows > 65535).  validate != 0 copies
+ * the lengths and the rectangle's first `width` columns to the host first.
+ * out is the same function of the named tokens as pkv_paged_attention's.  Rows whose
+ * live cells are block structured (cell t = B * block_size + t % block_size over each
+ * block of positions, B an allocatable block) take the block-table kernels, bit for
+ * bit what pkv_paged_attention gives with those blocks; other rows are read token by
+ * token.  With validate = 0 a live cell outside the slots is skipped and sets
+ * PKV_DEVERR_SLOT. */
+size_t pkv_workspace_bytes_slots(const pkv_pool_desc* pool, int64_t num_rows,
+                                 int32_t num_heads, int32_t width);
+pkv_status pkv_paged_attention_slots(const pkv_pool_desc* pool, void* out, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int64_t* slot_table, int32_t width,
+                                     int64_t row_stride, const int32_t* context_lens,
+                                     int64_t num_rows, int32_t num_heads, float scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t validate, void* stream);
+/* The host checks pkv_paged_attention_slots runs with validate != 0, on HOST arrays. */
+pkv_status pkv_check_attention_slots_host(const pkv_pool_desc* pool,
+                                          const int64_t* slot_table, int32_t width,
+                                          int64_t row_stride, const int32_t* context_lens,
+                                          int64_t num_rows, int32_t num_heads);
+
 /* Reads (and if `clear` is non-zero, resets) the current device's status word, a
  * bitwise OR of PKV_DEVERR_* raised since the last clear.  Synchronises `stream`. */
 pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
@@ -213,7 +251,9 @@ typedef enum pkv_phase {
   PKV_PHASE_KV_WRITE = 0,  /* the slot scatter kernel */
   PKV_PHASE_PLAN = 1,      /* the work-list kernel of pkv_paged_attention */
   PKV_PHASE_DECODE = 2,    /* the streaming online-softmax kernel */
-  PKV_PHASE_COMBINE = 3    /* the merge of split rows */
+  PKV_PHASE_COMBINE = 3,   /* the merge of split rows */
+  PKV_PHASE_TRANSLATE = 4, /* slot input: the rectangle's block-structure check */
+  PKV_PHASE_TOKEN_ROWS = 5 /* slot input: the rows read token by token */
 } pkv_phase;
 
 pkv_status pkv_timing_enable(int32_t on);
@@ -248,6 +288,15 @@ pkv_status pkv_graph_capture(const pkv_pool_desc* pool, void* k_cache, void* v_c
                              int64_t num_rows, int32_t num_heads, float scale,
                              void* workspace, size_t workspace_bytes,
                              pkv_step_graph** graph);
+/* The same, with the read addressed by a slot window (pkv_paged_attention_slots's
+ * arguments): the pages record their graphs over windows on the slot table. */
+pkv_status pkv_graph_capture_slots(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
+                                   const void* k, const void* v, const int64_t* slot_mapping,
+                                   void* out, const void* q, const int64_t* slot_table,
+                                   int32_t width, int64_t row_stride,
+                                   const int32_t* context_lens, int64_t num_rows,
+                                   int32_t num_heads, float scale, void* workspace,
+                                   size_t workspace_bytes, pkv_step_graph** graph);
 pkv_status pkv_graph_launch(const pkv_step_graph* graph, void* stream);
 pkv_status pkv_graph_destroy(pkv_step_graph* graph);
 

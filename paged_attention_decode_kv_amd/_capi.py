@@ -55,10 +55,18 @@ SIGNATURES = {
                                ctypes.POINTER(ctypes.c_int64), _i32]),
     "pkv_graph_capture": (_i32, [_PD, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32,
                                  _f, _p, _sz, ctypes.POINTER(ctypes.c_void_p)]),
+    "pkv_graph_capture_slots": (_i32, [_PD, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i64, _p,
+                                       _i64, _i32, _f, _p, _sz,
+                                       ctypes.POINTER(ctypes.c_void_p)]),
     "pkv_graph_launch": (_i32, [_p, _p]),
+    "pkv_workspace_bytes_slots": (_sz, [_PD, _i64, _i32, _i32]),
+    "pkv_paged_attention_slots": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _i64, _p, _i64, _i32,
+                                         _f, _p, _sz, _i32, _p]),
+    "pkv_check_attention_slots_host": (_i32, [_PD, _p, _i32, _i64, _p, _i64, _i32]),
     "pkv_graph_destroy": (_i32, [_p]),
 }
-PHASES = {"kv_write": 0, "plan": 1, "decode": 2, "combine": 3}
+PHASES = {"kv_write": 0, "plan": 1, "decode": 2, "combine": 3, "translate": 4,
+          "token_rows": 5}
 
 _lib = None
 

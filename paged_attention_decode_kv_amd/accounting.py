@@ -57,13 +57,22 @@ def widest_capture(budget_bytes: float, rows: int, heads: int,
 
 
 def algorithmic_bytes(context_lens, *, heads: int, kv_heads: int, head_dim: int,
-                      block_size: int, elem: int, write_tokens: int) -> dict:
-    """Bytes the step must move, split by component."""
+                      block_size: int, elem: int, write_tokens: int,
+                      address: str = "blocks") -> dict:
+    """Bytes the step must move, split by component.  ``address`` is how the read is
+    addressed: "blocks" reads one int32 block id per live block, "slots" one int64
+    rectangle cell per live position (Day 51, "Why it matters": the same information,
+    one cell per slot instead of one per block)."""
     ctx = np.asarray(context_lens, dtype=np.int64)
     rows = int(ctx.size)
     kv = int(ctx.sum()) * kv_heads * head_dim * elem * 2
     q_out = 2 * rows * heads * head_dim * elem
-    tables = int(np.sum(cdiv(ctx, block_size))) * 4 + rows * 4
+    if address == "blocks":
+        tables = int(np.sum(cdiv(ctx, block_size))) * 4 + rows * 4
+    elif address == "slots":
+        tables = int(ctx.sum()) * 8 + rows * 4
+    else:
+        raise ValueError(f"unknown address {address!r}")
     write = 2 * int(write_tokens) * kv_heads * head_dim * elem * 2
     read_total = kv + q_out + tables
     return {"kv": kv, "q_out": q_out, "tables": tables, "attention": read_total,

@@ -161,6 +161,71 @@ def paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     return out
 
 
+def _slot_window(slot_table: torch.Tensor, rows: int, dev: torch.device):
+    """(width, row_stride) of a [rows, width] int64 window whose cells are contiguous
+    along a row; the window may be a column slice of a wider table."""
+    if slot_table.dtype != torch.int64:
+        _raise("DTYPE", f"slot_table must be int64, got {slot_table.dtype}")
+    if not slot_table.is_cuda or slot_table.device != dev:
+        _raise("SHAPE", f"slot_table must be on {dev}")
+    if slot_table.dim() != 2 or slot_table.shape[0] != rows:
+        _raise("SHAPE", f"slot_table must be [{rows}, width]")
+    width = int(slot_table.shape[1])
+    if width < 1:
+        _raise("SHAPE", "slot_table width must be at least 1")
+    if slot_table.stride(1) != 1 or (rows > 1 and slot_table.stride(0) < width):
+        _raise("SHAPE", "slot_table rows must be contiguous, one row after another")
+    return width, int(slot_table.stride(0)) if rows > 1 else width
+
+
+def workspace_bytes_slots(k_cache: torch.Tensor, num_rows: int, num_heads: int, width: int,
+                          layout: str = "HND") -> int:
+    desc = pool_desc(k_cache, layout)
+    return int(_capi.lib().pkv_workspace_bytes_slots(ctypes.byref(desc), num_rows, num_heads,
+                                                     width))
+
+
+def paged_attention_slots(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          slot_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                          *, layout: str = "HND", out: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None,
+                          validate: bool = True) -> torch.Tensor:
+    """The decode read through a per-token slot rectangle ``slot_table`` [rows, width]
+    (int64, possibly a column window of a wider table); returns ``out``."""
+    rows = int(context_lens.shape[0]) if context_lens.dim() >= 1 else 0
+    if rows == 0:
+        _raise("EMPTY", "no rows")
+    desc = _pool_pair(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _device_tensor(q, "q", k_cache.dtype, dev)
+    _device_tensor(context_lens, "context_lens", torch.int32, dev)
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[2] != desc.head_dim:
+        _raise("SHAPE", f"q must be [{rows}, heads, {desc.head_dim}], got {tuple(q.shape)}")
+    if context_lens.dim() != 1:
+        _raise("SHAPE", "context_lens must be [rows]")
+    width, row_stride = _slot_window(slot_table, rows, dev)
+    heads = int(q.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, dev)
+        if out.shape != q.shape:
+            _raise("SHAPE", "out must have q's shape")
+    lib = _capi.lib()
+    need = int(lib.pkv_workspace_bytes_slots(ctypes.byref(desc), rows, heads, width))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        _raise("WORKSPACE", "workspace must be a contiguous tensor on the pool's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        _check(lib.pkv_paged_attention_slots(
+            ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(slot_table), width, row_stride, _ptr(context_lens), rows, heads,
+            float(scale), _ptr(workspace), ws_bytes, int(bool(validate)), _stream(k_cache)))
+    return out
+
+
 class StepGraph:
     """One captured decode step (pkv_graph_capture): kv_write then paged_attention over
     the tensors it was captured with, replayed by ``launch``.  Holds references to those
@@ -230,6 +295,42 @@ def capture_step(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                                    context_lens, out, workspace))
 
 
+def capture_step_slots(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                       q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       slot_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                       out: torch.Tensor, workspace: torch.Tensor, *,
+                       layout: str = "HND") -> StepGraph:
+    """Record kv_write + paged_attention_slots over these tensors into a graph."""
+    rows = int(context_lens.shape[0]) if context_lens.dim() == 1 else 0
+    if rows == 0:
+        _raise("EMPTY", "no rows")
+    desc = _pool_pair(k_cache, v_cache, layout)
+    dev = k_cache.device
+    for t, name in ((k, "k"), (v, "v"), (q, "q"), (out, "out")):
+        _device_tensor(t, name, k_cache.dtype, dev)
+    _device_tensor(slot_mapping, "slot_mapping", torch.int64, dev)
+    _device_tensor(context_lens, "context_lens", torch.int32, dev)
+    width, row_stride = _slot_window(slot_table, rows, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        _raise("WORKSPACE", "workspace must be a contiguous tensor on the pool's device")
+    kv_shape = (rows, desc.num_kv_heads, desc.head_dim)
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape or \
+            tuple(slot_mapping.shape) != (rows,):
+        _raise("SHAPE", f"k, v must be {kv_shape}, slot_mapping [{rows}]")
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[2] != desc.head_dim or \
+            out.shape != q.shape:
+        _raise("SHAPE", f"q and out must be [{rows}, heads, {desc.head_dim}]")
+    handle = ctypes.c_void_p()
+    with torch.cuda.device(dev):
+        _check(_capi.lib().pkv_graph_capture_slots(
+            ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k), _ptr(v),
+            _ptr(slot_mapping), _ptr(out), _ptr(q), _ptr(slot_table), width, row_stride,
+            _ptr(context_lens), rows, int(q.shape[1]), float(scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), ctypes.byref(handle)))
+    return StepGraph(handle, dev, (k, v, slot_mapping, q, k_cache, v_cache, slot_table,
+                                   context_lens, out, workspace))
+
+
 def device_status(device=None, clear: bool = True) -> int:
     """Bitwise OR of the device-side refusal bits raised since the last clear."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
@@ -283,6 +384,23 @@ def check_write_host(desc: _capi.PoolDesc, slot_mapping: np.ndarray) -> str:
     sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
     st = _capi.lib().pkv_check_write_host(ctypes.byref(desc),
                                           sm.ctypes.data_as(ctypes.c_void_p), sm.shape[0])
+    return _capi.STATUS_NAMES[st]
+
+
+def check_attention_slots_host(desc: _capi.PoolDesc, slot_table: np.ndarray,
+                               context_lens: np.ndarray, num_heads: int) -> str:
+    """Status name the library's host validator gives a read through a slot rectangle:
+    a [rows, width] int64 numpy array whose rows are contiguous (a column slice of a
+    wider table is passed with that table's row stride)."""
+    rect = np.asarray(slot_table)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if rect.dtype != np.int64 or rect.ndim != 2 or rect.shape[0] != ctx.shape[0] or \
+            rect.strides[1] != 8 or rect.strides[0] % 8 != 0:
+        raise ValueError("slot_table must be a 2-D int64 array with contiguous rows, "
+                         "one per length")
+    st = _capi.lib().pkv_check_attention_slots_host(
+        ctypes.byref(desc), rect.ctypes.data_as(ctypes.c_void_p), rect.shape[1],
+        rect.strides[0] // 8, ctx.ctypes.data_as(ctypes.c_void_p), ctx.shape[0], num_heads)
     return _capi.STATUS_NAMES[st]
 
 

@@ -11,6 +11,10 @@
 #include "internal.h"
 #include "pagedkv.h"
 
+struct pkv_step_graph {
+  hipGraphExec_t exec;
+};
+
 namespace {
 
 thread_local std::string g_detail;
@@ -184,9 +188,121 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
   a.deal_static = 1;
   a.query_group = 1;
   a.scale = scale;
+  a.row_flags = nullptr;
+  a.flag_stride = 0;
   const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads,
                                                  pool->head_dim, max_blocks, pool->block_size);
   return pkv::launch_paged_attention(a, ws, st);
+}
+
+// ---- slot input ----
+int64_t slot_ctx_limit(const pkv_pool_desc* p, int32_t width) {
+  const int64_t by_pool = p->num_blocks * p->block_size;
+  return width < by_pool ? width : by_pool;
+}
+
+// EMPTY, pool, SHAPE, UNSUPPORTED: everything that needs no data.
+pkv_status check_slots_shape(const pkv_pool_desc* pool, int32_t width, int64_t row_stride,
+                             int64_t num_rows, int32_t num_heads) {
+  if (num_rows == 0) return fail(PKV_ERR_EMPTY, "no rows");
+  pkv_status s = check_pool(pool);
+  if (s != PKV_OK) return s;
+  if (num_rows < 0) return fail(PKV_ERR_SHAPE, "num_rows %lld < 0", (long long)num_rows);
+  if (num_heads < 1 || num_heads % pool->num_kv_heads != 0)
+    return fail(PKV_ERR_SHAPE, "%d query heads is not a positive multiple of %d KV heads",
+                num_heads, pool->num_kv_heads);
+  if (width < 1) return fail(PKV_ERR_SHAPE, "width %d < 1", width);
+  if (row_stride < width)
+    return fail(PKV_ERR_SHAPE, "row_stride %lld < width %d", (long long)row_stride, width);
+  if (num_rows > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "num_rows %lld: built for at most 65535 rows",
+                (long long)num_rows);
+  if (width > (1 << 24))
+    return fail(PKV_ERR_UNSUPPORTED, "width %d tokens: built for at most 2^24", width);
+  return PKV_OK;
+}
+
+// CONTEXT_BOUNDS, then SLOT; `rect` is [num_rows][width] on the host.
+pkv_status check_slots_data(const pkv_pool_desc* pool, const int64_t* rect, int64_t rect_stride,
+                            int32_t width, const int32_t* ctx, int64_t num_rows) {
+  const int64_t limit = slot_ctx_limit(pool, width);
+  for (int64_t r = 0; r < num_rows; ++r) {
+    if (ctx[r] < 0 || ctx[r] > limit)
+      return fail(PKV_ERR_CONTEXT_BOUNDS, "context_lens[%lld] = %d outside [0, %lld]",
+                  (long long)r, ctx[r], (long long)limit);
+  }
+  const int64_t slots = pool->num_blocks * pool->block_size;
+  for (int64_t r = 0; r < num_rows; ++r) {
+    for (int64_t t = 0; t < ctx[r]; ++t) {
+      const int64_t v = rect[r * rect_stride + t];
+      if (v < 0 || v >= slots)
+        return fail(PKV_ERR_SLOT, "slot rectangle [%lld, %lld] = %lld outside [0, %lld)",
+                    (long long)r, (long long)t, (long long)v, (long long)slots);
+    }
+  }
+  return PKV_OK;
+}
+
+hipError_t launch_attention_slots(const pkv_pool_desc* pool, void* out, const void* q,
+                                  const void* k_cache, const void* v_cache,
+                                  const int64_t* slot_table, int32_t width,
+                                  int64_t row_stride, const int32_t* context_lens,
+                                  int64_t num_rows, int32_t num_heads, float scale,
+                                  void* workspace, hipStream_t st) {
+  pkv::AttnArgs a;
+  a.g = geom(pool);
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = nullptr;   // the derived table, set by the launcher
+  a.context_lens = context_lens;
+  a.num_rows = num_rows;
+  a.num_heads = num_heads;
+  a.max_blocks = (int32_t)(((int64_t)width + pool->block_size - 1) / pool->block_size);
+  a.ctx_limit = (int32_t)slot_ctx_limit(pool, width);
+  a.log2_chunk_min = log2i(pkv::tuning_chunk_min());
+  a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
+  a.target_items = 0;
+  a.deal_static = 1;
+  a.query_group = 1;
+  a.scale = scale;
+  a.row_flags = nullptr;
+  a.flag_stride = 0;
+  pkv::SlotArgs sa;
+  sa.slots = slot_table;
+  sa.row_stride = row_stride;
+  sa.width = width;
+  const pkv::Workspace ws = pkv::carve_slot_workspace(workspace, num_rows, num_heads,
+                                                      pool->head_dim, width,
+                                                      pool->block_size, &sa);
+  return pkv::launch_paged_attention_slots(a, sa, ws, st);
+}
+
+// Records what `record` enqueues on a private stream into an instantiated graph.  The
+// legacy default stream cannot be captured, and the caller's streams stay free of
+// capture state; nothing runs while recording.  Relaxed mode: a launcher's first use on
+// a device queries occupancy, which is not a stream operation but which the stricter
+// modes may refuse.
+template <typename F>
+pkv_status record_graph(F&& record, pkv_step_graph** graph) {
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "creating the capture stream");
+  hipGraph_t g = nullptr;
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+  if (e == hipSuccess) {
+    const hipError_t le = record(cs);
+    e = hipStreamEndCapture(cs, &g);   // always end, so the stream leaves capture mode
+    if (le != hipSuccess) e = le;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (e == hipSuccess) e = hipGraphInstantiateWithFlags(&exec, g, 0);
+  if (g) (void)hipGraphDestroy(g);
+  (void)hipStreamDestroy(cs);
+  if (e != hipSuccess) return hip_fail(e, "capturing the decode step");
+  *graph = new pkv_step_graph{exec};
+  return ok();
 }
 
 }  // namespace
@@ -319,6 +435,66 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
   return ok();
 }
 
+size_t pkv_workspace_bytes_slots(const pkv_pool_desc* pool, int64_t num_rows,
+                                 int32_t num_heads, int32_t width) {
+  if (check_slots_shape(pool, width, width, num_rows, num_heads) != PKV_OK) return 0;
+  return pkv::slot_workspace_bytes(num_rows, num_heads, pool->head_dim, width,
+                                   pool->block_size);
+}
+
+pkv_status pkv_check_attention_slots_host(const pkv_pool_desc* pool,
+                                          const int64_t* slot_table, int32_t width,
+                                          int64_t row_stride, const int32_t* context_lens,
+                                          int64_t num_rows, int32_t num_heads) {
+  pkv_status s = check_slots_shape(pool, width, row_stride, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  if (!slot_table || !context_lens) return fail(PKV_ERR_NULL, "rectangle or lengths NULL");
+  s = check_slots_data(pool, slot_table, row_stride, width, context_lens, num_rows);
+  return s == PKV_OK ? ok() : s;
+}
+
+pkv_status pkv_paged_attention_slots(const pkv_pool_desc* pool, void* out, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int64_t* slot_table, int32_t width,
+                                     int64_t row_stride, const int32_t* context_lens,
+                                     int64_t num_rows, int32_t num_heads, float scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t validate, void* stream) {
+  pkv_status s = check_slots_shape(pool, width, row_stride, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  if (!out || !q || !k_cache || !v_cache || !slot_table || !context_lens)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  const size_t need = pkv::slot_workspace_bytes(num_rows, num_heads, pool->head_dim, width,
+                                                pool->block_size);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  const int32_t max_blocks = (int32_t)(((int64_t)width + pool->block_size - 1) /
+                                       pool->block_size);
+  s = check_attention_items(pool, max_blocks, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (validate) {
+    std::vector<int32_t> ctx((size_t)num_rows);
+    std::vector<int64_t> rect((size_t)(num_rows * width));
+    hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(rect.data(), (size_t)width * sizeof(int64_t), slot_table,
+                           (size_t)row_stride * sizeof(int64_t),
+                           (size_t)width * sizeof(int64_t), (size_t)num_rows,
+                           hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "copying lengths and slots to the host");
+    s = check_slots_data(pool, rect.data(), width, width, ctx.data(), num_rows);
+    if (s != PKV_OK) return s;
+  }
+  hipError_t e = launch_attention_slots(pool, out, q, k_cache, v_cache, slot_table, width,
+                                        row_stride, context_lens, num_rows, num_heads, scale,
+                                        workspace, st);
+  if (e != hipSuccess) return hip_fail(e, "launching paged_attention_slots");
+  return ok();
+}
+
 pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
   if (!flags) return fail(PKV_ERR_NULL, "flags is NULL");
   hipError_t e = pkv::read_device_status(flags, clear, static_cast<hipStream_t>(stream));
@@ -357,7 +533,7 @@ pkv_status pkv_timing_enable(int32_t on) {
 pkv_status pkv_timing_read(int32_t phase, double* total_ms, int64_t* launches,
                            int32_t reset) {
   if (!total_ms || !launches) return fail(PKV_ERR_NULL, "output pointer is NULL");
-  if (phase < PKV_PHASE_KV_WRITE || phase > PKV_PHASE_COMBINE)
+  if (phase < PKV_PHASE_KV_WRITE || phase > PKV_PHASE_TOKEN_ROWS)
     return fail(PKV_ERR_SHAPE, "unknown phase %d", phase);
   hipError_t e = pkv::timing_read(phase, total_ms, launches, reset != 0);
   if (e != hipSuccess) return hip_fail(e, "reading kernel timing events");
@@ -367,10 +543,6 @@ pkv_status pkv_timing_read(int32_t phase, double* total_ms, int64_t* launches,
 // ---------------------------------------------------------------------------------
 // captured steps
 // ---------------------------------------------------------------------------------
-struct pkv_step_graph {
-  hipGraphExec_t exec;
-};
-
 pkv_status pkv_graph_capture(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
                              const void* k, const void* v, const int64_t* slot_mapping,
                              void* out, const void* q, const int32_t* block_tables,
@@ -392,30 +564,43 @@ pkv_status pkv_graph_capture(const pkv_pool_desc* pool, void* k_cache, void* v_c
   s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads);
   if (s != PKV_OK) return s;
 
-  // Capture on a private stream: the legacy default stream cannot be captured, and the
-  // caller's streams stay free of capture state.  Nothing runs during the capture.
-  // Relaxed mode: a launcher's first use on a device queries occupancy, which is not a
-  // stream operation but which the stricter modes may refuse.
-  hipStream_t cs = nullptr;
-  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
-  if (e != hipSuccess) return hip_fail(e, "creating the capture stream");
-  hipGraph_t g = nullptr;
-  e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
-  if (e == hipSuccess) {
-    hipError_t le = launch_write(pool, k_cache, v_cache, k, v, slot_mapping, num_rows, cs);
-    if (le == hipSuccess)
-      le = launch_attention(pool, out, q, k_cache, v_cache, block_tables, max_blocks_per_row,
+  return record_graph([&](hipStream_t cs) {
+    hipError_t e = launch_write(pool, k_cache, v_cache, k, v, slot_mapping, num_rows, cs);
+    if (e != hipSuccess) return e;
+    return launch_attention(pool, out, q, k_cache, v_cache, block_tables, max_blocks_per_row,
                             context_lens, num_rows, num_heads, scale, workspace, cs);
-    e = hipStreamEndCapture(cs, &g);   // always end, so the stream leaves capture mode
-    if (le != hipSuccess) e = le;
-  }
-  hipGraphExec_t exec = nullptr;
-  if (e == hipSuccess) e = hipGraphInstantiateWithFlags(&exec, g, 0);
-  if (g) (void)hipGraphDestroy(g);
-  (void)hipStreamDestroy(cs);
-  if (e != hipSuccess) return hip_fail(e, "capturing the decode step");
-  *graph = new pkv_step_graph{exec};
-  return ok();
+  }, graph);
+}
+
+pkv_status pkv_graph_capture_slots(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
+                                   const void* k, const void* v, const int64_t* slot_mapping,
+                                   void* out, const void* q, const int64_t* slot_table,
+                                   int32_t width, int64_t row_stride,
+                                   const int32_t* context_lens, int64_t num_rows,
+                                   int32_t num_heads, float scale, void* workspace,
+                                   size_t workspace_bytes, pkv_step_graph** graph) {
+  if (!graph) return fail(PKV_ERR_NULL, "graph is NULL");
+  *graph = nullptr;
+  pkv_status s = check_slots_shape(pool, width, row_stride, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  if (!k_cache || !v_cache || !k || !v || !slot_mapping || !out || !q || !slot_table ||
+      !context_lens)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  const size_t need = pkv::slot_workspace_bytes(num_rows, num_heads, pool->head_dim, width,
+                                                pool->block_size);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  const int32_t max_blocks = (int32_t)(((int64_t)width + pool->block_size - 1) /
+                                       pool->block_size);
+  s = check_attention_items(pool, max_blocks, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  return record_graph([&](hipStream_t cs) {
+    hipError_t e = launch_write(pool, k_cache, v_cache, k, v, slot_mapping, num_rows, cs);
+    if (e != hipSuccess) return e;
+    return launch_attention_slots(pool, out, q, k_cache, v_cache, slot_table, width,
+                                  row_stride, context_lens, num_rows, num_heads, scale,
+                                  workspace, cs);
+  }, graph);
 }
 
 pkv_status pkv_graph_launch(const pkv_step_graph* graph, void* stream) {

@@ -23,6 +23,9 @@ constexpr int kDefaultDealStatic = 1;
 constexpr int kDefaultLdsStage = 1;
 constexpr int kDefaultMaxQueryGroup = 8;
 
+// Slot input: tokens of one row that one workgroup of the translation pass checks.
+constexpr int kTranslateTokens = 1024;
+
 int tuning_chunk_min();
 int tuning_chunk_max();
 int tuning_decode_waves();
@@ -60,8 +63,11 @@ struct WriteArgs {
 struct Workspace {
   int4* entries;        // [max_entries]: {row, chunk (-1: pad row), chunks in row, context_len}
   int32_t* counters;    // [0] entries, [1] queue ticket, [2] chunk length, [3] its log2,
-                        // [4] section-A entries, [5] section-A+B entries
-  float* partials;      // [rows][heads][max_chunks][head_dim + 2]: m (log2 units), l, acc
+                        // [4] section-A entries, [5] section-A+B entries,
+                        // [6] rows read token by token (slot input)
+  int32_t* row_ctx;     // [rows]: each row's length as the block path reads it
+  int32_t* irregular;   // [rows]: the rows read token by token, counters[6] of them
+  float* partials;      // [rows][heads][max_chunks][head_dim + 4]: m (log2 units), l, -, -, acc
   int64_t max_entries;
   int32_t max_chunks;
 };
@@ -84,6 +90,22 @@ struct AttnArgs {
   int32_t deal_static;     // 1: whole rounds of full chunks are dealt without the queue
   int32_t query_group;     // query heads per work item (they share one KV head)
   float scale;
+  // slot input only (else null / 0): [rows][flag_stride], nonzero where a row's live
+  // slots are not block structured; such rows are left to the token-by-token kernel
+  const int32_t* row_flags;
+  int32_t flag_stride;
+};
+
+// The slot rectangle of a read addressed per token, and what the translation pass
+// derives from it.
+struct SlotArgs {
+  const int64_t* slots;    // [rows][row_stride]; cell (r, t) is the slot of position t
+  int64_t row_stride;      // elements, >= width
+  int32_t width;
+  int32_t max_blocks;      // cdiv(width, block_size): width of the derived block table
+  int32_t flag_stride;     // cdiv(width, kTranslateTokens)
+  int32_t* block_tables;   // out: [rows][max_blocks] derived block ids (live blocks only)
+  int32_t* row_flags;      // out: [rows][flag_stride]
 };
 
 size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
@@ -91,8 +113,17 @@ size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
 Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads,
                           int32_t head_dim, int32_t max_blocks, int32_t block_size);
 
+// Slot input: the derived table and flags, then the block-path workspace.
+size_t slot_workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
+                            int32_t width, int32_t block_size);
+Workspace carve_slot_workspace(void* base, int64_t num_rows, int32_t num_heads,
+                               int32_t head_dim, int32_t width, int32_t block_size,
+                               SlotArgs* s);
+
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream);
+hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& s,
+                                        const Workspace& ws, hipStream_t stream);
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream);
 
 // Event-pair timing of kernel phases (pkv_timing_*).  begin/end bracket one launch.

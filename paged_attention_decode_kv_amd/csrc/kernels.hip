@@ -193,12 +193,24 @@ __device__ int block_exclusive_scan(int x, int* s_wave, int* total) {
   return prefix;
 }
 
-__device__ __forceinline__ int clamp_ctx(int ctx, int limit) {
-  if (ctx < 0 || ctx > limit) {
-    atomicOr(&g_status, PKV_DEVERR_CONTEXT_BOUNDS);
-    ctx = ctx < 0 ? 0 : limit;
+// A row's length as the block path reads it: clamped to what the table addresses (the
+// first pass reports a bad length), and 0 for a row of a slot input whose live slots
+// are not block structured, which the token-by-token kernel reads instead.
+__device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool report,
+                                        bool* irregular) {
+  int ctx = a.context_lens[r];
+  if (ctx < 0 || ctx > a.ctx_limit) {
+    if (report) atomicOr(&g_status, PKV_DEVERR_CONTEXT_BOUNDS);
+    ctx = ctx < 0 ? 0 : a.ctx_limit;
   }
-  return ctx;
+  bool irr = false;
+  if (a.row_flags != nullptr && ctx > 0) {
+    const int32_t* f = a.row_flags + r * a.flag_stride;
+    const int n = (ctx + kTranslateTokens - 1) / kTranslateTokens;
+    for (int c = 0; c < n; ++c) irr |= f[c] != 0;
+  }
+  if (irregular) *irregular = irr;
+  return irr ? 0 : ctx;
 }
 
 // Chooses the chunk length and writes the work list.
@@ -211,7 +223,9 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int limit) {
 //   B. every row's trailing partial chunk, by length, longest first;
 //   C. one zero-output entry per padding row.
 // counters[0] = entries, [1] = queue ticket (reset to 0), [2] = P, [3] = log2 P,
-// [4] = entries in section A, [5] = entries in sections A and B.
+// [4] = entries in section A, [5] = entries in sections A and B, [6] = rows of a slot
+// input left to the token-by-token kernel (listed in ws.irregular).  Every row's
+// length as read here goes to ws.row_ctx for the combine kernel.
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspace ws) {
   constexpr int kMaxChunk = kMaxChunkTokens;
   constexpr int kCand = 6;                 // chunk_max / chunk_min <= 32
@@ -219,19 +233,26 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
   __shared__ int s_bin_start[kMaxChunk];   // first B position of each remainder length
   __shared__ int s_bin_fill[kMaxChunk];
   __shared__ int s_pad_fill;
+  __shared__ int s_irregular;
   __shared__ int s_cand[kCand];
   const int t = threadIdx.x;
   const int lane = t & 63;
   if (t < kCand) s_cand[t] = 0;
-  if (t == 0) s_pad_fill = 0;
+  if (t == 0) {
+    s_pad_fill = 0;
+    s_irregular = 0;
+  }
   __syncthreads();
 
-  // pass 0: chunk count of every candidate length
+  // pass 0: chunk count of every candidate length; row lengths; irregular rows
   const int lmin = a.log2_chunk_min;
   const int ncand = a.log2_chunk_max - lmin + 1;
   int cnt[kCand] = {0, 0, 0, 0, 0, 0};
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
-    const int ctx = clamp_ctx(a.context_lens[r], a.ctx_limit);
+    bool irr;
+    const int ctx = plan_ctx(a, r, true, &irr);
+    ws.row_ctx[r] = ctx;
+    if (irr) ws.irregular[atomicAdd(&s_irregular, 1)] = (int)r;
 #pragma unroll
     for (int k = 0; k < kCand; ++k) cnt[k] += (ctx + (1 << (lmin + k)) - 1) >> (lmin + k);
   }
@@ -258,11 +279,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
   int total_a = 0, n_pad = 0;
   for (int64_t base = 0; base < a.num_rows; base += kPlanThreads) {
     const int64_t r = base + t;
-    int ctx = 0;
-    if (r < a.num_rows) {
-      ctx = a.context_lens[r];
-      ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
-    }
+    const int ctx = r < a.num_rows ? plan_ctx(a, r, false, nullptr) : 0;
     const int full = ctx >> lp;
     const int nch = (ctx + P - 1) >> lp;
     int tile_a, tile_pad;
@@ -299,8 +316,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
   __syncthreads();
   // pass 2: place sections B and C
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
-    int ctx = a.context_lens[r];
-    ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
+    const int ctx = plan_ctx(a, r, false, nullptr);
     const int rem = ctx & (P - 1);
     const int nch = (ctx + P - 1) >> lp;
     if (rem != 0) {
@@ -318,6 +334,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
     ws.counters[3] = lp;
     ws.counters[4] = total_a;
     ws.counters[5] = total_a + total_b;
+    ws.counters[6] = s_irregular;
   }
 }
 
@@ -748,8 +765,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
   __shared__ float s_acc[W][D];
   const int h = blockIdx.x;
   const int64_t r = blockIdx.y;
-  int ctx = a.context_lens[r];
-  ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
+  const int ctx = ws.row_ctx[r];
   const int lp = ws.counters[3];
   const int nch = (ctx + (1 << lp) - 1) >> lp;
   if (nch <= 1) return;
@@ -810,6 +826,183 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
 }
 
 // ------------------------------------------------------------------------- //
+// slot input
+// ------------------------------------------------------------------------- //
+// The translation pass of a read addressed by a slot rectangle.  A row whose live
+// cells are block structured (cell t = B * block_size + t % block_size for every t of
+// block t / block_size, B an allocatable block) is exactly a block-table row: its block
+// ids go to a derived table and the block path reads it.  Any other row is flagged and
+// read token by token.  One workgroup per (row, kTranslateTokens positions); each
+// writes its flag whether or not it found anything, so nothing needs clearing first.
+constexpr int kTranslateThreads = 256;
+
+__global__ void __launch_bounds__(kTranslateThreads) translate_slots_kernel(AttnArgs a,
+                                                                           SlotArgs sa) {
+  const int64_t r = blockIdx.y;
+  int ctx = a.context_lens[r];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
+  const int64_t* row = sa.slots + r * sa.row_stride;
+  const int bs_mask = a.g.block_size - 1;
+  const int64_t n_slots = a.g.num_blocks * a.g.block_size;
+  const int t_base = blockIdx.x * kTranslateTokens;
+  const int t_end = min(ctx, t_base + kTranslateTokens);
+  bool bad = false;
+  for (int t = t_base + threadIdx.x; t < t_end; t += kTranslateThreads) {
+    const int off = t & bs_mask;
+    const int64_t slot = row[t];
+    const int64_t first = off == 0 ? slot : row[t - off];   // the block's first cell
+    const bool ok = first >= 0 && first < n_slots && (first & bs_mask) == 0 &&
+                    slot == first + off;
+    bad |= !ok;
+    if (off == 0 && ok)
+      sa.block_tables[r * sa.max_blocks + (t >> a.g.log2_bs)] =
+          (int32_t)(first >> a.g.log2_bs);
+  }
+  const int any = __syncthreads_or(bad ? 1 : 0);
+  if (threadIdx.x == 0) sa.row_flags[r * sa.flag_stride + blockIdx.x] = any;
+}
+
+// The rows of a slot input that are not block structured, one (row, query head) per
+// workgroup at a time: each 16-lane group (bf16 x 128) takes one token, loads its
+// slot, then the token's K and V through that slot, and folds it into its own online
+// softmax; the groups and the waves are merged at the end of the item.  A live slot
+// outside the allocatable slots is skipped and reported.  Runs after the block path,
+// which wrote zeros for these rows.
+constexpr int kTokenRowThreads = 256;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kTokenRowThreads)
+token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
+  using Sh = Shape<T, D>;
+  using El = Elem<T>;
+  constexpr int E = Sh::E, LPT = Sh::LPT, TPS = Sh::TPS, U = Sh::U;
+  constexpr int ES = sizeof(T);
+  constexpr int WAVES = kTokenRowThreads / 64;
+  constexpr int STEP = WAVES * TPS * U;
+  __shared__ float s_m[WAVES], s_l[WAVES];
+  __shared__ float s_acc[WAVES][D];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane / LPT;
+  const int sub = lane % LPT;
+  const int heads = a.num_heads;
+  const int qpkv = heads / a.g.kv_heads;
+  const int n_items = ws.counters[6] * heads;
+  const int64_t n_slots = a.g.num_blocks * a.g.block_size;
+  const int log2_bs = a.g.log2_bs;
+  const int bs_mask = a.g.block_size - 1;
+  const int64_t tok_bytes = a.g.tok_stride * ES;
+  const int64_t blk_bytes = a.g.blk_stride * ES;
+  const int64_t head_bytes = a.g.head_stride * ES;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+  bool bad = false;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int r = __builtin_amdgcn_readfirstlane(ws.irregular[item / heads]);
+    const int h = item % heads;
+    int ctx = a.context_lens[r];
+    ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
+    ctx = __builtin_amdgcn_readfirstlane(ctx);
+    const int64_t rh = (int64_t)r * heads + h;
+    const uint4 qv = load16(static_cast<const T*>(a.q) + rh * D + sub * E);
+    const int64_t lane_off = (int64_t)(h / qpkv) * head_bytes + sub * E * ES;
+    const int64_t* row = sa.slots + (int64_t)r * sa.row_stride;
+    float m = -INFINITY, l = 0.f, acc[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] = 0.f;
+    for (int t0 = wave * TPS * U; t0 < ctx; t0 += STEP) {
+      uint4 kr[U], vr[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * TPS + g;
+        ok[u] = false;
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+        if (t < ctx) {
+          const int64_t slot = row[t];
+          if (slot >= 0 && slot < n_slots) {
+            ok[u] = true;
+            const int64_t off = (slot >> log2_bs) * blk_bytes + (slot & bs_mask) * tok_bytes +
+                                lane_off;
+            kr[u] = load16_stream(kpool + off);
+            vr[u] = load16_stream(vpool + off);
+          } else {
+            bad = true;
+          }
+        }
+      }
+      float sc[U];
+      float smax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float d = group_sum<LPT>(El::dot(qv, kr[u], 0.f));
+        sc[u] = ok[u] ? d * scale_log2 : -INFINITY;
+        smax = fmaxf(smax, sc[u]);
+      }
+      const float m_new = fmaxf(m, smax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[i] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = __builtin_amdgcn_exp2f(sc[u] - m_use);
+        l += p;
+        El::axpy(p, vr[u], acc);
+      }
+      m = m_new;
+    }
+    // merge the lane groups, then the waves
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      const float m_o = __shfl_xor(m, off);
+      const float l_o = __shfl_xor(l, off);
+      const float mx = fmaxf(m, m_o);
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      const float fa = __builtin_amdgcn_exp2f(m - mu);
+      const float fb = __builtin_amdgcn_exp2f(m_o - mu);
+      l = l * fa + l_o * fb;
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[i] = acc[i] * fa + __shfl_xor(acc[i], off) * fb;
+      m = mx;
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) s_acc[wave][sub * E + i] = acc[i];
+      if (sub == 0) {
+        s_m[wave] = m;
+        s_l[wave] = l;
+      }
+    }
+    __syncthreads();
+    if (wave == 0 && g == 0) {
+      float mx = s_m[0];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[w]);
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      float lt = 0.f, y[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) y[i] = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float f = __builtin_amdgcn_exp2f(s_m[w] - mu);
+        lt += s_l[w] * f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) y[i] += s_acc[w][sub * E + i] * f;
+      }
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;   // every live slot skipped: zeros
+#pragma unroll
+      for (int i = 0; i < E; ++i) y[i] *= inv;
+      store16(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(y));
+    }
+    __syncthreads();
+  }
+  if (bad) atomicOr(&g_status, PKV_DEVERR_SLOT);
+}
+
+// ------------------------------------------------------------------------- //
 // launchers
 // ------------------------------------------------------------------------- //
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -824,7 +1017,8 @@ size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
   const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_min());
   const int64_t entries = num_rows * (mc > 1 ? mc : 1);
   int64_t bytes = align_up(entries * (int64_t)sizeof(int4), 256);
-  bytes += 256;   // counters
+  bytes += 256;                                    // counters
+  bytes += 2 * align_up(num_rows * 4, 256);        // row lengths, irregular rows
   bytes += align_up(num_rows * num_heads * mc * (int64_t)(head_dim + 4) * 4, 256);
   return (size_t)bytes;
 }
@@ -840,10 +1034,43 @@ Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads, int32
   p += align_up(w.max_entries * (int64_t)sizeof(int4), 256);
   w.counters = reinterpret_cast<int32_t*>(p);
   p += 256;
+  w.row_ctx = reinterpret_cast<int32_t*>(p);
+  p += align_up(num_rows * 4, 256);
+  w.irregular = reinterpret_cast<int32_t*>(p);
+  p += align_up(num_rows * 4, 256);
   w.partials = reinterpret_cast<float*>(p);
   (void)num_heads;
   (void)head_dim;
   return w;
+}
+
+static int32_t slot_table_blocks(int32_t width, int32_t block_size) {
+  return (int32_t)(((int64_t)width + block_size - 1) / block_size);
+}
+static int32_t slot_flag_stride(int32_t width) {
+  return (int32_t)(((int64_t)width + kTranslateTokens - 1) / kTranslateTokens);
+}
+
+size_t slot_workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
+                            int32_t width, int32_t block_size) {
+  const int32_t mb = slot_table_blocks(width, block_size);
+  int64_t bytes = align_up(num_rows * mb * 4, 256);
+  bytes += align_up(num_rows * slot_flag_stride(width) * 4, 256);
+  return (size_t)bytes + workspace_bytes(num_rows, num_heads, head_dim, mb, block_size);
+}
+
+Workspace carve_slot_workspace(void* base, int64_t num_rows, int32_t num_heads,
+                               int32_t head_dim, int32_t width, int32_t block_size,
+                               SlotArgs* sa) {
+  const int32_t mb = slot_table_blocks(width, block_size);
+  sa->max_blocks = mb;
+  sa->flag_stride = slot_flag_stride(width);
+  char* p = static_cast<char*>(base);
+  sa->block_tables = reinterpret_cast<int32_t*>(p);
+  p += align_up(num_rows * mb * 4, 256);
+  sa->row_flags = reinterpret_cast<int32_t*>(p);
+  p += align_up(num_rows * sa->flag_stride * 4, 256);
+  return carve_workspace(p, num_rows, num_heads, head_dim, mb, block_size);
 }
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
@@ -961,6 +1188,71 @@ hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws,
     default:
       return hipErrorInvalidValue;
   }
+}
+
+static hipError_t device_cus(int* cus) {
+  static int count[64] = {0};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 64) return hipErrorInvalidDevice;
+  if (count[dev] == 0) {
+    int n = 0;
+    err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    count[dev] = n > 0 ? n : 1;
+  }
+  *cus = count[dev];
+  return hipSuccess;
+}
+
+template <typename T, int D>
+static void launch_token_rows(const AttnArgs& a, const SlotArgs& sa, const Workspace& ws,
+                              int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((token_rows_kernel<T, D>), dim3(grid), dim3(kTokenRowThreads), 0,
+                     stream, a, sa, ws, a.scale * 1.4426950408889634f);
+}
+
+hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
+                                        const Workspace& ws, hipStream_t stream) {
+  AttnArgs b = a;
+  b.block_tables = sa.block_tables;
+  b.max_blocks = sa.max_blocks;
+  b.row_flags = sa.row_flags;
+  b.flag_stride = sa.flag_stride;
+  timing_begin(PKV_PHASE_TRANSLATE, stream);
+  hipLaunchKernelGGL(translate_slots_kernel, dim3((unsigned)sa.flag_stride, (unsigned)a.num_rows),
+                     dim3(kTranslateThreads), 0, stream, b, sa);
+  timing_end(PKV_PHASE_TRANSLATE, stream);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = launch_paged_attention(b, ws, stream);
+  if (err != hipSuccess) return err;
+  // the rows the block path could not take: one workgroup per CU works through them
+  // (the count is on the device; with none, every workgroup exits at once)
+  int cus = 0;
+  err = device_cus(&cus);
+  if (err != hipSuccess) return err;
+  timing_begin(PKV_PHASE_TOKEN_ROWS, stream);
+  const bool f32 = a.g.dtype == PKV_F32;
+  switch (a.g.head_dim) {
+    case 64:
+      f32 ? launch_token_rows<float, 64>(b, sa, ws, cus, stream)
+          : launch_token_rows<uint16_t, 64>(b, sa, ws, cus, stream);
+      break;
+    case 128:
+      f32 ? launch_token_rows<float, 128>(b, sa, ws, cus, stream)
+          : launch_token_rows<uint16_t, 128>(b, sa, ws, cus, stream);
+      break;
+    case 256:
+      f32 ? launch_token_rows<float, 256>(b, sa, ws, cus, stream)
+          : launch_token_rows<uint16_t, 256>(b, sa, ws, cus, stream);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  timing_end(PKV_PHASE_TOKEN_ROWS, stream);
+  return hipGetLastError();
 }
 
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream) {

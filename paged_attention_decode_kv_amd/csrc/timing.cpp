@@ -11,7 +11,7 @@
 namespace pkv {
 namespace {
 
-constexpr int kPhases = 4;
+constexpr int kPhases = 6;
 
 struct PhaseLog {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;  // recorded, not yet read

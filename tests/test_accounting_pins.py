@@ -84,3 +84,18 @@ def test_algorithmic_bytes_components():
     assert b["kv_write"] == 2 * 3 * 2 * 64 * 2 * 2
     assert b["total"] == b["kv"] + b["q_out"] + b["tables"] + b["kv_write"]
     assert acc.row_heads(lens, 4) == 8
+
+
+def test_slot_addressing_bytes():
+    """One int64 cell per live position instead of one int32 id per live block: at
+    block size 16 the rectangle holds 16x the cells (Day 51, "Why it matters"), 32x the
+    bytes."""
+    lens = np.array([16, 48, 0, 160])
+    kw = dict(heads=4, kv_heads=2, head_dim=64, block_size=16, elem=2, write_tokens=4)
+    blocks = acc.algorithmic_bytes(lens, **kw)
+    slots = acc.algorithmic_bytes(lens, address="slots", **kw)
+    assert slots["tables"] == (16 + 48 + 160) * 8 + 4 * 4
+    assert (slots["tables"] - 16) == 32 * (blocks["tables"] - 16)
+    assert slots["kv"] == blocks["kv"] and slots["kv_write"] == blocks["kv_write"]
+    with pytest.raises(ValueError):
+        acc.algorithmic_bytes(lens, address="rows", **kw)

@@ -177,3 +177,67 @@ def test_row_buckets():
         bucket_for(b, 17)
     with pytest.raises(binding.PagedKVError, match="EMPTY"):
         bucket_for(b, 0)
+
+
+def _slot_cases():
+    w = wl.make_custom([16, 40, 0, 7], heads=4, kv_heads=2, head_dim=64, num_blocks=12,
+                       max_blocks=4, seed=5)
+    sink = w.num_blocks * w.block_size
+    table = np.full((w.rows, 64), -7, dtype=np.int64)
+    for r in range(w.rows):
+        for t in range(int(w.context_lens[r])):
+            table[r, t] = int(w.block_tables[r, t // 16]) * 16 + t % 16
+    rect = table[:, :48]                            # a window on a wider table
+    cases = [("legal window", rect, w.context_lens)]
+    ctx = w.context_lens.copy(); ctx[1] = -3
+    cases.append(("negative length", rect, ctx))
+    ctx = w.context_lens.copy(); ctx[3] = 49
+    cases.append(("past the window", rect, ctx))
+    ctx = w.context_lens.copy(); ctx[3] = 48
+    cases.append(("length fills the window", rect, ctx))
+    for bad in (-1, sink, sink + 5):
+        r2 = table.copy()[:, :48]
+        r2[1, 39] = bad
+        cases.append((f"live cell {bad}", r2, w.context_lens))
+    r2 = table.copy()[:, :48]
+    r2[1, 40:] = sink + 99
+    r2[2, :] = -1
+    cases.append(("junk past the length", r2, w.context_lens))
+    r2 = table.copy()[:, :48]
+    r2[0, 0] = -1
+    ctx = w.context_lens.copy(); ctx[3] = 49
+    cases.append(("bounds before slots", r2, ctx))
+    cases.append(("zero width", table[:, :0], np.zeros_like(w.context_lens)))
+    assert len(cases) == 10
+    return w, cases
+
+
+@pytest.mark.parametrize("idx", range(10))
+def test_slot_refusals_match_the_oracle(lib, idx):
+    w, cases = _slot_cases()
+    name, rect, ctx = cases[idx]
+    k, v = wl.history_host(w)
+    want = _oracle_code(lambda: oracle.validate_attention_slots(
+        w.q, k, v, rect, ctx, num_blocks=w.num_blocks, block_size=w.block_size,
+        layout=w.layout, dtype=w.dtype))
+    d = binding.host_desc(w.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype,
+                          w.layout)
+    assert binding.check_attention_slots_host(d, rect, ctx, w.heads) == want, name
+
+
+def test_slot_shape_refusals(lib):
+    w, cases = _slot_cases()
+    rect, ctx = cases[0][1], cases[0][2]
+    d = binding.host_desc(w.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype,
+                          w.layout)
+    assert binding.check_attention_slots_host(d, rect[:0], ctx[:0], w.heads) == "EMPTY"
+    assert binding.check_attention_slots_host(d, rect, ctx, 3) == "SHAPE"
+    p = ctypes.c_void_p(16)
+    # a row stride shorter than the width
+    assert _capi.STATUS_NAMES[lib.pkv_check_attention_slots_host(
+        ctypes.byref(d), p, 48, 47, p, 4, 4)] == "SHAPE"
+    assert _capi.STATUS_NAMES[lib.pkv_check_attention_slots_host(
+        ctypes.byref(d), p, (1 << 24) + 1, (1 << 24) + 1, p, 4, 4)] == "UNSUPPORTED"
+    assert lib.pkv_workspace_bytes_slots(ctypes.byref(d), 4, 4, 0) == 0
+    assert lib.pkv_workspace_bytes_slots(ctypes.byref(d), 4, 4, 48) > \
+        lib.pkv_workspace_bytes(ctypes.byref(d), 4, 4, 3)

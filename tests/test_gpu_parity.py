@@ -11,12 +11,14 @@ sampled rows, each recomputed by the oracle from a host copy of just the blocks 
 rows name (block relabelling leaves the oracle's result unchanged, a pinned invariant).
 """
 
+import zlib
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from paged_attention_decode_kv_amd import binding
+from paged_attention_decode_kv_amd import _capi, binding
 from paged_attention_decode_kv_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -550,3 +552,248 @@ def test_caller_stream_capture_of_the_step():
             # the second replay writes the same vectors into the same slots
             assert np.array_equal(to_host(st.k_cache, "bf16")[:nb], kw[:nb])
             assert np.array_equal(to_host(st.v_cache, "bf16")[:nb], vw[:nb])
+
+
+# --------------------------------------------------------------------------- #
+# the read through a per-token slot rectangle
+# --------------------------------------------------------------------------- #
+def _block_table_rect(w, width, stride, junk=-7):
+    """The slot window a slot table holds for ``w``'s block placement, as a
+    [rows, width] view of a [rows, stride] table; junk past each row's length."""
+    t = np.arange(width)
+    bt = np.where(w.block_tables >= 0, w.block_tables, 0).astype(np.int64)
+    rect = bt[:, t // w.block_size] * w.block_size + t % w.block_size
+    table = np.full((w.rows, stride), junk, dtype=np.int64)
+    table[:, :width] = np.where(t[None, :] < w.context_lens[:, None], rect, junk)
+    return table
+
+
+def _scatter_rows(w, table, rows, rng):
+    """Rewrite the live cells of ``rows`` (but each row's newest cell, its write slot)
+    with distinct random slots that no other row uses."""
+    sink = w.num_blocks * w.block_size
+    used = set()
+    for r in range(w.rows):
+        n = int(w.context_lens[r])
+        if r not in rows:
+            used.update(table[r, :n].tolist())
+        elif n:
+            used.add(int(table[r, n - 1]))
+    free = iter(s for s in rng.permutation(sink).tolist() if s not in used)
+    for r in rows:
+        n = int(w.context_lens[r])
+        for t in range(n - 1):
+            table[r, t] = next(free)
+    return table
+
+
+def _slot_run(st, table, width, *, validate=True, out=None):
+    w = st.w
+    binding.kv_write(st.k_new, st.v_new, st.slots, st.k_cache, st.v_cache, layout=w.layout,
+                     validate=validate)
+    tab = to_dev(table)
+    got = binding.paged_attention_slots(st.q, st.k_cache, st.v_cache, tab[:, :width],
+                                        st.lens, w.scale, layout=w.layout, out=out,
+                                        validate=validate)
+    torch.cuda.synchronize()
+    return got
+
+
+def _slot_oracle(w, k_host, v_host, table, width):
+    kw, vw = k_host.copy(), v_host.copy()
+    oracle.kv_write(kw, vw, w.k_new, w.v_new, w.slot_mapping, num_blocks=w.num_blocks,
+                    block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+    return oracle.paged_attention_slots(w.q, kw, vw, table[:, :width], w.context_lens,
+                                        w.scale, num_blocks=w.num_blocks,
+                                        block_size=w.block_size, layout=w.layout,
+                                        dtype=w.dtype)
+
+
+SLOT_CASES = [
+    # name, lens, heads, kv_heads, head_dim, block_size, dtype, layout
+    ("tiny-f32-HND", [16, 40], 4, 4, 64, 16, "f32", "HND"),
+    ("tiny-f32-NHD", [16, 40, 0, 3], 4, 4, 64, 16, "f32", "NHD"),
+    ("ragged-bf16", [1, 17, 0, 300, 1024, 1025, 2100, 64], 8, 8, 128, 16, "bf16", "HND"),
+    ("gqa-bf16", [700, 0, 33, 1500, 129], 16, 4, 128, 16, "bf16", "HND"),
+    ("d256-bs32", [90, 513, 0, 1], 4, 2, 256, 32, "bf16", "NHD"),
+]
+
+
+@pytest.mark.parametrize("case", SLOT_CASES, ids=[c[0] for c in SLOT_CASES])
+def test_block_structured_slots_equal_block_tables(case):
+    """A window whose live cells follow the block placement takes the block path: bit
+    for bit the block-table read, and the oracle's value."""
+    name, lens, heads, kvh, d, bs, dtype, layout = case
+    w = wl.make_custom(lens, heads=heads, kv_heads=kvh, head_dim=d, block_size=bs,
+                       dtype=dtype, layout=layout, seed=zlib.crc32(name.encode()))
+    width = w.max_blocks * w.block_size
+    table = _block_table_rect(w, width, width + 37)
+    say(f"slots {name}: lens {lens} width {width}")
+    st = Step(w, host_history=True)
+    ref_block = st.run()
+    blk = to_host(ref_block, dtype).copy()
+    st2 = Step(w, host_history=True)
+    got = _slot_run(st2, table, width)
+    assert np.array_equal(to_host(got, dtype), blk), "slot window differs from block tables"
+    ref = _slot_oracle(w, st.k_host, st.v_host, table, width)
+    assert_close(to_host(got, dtype), ref, dtype, name)
+    assert binding.device_status(DEV, clear=True) == 0
+
+
+@pytest.mark.parametrize("case", SLOT_CASES, ids=[c[0] for c in SLOT_CASES])
+def test_scattered_slots_are_read_token_by_token(case):
+    """Rows whose live cells name scattered slots (and a mix with block-structured
+    rows and padding) match the oracle."""
+    name, lens, heads, kvh, d, bs, dtype, layout = case
+    w = wl.make_custom(lens, heads=heads, kv_heads=kvh, head_dim=d, block_size=bs,
+                       dtype=dtype, layout=layout, num_blocks=sum(wl.cdiv(c, bs) for c in lens) + 40,
+                       seed=zlib.crc32(name.encode()) + 1)
+    width = w.max_blocks * w.block_size
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    live = [r for r in range(w.rows) if w.context_lens[r] > 0]
+    scattered = live[::2]
+    table = _scatter_rows(w, _block_table_rect(w, width, width), scattered, rng)
+    say(f"scattered {name}: rows {scattered} of {w.rows}")
+    st = Step(w, host_history=True)
+    got = _slot_run(st, table, width)
+    ref = _slot_oracle(w, st.k_host, st.v_host, table, width)
+    assert_close(to_host(got, dtype), ref, dtype, name)
+    assert binding.device_status(DEV, clear=True) == 0
+
+
+def test_one_moved_token_past_the_first_translation_chunk():
+    """A single cell that breaks the block structure at position > 1024 sends its row
+    token by token; the other rows stay on the block path, bit for bit."""
+    w = wl.make_custom([3000, 2500, 900], heads=8, kv_heads=8, head_dim=128, dtype="bf16",
+                       num_blocks=600, seed=77)
+    width = w.max_blocks * w.block_size
+    table = _block_table_rect(w, width, width)
+    used = set(np.concatenate([table[r, :w.context_lens[r]] for r in range(3)]).tolist())
+    spare = next(s for s in range(w.num_blocks * 16) if s not in used)
+    table[0, 2049] = spare                      # translation chunk 2 of row 0
+    say("moved token: row 0 position 2049")
+    st = Step(w, host_history=True)
+    got = to_host(_slot_run(st, table, width), "bf16")
+    ref = _slot_oracle(w, st.k_host, st.v_host, table, width)
+    assert_close(got, ref, "bf16", "moved token")
+    blk = to_host(Step(w, host_history=True).run(), "bf16")
+    assert np.array_equal(got[1:], blk[1:])     # untouched rows: the block path
+    assert not np.array_equal(got[0], blk[0])
+
+
+def test_slot_refusals_touch_nothing():
+    w = wl.make_custom([40, 16, 0], heads=4, kv_heads=4, head_dim=64, dtype="f32", seed=9)
+    width = w.max_blocks * w.block_size
+    st = Step(w, host_history=True)
+    tab = to_dev(_block_table_rect(w, width, width))
+    out = torch.full_like(st.q, 3.0)
+    sink = w.num_blocks * w.block_size
+    for row, t, bad, code in ((0, 39, -1, "SLOT"), (1, 0, sink, "SLOT"),
+                              (0, 5, sink + 1, "SLOT")):
+        t2 = tab.clone()
+        t2[row, t] = bad
+        with pytest.raises(binding.PagedKVError, match=code):
+            binding.paged_attention_slots(st.q, st.k_cache, st.v_cache, t2, st.lens,
+                                          w.scale, out=out)
+    lens = st.lens.clone()
+    lens[1] = width + 1
+    with pytest.raises(binding.PagedKVError, match="CONTEXT_BOUNDS"):
+        binding.paged_attention_slots(st.q, st.k_cache, st.v_cache, tab, lens, w.scale,
+                                      out=out)
+    with pytest.raises(binding.PagedKVError, match="DTYPE"):
+        binding.paged_attention_slots(st.q, st.k_cache, st.v_cache, tab.int(), st.lens,
+                                      w.scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+def test_bad_live_slot_without_validation_is_skipped_and_reported():
+    """validate=False: a live cell outside the slots is skipped (the kernel never reads
+    it) and raises the SLOT status bit; rows without one are still exact."""
+    w = wl.make_custom([40, 16, 33], heads=4, kv_heads=4, head_dim=64, dtype="f32", seed=4)
+    width = w.max_blocks * w.block_size
+    table = _block_table_rect(w, width, width)
+    table[0, 3] = -(1 << 40)
+    table[2, 7] = w.num_blocks * w.block_size + 12345
+    st = Step(w, host_history=True)
+    binding.device_status(DEV, clear=True)
+    got = to_host(_slot_run(st, table, width, validate=False), "f32")
+    assert binding.device_status(DEV, clear=True) & _capi.DEVERR_SLOT
+    ok = table.copy()
+    ok[0, 3] = ok[0, 2]
+    ok[2, 7] = ok[2, 6]
+    ref = _slot_oracle(w, st.k_host, st.v_host, ok, width)
+    assert_close(got[1:2], ref[1:2], "f32", "clean row")
+    assert np.all(np.isfinite(got))
+
+
+def test_config5_as_a_slot_window():
+    """The full-width batch read through its slot window (256 x 8192 int64 cells, a
+    view of a wider table): every output bit-identical to the block-table read, and
+    sampled rows against the oracle."""
+    w = wl.make_config(5)
+    width = w.max_blocks * w.block_size
+    st = Step(w)
+    say(f"config 5 slot window {w.rows} x {width}")
+    blk = to_host(st.run(validate=False), "bf16").copy()
+    t = torch.arange(width, device=DEV)
+    tables = st.tables.long().clamp_min(0)
+    rect = tables[:, t // w.block_size] * w.block_size + t % w.block_size
+    table = torch.full((w.rows, width + 64), -1, dtype=torch.int64, device=DEV)
+    table[:, :width] = torch.where(t[None, :] < st.lens[:, None].long(), rect, -1)
+    got = binding.paged_attention_slots(st.q, st.k_cache, st.v_cache, table[:, :width],
+                                        st.lens, w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(got, "bf16"), blk)
+    rng = np.random.default_rng(12)
+    live = [r for r in range(w.rows) if w.context_lens[r] > 0]
+    rows = sorted(rng.choice(live, 6, replace=False).tolist())
+    ref = oracle_rows(st, rows)
+    assert_close(blk[rows], ref, "bf16", "config 5 slot window")
+
+
+def test_captured_slot_window_step():
+    """pkv_graph_capture_slots recorded over an all-padding batch replays real steps
+    whose slot windows are written into the same table: bit for bit the eager slot
+    read, with block-structured and scattered rows."""
+    w = wl.make_custom([300, 0, 1100, 57, 2000, 16], heads=8, kv_heads=2, head_dim=128,
+                       dtype="bf16", num_blocks=400, seed=31)
+    width = w.max_blocks * w.block_size
+    table_host = _block_table_rect(w, width, width + 16)
+    table_host = _scatter_rows(w, table_host, [2, 3], np.random.default_rng(2))
+    st = Step(w, host_history=True)
+    k_host, v_host = st.k_host, st.v_host
+    table = torch.full((w.rows, width + 16), -1, dtype=torch.int64, device=DEV)
+    out = torch.empty_like(st.q)
+    ws = torch.empty(binding.workspace_bytes_slots(st.k_cache, w.rows, w.heads, width),
+                     dtype=torch.uint8, device=DEV)
+    real = [t.clone() for t in (st.q, st.k_new, st.v_new, st.slots, st.lens)]
+    st.lens.zero_()
+    st.slots.fill_(w.sink)
+    say(f"captured slot window: rows {w.rows} width {width}")
+    graph = binding.capture_step_slots(st.k_new, st.v_new, st.slots, st.q, st.k_cache,
+                                       st.v_cache, table[:, :width], st.lens, w.scale, out,
+                                       ws)
+    out.fill_(5.0)
+    graph.launch()
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    for dst, src in zip((st.q, st.k_new, st.v_new, st.slots, st.lens), real):
+        dst.copy_(src)
+    table.copy_(to_dev(table_host))
+    torch.cuda.synchronize()
+    replays = []
+    for _ in range(2):
+        st.k_cache.copy_(to_dev(k_host, "bf16"))
+        st.v_cache.copy_(to_dev(v_host, "bf16"))
+        graph.launch()
+        torch.cuda.synchronize()
+        replays.append(to_host(out, "bf16").copy())
+    graph.destroy()
+    st2 = Step(w, host_history=True)
+    eager = to_host(_slot_run(st2, table_host, width), "bf16")
+    for got in replays:
+        assert np.array_equal(got, eager)
+    ref = _slot_oracle(w, k_host, v_host, table_host, width)
+    assert_close(eager, ref, "bf16", "captured slot window")
+    assert binding.device_status(DEV, clear=True) == 0
