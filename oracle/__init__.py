@@ -18,6 +18,9 @@ pages:
   ``rebuild_mapping`` construction (Day 51, "What I added today") and the
   block-id addressing ``block_id * block_size + offset`` (Day 51, "Why it
   matters").
+* ``paged_attention_multi``: several new tokens (queries) per row, each
+  attending causally over the positions up to its own (Day 59, "Why it
+  matters": the rectangle's query_len axis).
 * ``paged_attention_slots``: the same read addressed by a per-token slot
   rectangle handed in directly, a window on the persistent slot table (Day 51,
   "What I added today").
@@ -36,11 +39,13 @@ from .decode import (  # noqa: F401
     gather,
     kv_write,
     paged_attention,
+    paged_attention_multi,
     paged_attention_slots,
     rebuild_mapping,
     sink_slot,
     slot_view,
     validate_attention,
+    validate_attention_multi,
     validate_attention_slots,
     validate_write,
 )

@@ -158,6 +158,16 @@ def validate_attention(q, k_cache, v_cache, block_tables, context_lens, *, num_b
       live prefix, -1 included, are never read (Day 59, "Why it matters") and are
       not checked.
     """
+    limit = _check_read_shape(q, k_cache, v_cache, block_tables, context_lens,
+                              num_blocks=num_blocks, block_size=block_size, layout=layout,
+                              dtype=dtype)
+    _check_lengths(context_lens, limit)
+    _check_block_ids(block_tables, context_lens, num_blocks, block_size)
+
+
+def _check_read_shape(q, k_cache, v_cache, block_tables, context_lens, *, num_blocks,
+                      block_size, layout, dtype):
+    """EMPTY, DTYPE and SHAPE of the read; returns the largest legal length."""
     ctx = np.asarray(context_lens)
     bt = np.asarray(block_tables)
     r = int(ctx.shape[0]) if ctx.ndim >= 1 else 0
@@ -182,14 +192,22 @@ def validate_attention(q, k_cache, v_cache, block_tables, context_lens, *, num_b
         raise Refusal("SHAPE", f"{h} query heads is not a multiple of {hkv} KV heads")
     if ctx.shape != (r,) or bt.ndim != 2 or bt.shape[0] != r or bt.shape[1] < 1:
         raise Refusal("SHAPE", "block_tables must be [rows, max_blocks>=1], context_lens [rows]")
-    m = int(bt.shape[1])
-    limit = min(m * block_size, num_blocks * block_size)
+    return min(int(bt.shape[1]) * block_size, num_blocks * block_size)
+
+
+def _check_lengths(context_lens, limit):
+    ctx = np.asarray(context_lens)
     bad = np.nonzero((ctx < 0) | (ctx > limit))[0]
     if bad.size:
         i = int(bad[0])
         raise Refusal("CONTEXT_BOUNDS",
                       f"context_lens[{i}] = {int(ctx[i])} outside [0, {limit}]")
-    for row in range(r):
+
+
+def _check_block_ids(block_tables, context_lens, num_blocks, block_size):
+    ctx = np.asarray(context_lens)
+    bt = np.asarray(block_tables)
+    for row in range(int(ctx.shape[0])):
         live = -(-int(ctx[row]) // block_size)
         ids = bt[row, :live]
         wrong = np.nonzero((ids < 0) | (ids >= num_blocks))[0]
@@ -254,6 +272,34 @@ def validate_attention_slots(q, k_cache, v_cache, slot_rect, context_lens, *, nu
             t = int(wrong[0])
             raise Refusal("SLOT", f"slot rectangle [{row}, {t}] = {int(cells[t])} "
                                   f"outside [0, {slots})")
+
+
+def validate_attention_multi(q, k_cache, v_cache, block_tables, context_lens, *,
+                             num_blocks, block_size, layout, dtype):
+    """Refusals of the multi-token read, in the order EMPTY, DTYPE, SHAPE,
+    CONTEXT_BOUNDS, BLOCK_ID: those of the decode read, with q
+    ``[rows, query_len, heads, head_dim]`` and one more bound, a live row's length
+    counting its query_len new tokens, so it is 0 or at least query_len."""
+    ctx = np.asarray(context_lens)
+    r = int(ctx.shape[0]) if ctx.ndim >= 1 else 0
+    if r == 0:
+        raise Refusal("EMPTY", "no rows")
+    _check_pool(k_cache, v_cache, num_blocks, block_size, layout, dtype)
+    if q.dtype != _STORAGE[dtype]:
+        raise Refusal("DTYPE", "q storage does not match the declared dtype")
+    if q.ndim != 4 or q.shape[0] != r or q.shape[1] < 1:
+        raise Refusal("SHAPE", f"q shape {q.shape} is not [rows={r}, query_len>=1, heads, d]")
+    n_q = int(q.shape[1])
+    limit = _check_read_shape(q[:, 0], k_cache, v_cache, block_tables, context_lens,
+                              num_blocks=num_blocks, block_size=block_size, layout=layout,
+                              dtype=dtype)
+    _check_lengths(context_lens, limit)
+    short = np.nonzero((ctx > 0) & (ctx < n_q))[0]
+    if short.size:
+        i = int(short[0])
+        raise Refusal("CONTEXT_BOUNDS", f"context_lens[{i}] = {int(ctx[i])} is live but "
+                                        f"shorter than query_len {n_q}")
+    _check_block_ids(block_tables, context_lens, num_blocks, block_size)
 
 
 # --------------------------------------------------------------------------- #
@@ -386,5 +432,52 @@ def _attend(q, k_cache, v_cache, mapping, live, context_lens, scale, layout, dty
     probs = weights / denom
     # weighted sum of V: [R, H, 1, W] @ [R, H, W, D]
     out = np.matmul(probs, vg.transpose(0, 2, 1, 3))[:, :, 0, :]
+    out[~has_keys] = 0.0
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# several new tokens per row
+# --------------------------------------------------------------------------- #
+def paged_attention_multi(q, k_cache, v_cache, block_tables, context_lens, scale, *,
+                          num_blocks, block_size, layout, dtype):
+    """The read with query_len new tokens per row, float64
+    ``[rows, query_len, heads, head_dim]``.
+
+    The rectangle of Day 59 ("Why it matters") has a query_len axis beside rows and
+    heads; query i of row r is the token at position len_r - query_len + i, and it
+    attends causally, over the positions t <= its own.  The scores are
+    [rows, heads, query_len, width]; a length-0 row's outputs are zero.
+    """
+    validate_attention_multi(q, k_cache, v_cache, block_tables, context_lens,
+                             num_blocks=num_blocks, block_size=block_size, layout=layout,
+                             dtype=dtype)
+    rows, n_q, heads, head_dim = q.shape
+    kv_heads = k_cache.shape[1] if layout == "HND" else k_cache.shape[2]
+    kv_of_head = np.arange(heads) // (heads // kv_heads)
+    mapping, live = rebuild_mapping(block_tables, context_lens, block_size)
+    width = mapping.shape[1]
+    out = np.zeros((rows, n_q, heads, head_dim), dtype=np.float64)
+    if width == 0:
+        return out
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    kg = gather(k_cache, mapping, layout, dtype)[:, :, kv_of_head, :]  # [R, W, H, D]
+    vg = gather(v_cache, mapping, layout, dtype)[:, :, kv_of_head, :]
+    qf = decode_storage(q, dtype).transpose(0, 2, 1, 3)                 # [R, H, n_q, D]
+    scores = float(scale) * np.matmul(qf, kg.transpose(0, 2, 3, 1))     # [R, H, n_q, W]
+    # query i sees t <= len - n_q + i (which also keeps t < len)
+    last = ctx[:, None] - n_q + np.arange(n_q)[None, :]                 # [R, n_q]
+    t = np.arange(width)
+    visible = t[None, None, :] <= last[:, :, None]                      # [R, n_q, W]
+    scores = np.where(visible[:, None, :, :], scores, -np.inf)
+    has_keys = ctx > 0
+    peak = np.max(scores, axis=-1, keepdims=True)
+    peak = np.where(has_keys[:, None, None, None], peak, 0.0)
+    weights = np.exp(scores - peak)
+    denom = np.sum(weights, axis=-1, keepdims=True)
+    denom = np.where(has_keys[:, None, None, None], denom, 1.0)
+    probs = weights / denom
+    res = np.matmul(probs, vg.transpose(0, 2, 1, 3))                   # [R, H, n_q, D]
+    out = res.transpose(0, 2, 1, 3).copy()
     out[~has_keys] = 0.0
     return out

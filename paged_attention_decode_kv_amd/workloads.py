@@ -80,12 +80,14 @@ class Workload:
     num_blocks: int
     context_lens: np.ndarray          # int32 [rows]
     block_tables: np.ndarray          # int32 [rows, max_blocks], -1 past the live prefix
-    slot_mapping: np.ndarray          # int64 [rows]: this step's write slot per row
-    q: np.ndarray                     # storage [rows, heads, head_dim]
-    k_new: np.ndarray                 # storage [rows, kv_heads, head_dim]
+    slot_mapping: np.ndarray          # int64 [rows * query_len]: this step's write slots
+    q: np.ndarray                     # storage [rows, heads, head_dim], or with
+                                      # query_len > 1 [rows, query_len, heads, head_dim]
+    k_new: np.ndarray                 # storage [rows * query_len, kv_heads, head_dim]
     v_new: np.ndarray
     scale: float
     meta: dict = field(default_factory=dict)
+    query_len: int = 1                # new tokens (queries) per row this step
 
     @property
     def max_blocks(self) -> int:
@@ -137,35 +139,42 @@ def _place_blocks(rng, context_lens, block_size, num_blocks, max_blocks):
     return tables
 
 
-def _write_slots(context_lens, block_tables, block_size, num_blocks):
-    """The step's write slot per row: the row's last live position (its length
-    includes the token written this step), or the sink slot for a pad row."""
-    slots = np.empty(len(context_lens), dtype=np.int64)
+def _write_slots(context_lens, block_tables, block_size, num_blocks, query_len=1):
+    """The step's write slots, query_len per row: the row's last query_len live
+    positions (its length includes the tokens written this step), or the sink slot for
+    every token of a pad row."""
+    slots = np.empty(len(context_lens) * query_len, dtype=np.int64)
     for r, c in enumerate(context_lens):
-        if c == 0:
-            slots[r] = num_blocks * block_size
-        else:
-            pos = int(c) - 1
-            slots[r] = int(block_tables[r, pos // block_size]) * block_size + pos % block_size
+        for i in range(query_len):
+            if c == 0:
+                slots[r * query_len + i] = num_blocks * block_size
+            else:
+                pos = int(c) - query_len + i
+                slots[r * query_len + i] = (int(block_tables[r, pos // block_size]) *
+                                            block_size + pos % block_size)
     return slots
 
 
 def _finish(name, seed, rng, lens, *, heads, kv_heads, head_dim, block_size, dtype,
-            layout, num_blocks, max_blocks, meta=None):
+            layout, num_blocks, max_blocks, meta=None, query_len=1):
     lens = np.asarray(lens, dtype=np.int32)
+    if np.any((lens > 0) & (lens < query_len)):
+        raise ValueError("a live row must hold at least its query_len new tokens")
     tables = _place_blocks(rng, lens, block_size, num_blocks, max_blocks)
-    slots = _write_slots(lens, tables, block_size, num_blocks)
+    slots = _write_slots(lens, tables, block_size, num_blocks, query_len)
     rows = len(lens)
-    q = to_storage(rng.standard_normal((rows, heads, head_dim), dtype=np.float32), dtype)
-    k_new = to_storage(rng.standard_normal((rows, kv_heads, head_dim), dtype=np.float32),
-                       dtype)
-    v_new = to_storage(rng.standard_normal((rows, kv_heads, head_dim), dtype=np.float32),
-                       dtype)
+    q_shape = (rows, heads, head_dim) if query_len == 1 else \
+        (rows, query_len, heads, head_dim)
+    q = to_storage(rng.standard_normal(q_shape, dtype=np.float32), dtype)
+    new_shape = (rows * query_len, kv_heads, head_dim)
+    k_new = to_storage(rng.standard_normal(new_shape, dtype=np.float32), dtype)
+    v_new = to_storage(rng.standard_normal(new_shape, dtype=np.float32), dtype)
     return Workload(name=name, seed=seed, rows=rows, heads=heads, kv_heads=kv_heads,
                     head_dim=head_dim, block_size=block_size, dtype=dtype, layout=layout,
                     num_blocks=num_blocks, context_lens=lens, block_tables=tables,
                     slot_mapping=slots, q=q, k_new=k_new, v_new=v_new,
-                    scale=1.0 / math.sqrt(head_dim), meta=dict(meta or {}))
+                    scale=1.0 / math.sqrt(head_dim), meta=dict(meta or {}),
+                    query_len=query_len)
 
 
 def _lognormal_lens(rng, n, median, sigma, hi):
@@ -176,34 +185,47 @@ def _lognormal_lens(rng, n, median, sigma, hi):
 # --------------------------------------------------------------------------- #
 # the five named configurations
 # --------------------------------------------------------------------------- #
-def make_config(index: int, layout: str = "HND", kv_heads: int | None = None) -> Workload:
+def make_config(index: int, layout: str = "HND", kv_heads: int | None = None,
+                query_len: int = 1) -> Workload:
     """Build configuration ``index`` (1..5) with seed = index.
 
     ``kv_heads`` gives the grouped-query variant of a configuration: the same lengths,
     placement and query heads, with fewer KV heads (query head h reads KV head
     h // (heads // kv_heads)); the pool shrinks by heads / kv_heads.  The named
-    configurations themselves have kv_heads == heads."""
-    w = _make_config(index, layout, kv_heads)
+    configurations themselves have kv_heads == heads.
+
+    ``query_len`` gives the multi-token variant: every row gets query_len new tokens
+    (queries), its last query_len positions, and a live row shorter than query_len is
+    lengthened to query_len.  The draws are the same up to the shapes of q and the new
+    K/V."""
+    w = _make_config(index, layout, kv_heads, query_len)
     if kv_heads is not None:
         w.name = f"{w.name}-gqa{w.heads // w.kv_heads}"
+    if query_len != 1:
+        w.name = f"{w.name}-q{query_len}"
     return w
 
 
-def _make_config(index, layout, kv_heads_override):
+def _make_config(index, layout, kv_heads_override, query_len=1):
     seed = int(index)
     rng = np.random.default_rng(seed)
     name = CONFIG_NAMES[index]
     bs = 16
+
+    def fin(name, seed, rng, lens, **kw):   # multi-token: live rows hold query_len tokens
+        lens = np.asarray(lens, dtype=np.int64)
+        lens = np.where(lens > 0, np.maximum(lens, query_len), 0)
+        return _finish(name, seed, rng, lens, query_len=query_len, **kw)
     if index == 1:
         lens = [16, 40]
-        return _finish(name, seed, rng, lens, heads=4, kv_heads=kv_heads_override or 4,
+        return fin(name, seed, rng, lens, heads=4, kv_heads=kv_heads_override or 4,
                        head_dim=64,
                        block_size=bs, dtype="f32", layout=layout, num_blocks=8,
                        max_blocks=3)
     if index == 2:
         lens = [2048] * 8
         nb = sum(cdiv(c, bs) for c in lens)
-        return _finish(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
+        return fin(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
                        block_size=bs, dtype="bf16", layout=layout, num_blocks=nb,
                        max_blocks=2048 // bs)
     if index == 3:
@@ -212,14 +234,14 @@ def _make_config(index, layout, kv_heads_override):
         lens = np.zeros(34, dtype=np.int64)
         lens[np.setdiff1d(np.arange(34), pads)] = live
         nb = math.ceil(1.2 * sum(cdiv(c, bs) for c in lens))
-        return _finish(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
+        return fin(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
                        block_size=bs, dtype="bf16", layout=layout, num_blocks=nb,
                        max_blocks=8192 // bs, meta={"pad_rows": pads.tolist()})
     if index == 4:
         lens = _lognormal_lens(rng, 256, 256, 1.0, 2048)
         forced = int(rng.integers(256))
         lens[forced] = 2048
-        return _finish(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
+        return fin(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
                        block_size=bs, dtype="bf16", layout=layout,
                        num_blocks=256 * 2048 // bs, max_blocks=2048 // bs,
                        meta={"forced_row": forced})
@@ -227,7 +249,7 @@ def _make_config(index, layout, kv_heads_override):
         body = _lognormal_lens(rng, 232, 1024, 1.2, 8192)
         lens = np.concatenate([body, np.full(8, 8192), np.zeros(16, dtype=np.int64)])
         lens = lens[rng.permutation(256)]
-        return _finish(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
+        return fin(name, seed, rng, lens, heads=32, kv_heads=kv_heads_override or 32, head_dim=128,
                        block_size=bs, dtype="bf16", layout=layout,
                        num_blocks=256 * 8192 // bs, max_blocks=8192 // bs)
     raise ValueError(f"no configuration {index}")
@@ -235,7 +257,7 @@ def _make_config(index, layout, kv_heads_override):
 
 def make_custom(context_lens, *, heads=4, kv_heads=None, head_dim=64, block_size=16,
                 dtype="f32", layout="HND", num_blocks=None, max_blocks=None, seed=0,
-                name="custom") -> Workload:
+                name="custom", query_len=1) -> Workload:
     """A small workload for tests: explicit lengths, seeded placement and values."""
     kv_heads = heads if kv_heads is None else kv_heads
     lens = [int(c) for c in context_lens]
@@ -247,7 +269,7 @@ def make_custom(context_lens, *, heads=4, kv_heads=None, head_dim=64, block_size
     rng = np.random.default_rng(seed)
     return _finish(name, seed, rng, lens, heads=heads, kv_heads=kv_heads,
                    head_dim=head_dim, block_size=block_size, dtype=dtype, layout=layout,
-                   num_blocks=num_blocks, max_blocks=max_blocks)
+                   num_blocks=num_blocks, max_blocks=max_blocks, query_len=query_len)
 
 
 # --------------------------------------------------------------------------- #
