@@ -69,6 +69,9 @@ def parse():
                     help="graph (default): time the two library calls per step, then replays "
                          "of one HIP graph recorded from them, and report the replays as "
                          "value; eager: time and report the library calls only")
+    ap.add_argument("--query-len", type=int, default=1,
+                    help="new tokens (queries) per row: >1 runs the multi-token read "
+                         "(speculative decoding's drafts) on the same lengths")
     ap.add_argument("--address", default="blocks", choices=["blocks", "slots"],
                     help="how the read is addressed: block tables (default), or the "
                          "per-token int64 slot window of a wider slot table")
@@ -139,20 +142,25 @@ def cpu_baseline(w, k_cache, v_cache, budget_s, min_rows=0):
         idx = torch.from_numpy(np.append(blocks, w.num_blocks).astype(np.int64)).to(k_cache.device)
         kh = _host(k_cache.index_select(0, idx), w.dtype)
         vh = _host(v_cache.index_select(0, idx), w.dtype)
+        nq = w.query_len
         bt = np.full((len(part), w.max_blocks), -1, dtype=np.int32)
-        sm = np.empty(len(part), dtype=np.int64)
+        sm = np.empty(len(part) * nq, dtype=np.int64)
         for i, r in enumerate(part):
             live = wl.cdiv(w.context_lens[r], w.block_size)
             bt[i, :live] = [remap[int(b)] for b in w.block_tables[r, :live]]
-            s = int(w.slot_mapping[r])
-            sm[i] = (n * w.block_size if w.context_lens[r] == 0 else
-                     remap[s // w.block_size] * w.block_size + s % w.block_size)
+            for j in range(nq):
+                s = int(w.slot_mapping[r * nq + j])
+                sm[i * nq + j] = (n * w.block_size if w.context_lens[r] == 0 else
+                                  remap[s // w.block_size] * w.block_size + s % w.block_size)
+        kv_shape = (w.rows, nq, w.kv_heads, w.head_dim)
+        k_new = w.k_new.reshape(kv_shape)[part].reshape(-1, w.kv_heads, w.head_dim)
+        v_new = w.v_new.reshape(kv_shape)[part].reshape(-1, w.kv_heads, w.head_dim)
+        read = oracle.paged_attention if nq == 1 else oracle.paged_attention_multi
         t0 = time.perf_counter()
-        oracle.kv_write(kh, vh, w.k_new[part], w.v_new[part], sm, num_blocks=n,
+        oracle.kv_write(kh, vh, k_new, v_new, sm, num_blocks=n,
                         block_size=w.block_size, layout=w.layout, dtype=w.dtype)
-        out = oracle.paged_attention(w.q[part], kh, vh, bt, w.context_lens[part], w.scale,
-                                     num_blocks=n, block_size=w.block_size, layout=w.layout,
-                                     dtype=w.dtype)
+        out = read(w.q[part], kh, vh, bt, w.context_lens[part], w.scale, num_blocks=n,
+                   block_size=w.block_size, layout=w.layout, dtype=w.dtype)
         spent += time.perf_counter() - t0
         outputs.append(out)
         lens = w.context_lens[part]
@@ -191,6 +199,22 @@ def check_outputs(out, rows, ref, dtype):
     return {"rows": int(len(rows)), "max_abs_err": float(err.max()), "ok": ok}
 
 
+class _CallerGraph:
+    """A step whose library calls are recorded by torch's stream capture (the calls are
+    capturable with validate off), replayed like the library's own captured steps."""
+
+    def __init__(self, step, torch):
+        self._g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self._g):
+            step()
+
+    def launch(self):
+        self._g.replay()
+
+    def destroy(self):
+        self._g = None
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -216,7 +240,10 @@ def main():
     binding.set_tuning(args.chunk_min, args.chunk_max, args.decode_waves,
                        args.items_per_group, args.deal, args.staging, args.max_query_group)
     tuning = binding.get_tuning()
-    w = wl.make_config(args.config, layout=args.layout, kv_heads=args.kv_heads or None)
+    if args.query_len > 1 and args.address != "blocks":
+        raise SystemExit("--query-len > 1 reads through block tables only")
+    w = wl.make_config(args.config, layout=args.layout, kv_heads=args.kv_heads or None,
+                       query_len=args.query_len)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
     log(f"workload {w.name}: rows={w.rows} heads={w.heads} d={w.head_dim} bs={w.block_size} "
         f"{w.dtype} {w.layout}; pool {w.pool_bytes / 1e9:.2f} GB; "
@@ -252,6 +279,9 @@ def main():
         slot_win = slot_table[:, :width]
         del t, cells
         ws_bytes = binding.workspace_bytes_slots(k_cache, w.rows, w.heads, width, w.layout)
+    elif w.query_len > 1:
+        ws_bytes = binding.workspace_bytes_multi(k_cache, w.rows, w.query_len, w.heads,
+                                                 w.max_blocks, w.layout)
     else:
         ws_bytes = binding.workspace_bytes(k_cache, w.rows, w.heads, w.max_blocks, w.layout)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
@@ -268,6 +298,10 @@ def main():
                          validate=validate)
         if slot_win is not None:
             binding.paged_attention_slots(q, k_cache, v_cache, slot_win, lens, w.scale,
+                                          layout=w.layout, out=out, workspace=ws,
+                                          validate=validate)
+        elif w.query_len > 1:
+            binding.paged_attention_multi(q, k_cache, v_cache, tables, lens, w.scale,
                                           layout=w.layout, out=out, workspace=ws,
                                           validate=validate)
         else:
@@ -303,6 +337,8 @@ def main():
             graph = binding.capture_step_slots(k_new, v_new, slots, q, k_cache, v_cache,
                                                slot_win, lens, w.scale, out, ws,
                                                layout=w.layout)
+        elif w.query_len > 1:
+            graph = _CallerGraph(step, torch)     # the calls captured on a side stream
         else:
             graph = binding.capture_step(k_new, v_new, slots, q, k_cache, v_cache, tables,
                                          lens, w.scale, out, ws, layout=w.layout)
@@ -337,7 +373,8 @@ def main():
     step_s = graph_s if args.launch == "graph" else eager_s
     elem = 2 if w.dtype == "bf16" else 4
     shape = dict(heads=w.heads, kv_heads=w.kv_heads, head_dim=w.head_dim,
-                 block_size=w.block_size, elem=elem, write_tokens=w.rows)
+                 block_size=w.block_size, elem=elem, write_tokens=w.rows * w.query_len,
+                 query_len=w.query_len)
     b = acc.algorithmic_bytes(w.context_lens, address=args.address, **shape)
     # the decode kernel reads block ids in both modes (with slots, the table the
     # translation pass derived from the window)
@@ -382,6 +419,7 @@ def main():
                             "paged_attention_slots through a [rows, width] int64 slot "
                             "window")),
             "address": args.address,
+            "query_len": w.query_len,
             "rows": w.rows,
             "heads": w.heads,
             "kv_heads": w.kv_heads,

@@ -162,6 +162,40 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
                                int32_t num_heads, float scale, void* workspace,
                                size_t workspace_bytes, int32_t validate, void* stream);
 
+/* The read with several new tokens (queries) per row: speculative decoding's draft
+ * tokens, or a chunk of a prompt, over the same paged history (Day 59, "Why it
+ * matters": the read's rectangle has a query_len axis beside rows and heads).
+ *   q, out        [num_rows][query_len][num_heads][head_dim], pool dtype
+ *   query_len     1..64 new tokens per row; query i of row r is the token at position
+ *                 context_lens[r] - query_len + i (its K/V written by pkv_kv_write with
+ *                 num_rows * query_len tokens before this call)
+ *   context_lens  [num_rows] int32: 0 (a padding row, all outputs zero) or in
+ *                 [query_len, min(max_blocks * block_size, num_blocks * block_size)]
+ *   block_tables, scale, workspace, validate, stream: as in pkv_paged_attention; the
+ *                 workspace is pkv_workspace_bytes_multi(...)
+ * out[r,i,h,:] = sum_t softmax_t(scale * q[r,i,h,:].K[t]) V[t] over
+ * t <= context_lens[r] - query_len + i (causal), accumulated in float32.  One K/V read
+ * serves up to 8 query vectors (new tokens x query heads of one KV head).  Refusals:
+ * those of pkv_paged_attention, in its order, with CONTEXT_BOUNDS also for a live row
+ * shorter than query_len (after the range check, before BLOCK_ID); SHAPE for
+ * query_len < 1, UNSUPPORTED above 64.  query_len = 1 is pkv_paged_attention. */
+size_t pkv_workspace_bytes_multi(const pkv_pool_desc* pool, int64_t num_rows,
+                                 int32_t query_len, int32_t num_heads,
+                                 int32_t max_blocks_per_row);
+pkv_status pkv_paged_attention_multi(const pkv_pool_desc* pool, void* out, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_row,
+                                     const int32_t* context_lens, int64_t num_rows,
+                                     int32_t query_len, int32_t num_heads, float scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t validate, void* stream);
+/* The host checks pkv_paged_attention_multi runs with validate != 0, on HOST arrays. */
+pkv_status pkv_check_attention_multi_host(const pkv_pool_desc* pool,
+                                          const int32_t* block_tables,
+                                          int32_t max_blocks_per_row,
+                                          const int32_t* context_lens, int64_t num_rows,
+                                          int32_t query_len, int32_t num_heads);
+
 /* The decode read addressed by a per-token slot rectangle instead of block tables
  * (Day 51, "What I added today": the step reads through a persistent
  * [max_batch, max_model_len] int64 slot table, handed over as the window

@@ -59,6 +59,10 @@ SIGNATURES = {
                                        _i64, _i32, _f, _p, _sz,
                                        ctypes.POINTER(ctypes.c_void_p)]),
     "pkv_graph_launch": (_i32, [_p, _p]),
+    "pkv_workspace_bytes_multi": (_sz, [_PD, _i64, _i32, _i32, _i32]),
+    "pkv_paged_attention_multi": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32, _i32,
+                                         _f, _p, _sz, _i32, _p]),
+    "pkv_check_attention_multi_host": (_i32, [_PD, _p, _i32, _p, _i64, _i32, _i32]),
     "pkv_workspace_bytes_slots": (_sz, [_PD, _i64, _i32, _i32]),
     "pkv_paged_attention_slots": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _i64, _p, _i64, _i32,
                                          _f, _p, _sz, _i32, _p]),

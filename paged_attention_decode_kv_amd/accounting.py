@@ -58,15 +58,16 @@ def widest_capture(budget_bytes: float, rows: int, heads: int,
 
 def algorithmic_bytes(context_lens, *, heads: int, kv_heads: int, head_dim: int,
                       block_size: int, elem: int, write_tokens: int,
-                      address: str = "blocks") -> dict:
+                      address: str = "blocks", query_len: int = 1) -> dict:
     """Bytes the step must move, split by component.  ``address`` is how the read is
     addressed: "blocks" reads one int32 block id per live block, "slots" one int64
     rectangle cell per live position (Day 51, "Why it matters": the same information,
-    one cell per slot instead of one per block)."""
+    one cell per slot instead of one per block).  ``query_len`` new tokens per row
+    each bring a query and an output; K and V are still read once per KV head."""
     ctx = np.asarray(context_lens, dtype=np.int64)
     rows = int(ctx.size)
     kv = int(ctx.sum()) * kv_heads * head_dim * elem * 2
-    q_out = 2 * rows * heads * head_dim * elem
+    q_out = 2 * rows * query_len * heads * head_dim * elem
     if address == "blocks":
         tables = int(np.sum(cdiv(ctx, block_size))) * 4 + rows * 4
     elif address == "slots":

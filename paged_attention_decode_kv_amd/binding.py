@@ -161,6 +161,58 @@ def paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     return out
 
 
+def workspace_bytes_multi(k_cache: torch.Tensor, num_rows: int, query_len: int,
+                          num_heads: int, max_blocks: int, layout: str = "HND") -> int:
+    desc = pool_desc(k_cache, layout)
+    return int(_capi.lib().pkv_workspace_bytes_multi(ctypes.byref(desc), num_rows, query_len,
+                                                     num_heads, max_blocks))
+
+
+def paged_attention_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          scale: float, *, layout: str = "HND",
+                          out: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None,
+                          validate: bool = True) -> torch.Tensor:
+    """The read with ``q`` [rows, query_len, heads, head_dim]: query i of a row is its
+    token at position len - query_len + i and attends causally; returns ``out``."""
+    rows = int(context_lens.shape[0]) if context_lens.dim() >= 1 else 0
+    if rows == 0:
+        _raise("EMPTY", "no rows")
+    desc = _pool_pair(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _device_tensor(q, "q", k_cache.dtype, dev)
+    _device_tensor(block_tables, "block_tables", torch.int32, dev)
+    _device_tensor(context_lens, "context_lens", torch.int32, dev)
+    if q.dim() != 4 or q.shape[0] != rows or q.shape[3] != desc.head_dim:
+        _raise("SHAPE", f"q must be [{rows}, query_len, heads, {desc.head_dim}], "
+                        f"got {tuple(q.shape)}")
+    query_len, heads = int(q.shape[1]), int(q.shape[2])
+    if context_lens.dim() != 1 or block_tables.dim() != 2 or block_tables.shape[0] != rows:
+        _raise("SHAPE", "block_tables must be [rows, max_blocks], context_lens [rows]")
+    max_blocks = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, dev)
+        if out.shape != q.shape:
+            _raise("SHAPE", "out must have q's shape")
+    lib = _capi.lib()
+    need = int(lib.pkv_workspace_bytes_multi(ctypes.byref(desc), rows, query_len, heads,
+                                             max_blocks))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        _raise("WORKSPACE", "workspace must be a contiguous tensor on the pool's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        _check(lib.pkv_paged_attention_multi(
+            ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_tables), max_blocks, _ptr(context_lens), rows, query_len, heads,
+            float(scale), _ptr(workspace), ws_bytes, int(bool(validate)), _stream(k_cache)))
+    return out
+
+
 def _slot_window(slot_table: torch.Tensor, rows: int, dev: torch.device):
     """(width, row_stride) of a [rows, width] int64 window whose cells are contiguous
     along a row; the window may be a column slice of a wider table."""
@@ -401,6 +453,19 @@ def check_attention_slots_host(desc: _capi.PoolDesc, slot_table: np.ndarray,
     st = _capi.lib().pkv_check_attention_slots_host(
         ctypes.byref(desc), rect.ctypes.data_as(ctypes.c_void_p), rect.shape[1],
         rect.strides[0] // 8, ctx.ctypes.data_as(ctypes.c_void_p), ctx.shape[0], num_heads)
+    return _capi.STATUS_NAMES[st]
+
+
+def check_attention_multi_host(desc: _capi.PoolDesc, block_tables: np.ndarray,
+                               context_lens: np.ndarray, query_len: int,
+                               num_heads: int) -> str:
+    """Status name the library's host validator gives a multi-token read."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    m = bt.shape[1] if bt.ndim == 2 else 0
+    st = _capi.lib().pkv_check_attention_multi_host(
+        ctypes.byref(desc), bt.ctypes.data_as(ctypes.c_void_p), m,
+        ctx.ctypes.data_as(ctypes.c_void_p), ctx.shape[0], query_len, num_heads)
     return _capi.STATUS_NAMES[st]
 
 

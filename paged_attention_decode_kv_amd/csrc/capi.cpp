@@ -111,13 +111,22 @@ pkv_status check_attention_shape(const pkv_pool_desc* pool, int32_t max_blocks,
   return PKV_OK;
 }
 
+// CONTEXT_BOUNDS, then (query_len > 1) live rows shorter than their new tokens, then
+// BLOCK_ID.
 pkv_status check_attention_data(const pkv_pool_desc* pool, const int32_t* bt,
-                                int32_t max_blocks, const int32_t* ctx, int64_t num_rows) {
+                                int32_t max_blocks, const int32_t* ctx, int64_t num_rows,
+                                int32_t query_len = 1) {
   const int64_t limit = ctx_limit_of(pool, max_blocks);
   for (int64_t r = 0; r < num_rows; ++r) {
     if (ctx[r] < 0 || ctx[r] > limit)
       return fail(PKV_ERR_CONTEXT_BOUNDS, "context_lens[%lld] = %d outside [0, %lld]",
                   (long long)r, ctx[r], (long long)limit);
+  }
+  for (int64_t r = 0; r < num_rows; ++r) {
+    if (ctx[r] > 0 && ctx[r] < query_len)
+      return fail(PKV_ERR_CONTEXT_BOUNDS,
+                  "context_lens[%lld] = %d is live but shorter than query_len %d",
+                  (long long)r, ctx[r], query_len);
   }
   for (int64_t r = 0; r < num_rows; ++r) {
     const int64_t live = (ctx[r] + (int64_t)pool->block_size - 1) / pool->block_size;
@@ -169,7 +178,8 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
                             const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int32_t max_blocks,
                             const int32_t* context_lens, int64_t num_rows, int32_t num_heads,
-                            float scale, void* workspace, hipStream_t st) {
+                            float scale, void* workspace, hipStream_t st,
+                            int32_t query_len = 1) {
   pkv::AttnArgs a;
   a.g = geom(pool);
   a.out = out;
@@ -187,10 +197,11 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
   a.target_items = 0;
   a.deal_static = 1;
   a.query_group = 1;
+  a.query_len = query_len;
   a.scale = scale;
   a.row_flags = nullptr;
   a.flag_stride = 0;
-  const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads,
+  const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads * query_len,
                                                  pool->head_dim, max_blocks, pool->block_size);
   return pkv::launch_paged_attention(a, ws, st);
 }
@@ -266,6 +277,7 @@ hipError_t launch_attention_slots(const pkv_pool_desc* pool, void* out, const vo
   a.target_items = 0;
   a.deal_static = 1;
   a.query_group = 1;
+  a.query_len = 1;
   a.scale = scale;
   a.row_flags = nullptr;
   a.flag_stride = 0;
@@ -492,6 +504,78 @@ pkv_status pkv_paged_attention_slots(const pkv_pool_desc* pool, void* out, const
                                         row_stride, context_lens, num_rows, num_heads, scale,
                                         workspace, st);
   if (e != hipSuccess) return hip_fail(e, "launching paged_attention_slots");
+  return ok();
+}
+
+// ---- several new tokens per row ----
+static pkv_status check_multi_shape(const pkv_pool_desc* pool, int32_t max_blocks,
+                                    int64_t num_rows, int32_t query_len, int32_t num_heads) {
+  pkv_status s = check_attention_shape(pool, max_blocks, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  if (query_len < 1) return fail(PKV_ERR_SHAPE, "query_len %d < 1", query_len);
+  if (query_len > 64)
+    return fail(PKV_ERR_UNSUPPORTED, "query_len %d: built for at most 64", query_len);
+  return PKV_OK;
+}
+
+size_t pkv_workspace_bytes_multi(const pkv_pool_desc* pool, int64_t num_rows,
+                                 int32_t query_len, int32_t num_heads,
+                                 int32_t max_blocks_per_row) {
+  if (check_multi_shape(pool, max_blocks_per_row, num_rows, query_len, num_heads) != PKV_OK)
+    return 0;
+  return pkv::workspace_bytes(num_rows, num_heads * query_len, pool->head_dim,
+                              max_blocks_per_row, pool->block_size);
+}
+
+pkv_status pkv_check_attention_multi_host(const pkv_pool_desc* pool,
+                                          const int32_t* block_tables,
+                                          int32_t max_blocks_per_row,
+                                          const int32_t* context_lens, int64_t num_rows,
+                                          int32_t query_len, int32_t num_heads) {
+  pkv_status s = check_multi_shape(pool, max_blocks_per_row, num_rows, query_len, num_heads);
+  if (s != PKV_OK) return s;
+  if (!block_tables || !context_lens) return fail(PKV_ERR_NULL, "table or lengths NULL");
+  s = check_attention_data(pool, block_tables, max_blocks_per_row, context_lens, num_rows,
+                           query_len);
+  return s == PKV_OK ? ok() : s;
+}
+
+pkv_status pkv_paged_attention_multi(const pkv_pool_desc* pool, void* out, const void* q,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_row,
+                                     const int32_t* context_lens, int64_t num_rows,
+                                     int32_t query_len, int32_t num_heads, float scale,
+                                     void* workspace, size_t workspace_bytes,
+                                     int32_t validate, void* stream) {
+  pkv_status s = check_multi_shape(pool, max_blocks_per_row, num_rows, query_len, num_heads);
+  if (s != PKV_OK) return s;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  const size_t need = pkv::workspace_bytes(num_rows, num_heads * query_len, pool->head_dim,
+                                           max_blocks_per_row, pool->block_size);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads * query_len);
+  if (s != PKV_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (validate) {
+    std::vector<int32_t> ctx((size_t)num_rows);
+    std::vector<int32_t> bt((size_t)(num_rows * max_blocks_per_row));
+    hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(bt.data(), block_tables, bt.size() * sizeof(int32_t),
+                         hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "copying lengths and tables to the host");
+    s = check_attention_data(pool, bt.data(), max_blocks_per_row, ctx.data(), num_rows,
+                             query_len);
+    if (s != PKV_OK) return s;
+  }
+  hipError_t e = launch_attention(pool, out, q, k_cache, v_cache, block_tables,
+                                  max_blocks_per_row, context_lens, num_rows, num_heads, scale,
+                                  workspace, st, query_len);
+  if (e != hipSuccess) return hip_fail(e, "launching paged_attention_multi");
   return ok();
 }
 

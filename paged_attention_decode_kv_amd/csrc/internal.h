@@ -83,12 +83,14 @@ struct AttnArgs {
   int64_t num_rows;
   int32_t num_heads;
   int32_t max_blocks;
-  int32_t ctx_limit;    // min(max_blocks * block_size, num_blocks * block_size)
+  int32_t ctx_limit;    // min(max_blocks * block_size, num_blocks * block_size), or with a
+                        // slot input min(width, num_blocks * block_size)
   int32_t log2_chunk_min;  // the plan's chunk length range (powers of two)
   int32_t log2_chunk_max;
   int32_t target_items;    // items the plan aims for (set by the launcher)
   int32_t deal_static;     // 1: whole rounds of full chunks are dealt without the queue
-  int32_t query_group;     // query heads per work item (they share one KV head)
+  int32_t query_group;     // query vectors per work item (they share one KV head)
+  int32_t query_len;       // new tokens (queries) per row: 1 for decode
   float scale;
   // slot input only (else null / 0): [rows][flag_stride], nonzero where a row's live
   // slots are not block structured; such rows are left to the token-by-token kernel

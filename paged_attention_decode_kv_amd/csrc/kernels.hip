@@ -203,6 +203,8 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
     if (report) atomicOr(&g_status, PKV_DEVERR_CONTEXT_BOUNDS);
     ctx = ctx < 0 ? 0 : a.ctx_limit;
   }
+  // a live row shorter than its new tokens: its earliest queries see nothing (zeros)
+  if (report && ctx > 0 && ctx < a.query_len) atomicOr(&g_status, PKV_DEVERR_CONTEXT_BOUNDS);
   bool irr = false;
   if (a.row_flags != nullptr && ctx > 0) {
     const int32_t* f = a.row_flags + r * a.flag_stride;
@@ -266,7 +268,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
   __syncthreads();
   int lp = lmin;
   for (int k = ncand - 1; k >= 0; --k) {
-    if ((int64_t)s_cand[k] * (a.num_heads / a.query_group) >= a.target_items) {
+    if ((int64_t)s_cand[k] * (a.query_len * a.num_heads / a.query_group) >= a.target_items) {
       lp = lmin + k;
       break;
     }
@@ -362,12 +364,27 @@ struct Shape {
   static_assert(kMaxChunkTokens / 16 <= 128, "block ids of a chunk: two per lane");
 };
 
+// Query vectors.  A row has query_len x heads of them, one per (new token i, query
+// head h), numbered v = h * query_len + i: the vectors of one KV head are consecutive
+// (KV head of v = v / (query_len * heads per KV head)).  With one new token per row,
+// v = h.  Vector v's q and out are [row][i][h][:]; query i sits at position
+// len - query_len + i and sees positions up to its own.
+__device__ __forceinline__ int64_t vec_slot(const AttnArgs& a, int64_t r, int v) {
+  const int h = v / a.query_len;
+  const int i = v - h * a.query_len;
+  return (r * a.query_len + i) * a.num_heads + h;
+}
+__device__ __forceinline__ int vec_query(const AttnArgs& a, int v) {
+  return v % a.query_len;
+}
+
 // Everything a work item needs before its first K/V load.  An item is (row, chunk of
-// the row's history, group of QG query heads that share one KV head).
+// the row's history, group of QG query vectors that share one KV head).
 template <int QG>
 struct ItemMeta {
-  int r, hg, chunk, nch, ctx;   // hg: query-head group; heads hg*QG .. hg*QG + QG - 1
-  uint4 q[QG];   // this lane's 16 bytes of each head's query
+  int r, hg, chunk, nch, ctx;   // hg: vector group; vectors hg*QG .. hg*QG + QG - 1
+  uint4 q[QG];   // this lane's 16 bytes of each vector's query
+  int last[QG];  // each vector's last visible position (len - query_len + i)
   int blk;       // lane i: block id of the chunk's i-th block
   int blk_hi;    // lane i: block id of the chunk's (64 + i)-th block
 };
@@ -384,7 +401,7 @@ template <typename T, int D, int QG>
 __device__ __forceinline__ ItemMeta<QG> finish_meta(const AttnArgs& a, int4 ent, int item,
                                                     int lp, int log2_bs, int lane, int sub) {
   constexpr int E = Elem<T>::kPerLane;
-  const int groups = a.num_heads / QG;
+  const int groups = a.query_len * a.num_heads / QG;
   ItemMeta<QG> m;
   const int e = item / groups;
   m.hg = item - e * groups;
@@ -393,14 +410,17 @@ __device__ __forceinline__ ItemMeta<QG> finish_meta(const AttnArgs& a, int4 ent,
   m.nch = __builtin_amdgcn_readfirstlane(ent.z);
   m.ctx = __builtin_amdgcn_readfirstlane(ent.w);
 #pragma unroll
-  for (int j = 0; j < QG; ++j) m.q[j] = make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < QG; ++j) {
+    m.q[j] = make_uint4(0, 0, 0, 0);
+    m.last[j] = m.ctx - a.query_len + vec_query(a, m.hg * QG + j);
+  }
   m.blk = 0;
   m.blk_hi = 0;
   if (m.chunk >= 0) {
-    const int64_t rh = (int64_t)m.r * a.num_heads + (int64_t)m.hg * QG;
 #pragma unroll
     for (int j = 0; j < QG; ++j)
-      m.q[j] = load16(static_cast<const T*>(a.q) + (rh + j) * D + sub * E);
+      m.q[j] = load16(static_cast<const T*>(a.q) + vec_slot(a, m.r, m.hg * QG + j) * D +
+                      sub * E);
     const int t_begin = m.chunk << lp;
     const int t_end = min(m.ctx, t_begin + (1 << lp));
     const int j0 = t_begin >> log2_bs;
@@ -470,9 +490,9 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   __shared__ float s_m[2][QG][WAVES], s_l[2][QG][WAVES];
   __shared__ float s_acc[2][QG][WAVES][D];
 
-  const int heads = a.num_heads;
-  const int groups = heads / QG;              // items per work-list entry
-  const int qpkv = heads / a.g.kv_heads;      // query heads per KV head
+  const int n_vec = a.query_len * a.num_heads;   // query vectors per row
+  const int groups = n_vec / QG;                 // items per work-list entry
+  const int vpkv = n_vec / a.g.kv_heads;         // query vectors per KV head
   const int lp = ws.counters[3];
   const int P = 1 << lp;
   const int n_static = ws.counters[4] * groups;   // section A items
@@ -539,7 +559,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     const int t_begin = chunk * P;
     const int t_end = min(__builtin_amdgcn_readfirstlane(cur.ctx), t_begin + P);
     const int j0 = t_begin >> log2_bs;
-    const int64_t head_off = (int64_t)(hg * QG / qpkv) * head_bytes;
+    const int64_t head_off = (int64_t)(hg * QG / vpkv) * head_bytes;
 
     float m[QG], l[QG], acc[QG][E];
 #pragma unroll
@@ -549,6 +569,12 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 #pragma unroll
       for (int i = 0; i < E; ++i) acc[j][i] = 0.f;
     }
+
+    // each vector's last visible position, relative to the chunk start
+    int last_rel[QG];
+#pragma unroll
+    for (int j = 0; j < QG; ++j)
+      last_rel[j] = __builtin_amdgcn_readfirstlane(cur.last[j]) - t_begin;
 
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
     // Descriptors of sub-chunk s's K and V: they end after its valid tokens, so the
@@ -605,15 +631,17 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
           vr[u] = buffer_load16(vsrc, voff[u]);
         }
       }
-      // fold the sub-chunk into every head of the group: one K/V load, QG heads
+      // fold the sub-chunk into every vector of the group: one K/V load, QG vectors,
+      // each seeing the positions up to its own (the causal limit of several new tokens)
 #pragma unroll
       for (int j = 0; j < QG; ++j) {
+        const int nv = min(nvalid, last_rel[j] - s * CH + 1);
         float sc[U];
         float smax = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const float d = group_sum<LPT>(El::dot(cur.q[j], kr[u], 0.f));
-          sc[u] = u * TPS + g < nvalid ? d * scale_log2 : -INFINITY;
+          sc[u] = u * TPS + g < nv ? d * scale_log2 : -INFINITY;
           smax = fmaxf(smax, sc[u]);
         }
         const float m_new = fmaxf(m[j], smax);
@@ -681,26 +709,29 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
           float mx = s_m[buf][j][0];
 #pragma unroll
           for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[buf][j][w]);
+          // -inf only for a vector whose causal limit precedes this whole chunk
+          const float mu = mx == -INFINITY ? 0.f : mx;
           lj = 0.f;
 #pragma unroll
           for (int i = 0; i < E; ++i) aj[i] = 0.f;
 #pragma unroll
           for (int w = 0; w < WAVES; ++w) {
-            const float f = __builtin_amdgcn_exp2f(s_m[buf][j][w] - mx);   // mx is finite
+            const float f = __builtin_amdgcn_exp2f(s_m[buf][j][w] - mu);
             lj += s_l[buf][j][w] * f;
 #pragma unroll
             for (int i = 0; i < E; ++i) aj[i] += s_acc[buf][j][w][sub * E + i] * f;
           }
           mj = mx;
         }
-        const int64_t rh = (int64_t)cur.r * heads + (int64_t)hg * QG + j;
+        const int v = hg * QG + j;
         if (cur.nch == 1) {
-          const float inv = 1.0f / lj;
+          const float inv = lj > 0.f ? 1.0f / lj : 0.f;
 #pragma unroll
           for (int i = 0; i < E; ++i) aj[i] *= inv;
-          store16(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(aj));
+          store16(static_cast<T*>(a.out) + vec_slot(a, cur.r, v) * D + sub * E, El::pack(aj));
         } else {
-          float* rec = ws.partials + (rh * ws.max_chunks + chunk) * (D + 4);
+          const int64_t rv = (int64_t)cur.r * n_vec + v;
+          float* rec = ws.partials + (rv * ws.max_chunks + chunk) * (D + 4);
           if (sub == 0) {
             rec[0] = mj;
             rec[1] = lj;
@@ -729,8 +760,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 #pragma unroll
       for (int j = 0; j < QG; ++j)
         if (j % WAVES == wave)
-          store16(static_cast<T*>(a.out) + ((int64_t)r * heads + (int64_t)hgp * QG + j) * D +
-                      sub * E,
+          store16(static_cast<T*>(a.out) + vec_slot(a, r, hgp * QG + j) * D + sub * E,
                   make_uint4(0, 0, 0, 0));
     }
   }
@@ -752,26 +782,27 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One workgroup per (head, row) of a row split into several chunks.  Chunk c of the
-// row carries (m_c, l_c, acc_c); the result is sum_c 2^(m_c - M) acc_c divided by
-// sum_c 2^(m_c - M) l_c with M = max_c m_c.  Each wave sums a fixed subset of the
+// One workgroup per (query vector, row) of a row split into several chunks.  Chunk c
+// of the row carries (m_c, l_c, acc_c); the result is sum_c 2^(m_c - M) acc_c divided
+// by sum_c 2^(m_c - M) l_c with M = max_c m_c.  Each wave sums a fixed subset of the
 // chunks (c = wave mod 4) and the four partial sums are added in wave order, so the
-// result does not depend on scheduling.
+// result does not depend on scheduling.  A chunk wholly past a vector's causal limit
+// carries m = -inf and l = 0 and adds nothing.
 template <typename T, int D>
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Workspace ws) {
   constexpr int PER = D / 64;     // dims per lane
   constexpr int W = kCombineThreads / 64;
   __shared__ float s_red[W];
   __shared__ float s_acc[W][D];
-  const int h = blockIdx.x;
+  const int v = blockIdx.x;
   const int64_t r = blockIdx.y;
   const int ctx = ws.row_ctx[r];
   const int lp = ws.counters[3];
   const int nch = (ctx + (1 << lp) - 1) >> lp;
   if (nch <= 1) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t rh = r * a.num_heads + h;
-  const float* rec = ws.partials + rh * ws.max_chunks * (D + 4);
+  const int64_t rv = r * (a.query_len * a.num_heads) + v;
+  const float* rec = ws.partials + rv * ws.max_chunks * (D + 4);
 
   float mx = -INFINITY;
   for (int c = threadIdx.x; c < nch; c += kCombineThreads) mx = fmaxf(mx, rec[c * (D + 4)]);
@@ -781,6 +812,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
   mx = s_red[0];
 #pragma unroll
   for (int w = 1; w < W; ++w) mx = fmaxf(mx, s_red[w]);
+  if (mx == -INFINITY) mx = 0.f;   // only a row whose length was out of bounds
   __syncthreads();
 
   float l = 0.f, acc[PER];
@@ -803,8 +835,8 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
   float lt = 0.f;
 #pragma unroll
   for (int w = 0; w < W; ++w) lt += s_red[w];
-  const float inv = 1.0f / lt;
-  T* outp = static_cast<T*>(a.out) + rh * D + lane * PER;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  T* outp = static_cast<T*>(a.out) + vec_slot(a, r, v) * D + lane * PER;
   float y[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -1111,7 +1143,7 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
   int64_t grid = (int64_t)num_cu[dev] * per_cu[dev];
-  const int64_t most = ws.max_entries * (a.num_heads / QG);
+  const int64_t most = ws.max_entries * (a.query_len * a.num_heads / QG);
   if (grid > most) grid = most;
   AttnArgs pa = a;
   pa.query_group = QG;
@@ -1126,22 +1158,24 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   timing_end(PKV_PHASE_DECODE, stream);
   if (ws.max_chunks > 1) {
     timing_begin(PKV_PHASE_COMBINE, stream);
-    hipLaunchKernelGGL((combine_kernel<T, D>), dim3(a.num_heads, (unsigned)a.num_rows),
+    hipLaunchKernelGGL((combine_kernel<T, D>),
+                       dim3(a.query_len * a.num_heads, (unsigned)a.num_rows),
                        dim3(kCombineThreads), 0, stream, a, ws);
     timing_end(PKV_PHASE_COMBINE, stream);
   }
   return hipGetLastError();
 }
 
-// query heads per work item: the largest of 8, 4, 2, 1 that divides the number of query
-// heads per KV head and is at most the tuning cap (4 for head_dim 256, whose per-head
-// merge buffers would not fit in LDS beside the K/V stages at 8)
+// query vectors per work item: the largest of 8, 4, 2, 1 that divides the number of
+// query vectors per KV head (query heads per KV head x new tokens per row) and is at
+// most the tuning cap (4 for head_dim 256, whose per-vector merge buffers would not fit
+// in LDS beside the K/V stages at 8)
 static int query_group_of(const AttnArgs& a) {
-  const int qpkv = a.num_heads / a.g.kv_heads;
+  const int vpkv = a.query_len * (a.num_heads / a.g.kv_heads);
   int cap = tuning_max_query_group();
   if (a.g.head_dim >= 256 && cap > 4) cap = 4;
   for (int qg = 8; qg > 1; qg >>= 1)
-    if (qg <= cap && qpkv % qg == 0) return qg;
+    if (qg <= cap && vpkv % qg == 0) return qg;
   return 1;
 }
 

@@ -99,3 +99,13 @@ def test_slot_addressing_bytes():
     assert slots["kv"] == blocks["kv"] and slots["kv_write"] == blocks["kv_write"]
     with pytest.raises(ValueError):
         acc.algorithmic_bytes(lens, address="rows", **kw)
+
+
+def test_multi_token_bytes():
+    lens = np.array([16, 48, 0])
+    kw = dict(heads=4, kv_heads=2, head_dim=64, block_size=16, elem=2)
+    one = acc.algorithmic_bytes(lens, write_tokens=3, **kw)
+    four = acc.algorithmic_bytes(lens, write_tokens=12, query_len=4, **kw)
+    assert four["kv"] == one["kv"] and four["tables"] == one["tables"]
+    assert four["q_out"] == 4 * one["q_out"]
+    assert four["kv_write"] == 4 * one["kv_write"]

@@ -241,3 +241,49 @@ def test_slot_shape_refusals(lib):
     assert lib.pkv_workspace_bytes_slots(ctypes.byref(d), 4, 4, 0) == 0
     assert lib.pkv_workspace_bytes_slots(ctypes.byref(d), 4, 4, 48) > \
         lib.pkv_workspace_bytes(ctypes.byref(d), 4, 4, 3)
+
+
+def _multi_cases():
+    w = wl.make_custom([16, 40, 0, 7], heads=4, kv_heads=2, head_dim=64, num_blocks=12,
+                       max_blocks=4, seed=5, query_len=4)
+    cases = [("legal", w.block_tables, w.context_lens)]
+    ctx = w.context_lens.copy(); ctx[3] = 3
+    cases.append(("live row shorter than its queries", w.block_tables, ctx))
+    ctx = w.context_lens.copy(); ctx[3] = 4
+    cases.append(("exactly its queries", w.block_tables, ctx))
+    ctx = w.context_lens.copy(); ctx[1] = 65
+    cases.append(("past the table", w.block_tables, ctx))
+    bt = w.block_tables.copy(); bt[1, 2] = -1
+    cases.append(("-1 inside the live prefix", bt, w.context_lens))
+    ctx = w.context_lens.copy(); ctx[3] = 2
+    cases.append(("short row before a bad block", bt, ctx))
+    ctx = w.context_lens.copy(); ctx[3] = 2; ctx[0] = -1
+    cases.append(("range before short", w.block_tables, ctx))
+    return w, cases
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_multi_refusals_match_the_oracle(lib, idx):
+    w, cases = _multi_cases()
+    name, bt, ctx = cases[idx]
+    k, v = wl.history_host(w)
+    want = _oracle_code(lambda: oracle.validate_attention_multi(
+        w.q, k, v, bt, ctx, num_blocks=w.num_blocks, block_size=w.block_size,
+        layout=w.layout, dtype=w.dtype))
+    d = binding.host_desc(w.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype,
+                          w.layout)
+    assert binding.check_attention_multi_host(d, bt, ctx, 4, w.heads) == want, name
+
+
+def test_multi_query_len_limits(lib):
+    w, cases = _multi_cases()
+    d = binding.host_desc(w.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype,
+                          w.layout)
+    bt, ctx = cases[0][1], cases[0][2]
+    assert binding.check_attention_multi_host(d, bt, ctx, 0, w.heads) == "SHAPE"
+    assert binding.check_attention_multi_host(d, bt, ctx, 65, w.heads) == "UNSUPPORTED"
+    assert binding.check_attention_multi_host(d, bt[:0], ctx[:0], 4, w.heads) == "EMPTY"
+    one = lib.pkv_workspace_bytes(ctypes.byref(d), 4, 4, 4)
+    assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 1, 4, 4) == one
+    assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 4, 4, 4) > one
+    assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 0, 4, 4) == 0

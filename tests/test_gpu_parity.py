@@ -797,3 +797,128 @@ def test_captured_slot_window_step():
     ref = _slot_oracle(w, k_host, v_host, table_host, width)
     assert_close(eager, ref, "bf16", "captured slot window")
     assert binding.device_status(DEV, clear=True) == 0
+
+
+# --------------------------------------------------------------------------- #
+# several new tokens (queries) per row
+# --------------------------------------------------------------------------- #
+def _multi_run(w, st, *, validate=True, out=None):
+    binding.kv_write(st.k_new, st.v_new, st.slots, st.k_cache, st.v_cache, layout=w.layout,
+                     validate=validate)
+    got = binding.paged_attention_multi(st.q, st.k_cache, st.v_cache, st.tables, st.lens,
+                                        w.scale, layout=w.layout, out=out, validate=validate)
+    torch.cuda.synchronize()
+    return got
+
+
+def _multi_oracle(w, k_host, v_host):
+    kw, vw = k_host.copy(), v_host.copy()
+    oracle.kv_write(kw, vw, w.k_new, w.v_new, w.slot_mapping, num_blocks=w.num_blocks,
+                    block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+    return oracle.paged_attention_multi(w.q, kw, vw, w.block_tables, w.context_lens, w.scale,
+                                        num_blocks=w.num_blocks, block_size=w.block_size,
+                                        layout=w.layout, dtype=w.dtype)
+
+
+MULTI_CASES = [
+    # name, lens, query_len, heads, kv_heads, head_dim, block_size, dtype, layout
+    ("q2-f32", [16, 40, 0, 130], 2, 4, 4, 64, 16, "f32", "HND"),
+    ("q4-gqa4-bf16", [4, 300, 1025, 2050, 0, 77], 4, 16, 4, 128, 16, "bf16", "HND"),
+    ("q3-mha-nhd", [3, 50, 129, 700], 3, 8, 8, 128, 16, "bf16", "NHD"),
+    ("q5-gqa2-bs32", [5, 64, 900], 5, 8, 4, 64, 32, "bf16", "HND"),
+    ("q8-d256", [8, 200, 513], 8, 4, 2, 256, 16, "bf16", "HND"),
+    ("q16-mha", [16, 600, 2100, 0], 16, 8, 8, 128, 16, "bf16", "HND"),
+    ("q4-f32-d128", [4, 1000, 33], 4, 8, 2, 128, 16, "f32", "NHD"),
+]
+
+
+@pytest.mark.parametrize("chunk", [0, 32])
+@pytest.mark.parametrize("case", MULTI_CASES, ids=[c[0] for c in MULTI_CASES])
+def test_multi_token_rows(case, chunk):
+    """Several new tokens per row, each attending causally: every output against the
+    oracle, the written slots bit-exact.  chunk=32 pins 32-token chunks, so causal
+    limits fall inside and before split chunks."""
+    name, lens, n_q, heads, kvh, d, bs, dtype, layout = case
+    w = wl.make_custom(lens, heads=heads, kv_heads=kvh, head_dim=d, block_size=bs,
+                       dtype=dtype, layout=layout, query_len=n_q,
+                       seed=zlib.crc32(name.encode()))
+    say(f"multi {name} chunk {chunk}: lens {lens} q {n_q} heads {heads}/{kvh}")
+    saved = binding.get_tuning()
+    if chunk:
+        binding.set_tuning(chunk_min=chunk, chunk_max=chunk)
+    try:
+        st = Step(w, host_history=True)
+        got = _multi_run(w, st)
+    finally:
+        binding.set_tuning(**saved)
+    ref = _multi_oracle(w, st.k_host, st.v_host)
+    assert_close(to_host(got, dtype), ref, dtype, name)
+    assert binding.device_status(DEV, clear=True) == 0
+
+
+def test_one_query_per_row_is_the_decode_read():
+    w = wl.make_config(3)
+    st = Step(w)
+    blk = to_host(st.run(validate=False), "bf16").copy()
+    got = binding.paged_attention_multi(st.q[:, None], st.k_cache, st.v_cache, st.tables,
+                                        st.lens, w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(got[:, 0], "bf16"), blk)
+
+
+def test_multi_refusals_touch_nothing():
+    w = wl.make_custom([16, 40], heads=4, kv_heads=4, head_dim=64, dtype="f32",
+                       query_len=4, seed=3)
+    st = Step(w, host_history=True)
+    out = torch.full_like(st.q, 2.0)
+    lens = st.lens.clone()
+    lens[0] = 3
+    with pytest.raises(binding.PagedKVError, match="CONTEXT_BOUNDS"):
+        binding.paged_attention_multi(st.q, st.k_cache, st.v_cache, st.tables, lens,
+                                      w.scale, out=out)
+    with pytest.raises(binding.PagedKVError, match="SHAPE"):
+        binding.paged_attention_multi(st.q[:, 0], st.k_cache, st.v_cache, st.tables,
+                                      st.lens, w.scale)
+    torch.cuda.synchronize()
+    assert torch.all(out == 2.0)
+
+
+def test_config5_with_four_new_tokens_sampled():
+    """The full-width batch with four new tokens per row (a speculative-decoding step
+    of three drafts): sampled rows against the oracle, from a host copy of just the
+    blocks those rows name."""
+    w = wl.make_config(5, query_len=4)
+    st = Step(w)
+    say(f"{w.name}: q {tuple(st.q.shape)}")
+    got = to_host(_multi_run(w, st, validate=False), "bf16")
+    assert binding.device_status(DEV, clear=True) == 0
+    rng = np.random.default_rng(21)
+    live = [r for r in range(w.rows) if w.context_lens[r] > 0]
+    longest = int(np.argmax(w.context_lens))
+    rows = sorted(set(rng.choice(live, 5, replace=False).tolist() + [longest]))
+    pads = [r for r in range(w.rows) if w.context_lens[r] == 0]
+    assert np.all(got[pads] == 0)
+    blocks = wl.live_blocks(w, rows)
+    remap = {int(b): i for i, b in enumerate(blocks)}
+    idx = torch.from_numpy(np.append(blocks, w.num_blocks).astype(np.int64)).to(DEV)
+    k = to_host(st.k_cache.index_select(0, idx), "bf16")
+    v = to_host(st.v_cache.index_select(0, idx), "bf16")
+    n = len(blocks)
+    bt = np.full((len(rows), w.max_blocks), -1, dtype=np.int32)
+    sm = []
+    for a, r in enumerate(rows):
+        live_b = wl.cdiv(w.context_lens[r], w.block_size)
+        bt[a, :live_b] = [remap[int(b)] for b in w.block_tables[r, :live_b]]
+        for i in range(4):
+            s = int(w.slot_mapping[r * 4 + i])
+            sm.append(remap[s // w.block_size] * w.block_size + s % w.block_size)
+    k_new = w.k_new.reshape(w.rows, 4, w.kv_heads, w.head_dim)[rows].reshape(-1, w.kv_heads,
+                                                                           w.head_dim)
+    v_new = w.v_new.reshape(w.rows, 4, w.kv_heads, w.head_dim)[rows].reshape(-1, w.kv_heads,
+                                                                           w.head_dim)
+    oracle.kv_write(k, v, k_new, v_new, np.array(sm, dtype=np.int64), num_blocks=n,
+                    block_size=w.block_size, layout=w.layout, dtype="bf16")
+    ref = oracle.paged_attention_multi(w.q[rows], k, v, bt, w.context_lens[rows], w.scale,
+                                       num_blocks=n, block_size=w.block_size, layout=w.layout,
+                                       dtype="bf16")
+    assert_close(got[rows], ref, "bf16", w.name)
