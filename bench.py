@@ -63,6 +63,9 @@ def parse():
                     help="1: K/V straight to registers, 2: through an LDS stage")
     ap.add_argument("--max-query-group", type=int, default=0,
                     help="query heads sharing one K/V load under GQA (0: default)")
+    ap.add_argument("--mfma", type=int, default=0,
+                    help="1: groups of 8 or 16 query vectors per KV head on the matrix "
+                         "cores (library default), 2: always on the vector units")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="override the workload's KV heads (grouped-query variant)")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
@@ -238,7 +241,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     binding.set_tuning(args.chunk_min, args.chunk_max, args.decode_waves,
-                       args.items_per_group, args.deal, args.staging, args.max_query_group)
+                       args.items_per_group, args.deal, args.staging, args.max_query_group,
+                       args.mfma)
     tuning = binding.get_tuning()
     if args.query_len > 1 and args.address != "blocks":
         raise SystemExit("--query-len > 1 reads through block tables only")

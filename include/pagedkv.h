@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /* Element type of q, out, the new K/V and both pools. */
 typedef enum pkv_dtype {
@@ -246,7 +246,8 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *   chunk_min, chunk_max  powers of two in [32, 2048], chunk_max/chunk_min <= 32
  *                         (defaults 128, 2048)
  *   decode_waves          64-lane waves per workgroup: 1, 2, 4 or 8 (default 8)
- *   items_per_group       default 16
+ *   items_per_group       default 16 (the matrix-core fold, whose items carry 8 or 16
+ *                         query vectors, aims for a quarter of it)
  *   deal                  1: whole rounds of full-length chunks are dealt to workgroups
  *                         round robin and only the rest goes through the shared work
  *                         queue; 2: every item goes through the queue (default 1)
@@ -254,12 +255,16 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *                         2: each wave streams its next sub-chunk into an LDS stage by
  *                         direct buffer-to-LDS loads while folding the current one
  *                         (default 2)
- *   max_query_group       1, 2, 4 or 8 (default 8).  With grouped-query attention
- *                         (num_heads > num_kv_heads) one work item covers QG query heads
- *                         that share a KV head, QG the largest of 8, 4, 2, 1 that divides
- *                         num_heads / num_kv_heads and is at most max_query_group, so
- *                         each K/V sub-chunk is read once for QG heads; 1 reads it once
- *                         per query head
+ *   max_query_group       1, 2, 4, 8 or 16 (default 16).  A row has query_len x heads
+ *                         query vectors, and those of one KV head (query_len x
+ *                         num_heads / num_kv_heads of them) can share each K/V load: one
+ *                         work item covers QG of them, QG the largest power of two that
+ *                         divides that count and is at most max_query_group (at most 8 on
+ *                         the vector units, 4 at head_dim 256); 1 reads K/V once per
+ *                         vector
+ *   mfma                  1: a group of 8 or 16 vectors on a bfloat16 pool of head_dim 64
+ *                         or 128 is folded on the matrix cores (default); 2: always on
+ *                         the vector units
  * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it
  * before sizing workspaces.  Results do not depend on these values beyond float32
  * rounding order.  Returns UNSUPPORTED for other values. */
@@ -271,6 +276,7 @@ typedef struct pkv_tuning {
   int32_t deal;
   int32_t staging;
   int32_t max_query_group;
+  int32_t mfma;
 } pkv_tuning;
 
 pkv_status pkv_set_tuning(const pkv_tuning* tuning);

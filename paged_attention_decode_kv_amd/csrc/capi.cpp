@@ -589,11 +589,11 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
 pkv_status pkv_set_tuning(const pkv_tuning* t) {
   if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
   if (!pkv::set_tuning(t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group,
-                       t->deal, t->staging, t->max_query_group))
+                       t->deal, t->staging, t->max_query_group, t->mfma))
     return fail(PKV_ERR_UNSUPPORTED, "tuning chunk [%d, %d], waves %d, items/group %d, "
-                "deal %d, staging %d, query group %d not supported", t->chunk_min,
+                "deal %d, staging %d, query group %d, mfma %d not supported", t->chunk_min,
                 t->chunk_max, t->decode_waves, t->items_per_group, t->deal, t->staging,
-                t->max_query_group);
+                t->max_query_group, t->mfma);
   return ok();
 }
 
@@ -606,6 +606,7 @@ pkv_status pkv_get_tuning(pkv_tuning* t) {
   t->deal = pkv::tuning_deal_static() ? 1 : 2;
   t->staging = pkv::tuning_lds_stage() ? 2 : 1;
   t->max_query_group = pkv::tuning_max_query_group();
+  t->mfma = pkv::tuning_mfma() ? 1 : 2;
   return ok();
 }
 

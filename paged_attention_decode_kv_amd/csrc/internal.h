@@ -21,7 +21,8 @@ constexpr int kDefaultDecodeWaves = 8;
 constexpr int kDefaultItemsPerGroup = 16;
 constexpr int kDefaultDealStatic = 1;
 constexpr int kDefaultLdsStage = 1;
-constexpr int kDefaultMaxQueryGroup = 8;
+constexpr int kDefaultMaxQueryGroup = 16;
+constexpr int kDefaultMfma = 1;
 
 // Slot input: tokens of one row that one workgroup of the translation pass checks.
 constexpr int kTranslateTokens = 1024;
@@ -33,8 +34,9 @@ int tuning_items_per_group();
 int tuning_deal_static();
 int tuning_lds_stage();
 int tuning_max_query_group();
+int tuning_mfma();
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal, int staging, int max_query_group);
+                int deal, int staging, int max_query_group, int mfma);
 
 // Pool geometry in elements, derived from the descriptor.
 struct PoolGeom {

@@ -389,6 +389,20 @@ struct ItemMeta {
   int blk_hi;    // lane i: block id of the chunk's (64 + i)-th block
 };
 
+// The block ids of an item's chunk, two per lane: lane i holds the chunk's i-th and
+// (64 + i)-th (a chunk spans at most kMaxChunkTokens / 16 = 128 blocks).
+__device__ __forceinline__ void load_chunk_blocks(const AttnArgs& a, int r, int chunk, int ctx,
+                                                  int lp, int log2_bs, int lane, int& blk,
+                                                  int& blk_hi) {
+  const int t_begin = chunk << lp;
+  const int t_end = min(ctx, t_begin + (1 << lp));
+  const int j0 = t_begin >> log2_bs;
+  const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
+  const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks + j0;
+  if (lane < nblk) blk = bt[lane];
+  if (lane + 64 < nblk) blk_hi = bt[lane + 64];
+}
+
 // First half of fetching an item's metadata: the work-list entry load is issued and
 // its value is not consumed, so no wait is inserted here.
 __device__ __forceinline__ int4 issue_entry(const Workspace& ws, int item, int groups) {
@@ -421,14 +435,7 @@ __device__ __forceinline__ ItemMeta<QG> finish_meta(const AttnArgs& a, int4 ent,
     for (int j = 0; j < QG; ++j)
       m.q[j] = load16(static_cast<const T*>(a.q) + vec_slot(a, m.r, m.hg * QG + j) * D +
                       sub * E);
-    const int t_begin = m.chunk << lp;
-    const int t_end = min(m.ctx, t_begin + (1 << lp));
-    const int j0 = t_begin >> log2_bs;
-    // a chunk spans at most kMaxChunkTokens / 16 = 128 blocks
-    const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
-    const int32_t* bt = a.block_tables + (int64_t)m.r * a.max_blocks + j0;
-    if (lane < nblk) m.blk = bt[lane];
-    if (lane + 64 < nblk) m.blk_hi = bt[lane + 64];
+    load_chunk_blocks(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, m.blk, m.blk_hi);
   }
   return m;
 }
@@ -454,6 +461,71 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
   const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, kLoadNonTemporal);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// Sub-chunk addressing of one work item, shared by the decode kernels.  describe()
+// builds the buffer descriptors of sub-chunk s's K and V; they end after its valid
+// tokens, so the loads of masked tokens never reach memory.  A block id outside the
+// pool is skipped (no valid tokens) and noted in `bad`.
+struct ChunkAddr {
+  const char* kpool;
+  const char* vpool;
+  int64_t head_off, blk_bytes, tok_bytes;
+  int t_begin, t_end, j0, log2_bs, bs_mask;
+  int64_t num_blocks;
+  int blk, blk_hi;   // lane i: block ids i and 64 + i of the chunk
+
+  template <int CH>
+  __device__ __forceinline__ int describe(int s, __amdgpu_buffer_rsrc_t& ksrc,
+                                          __amdgpu_buffer_rsrc_t& vsrc, bool& bad) const {
+    const int t0 = t_begin + s * CH;
+    const int jb = (t0 >> log2_bs) - j0;   // block of this sub-chunk within the chunk
+    const int raw = jb < 64 ? __builtin_amdgcn_readlane(blk, jb)
+                            : __builtin_amdgcn_readlane(blk_hi, jb - 64);
+    const bool blk_ok = raw >= 0 && raw < num_blocks;
+    bad |= !blk_ok;
+    const int id = blk_ok ? raw : 0;
+    const int64_t off = head_off + (int64_t)id * blk_bytes + (int64_t)(t0 & bs_mask) * tok_bytes;
+    const int nvalid = blk_ok ? min(CH, t_end - t0) : 0;
+    const int bytes = (int)(nvalid * tok_bytes);
+    ksrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), 0, bytes,
+                                             kBufferFlags);
+    vsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), 0, bytes,
+                                             kBufferFlags);
+    return nvalid;
+  }
+};
+
+// Item order of the persistent decode kernels: whole rounds of the full chunks
+// (section A) are dealt round robin, workgroup g taking items g, g + G, ...; the rest
+// come from one shared ticket counter (n_dealt + ticket; anything at or past the data
+// items ends the stream).
+struct ItemOrder {
+  int static_next, stride, n_dealt;
+  __device__ __forceinline__ bool take(int& out) {   // true: a dealt item was taken
+    if (static_next < n_dealt) {
+      out = static_next;
+      static_next += stride;
+      return true;
+    }
+    return false;
+  }
+  // The first two items of a workgroup (all threads; may pass two barriers).
+  __device__ __forceinline__ void first_two(int& item, int& next, int32_t* ticket,
+                                            int* s_ticket) {
+    const bool st0 = take(item);
+    const bool st1 = take(next);
+    if (!st0 || !st1) {
+      if (threadIdx.x == 0) {
+        s_ticket[0] = st0 ? 0 : atomicAdd(ticket, 1);
+        s_ticket[1] = st1 ? 0 : atomicAdd(ticket, 1);
+      }
+      __syncthreads();
+      if (!st0) item = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[0]);
+      if (!st1) next = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[1]);
+      __syncthreads();
+    }
+  }
+};
 
 // The decode read.  Persistent workgroups process work items; an item is (chunk of a
 // row's history, group of QG query heads sharing one KV head), and the waves of a
@@ -513,32 +585,9 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
 
-  // Item indices: static ones from the deal, dynamic ones from the ticket counter
-  // (n_dealt + ticket; anything at or past n_data ends the stream).
-  int static_next = blockIdx.x;
-  auto take = [&](int& out) -> bool {        // true: a static item was taken
-    if (static_next < n_dealt) {
-      out = static_next;
-      static_next += G;
-      return true;
-    }
-    return false;
-  };
+  ItemOrder order{(int)blockIdx.x, G, n_dealt};
   int item, next;
-  {
-    const bool st0 = take(item);
-    const bool st1 = take(next);
-    if (!st0 || !st1) {
-      if (threadIdx.x == 0) {
-        s_ticket[0] = st0 ? 0 : atomicAdd(&ws.counters[1], 1);
-        s_ticket[1] = st1 ? 0 : atomicAdd(&ws.counters[1], 1);
-      }
-      __syncthreads();
-      if (!st0) item = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[0]);
-      if (!st1) next = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[1]);
-      __syncthreads();
-    }
-  }
+  order.first_two(item, next, &ws.counters[1], s_ticket);
   int buf = 0;
   bool bad_block = false;   // a live block id outside [0, num_blocks) was skipped
   Meta cur;
@@ -548,7 +597,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   while (item < n_data) {
     // the item after next: static, or a ticket whose value is needed only at the end
     int after = 0;
-    const bool after_static = take(after);
+    const bool after_static = order.take(after);
     if (!after_static && threadIdx.x == 0) after = atomicAdd(&ws.counters[1], 1);
     int4 next_ent = make_int4(0, -1, 0, 0);
     if (next < n_data) next_ent = issue_entry(ws, next, groups);
@@ -577,24 +626,10 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       last_rel[j] = __builtin_amdgcn_readfirstlane(cur.last[j]) - t_begin;
 
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
-    // Descriptors of sub-chunk s's K and V: they end after its valid tokens, so the
-    // loads of masked tokens never reach memory.  Returns the valid-token count.
+    const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end, j0,
+                       log2_bs, bs_mask, a.g.num_blocks, cur.blk, cur.blk_hi};
     auto describe = [&](int s, __amdgpu_buffer_rsrc_t& ksrc, __amdgpu_buffer_rsrc_t& vsrc) {
-      const int t0 = t_begin + s * CH;
-      const int jb = (t0 >> log2_bs) - j0;   // block of this sub-chunk within the chunk
-      const int raw = jb < 64 ? __builtin_amdgcn_readlane(cur.blk, jb)
-                              : __builtin_amdgcn_readlane(cur.blk_hi, jb - 64);
-      const bool blk_ok = raw >= 0 && raw < a.g.num_blocks;
-      bad_block |= !blk_ok;
-      const int blk = blk_ok ? raw : 0;
-      const int64_t off = head_off + (int64_t)blk * blk_bytes + (int64_t)(t0 & bs_mask) * tok_bytes;
-      const int nvalid = blk_ok ? min(CH, t_end - t0) : 0;
-      const int bytes = (int)(nvalid * tok_bytes);
-      ksrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), 0, bytes,
-                                               kBufferFlags);
-      vsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), 0, bytes,
-                                               kBufferFlags);
-      return nvalid;
+      return ca.describe<CH>(s, ksrc, vsrc, bad_block);
     };
     auto stage_in = [&](int s) {   // sub-chunk s -> this wave's LDS stage
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
@@ -767,6 +802,294 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 }
 
 // ------------------------------------------------------------------------- //
+// decode on the matrix cores
+// ------------------------------------------------------------------------- //
+// With 8 or 16 query vectors per KV head (grouped heads x new tokens), the fold of a
+// 16-token sub-chunk is two small dense products per item:
+//   S^T[16 tokens x 16 vectors]  = K[16 x d] . Q^T[d x 16]   (v_mfma_f32_16x16x32_bf16)
+//   O^T[d x 16 vectors]         += V^T[d x 16] . P^T[16 x 16] (v_mfma_f32_16x16x16_bf16)
+// K comes from the LDS stage row by row; V^T by transposing LDS reads
+// (ds_read_b64_tr_b16); the scores' result layout (lane: one vector, four tokens) is
+// already the P^T operand, so nothing moves between lanes but the running maxima.
+// P goes in as two bfloat16 parts (hi + the rounding residue), keeping the weights at
+// float precision.  Lane l owns vector l % 16 and rows 4 (l / 16) .. +3 of each tile.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 4 bf16 of a transposing LDS read: within each 16-lane group the four rows addressed by
+// lanes 4r .. 4r + 3 (8 bytes each) come back one column per lane.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+template <int D>
+struct MfmaMeta {
+  int r, hg, chunk, nch, ctx;
+  int last;           // lane: last visible position of vector hg*QG + l%16 (-1: none)
+  uint4 q[D / 32];    // lane: 8 dims (32 s + 8 (l/16) ..) of that vector's query
+  int blk, blk_hi;
+};
+
+template <int D, int QG>
+__device__ __forceinline__ MfmaMeta<D> finish_meta_mfma(const AttnArgs& a, int4 ent, int item,
+                                                        int lp, int log2_bs, int lane) {
+  const int groups = a.query_len * a.num_heads / QG;
+  const int col = lane & 15, grp = lane >> 4;
+  MfmaMeta<D> m;
+  const int e = item / groups;
+  m.hg = item - e * groups;
+  m.r = __builtin_amdgcn_readfirstlane(ent.x);
+  m.chunk = __builtin_amdgcn_readfirstlane(ent.y);
+  m.nch = __builtin_amdgcn_readfirstlane(ent.z);
+  m.ctx = __builtin_amdgcn_readfirstlane(ent.w);
+  const int v = m.hg * QG + col;
+  m.last = col < QG ? m.ctx - a.query_len + vec_query(a, v) : -1;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) m.q[s] = make_uint4(0, 0, 0, 0);
+  m.blk = 0;
+  m.blk_hi = 0;
+  if (m.chunk >= 0) {
+    if (col < QG) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + vec_slot(a, m.r, v) * D + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) m.q[s] = load16(qp + 32 * s);
+    }
+    load_chunk_blocks(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, m.blk, m.blk_hi);
+  }
+  return m;
+}
+
+// Same schedule, staging and partial records as decode_kernel (bfloat16 pools, head_dim
+// 64 or 128, sub-chunks of 16 tokens).  After its last fold a wave parks its state,
+// [QG][D] floats, in its own stage, and the waves are merged from there.
+template <int D, int WAVES, int QG>
+__global__ void __launch_bounds__(WAVES * 64)
+decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
+  using T = uint16_t;
+  using S = Shape<T, D>;
+  using Meta = MfmaMeta<D>;
+  constexpr int E = S::E, TPS = S::TPS, U = S::U, CH = S::CH, LPT = S::LPT;
+  constexpr int ES = sizeof(T);
+  static_assert(CH == 16, "one 16-token tile per sub-chunk");
+  static_assert(QG == 8 || QG == 16, "8 or 16 query vectors per item");
+  constexpr int NS = D / 32;      // score products (32 dims each)
+  constexpr int NO = D / 16;      // output tiles (16 dims each)
+  constexpr int ROW = D * ES;     // bytes of one token's vector in a stage
+  constexpr int PER = D / 64;     // dims per lane in the merge
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane / LPT;       // DMA: token of a wave load
+  const int sub = lane % LPT;     // DMA: 16-byte piece
+  const int col = lane & 15;      // matrix cores: vector (and K row) of this lane
+  const int grp = lane >> 4;      // matrix cores: row group of this lane
+
+  __shared__ __attribute__((aligned(16))) uint4 s_stage[WAVES][2 * U][64];
+  static_assert(QG * D * 4 <= 2 * U * 64 * 16, "a wave's merge state fits its stage");
+  __shared__ int s_ticket[2];
+  __shared__ float s_m[2][QG][WAVES], s_l[2][QG][WAVES];
+
+  const int n_vec = a.query_len * a.num_heads;
+  const int groups = n_vec / QG;
+  const int vpkv = n_vec / a.g.kv_heads;
+  const int lp = ws.counters[3];
+  const int P = 1 << lp;
+  const int n_static = ws.counters[4] * groups;
+  const int n_data = ws.counters[5] * groups;
+  const int n_items = ws.counters[0] * groups;
+  const int G = gridDim.x;
+  const int n_dealt = a.deal_static ? n_static / G * G : 0;
+  const int log2_bs = a.g.log2_bs;
+  const int bs_mask = a.g.block_size - 1;
+  const int64_t tok_bytes = a.g.tok_stride * ES;
+  const int64_t blk_bytes = a.g.blk_stride * ES;
+  const int64_t head_bytes = a.g.head_stride * ES;
+  uint32_t voff[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    voff[u] = (uint32_t)((u * TPS + g) * tok_bytes + sub * E * ES);
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+  const char* st_k = reinterpret_cast<const char*>(&s_stage[wave][0][0]);
+  const char* st_v = reinterpret_cast<const char*>(&s_stage[wave][U][0]);
+  // this lane's K row (token col, 8 dims at 8 grp) and V^T row addresses in a stage
+  const char* k_row = st_k + col * ROW + 8 * grp * ES;
+  const char* v_row = st_v + (4 * grp + (col >> 2)) * ROW + 4 * (col & 3) * ES;
+
+  ItemOrder order{(int)blockIdx.x, G, n_dealt};
+  int item, next;
+  order.first_two(item, next, &ws.counters[1], s_ticket);
+  int buf = 0;
+  bool bad_block = false;
+  Meta cur;
+  if (item < n_data)
+    cur = finish_meta_mfma<D, QG>(a, issue_entry(ws, item, groups), item, lp, log2_bs, lane);
+
+  while (item < n_data) {
+    int after = 0;
+    const bool after_static = order.take(after);
+    if (!after_static && threadIdx.x == 0) after = atomicAdd(&ws.counters[1], 1);
+    int4 next_ent = make_int4(0, -1, 0, 0);
+    if (next < n_data) next_ent = issue_entry(ws, next, groups);
+
+    const int chunk = __builtin_amdgcn_readfirstlane(cur.chunk);
+    const int hg = __builtin_amdgcn_readfirstlane(cur.hg);
+    const int t_begin = chunk * P;
+    const int t_end = min(__builtin_amdgcn_readfirstlane(cur.ctx), t_begin + P);
+    const int j0 = t_begin >> log2_bs;
+    const int64_t head_off = (int64_t)(hg * QG / vpkv) * head_bytes;
+    const int last_rel = cur.last - t_begin;      // this lane's vector
+
+    f32x4_t acc[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) acc[o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    const int n_sub = (t_end - t_begin + CH - 1) / CH;
+    const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end, j0,
+                       log2_bs, bs_mask, a.g.num_blocks, cur.blk, cur.blk_hi};
+    auto stage_in = [&](int s) {
+      __amdgpu_buffer_rsrc_t ksrc, vsrc;
+      ca.describe<CH>(s, ksrc, vsrc, bad_block);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        buffer_load16_lds(ksrc, voff[u], &s_stage[wave][u][0]);
+        buffer_load16_lds(vsrc, voff[u], &s_stage[wave][U + u][0]);
+      }
+    };
+    if (wave < n_sub) stage_in(wave);
+    for (int s = wave; s < n_sub; s += WAVES) {
+      __amdgpu_buffer_rsrc_t ksrc, vsrc;
+      const int nvalid = ca.describe<CH>(s, ksrc, vsrc, bad_block);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this wave's stage has landed
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < NS; ++ds) {
+        const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(k_row + 32 * ds * ES);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, __builtin_bit_cast(bf16x8_t, cur.q[ds]),
+                                                     sc, 0, 0, 0);
+      }
+      i16x4_t vt[NO];
+#pragma unroll
+      for (int o = 0; o < NO; ++o) vt[o] = lds_read_tr16(v_row + 16 * o * ES);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // stage read before it is refilled
+      if (s + WAVES < n_sub) stage_in(s + WAVES);
+
+      // online softmax of this tile for the lane's vector (tokens 4 grp .. 4 grp + 3)
+      const int vis = min(nvalid, last_rel - s * CH + 1);
+      float x[4], tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = 4 * grp + e < vis ? sc[e] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[e]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m, tmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      l *= alpha;
+#pragma unroll
+      for (int o = 0; o < NO; ++o) acc[o] *= alpha;
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+        l += p[e];
+      }
+      const uint32_t h01 = Elem<uint16_t>::cvt2(p[0], p[1]);
+      const uint32_t h23 = Elem<uint16_t>::cvt2(p[2], p[3]);
+      const uint32_t l01 = Elem<uint16_t>::cvt2(p[0] - __uint_as_float(h01 << 16),
+                                                p[1] - __uint_as_float(h01 & 0xffff0000u));
+      const uint32_t l23 = Elem<uint16_t>::cvt2(p[2] - __uint_as_float(h23 << 16),
+                                                p[3] - __uint_as_float(h23 & 0xffff0000u));
+      const i16x4_t ph = __builtin_bit_cast(i16x4_t, make_uint2(h01, h23));
+      const i16x4_t pl = __builtin_bit_cast(i16x4_t, make_uint2(l01, l23));
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        acc[o] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[o], ph, acc[o], 0, 0, 0);
+        acc[o] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[o], pl, acc[o], 0, 0, 0);
+      }
+      m = m_new;
+    }
+
+    const Meta nxt = finish_meta_mfma<D, QG>(a, next_ent, next, lp, log2_bs, lane);
+    l += __shfl_xor(l, 16);        // the four row groups' denominators
+    l += __shfl_xor(l, 32);
+    // park this wave's state in its own stage (its last stage read has completed)
+    float* park = reinterpret_cast<float*>(&s_stage[wave][0][0]);
+    if (col < QG) {
+#pragma unroll
+      for (int o = 0; o < NO; ++o)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) park[col * D + 16 * o + 4 * grp + e] = acc[o][e];
+      if (grp == 0) {
+        s_m[buf][col][wave] = m;
+        s_l[buf][col][wave] = l;
+      }
+    }
+    if (!after_static && threadIdx.x == 0) s_ticket[buf] = after;
+    __syncthreads();
+    if (!after_static) after = n_dealt + __builtin_amdgcn_readfirstlane(s_ticket[buf]);
+    // merge the waves: wave w finishes vectors w, w + WAVES, ...
+    for (int j = wave; j < QG; j += WAVES) {
+      float mx = s_m[buf][j][0];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) mx = fmaxf(mx, s_m[buf][j][w]);
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      float lj = 0.f, y[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) y[i] = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float f = __builtin_amdgcn_exp2f(s_m[buf][j][w] - mu);
+        lj += s_l[buf][j][w] * f;
+        const float* pw = reinterpret_cast<const float*>(&s_stage[w][0][0]) + j * D + lane * PER;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) y[i] += pw[i] * f;
+      }
+      const int v = hg * QG + j;
+      if (cur.nch == 1) {
+        const float inv = lj > 0.f ? 1.0f / lj : 0.f;
+        T* op = static_cast<T*>(a.out) + vec_slot(a, cur.r, v) * D + lane * PER;
+        if constexpr (PER == 1) {
+          op[0] = (uint16_t)(Elem<uint16_t>::cvt2(y[0] * inv, 0.f) & 0xffffu);
+        } else {
+#pragma unroll
+          for (int i = 0; i < PER; i += 2)
+            *reinterpret_cast<uint32_t*>(op + i) = Elem<uint16_t>::cvt2(y[i] * inv, y[i + 1] * inv);
+        }
+      } else {
+        float* rec = ws.partials + (((int64_t)cur.r * n_vec + v) * ws.max_chunks + chunk) * (D + 4);
+        if (lane == 0) {
+          rec[0] = mx;
+          rec[1] = lj;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) rec[4 + lane * PER + i] = y[i];
+      }
+    }
+    __syncthreads();     // every stage is free again before the next item streams in
+    buf ^= 1;
+    item = next;
+    cur = nxt;
+    next = after;
+  }
+  if (bad_block && lane == 0) atomicOr(&g_status, PKV_DEVERR_BLOCK_ID);
+  for (int it = n_data + (int)blockIdx.x; it < n_items; it += G) {
+    const int e = it / groups;
+    const int hgp = it - e * groups;
+    const int r = ws.entries[e].x;
+    for (int j = wave; j < QG; j += WAVES) {
+      T* op = static_cast<T*>(a.out) + vec_slot(a, r, hgp * QG + j) * D + lane * PER;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) op[i] = 0;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- //
 // combine
 // ------------------------------------------------------------------------- //
 constexpr int kCombineThreads = 256;
@@ -782,78 +1105,54 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One workgroup per (query vector, row) of a row split into several chunks.  Chunk c
-// of the row carries (m_c, l_c, acc_c); the result is sum_c 2^(m_c - M) acc_c divided
-// by sum_c 2^(m_c - M) l_c with M = max_c m_c.  Each wave sums a fixed subset of the
-// chunks (c = wave mod 4) and the four partial sums are added in wave order, so the
-// result does not depend on scheduling.  A chunk wholly past a vector's causal limit
-// carries m = -inf and l = 0 and adds nothing.
+// One wave per (row, query vector) of a row split into several chunks, four waves to
+// a workgroup.  Chunk c of the row carries (m_c, l_c, acc_c); the result is
+// sum_c 2^(m_c - M) acc_c divided by sum_c 2^(m_c - M) l_c with M = max_c m_c, summed in
+// chunk order, so it does not depend on scheduling.  Lane i holds dims i * D/64 .. of
+// the vector.  A chunk wholly past a vector's causal limit carries m = -inf and l = 0
+// and adds nothing.
 template <typename T, int D>
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Workspace ws) {
   constexpr int PER = D / 64;     // dims per lane
   constexpr int W = kCombineThreads / 64;
-  __shared__ float s_red[W];
-  __shared__ float s_acc[W][D];
-  const int v = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int n_vec = a.query_len * a.num_heads;
+  const int v = blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t r = blockIdx.y;
+  if (v >= n_vec) return;
   const int ctx = ws.row_ctx[r];
   const int lp = ws.counters[3];
   const int nch = (ctx + (1 << lp) - 1) >> lp;
   if (nch <= 1) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t rv = r * (a.query_len * a.num_heads) + v;
-  const float* rec = ws.partials + rv * ws.max_chunks * (D + 4);
+  const float* rec = ws.partials + (r * n_vec + v) * ws.max_chunks * (D + 4);
 
   float mx = -INFINITY;
-  for (int c = threadIdx.x; c < nch; c += kCombineThreads) mx = fmaxf(mx, rec[c * (D + 4)]);
+  for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, rec[c * (D + 4)]);
   mx = wave_max(mx);
-  if (lane == 0) s_red[wave] = mx;
-  __syncthreads();
-  mx = s_red[0];
-#pragma unroll
-  for (int w = 1; w < W; ++w) mx = fmaxf(mx, s_red[w]);
   if (mx == -INFINITY) mx = 0.f;   // only a row whose length was out of bounds
-  __syncthreads();
-
   float l = 0.f, acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int c = threadIdx.x; c < nch; c += kCombineThreads)
-    l += rec[c * (D + 4) + 1] * __builtin_amdgcn_exp2f(rec[c * (D + 4)] - mx);
-  for (int c = wave; c < nch; c += W) {
+#pragma unroll 4
+  for (int c = 0; c < nch; ++c) {
     const float* p = rec + c * (D + 4);
     const float f = __builtin_amdgcn_exp2f(p[0] - mx);
+    l += p[1] * f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] += p[4 + lane * PER + i] * f;
   }
-  l = wave_sum(l);
-  if (lane == 0) s_red[wave] = l;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) s_acc[wave][lane * PER + i] = acc[i];
-  __syncthreads();
-  if (wave != 0) return;
-  float lt = 0.f;
-#pragma unroll
-  for (int w = 0; w < W; ++w) lt += s_red[w];
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
   T* outp = static_cast<T*>(a.out) + vec_slot(a, r, v) * D + lane * PER;
-  float y[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) s += s_acc[w][lane * PER + i];
-    y[i] = s * inv;
-  }
   if constexpr (sizeof(T) == 4) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) outp[i] = y[i];
+    for (int i = 0; i < PER; ++i) outp[i] = acc[i] * inv;
   } else if constexpr (PER == 1) {
-    outp[0] = (uint16_t)(Elem<uint16_t>::cvt2(y[0], 0.f) & 0xffffu);
+    outp[0] = (uint16_t)(Elem<uint16_t>::cvt2(acc[0] * inv, 0.f) & 0xffffu);
   } else {
 #pragma unroll
     for (int i = 0; i < PER; i += 2)
-      *reinterpret_cast<uint32_t*>(outp + i) = Elem<uint16_t>::cvt2(y[i], y[i + 1]);
+      *reinterpret_cast<uint32_t*>(outp + i) = Elem<uint16_t>::cvt2(acc[i] * inv,
+                                                                    acc[i + 1] * inv);
   }
 }
 
@@ -1122,9 +1421,11 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int WAVES, bool LDS_STAGE, int QG>
+template <typename T, int D, int WAVES, bool LDS_STAGE, int QG, bool MFMA = false>
 static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
-  auto kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
+  void (*kern)(AttnArgs, Workspace, float);
+  if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG>;
+  else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
   static int per_cu[64] = {0};   // occupancy per device, computed once
   static int num_cu[64] = {0};
   int dev = 0;
@@ -1147,7 +1448,10 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   if (grid > most) grid = most;
   AttnArgs pa = a;
   pa.query_group = QG;
-  pa.target_items = (int32_t)(grid * tuning_items_per_group());
+  // an item on the matrix cores carries 8 or 16 query vectors: a quarter as many items
+  // keep the workgroups as busy (measured best at the full-width batch's lengths)
+  const int per_group = MFMA ? (tuning_items_per_group() + 3) / 4 : tuning_items_per_group();
+  pa.target_items = (int32_t)(grid * per_group);
   pa.deal_static = tuning_deal_static();
   timing_begin(PKV_PHASE_PLAN, stream);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa, ws);
@@ -1158,8 +1462,10 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   timing_end(PKV_PHASE_DECODE, stream);
   if (ws.max_chunks > 1) {
     timing_begin(PKV_PHASE_COMBINE, stream);
+    const int waves = kCombineThreads / 64;
     hipLaunchKernelGGL((combine_kernel<T, D>),
-                       dim3(a.query_len * a.num_heads, (unsigned)a.num_rows),
+                       dim3((a.query_len * a.num_heads + waves - 1) / waves,
+                            (unsigned)a.num_rows),
                        dim3(kCombineThreads), 0, stream, a, ws);
     timing_end(PKV_PHASE_COMBINE, stream);
   }
@@ -1173,15 +1479,34 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
 static int query_group_of(const AttnArgs& a) {
   const int vpkv = a.query_len * (a.num_heads / a.g.kv_heads);
   int cap = tuning_max_query_group();
+  if (cap > 8) cap = 8;
   if (a.g.head_dim >= 256 && cap > 4) cap = 4;
   for (int qg = 8; qg > 1; qg >>= 1)
     if (qg <= cap && vpkv % qg == 0) return qg;
   return 1;
 }
 
+// query vectors per item on the matrix cores: 16 or 8 when that many share a KV head
+// (and the tuning allows it), else 0 (the vector units take the call)
+static int mfma_group_of(const AttnArgs& a) {
+  if (!tuning_mfma() || a.g.dtype != PKV_BF16 || a.g.head_dim > 128) return 0;
+  const int vpkv = a.query_len * (a.num_heads / a.g.kv_heads);
+  const int cap = tuning_max_query_group();
+  for (int qg = 16; qg >= 8; qg >>= 1)
+    if (qg <= cap && vpkv % qg == 0) return qg;
+  return 0;
+}
+
 template <typename T, int D>
 static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws,
                                   hipStream_t stream) {
+  if constexpr (sizeof(T) == 2 && D <= 128) {
+    switch (mfma_group_of(a)) {
+      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream);
+      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream);
+      default: break;
+    }
+  }
   switch (query_group_of(a)) {
     case 8:
       if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream);

@@ -102,6 +102,7 @@ std::atomic<int> g_items_per_group{kDefaultItemsPerGroup};
 std::atomic<int> g_deal_static{kDefaultDealStatic};
 std::atomic<int> g_lds_stage{kDefaultLdsStage};
 std::atomic<int> g_max_query_group{kDefaultMaxQueryGroup};
+std::atomic<int> g_mfma{kDefaultMfma};
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 }  // namespace
@@ -113,11 +114,13 @@ int tuning_items_per_group() { return g_items_per_group.load(std::memory_order_r
 int tuning_deal_static() { return g_deal_static.load(std::memory_order_relaxed); }
 int tuning_lds_stage() { return g_lds_stage.load(std::memory_order_relaxed); }
 int tuning_max_query_group() { return g_max_query_group.load(std::memory_order_relaxed); }
+int tuning_mfma() { return g_mfma.load(std::memory_order_relaxed); }
 
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal, int staging, int max_query_group) {
+                int deal, int staging, int max_query_group, int mfma) {
   const int lo = chunk_min ? chunk_min : tuning_chunk_min();
   const int hi = chunk_max ? chunk_max : tuning_chunk_max();
+  // validate everything before changing anything
   if (!pow2_in(lo, kMinChunkTokens, kMaxChunkTokens) ||
       !pow2_in(hi, kMinChunkTokens, kMaxChunkTokens) || lo > hi || hi / lo > 32)
     return false;
@@ -127,16 +130,18 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
   if (items_per_group < 0 || items_per_group > 1024) return false;
   if (deal < 0 || deal > 2) return false;
   if (staging < 0 || staging > 2) return false;
-  if (staging != 0) g_lds_stage.store(staging == 2 ? 1 : 0);
   if (max_query_group != 0 && max_query_group != 1 && max_query_group != 2 &&
-      max_query_group != 4 && max_query_group != 8)
+      max_query_group != 4 && max_query_group != 8 && max_query_group != 16)
     return false;
-  if (max_query_group != 0) g_max_query_group.store(max_query_group);
-  if (deal != 0) g_deal_static.store(deal == 1 ? 1 : 0);
+  if (mfma < 0 || mfma > 2) return false;
   g_chunk_min.store(lo);
   g_chunk_max.store(hi);
   if (decode_waves != 0) g_decode_waves.store(decode_waves);
   if (items_per_group != 0) g_items_per_group.store(items_per_group);
+  if (deal != 0) g_deal_static.store(deal == 1 ? 1 : 0);
+  if (staging != 0) g_lds_stage.store(staging == 2 ? 1 : 0);
+  if (max_query_group != 0) g_max_query_group.store(max_query_group);
+  if (mfma != 0) g_mfma.store(mfma == 1 ? 1 : 0);
   return true;
 }
 

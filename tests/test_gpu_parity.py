@@ -413,7 +413,7 @@ GQA_CASES = [
 
 
 @pytest.mark.parametrize("case", GQA_CASES, ids=lambda c: f"{c[4]}-{c[5]}-d{c[3]}-h{c[1]}/{c[2]}")
-@pytest.mark.parametrize("max_group", [8, 1])
+@pytest.mark.parametrize("max_group", [16, 8, 1])
 def test_grouped_query_heads(case, max_group):
     """Grouped-query attention: one K/V load serves up to 8 query heads (max_group 8) or
     one (max_group 1); both match the oracle."""
@@ -922,3 +922,45 @@ def test_config5_with_four_new_tokens_sampled():
                                        num_blocks=n, block_size=w.block_size, layout=w.layout,
                                        dtype="bf16")
     assert_close(got[rows], ref, "bf16", w.name)
+
+
+# --------------------------------------------------------------------------- #
+# the matrix-core fold (8 or 16 query vectors per KV head, bfloat16, d 64/128)
+# --------------------------------------------------------------------------- #
+MFMA_CASES = [
+    # name, lens, query_len, heads, kv_heads, head_dim, layout
+    ("gqa8-d128", [1, 17, 0, 300, 1025, 2050, 64], 1, 32, 4, 128, "HND"),
+    ("gqa16-d128-nhd", [5, 700, 129, 0, 2000], 1, 32, 2, 128, "NHD"),
+    ("gqa16-d64", [33, 1, 900, 16], 1, 16, 1, 64, "HND"),
+    ("q4-gqa4", [4, 90, 1500, 0, 77], 4, 8, 2, 128, "HND"),
+    ("q8-mha-d64-nhd", [8, 300, 31, 1100], 8, 4, 4, 64, "NHD"),
+    ("q16-mha", [16, 600, 2100], 16, 4, 4, 128, "HND"),
+    ("q2-gqa8", [2, 40, 513], 2, 32, 4, 128, "HND"),
+]
+
+
+@pytest.mark.parametrize("mfma", [1, 2])
+@pytest.mark.parametrize("chunk", [0, 32])
+@pytest.mark.parametrize("case", MFMA_CASES, ids=[c[0] for c in MFMA_CASES])
+def test_matrix_core_groups(case, chunk, mfma):
+    """Groups of 8 or 16 query vectors per KV head on the matrix cores (mfma=1) and on
+    the vector units (mfma=2), default and 32-token chunks: every output against the
+    oracle."""
+    name, lens, n_q, heads, kvh, d, layout = case
+    w = wl.make_custom(lens, heads=heads, kv_heads=kvh, head_dim=d, dtype="bf16",
+                       layout=layout, query_len=n_q, seed=zlib.crc32(name.encode()) + 5)
+    say(f"matrix cores {name} chunk {chunk} mfma {mfma}")
+    saved = binding.get_tuning()
+    binding.set_tuning(chunk_min=chunk, chunk_max=chunk, mfma=mfma)
+    try:
+        st = Step(w, host_history=True)
+        if n_q == 1:
+            got = st.run()
+        else:
+            got = _multi_run(w, st)
+    finally:
+        binding.set_tuning(**saved)
+    ref = _multi_oracle(w, st.k_host, st.v_host) if n_q > 1 else \
+        oracle_full(w, st.k_host, st.v_host)[0]
+    assert_close(to_host(got, "bf16"), ref, "bf16", name)
+    assert binding.device_status(DEV, clear=True) == 0
