@@ -94,14 +94,15 @@ def traffic_per_launch(config_name, layout):
     the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            records = json.load(f).get("records", [])
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    if rec.get("workload") != config_name or rec.get("layout") != layout:
-        return None
-    return rec.get("bytes_per_launch")
+    src = kernel_source_hash()
+    for rec in records:
+        if (rec.get("kernel_source_sha256") == src and rec.get("workload") == config_name
+                and rec.get("layout") == layout):
+            return rec.get("bytes_per_launch")
+    return None
 
 
 def blas_threads():
