@@ -78,6 +78,11 @@ def parse():
     ap.add_argument("--address", default="blocks", choices=["blocks", "slots"],
                     help="how the read is addressed: block tables (default), or the "
                          "per-token int64 slot window of a wider slot table")
+    ap.add_argument("--scatter-rows", type=int, default=0,
+                    help="with --address slots: shuffle the live cells of this many of "
+                         "the longest rows among themselves (the same tokens, so the same "
+                         "result, but no block structure: those rows take the "
+                         "token-by-token kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
@@ -272,6 +277,8 @@ def main():
     out = torch.empty_like(q)
     width = w.max_blocks * w.block_size
     slot_win = None
+    scattered = [] if args.address != "slots" else \
+        np.argsort(-w.context_lens, kind="stable")[:args.scatter_rows].tolist()
     if args.address == "slots":
         # the slot table a serving loop keeps: [rows, width + 64] int64, each row's live
         # positions holding block id * block size + offset of the same placement, junk
@@ -281,6 +288,12 @@ def main():
             t % w.block_size
         slot_table = torch.full((w.rows, width + 64), -1, dtype=torch.int64, device=dev)
         slot_table[:, :width] = torch.where(t[None, :] < lens[:, None].long(), cells, -1)
+        if args.scatter_rows:
+            gen = torch.Generator(device=dev).manual_seed(99)
+            for r in scattered:
+                n = int(w.context_lens[r])
+                perm = torch.randperm(n, generator=gen, device=dev)
+                slot_table[r, :n] = slot_table[r, :n][perm]
         slot_win = slot_table[:, :width]
         del t, cells
         ws_bytes = binding.workspace_bytes_slots(k_cache, w.rows, w.heads, width, w.layout)
@@ -382,25 +395,38 @@ def main():
                  query_len=w.query_len)
     b = acc.algorithmic_bytes(w.context_lens, address=args.address, **shape)
     # the decode kernel reads block ids in both modes (with slots, the table the
-    # translation pass derived from the window)
-    dec_bytes = acc.algorithmic_bytes(w.context_lens, **shape)["attention"]
+    # translation pass derived from the window); rows whose slots were scattered are
+    # read by the token-by-token kernel instead, which reads their slot cells
+    reg_lens = w.context_lens.copy()
+    reg_lens[scattered] = 0
+    dec_bytes = acc.algorithmic_bytes(reg_lens, **shape)["attention"]
     rh = acc.row_heads(w.context_lens, w.heads)
     avg = {ph: (ms / n if n else None) for ph, (ms, n) in phases.items()}
     for ph, (ms, n) in phases.items():
         if n:
             log(f"  {ph:9s} {n:5d} launches, avg {ms / n * 1e3:9.2f} us")
     dec_s = avg["decode"] * 1e-3
-    achieved = dec_bytes / dec_s / 1e9
+    kernel, kern_s, kern_bytes = "decode_kernel", dec_s, dec_bytes
+    traffic = traffic_per_launch(w.name, w.layout)
+    if scattered and avg.get("token_rows"):
+        tok_lens = np.zeros_like(w.context_lens)
+        tok_lens[scattered] = w.context_lens[scattered]
+        tok_s = avg["token_rows"] * 1e-3
+        if tok_s > dec_s:   # the dominant kernel is the token-by-token one
+            kernel, kern_s = "token_rows_kernel", tok_s
+            kern_bytes = acc.algorithmic_bytes(tok_lens, address="slots", **shape)["attention"]
+        traffic = None        # the committed counters are for the unscattered batch
+    achieved = kern_bytes / kern_s / 1e9
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 2),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": traffic_per_launch(w.name, w.layout),
-        "kernel": "decode_kernel",
-        "kernel_avg_us": round(dec_s * 1e6, 2),
-        "bytes_per_launch": dec_bytes,
+        "traffic": traffic,
+        "kernel": kernel,
+        "kernel_avg_us": round(kern_s * 1e6, 2),
+        "bytes_per_launch": kern_bytes,
     }
     result = {
         "metric": METRIC,
@@ -424,6 +450,7 @@ def main():
                             "paged_attention_slots through a [rows, width] int64 slot "
                             "window")),
             "address": args.address,
+            "scattered_rows": args.scatter_rows,
             "query_len": w.query_len,
             "rows": w.rows,
             "heads": w.heads,

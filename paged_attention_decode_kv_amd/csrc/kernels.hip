@@ -197,7 +197,7 @@ __device__ int block_exclusive_scan(int x, int* s_wave, int* total) {
 // first pass reports a bad length), and 0 for a row of a slot input whose live slots
 // are not block structured, which the token-by-token kernel reads instead.
 __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool report,
-                                        bool* irregular) {
+                                        bool* irregular, int* clamped = nullptr) {
   int ctx = a.context_lens[r];
   if (ctx < 0 || ctx > a.ctx_limit) {
     if (report) atomicOr(&g_status, PKV_DEVERR_CONTEXT_BOUNDS);
@@ -212,6 +212,7 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
     for (int c = 0; c < n; ++c) irr |= f[c] != 0;
   }
   if (irregular) *irregular = irr;
+  if (clamped) *clamped = ctx;
   return irr ? 0 : ctx;
 }
 
@@ -227,7 +228,7 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 // counters[0] = entries, [1] = queue ticket (reset to 0), [2] = P, [3] = log2 P,
 // [4] = entries in section A, [5] = entries in sections A and B, [6] = rows of a slot
 // input left to the token-by-token kernel (listed in ws.irregular).  Every row's
-// length as read here goes to ws.row_ctx for the combine kernel.
+// clamped length goes to ws.row_ctx for the combine kernel.
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspace ws) {
   constexpr int kMaxChunk = kMaxChunkTokens;
   constexpr int kCand = 6;                 // chunk_max / chunk_min <= 32
@@ -252,8 +253,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
   int cnt[kCand] = {0, 0, 0, 0, 0, 0};
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
     bool irr;
-    const int ctx = plan_ctx(a, r, true, &irr);
-    ws.row_ctx[r] = ctx;
+    int full_ctx;
+    const int ctx = plan_ctx(a, r, true, &irr, &full_ctx);
+    // (a row read token by token keeps its length here: its chunks are combined too)
+    ws.row_ctx[r] = full_ctx;
     if (irr) ws.irregular[atomicAdd(&s_irregular, 1)] = (int)r;
 #pragma unroll
     for (int k = 0; k < kCand; ++k) cnt[k] += (ctx + (1 << (lmin + k)) - 1) >> (lmin + k);
@@ -1193,12 +1196,14 @@ __global__ void __launch_bounds__(kTranslateThreads) translate_slots_kernel(Attn
   if (threadIdx.x == 0) sa.row_flags[r * sa.flag_stride + blockIdx.x] = any;
 }
 
-// The rows of a slot input that are not block structured, one (row, query head) per
-// workgroup at a time: each 16-lane group (bf16 x 128) takes one token, loads its
-// slot, then the token's K and V through that slot, and folds it into its own online
-// softmax; the groups and the waves are merged at the end of the item.  A live slot
-// outside the allocatable slots is skipped and reported.  Runs after the block path,
-// which wrote zeros for these rows.
+// The rows of a slot input that are not block structured.  An item is (chunk of a row,
+// row, query head), chunk index slowest: chunks have the decode kernel's length, and a split row
+// leaves partial records for the combine kernel just as the decode kernel does.  Each
+// 16-lane group (bf16 x 128) takes one token, loads its slot, then the token's K and V
+// through that slot, and folds it into its own online softmax; the groups and the waves
+// are merged at the end of the item.  A live slot outside the allocatable slots is
+// skipped and reported.  Runs after the decode kernel (which wrote zeros for these rows)
+// and before the combine kernel.
 constexpr int kTokenRowThreads = 256;
 
 template <typename T, int D>
@@ -1218,7 +1223,9 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
   const int sub = lane % LPT;
   const int heads = a.num_heads;
   const int qpkv = heads / a.g.kv_heads;
-  const int n_items = ws.counters[6] * heads;
+  const int lp = ws.counters[3];
+  const int mch = ws.max_chunks;
+  const int64_t n_items = (int64_t)ws.counters[6] * heads * mch;
   const int64_t n_slots = a.g.num_blocks * a.g.block_size;
   const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
@@ -1228,12 +1235,19 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
   bool bad = false;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int r = __builtin_amdgcn_readfirstlane(ws.irregular[item / heads]);
-    const int h = item % heads;
-    int ctx = a.context_lens[r];
-    ctx = ctx < 0 ? 0 : (ctx > a.ctx_limit ? a.ctx_limit : ctx);
-    ctx = __builtin_amdgcn_readfirstlane(ctx);
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    // chunk slowest: every row's first chunk comes first, so the items that exist are
+    // spread over the grid rather than bunched by the grid stride
+    const int64_t per_chunk = (int64_t)ws.counters[6] * heads;
+    const int chunk = (int)(item / per_chunk);
+    const int64_t rest = item - chunk * per_chunk;
+    const int h = (int)(rest % heads);
+    const int r = __builtin_amdgcn_readfirstlane(ws.irregular[rest / heads]);
+    const int ctx = __builtin_amdgcn_readfirstlane(ws.row_ctx[r]);
+    const int nch = (ctx + (1 << lp) - 1) >> lp;
+    if (chunk >= nch) continue;            // uniform over the workgroup
+    const int t_begin = chunk << lp;
+    const int t_end = min(ctx, t_begin + (1 << lp));
     const int64_t rh = (int64_t)r * heads + h;
     const uint4 qv = load16(static_cast<const T*>(a.q) + rh * D + sub * E);
     const int64_t lane_off = (int64_t)(h / qpkv) * head_bytes + sub * E * ES;
@@ -1241,7 +1255,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
     float m = -INFINITY, l = 0.f, acc[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) acc[i] = 0.f;
-    for (int t0 = wave * TPS * U; t0 < ctx; t0 += STEP) {
+    for (int t0 = t_begin + wave * TPS * U; t0 < t_end; t0 += STEP) {
       uint4 kr[U], vr[U];
       bool ok[U];
 #pragma unroll
@@ -1250,7 +1264,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
         ok[u] = false;
         kr[u] = make_uint4(0, 0, 0, 0);
         vr[u] = make_uint4(0, 0, 0, 0);
-        if (t < ctx) {
+        if (t < t_end) {
           const int64_t slot = row[t];
           if (slot >= 0 && slot < n_slots) {
             ok[u] = true;
@@ -1323,10 +1337,23 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
 #pragma unroll
         for (int i = 0; i < E; ++i) y[i] += s_acc[w][sub * E + i] * f;
       }
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;   // every live slot skipped: zeros
+      if (nch == 1) {
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;   // every live slot skipped: zeros
 #pragma unroll
-      for (int i = 0; i < E; ++i) y[i] *= inv;
-      store16(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(y));
+        for (int i = 0; i < E; ++i) y[i] *= inv;
+        store16(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(y));
+      } else {
+        float* rec = ws.partials + (rh * ws.max_chunks + chunk) * (D + 4);
+        if (sub == 0) {
+          rec[0] = mx;
+          rec[1] = lt;
+        }
+#pragma unroll
+        for (int i = 0; i < E; i += 4)
+          store16(rec + 4 + sub * E + i, make_uint4(__float_as_uint(y[i]), __float_as_uint(y[i + 1]),
+                                                    __float_as_uint(y[i + 2]),
+                                                    __float_as_uint(y[i + 3])));
+      }
     }
     __syncthreads();
   }
@@ -1421,8 +1448,21 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// the merge of split rows (nothing to do when no row can split)
+template <typename T, int D>
+static void launch_combine_t(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
+  if (ws.max_chunks <= 1) return;
+  timing_begin(PKV_PHASE_COMBINE, stream);
+  const int waves = kCombineThreads / 64;
+  hipLaunchKernelGGL((combine_kernel<T, D>),
+                     dim3((a.query_len * a.num_heads + waves - 1) / waves, (unsigned)a.num_rows),
+                     dim3(kCombineThreads), 0, stream, a, ws);
+  timing_end(PKV_PHASE_COMBINE, stream);
+}
+
 template <typename T, int D, int WAVES, bool LDS_STAGE, int QG, bool MFMA = false>
-static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
+static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
+                                  bool combine) {
   void (*kern)(AttnArgs, Workspace, float);
   if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG>;
   else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
@@ -1460,15 +1500,7 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, pa, ws,
                      scale_log2);
   timing_end(PKV_PHASE_DECODE, stream);
-  if (ws.max_chunks > 1) {
-    timing_begin(PKV_PHASE_COMBINE, stream);
-    const int waves = kCombineThreads / 64;
-    hipLaunchKernelGGL((combine_kernel<T, D>),
-                       dim3((a.query_len * a.num_heads + waves - 1) / waves,
-                            (unsigned)a.num_rows),
-                       dim3(kCombineThreads), 0, stream, a, ws);
-    timing_end(PKV_PHASE_COMBINE, stream);
-  }
+  if (combine) launch_combine_t<T, D>(a, ws, stream);
   return hipGetLastError();
 }
 
@@ -1498,54 +1530,71 @@ static int mfma_group_of(const AttnArgs& a) {
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws,
-                                  hipStream_t stream) {
+static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
+                                  bool combine) {
   if constexpr (sizeof(T) == 2 && D <= 128) {
     switch (mfma_group_of(a)) {
-      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream);
-      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream);
+      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream, combine);
+      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream, combine);
       default: break;
     }
   }
   switch (query_group_of(a)) {
     case 8:
-      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream);
+      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream, combine);
       break;
-    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, stream);
-    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, stream);
+    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, stream, combine);
+    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, stream, combine);
     default: break;
   }
   if (tuning_lds_stage()) {
     switch (tuning_decode_waves()) {
-      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, stream);
-      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, stream);
-      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, stream);
-      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, stream);
+      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, stream, combine);
+      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, stream, combine);
+      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, stream, combine);
+      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, stream, combine);
     }
   }
   switch (tuning_decode_waves()) {
-    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, stream);
-    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, stream);
-    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, stream);
-    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, stream);
+    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, stream, combine);
+    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, stream, combine);
+    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, stream, combine);
+    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, stream, combine);
   }
 }
 
-hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws,
-                                  hipStream_t stream) {
+hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
+                                  bool combine) {
   const bool f32 = a.g.dtype == PKV_F32;
   switch (a.g.head_dim) {
     case 64:
-      return f32 ? launch_decode_t<float, 64>(a, ws, stream)
-                 : launch_decode_t<uint16_t, 64>(a, ws, stream);
+      return f32 ? launch_decode_t<float, 64>(a, ws, stream, combine)
+                 : launch_decode_t<uint16_t, 64>(a, ws, stream, combine);
     case 128:
-      return f32 ? launch_decode_t<float, 128>(a, ws, stream)
-                 : launch_decode_t<uint16_t, 128>(a, ws, stream);
+      return f32 ? launch_decode_t<float, 128>(a, ws, stream, combine)
+                 : launch_decode_t<uint16_t, 128>(a, ws, stream, combine);
     case 256:
-      return f32 ? launch_decode_t<float, 256>(a, ws, stream)
-                 : launch_decode_t<uint16_t, 256>(a, ws, stream);
+      return f32 ? launch_decode_t<float, 256>(a, ws, stream, combine)
+                 : launch_decode_t<uint16_t, 256>(a, ws, stream, combine);
     default:
       return hipErrorInvalidValue;
+  }
+}
+
+static void launch_combine(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
+  const bool f32 = a.g.dtype == PKV_F32;
+  switch (a.g.head_dim) {
+    case 64:
+      f32 ? launch_combine_t<float, 64>(a, ws, stream) : launch_combine_t<uint16_t, 64>(a, ws, stream);
+      break;
+    case 128:
+      f32 ? launch_combine_t<float, 128>(a, ws, stream)
+          : launch_combine_t<uint16_t, 128>(a, ws, stream);
+      break;
+    default:
+      f32 ? launch_combine_t<float, 256>(a, ws, stream)
+          : launch_combine_t<uint16_t, 256>(a, ws, stream);
+      break;
   }
 }
 
@@ -1585,13 +1634,14 @@ hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
   timing_end(PKV_PHASE_TRANSLATE, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_paged_attention(b, ws, stream);
+  err = launch_paged_attention(b, ws, stream, /*combine=*/false);
   if (err != hipSuccess) return err;
-  // the rows the block path could not take: one workgroup per CU works through them
-  // (the count is on the device; with none, every workgroup exits at once)
+  // the rows the block path could not take, then the merge of every split row: the
+  // count is on the device, and with none every workgroup exits at once
   int cus = 0;
   err = device_cus(&cus);
   if (err != hipSuccess) return err;
+  cus *= 4;
   timing_begin(PKV_PHASE_TOKEN_ROWS, stream);
   const bool f32 = a.g.dtype == PKV_F32;
   switch (a.g.head_dim) {
@@ -1611,6 +1661,9 @@ hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
       return hipErrorInvalidValue;
   }
   timing_end(PKV_PHASE_TOKEN_ROWS, stream);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  launch_combine(b, ws, stream);
   return hipGetLastError();
 }
 

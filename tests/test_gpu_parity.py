@@ -640,10 +640,12 @@ def test_block_structured_slots_equal_block_tables(case):
     assert binding.device_status(DEV, clear=True) == 0
 
 
+@pytest.mark.parametrize("chunk", [0, 32])
 @pytest.mark.parametrize("case", SLOT_CASES, ids=[c[0] for c in SLOT_CASES])
-def test_scattered_slots_are_read_token_by_token(case):
+def test_scattered_slots_are_read_token_by_token(case, chunk):
     """Rows whose live cells name scattered slots (and a mix with block-structured
-    rows and padding) match the oracle."""
+    rows and padding) match the oracle; chunk=32 splits the token-by-token rows into
+    many chunks, merged by the combine kernel."""
     name, lens, heads, kvh, d, bs, dtype, layout = case
     w = wl.make_custom(lens, heads=heads, kv_heads=kvh, head_dim=d, block_size=bs,
                        dtype=dtype, layout=layout, num_blocks=sum(wl.cdiv(c, bs) for c in lens) + 40,
@@ -653,9 +655,15 @@ def test_scattered_slots_are_read_token_by_token(case):
     live = [r for r in range(w.rows) if w.context_lens[r] > 0]
     scattered = live[::2]
     table = _scatter_rows(w, _block_table_rect(w, width, width), scattered, rng)
-    say(f"scattered {name}: rows {scattered} of {w.rows}")
+    say(f"scattered {name} chunk {chunk}: rows {scattered} of {w.rows}")
     st = Step(w, host_history=True)
-    got = _slot_run(st, table, width)
+    saved = binding.get_tuning()
+    if chunk:
+        binding.set_tuning(chunk_min=chunk, chunk_max=chunk)
+    try:
+        got = _slot_run(st, table, width)
+    finally:
+        binding.set_tuning(**saved)
     ref = _slot_oracle(w, st.k_host, st.v_host, table, width)
     assert_close(to_host(got, dtype), ref, dtype, name)
     assert binding.device_status(DEV, clear=True) == 0
