@@ -313,7 +313,9 @@ pkv_status pkv_timing_read(int32_t phase, double* total_ms, int64_t* launches, i
  *   semantics: no host checks; bad lengths are clamped, bad block ids and slots
  *   skipped, and each raises its bit in the device status word.  A padding row
  *   (context_lens 0, slot_mapping the sink) reads nothing and writes only the sink.
- *   The tuning in force at capture time is frozen into the graph.
+ *   The tuning in force at capture time is frozen into the graph.  The recorded step
+ *   runs the slot scatter inside the work-list kernel's launch (neither reads what the
+ *   other writes), so a replay is one kernel shorter than the two calls.
  * Capture uses a private stream and needs no synchronisation of the caller's streams.
  * pkv_graph_launch enqueues one replay on `stream`, which must belong to the device that
  * was current at capture; replays of graphs sharing buffers must be ordered (one

@@ -160,9 +160,9 @@ pkv_status check_attention_items(const pkv_pool_desc* pool, int32_t max_blocks,
   return PKV_OK;
 }
 
-hipError_t launch_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache, const void* k,
-                        const void* v, const int64_t* slot_mapping, int64_t num_tokens,
-                        hipStream_t st) {
+pkv::WriteArgs write_args(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
+                          const void* k, const void* v, const int64_t* slot_mapping,
+                          int64_t num_tokens) {
   pkv::WriteArgs a;
   a.g = geom(pool);
   a.k_cache = k_cache;
@@ -171,7 +171,14 @@ hipError_t launch_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
   a.v = v;
   a.slot_mapping = slot_mapping;
   a.num_tokens = num_tokens;
-  return pkv::launch_kv_write(a, st);
+  return a;
+}
+
+hipError_t launch_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache, const void* k,
+                        const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                        hipStream_t st) {
+  return pkv::launch_kv_write(
+      write_args(pool, k_cache, v_cache, k, v, slot_mapping, num_tokens), st);
 }
 
 hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
@@ -179,7 +186,7 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
                             const int32_t* block_tables, int32_t max_blocks,
                             const int32_t* context_lens, int64_t num_rows, int32_t num_heads,
                             float scale, void* workspace, hipStream_t st,
-                            int32_t query_len = 1) {
+                            int32_t query_len = 1, const pkv::WriteArgs* write = nullptr) {
   pkv::AttnArgs a;
   a.g = geom(pool);
   a.out = out;
@@ -203,7 +210,7 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
   a.flag_stride = 0;
   const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads * query_len,
                                                  pool->head_dim, max_blocks, pool->block_size);
-  return pkv::launch_paged_attention(a, ws, st);
+  return pkv::launch_paged_attention(a, ws, st, true, write);
 }
 
 // ---- slot input ----
@@ -649,11 +656,11 @@ pkv_status pkv_graph_capture(const pkv_pool_desc* pool, void* k_cache, void* v_c
   s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads);
   if (s != PKV_OK) return s;
 
+  // the slot scatter rides in the plan kernel's launch: one kernel fewer per replay
+  const pkv::WriteArgs wa = write_args(pool, k_cache, v_cache, k, v, slot_mapping, num_rows);
   return record_graph([&](hipStream_t cs) {
-    hipError_t e = launch_write(pool, k_cache, v_cache, k, v, slot_mapping, num_rows, cs);
-    if (e != hipSuccess) return e;
     return launch_attention(pool, out, q, k_cache, v_cache, block_tables, max_blocks_per_row,
-                            context_lens, num_rows, num_heads, scale, workspace, cs);
+                            context_lens, num_rows, num_heads, scale, workspace, cs, 1, &wa);
   }, graph);
 }
 

@@ -125,9 +125,11 @@ Workspace carve_slot_workspace(void* base, int64_t num_rows, int32_t num_heads,
                                SlotArgs* s);
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
-// combine = false leaves split rows' partials for a later launch_combine (slot input)
+// combine = false leaves split rows' partials for a later launch_combine (slot input);
+// `write`, if given, is the step's slot scatter, run inside the plan kernel's launch
+// (a captured step)
 hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
-                                  bool combine = true);
+                                  bool combine = true, const WriteArgs* write = nullptr);
 hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& s,
                                         const Workspace& ws, hipStream_t stream);
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream);

@@ -1,26 +1,37 @@
 // gfx950 kernels of the batched paged-attention decode step.
 //
-//   kv_write_kernel  slot scatter of the step's new K/V (Day 55, "the capture list
-//                    moved to startup, and the dummy batch was all padding", "Why it
-//                    matters": pad rows write the sink slot)
-//   plan_kernel      one workgroup turns context_lens into a work list of
-//                    (row, chunk) entries, longest first, and resets the work queue
-//   decode_kernel    persistent workgroups pull (entry, query head) items from the
-//                    queue; each streams its chunk of the row's history through the
-//                    block table in 16-token sub-chunks and folds them into an online
-//                    softmax (Day 59, "the rectangle the read builds, and the tile
-//                    that replaces it", "What I added today" and "What I learned" 3-4)
-//   combine_kernel   merges the per-chunk (max, denominator, accumulator) partials of
-//                    rows longer than one chunk, in chunk order
+//   kv_write_kernel     slot scatter of the step's new K/V (Day 55, "the capture list
+//                       moved to startup, and the dummy batch was all padding", "Why it
+//                       matters": pad rows write the sink slot)
+//   plan_kernel         one workgroup turns context_lens into a work list of
+//                       (row, chunk) entries, longest first, and resets the work queue;
+//                       plan_write_kernel is the same with the scatter beside it (one
+//                       launch for a captured step)
+//   decode_kernel       persistent workgroups pull (entry, group of query vectors)
+//                       items; each streams its chunk of the row's history through the
+//                       block table in 16-token sub-chunks and folds them into online
+//                       softmax states on the vector units (Day 59, "the rectangle the
+//                       read builds, and the tile that replaces it", "What I added today"
+//                       and "What I learned" 3-4)
+//   decode_mfma_kernel  the same schedule for groups of 8 or 16 query vectors per KV
+//                       head, whose fold is a pair of small matrix products on the
+//                       matrix cores
+//   combine_kernel      merges the per-chunk (max, denominator, accumulator) partials of
+//                       rows longer than one chunk, in chunk order
+//   translate_slots_kernel, token_rows_kernel
+//                       the read through a per-token slot window (Day 51, "the read
+//                       rectangle stopped being built"): block-structured rows become a
+//                       derived block table, the rest are read token by token
 //
-// Lane mapping of one wave (64 lanes) inside the decode loop: a (token, KV head)
-// vector of head_dim elements is 16-byte pieces spread over LPT consecutive lanes
-// (LPT = head_dim * elem_bytes / 16; 16 lanes for bf16 x 128), so one 16-byte load
-// per lane moves TPS = 64 / LPT tokens and the load of one wave is a contiguous
+// Lane mapping of one wave (64 lanes) inside the vector-unit decode loop: a (token, KV
+// head) vector of head_dim elements is 16-byte pieces spread over LPT consecutive lanes
+// (LPT = head_dim * elem_bytes / 16; 16 lanes for bf16 x 128), so one 16-byte load per
+// lane moves TPS = 64 / LPT tokens and the load of one wave is a contiguous
 // TPS * head_dim run in the HND layout.  Each group of LPT lanes keeps its own online
 // softmax state over the tokens it loaded; the q.k partial dot is reduced inside the
-// group with DPP row operations, and the groups are merged once per item.  There is
-// no MFMA: with one query per head the work is a bandwidth-bound streaming read.
+// group with DPP row operations, and the groups are merged once per item.  With one
+// query vector per KV head the work is a bandwidth-bound streaming read; the matrix
+// cores take over only where 8 or more vectors share each K/V load.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -134,13 +145,18 @@ __device__ __forceinline__ void store16(void* p, const uint4& v) {
 // ------------------------------------------------------------------------- //
 // slot scatter
 // ------------------------------------------------------------------------- //
+// 16-byte pieces of the scatter: num_tokens x kv_heads x (head_dim / elements per piece)
 template <typename T>
-__global__ void __launch_bounds__(256) kv_write_kernel(WriteArgs a, int64_t sink) {
+__device__ __forceinline__ int64_t kv_write_pieces(const WriteArgs& a) {
+  return a.num_tokens * a.g.kv_heads * (a.g.head_dim / Elem<T>::kPerLane);
+}
+
+// Piece idx of the scatter: token idx / per_tok, one KV head's 16 bytes of K and of V.
+template <typename T>
+__device__ __forceinline__ void kv_write_piece(const WriteArgs& a, int64_t sink, int64_t idx) {
   constexpr int E = Elem<T>::kPerLane;
   const int per_head = a.g.head_dim / E;                 // 16-byte pieces per head vector
   const int64_t per_tok = (int64_t)a.g.kv_heads * per_head;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.num_tokens * per_tok) return;
   const int64_t i = idx / per_tok;
   const int c = (int)(idx - i * per_tok);
   const int h = c / per_head;
@@ -156,6 +172,12 @@ __global__ void __launch_bounds__(256) kv_write_kernel(WriteArgs a, int64_t sink
   const int64_t src = (i * a.g.kv_heads + h) * a.g.head_dim + d0;
   store16(static_cast<T*>(a.k_cache) + dst, load16(static_cast<const T*>(a.k) + src));
   store16(static_cast<T*>(a.v_cache) + dst, load16(static_cast<const T*>(a.v) + src));
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) kv_write_kernel(WriteArgs a, int64_t sink) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < kv_write_pieces<T>(a)) kv_write_piece<T>(a, sink, idx);
 }
 
 // ------------------------------------------------------------------------- //
@@ -229,7 +251,7 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 // [4] = entries in section A, [5] = entries in sections A and B, [6] = rows of a slot
 // input left to the token-by-token kernel (listed in ws.irregular).  Every row's
 // clamped length goes to ws.row_ctx for the combine kernel.
-__global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspace ws) {
+__device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   constexpr int kMaxChunk = kMaxChunkTokens;
   constexpr int kCand = 6;                 // chunk_max / chunk_min <= 32
   __shared__ int s_wave[kPlanThreads / 64];
@@ -341,6 +363,27 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspac
     ws.counters[5] = total_a + total_b;
     ws.counters[6] = s_irregular;
   }
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(AttnArgs a, Workspace ws) {
+  plan_body(a, ws);
+}
+
+// A captured step's first kernel: workgroup 0 plans the read while the others scatter
+// the step's new K/V (neither reads what the other writes; the decode kernel, launched
+// after it, reads both).
+template <typename T>
+__global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(AttnArgs a, Workspace ws,
+                                                                  WriteArgs w, int64_t sink) {
+  if (blockIdx.x == 0) {
+    plan_body(a, ws);
+    return;
+  }
+  const int64_t n = kv_write_pieces<T>(w);
+  const int64_t stride = (int64_t)(gridDim.x - 1) * kPlanThreads;
+  for (int64_t idx = (int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x; idx < n;
+       idx += stride)
+    kv_write_piece<T>(w, sink, idx);
 }
 
 // ------------------------------------------------------------------------- //
@@ -1462,7 +1505,7 @@ static void launch_combine_t(const AttnArgs& a, const Workspace& ws, hipStream_t
 
 template <typename T, int D, int WAVES, bool LDS_STAGE, int QG, bool MFMA = false>
 static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
-                                  bool combine) {
+                                  bool combine, const WriteArgs* write) {
   void (*kern)(AttnArgs, Workspace, float);
   if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG>;
   else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
@@ -1494,7 +1537,16 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   pa.target_items = (int32_t)(grid * per_group);
   pa.deal_static = tuning_deal_static();
   timing_begin(PKV_PHASE_PLAN, stream);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa, ws);
+  if (write) {   // the step's scatter rides along with the plan
+    const int64_t pieces = write->num_tokens * write->g.kv_heads *
+                           (write->g.head_dim * (int64_t)sizeof(T) / 16);
+    int64_t blocks = (pieces + kPlanThreads - 1) / kPlanThreads;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(plan_write_kernel<T>, dim3((unsigned)(1 + blocks)), dim3(kPlanThreads), 0,
+                       stream, pa, ws, *write, write->g.num_blocks * write->g.block_size);
+  } else {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, pa, ws);
+  }
   timing_end(PKV_PHASE_PLAN, stream);
   timing_begin(PKV_PHASE_DECODE, stream);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, pa, ws,
@@ -1531,51 +1583,51 @@ static int mfma_group_of(const AttnArgs& a) {
 
 template <typename T, int D>
 static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
-                                  bool combine) {
+                                  bool combine, const WriteArgs* write) {
   if constexpr (sizeof(T) == 2 && D <= 128) {
     switch (mfma_group_of(a)) {
-      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream, combine);
-      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream, combine);
+      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream, combine, write);
+      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream, combine, write);
       default: break;
     }
   }
   switch (query_group_of(a)) {
     case 8:
-      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream, combine);
+      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream, combine, write);
       break;
-    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, stream, combine);
-    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, stream, combine);
+    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, stream, combine, write);
+    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, stream, combine, write);
     default: break;
   }
   if (tuning_lds_stage()) {
     switch (tuning_decode_waves()) {
-      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, stream, combine);
-      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, stream, combine);
-      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, stream, combine);
-      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, stream, combine);
+      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, stream, combine, write);
+      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, stream, combine, write);
+      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, stream, combine, write);
+      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, stream, combine, write);
     }
   }
   switch (tuning_decode_waves()) {
-    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, stream, combine);
-    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, stream, combine);
-    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, stream, combine);
-    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, stream, combine);
+    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, stream, combine, write);
+    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, stream, combine, write);
+    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, stream, combine, write);
+    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, stream, combine, write);
   }
 }
 
 hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
-                                  bool combine) {
+                                  bool combine, const WriteArgs* write) {
   const bool f32 = a.g.dtype == PKV_F32;
   switch (a.g.head_dim) {
     case 64:
-      return f32 ? launch_decode_t<float, 64>(a, ws, stream, combine)
-                 : launch_decode_t<uint16_t, 64>(a, ws, stream, combine);
+      return f32 ? launch_decode_t<float, 64>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 64>(a, ws, stream, combine, write);
     case 128:
-      return f32 ? launch_decode_t<float, 128>(a, ws, stream, combine)
-                 : launch_decode_t<uint16_t, 128>(a, ws, stream, combine);
+      return f32 ? launch_decode_t<float, 128>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 128>(a, ws, stream, combine, write);
     case 256:
-      return f32 ? launch_decode_t<float, 256>(a, ws, stream, combine)
-                 : launch_decode_t<uint16_t, 256>(a, ws, stream, combine);
+      return f32 ? launch_decode_t<float, 256>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 256>(a, ws, stream, combine, write);
     default:
       return hipErrorInvalidValue;
   }
