@@ -287,3 +287,15 @@ def test_multi_query_len_limits(lib):
     assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 1, 4, 4) == one
     assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 4, 4, 4) > one
     assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 0, 4, 4) == 0
+
+
+def test_row_and_width_limits(lib):
+    """The library is built for at most 65535 rows and 2^24-token rows."""
+    d = binding.host_desc(64, 16, 4, 64, "bf16", "HND")
+    p = ctypes.c_void_p(16)
+    at = lambda rows, m: _capi.STATUS_NAMES[lib.pkv_check_attention_host(
+        ctypes.byref(d), p, m, p, rows, 4)]
+    assert at(65536, 4) == "UNSUPPORTED"
+    assert at(4, (1 << 24) // 16 + 1) == "UNSUPPORTED"
+    assert lib.pkv_workspace_bytes(ctypes.byref(d), 65535, 4, 4) > 0
+    assert lib.pkv_workspace_bytes(ctypes.byref(d), 65536, 4, 4) == 0

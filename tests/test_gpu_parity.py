@@ -972,3 +972,34 @@ def test_matrix_core_groups(case, chunk, mfma):
         oracle_full(w, st.k_host, st.v_host)[0]
     assert_close(to_host(got, "bf16"), ref, "bf16", name)
     assert binding.device_status(DEV, clear=True) == 0
+
+
+# --------------------------------------------------------------------------- #
+# many rows: the plan kernel walks the rows in several passes of 1024
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("rows,hi,dtype", [(4100, 64, "f32"), (65535, 16, "bf16")])
+def test_many_rows(rows, hi, dtype):
+    """Batches wider than the plan kernel's 1024 threads (its scans carry over from pass
+    to pass), up to the largest supported batch; every output against the oracle."""
+    rng = np.random.default_rng(rows)
+    lens = rng.integers(0, hi + 1, rows)
+    lens[rng.choice(rows, rows // 10, replace=False)] = 0
+    w = wl.make_custom(lens.tolist(), heads=2, kv_heads=1, head_dim=64, dtype=dtype,
+                       seed=rows)
+    say(f"many rows: {rows} rows, lengths 0..{hi}, {int(lens.sum())} tokens")
+    err = check_full(w)
+    say(f"  max err {err:.3e}")
+
+
+def test_many_rows_through_a_slot_window():
+    rows = 3000
+    rng = np.random.default_rng(8)
+    lens = rng.integers(0, 200, rows)
+    w = wl.make_custom(lens.tolist(), heads=2, kv_heads=2, head_dim=64, dtype="bf16", seed=8)
+    width = w.max_blocks * w.block_size
+    table = _block_table_rect(w, width, width + 3)
+    table = _scatter_rows(w, table, list(range(0, rows, 97)), rng)
+    st = Step(w, host_history=True)
+    got = _slot_run(st, table, width)
+    ref = _slot_oracle(w, st.k_host, st.v_host, table, width)
+    assert_close(to_host(got, "bf16"), ref, "bf16", "3000-row slot window")
