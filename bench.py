@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--mfma", type=int, default=0,
                     help="1: groups of 8 or 16 query vectors per KV head on the matrix "
                          "cores (library default), 2: always on the vector units")
+    ap.add_argument("--groups-per-cu", type=int, default=0,
+                    help="at most this many decode workgroups per compute unit")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="override the workload's KV heads (grouped-query variant)")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
@@ -248,7 +250,7 @@ def main():
     torch.cuda.set_device(dev)
     binding.set_tuning(args.chunk_min, args.chunk_max, args.decode_waves,
                        args.items_per_group, args.deal, args.staging, args.max_query_group,
-                       args.mfma)
+                       args.mfma, args.groups_per_cu)
     tuning = binding.get_tuning()
     if args.query_len > 1 and args.address != "blocks":
         raise SystemExit("--query-len > 1 reads through block tables only")

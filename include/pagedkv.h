@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 /* Element type of q, out, the new K/V and both pools. */
 typedef enum pkv_dtype {
@@ -265,6 +265,8 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *   mfma                  1: a group of 8 or 16 vectors on a bfloat16 pool of head_dim 64
  *                         or 128 is folded on the matrix cores (default); 2: always on
  *                         the vector units
+ *   groups_per_cu         at most this many decode workgroups per compute unit, 1..16
+ *                         (default 16: as many as fit)
  * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it
  * before sizing workspaces.  Results do not depend on these values beyond float32
  * rounding order.  Returns UNSUPPORTED for other values. */
@@ -277,6 +279,7 @@ typedef struct pkv_tuning {
   int32_t staging;
   int32_t max_query_group;
   int32_t mfma;
+  int32_t groups_per_cu;
 } pkv_tuning;
 
 pkv_status pkv_set_tuning(const pkv_tuning* tuning);

@@ -395,10 +395,10 @@ def device_status(device=None, clear: bool = True) -> int:
 
 def set_tuning(chunk_min: int = 0, chunk_max: int = 0, decode_waves: int = 0,
                items_per_group: int = 0, deal: int = 0, staging: int = 0,
-               max_query_group: int = 0, mfma: int = 0) -> None:
+               max_query_group: int = 0, mfma: int = 0, groups_per_cu: int = 0) -> None:
     """Set the decode work split (0 keeps a value); see pkv_set_tuning."""
     t = _capi.Tuning(chunk_min, chunk_max, decode_waves, items_per_group, deal, staging,
-                     max_query_group, mfma)
+                     max_query_group, mfma, groups_per_cu)
     _check(_capi.lib().pkv_set_tuning(ctypes.byref(t)))
 
 

@@ -202,6 +202,9 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
   a.log2_chunk_min = log2i(pkv::tuning_chunk_min());
   a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
   a.target_items = 0;
+  a.grid_groups = 0;
+  a.narrow_groups = 0;
+  a.narrow_items = 0;
   a.deal_static = 1;
   a.query_group = 1;
   a.query_len = query_len;
@@ -282,6 +285,9 @@ hipError_t launch_attention_slots(const pkv_pool_desc* pool, void* out, const vo
   a.log2_chunk_min = log2i(pkv::tuning_chunk_min());
   a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
   a.target_items = 0;
+  a.grid_groups = 0;
+  a.narrow_groups = 0;
+  a.narrow_items = 0;
   a.deal_static = 1;
   a.query_group = 1;
   a.query_len = 1;
@@ -596,11 +602,11 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
 pkv_status pkv_set_tuning(const pkv_tuning* t) {
   if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
   if (!pkv::set_tuning(t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group,
-                       t->deal, t->staging, t->max_query_group, t->mfma))
+                       t->deal, t->staging, t->max_query_group, t->mfma, t->groups_per_cu))
     return fail(PKV_ERR_UNSUPPORTED, "tuning chunk [%d, %d], waves %d, items/group %d, "
-                "deal %d, staging %d, query group %d, mfma %d not supported", t->chunk_min,
-                t->chunk_max, t->decode_waves, t->items_per_group, t->deal, t->staging,
-                t->max_query_group, t->mfma);
+                "deal %d, staging %d, query group %d, mfma %d, groups/CU %d not supported",
+                t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group, t->deal,
+                t->staging, t->max_query_group, t->mfma, t->groups_per_cu);
   return ok();
 }
 
@@ -614,6 +620,7 @@ pkv_status pkv_get_tuning(pkv_tuning* t) {
   t->staging = pkv::tuning_lds_stage() ? 2 : 1;
   t->max_query_group = pkv::tuning_max_query_group();
   t->mfma = pkv::tuning_mfma() ? 1 : 2;
+  t->groups_per_cu = pkv::tuning_groups_per_cu();
   return ok();
 }
 

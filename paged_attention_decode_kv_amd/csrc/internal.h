@@ -23,6 +23,7 @@ constexpr int kDefaultDealStatic = 1;
 constexpr int kDefaultLdsStage = 1;
 constexpr int kDefaultMaxQueryGroup = 16;
 constexpr int kDefaultMfma = 1;
+constexpr int kDefaultGroupsPerCu = 16;   // i.e. as many as fit
 
 // Slot input: tokens of one row that one workgroup of the translation pass checks.
 constexpr int kTranslateTokens = 1024;
@@ -35,8 +36,9 @@ int tuning_deal_static();
 int tuning_lds_stage();
 int tuning_max_query_group();
 int tuning_mfma();
+int tuning_groups_per_cu();
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal, int staging, int max_query_group, int mfma);
+                int deal, int staging, int max_query_group, int mfma, int groups_per_cu);
 
 // Pool geometry in elements, derived from the descriptor.
 struct PoolGeom {
@@ -66,7 +68,8 @@ struct Workspace {
   int4* entries;        // [max_entries]: {row, chunk (-1: pad row), chunks in row, context_len}
   int32_t* counters;    // [0] entries, [1] queue ticket, [2] chunk length, [3] its log2,
                         // [4] section-A entries, [5] section-A+B entries,
-                        // [6] rows read token by token (slot input)
+                        // [6] rows read token by token (slot input),
+                        // [7] decode workgroups that take part (the rest exit at once)
   int32_t* row_ctx;     // [rows]: each row's length as the block path reads it
   int32_t* irregular;   // [rows]: the rows read token by token, counters[6] of them
   float* partials;      // [rows][heads][max_chunks][head_dim + 4]: m (log2 units), l, -, -, acc
@@ -89,7 +92,10 @@ struct AttnArgs {
                         // slot input min(width, num_blocks * block_size)
   int32_t log2_chunk_min;  // the plan's chunk length range (powers of two)
   int32_t log2_chunk_max;
-  int32_t target_items;    // items the plan aims for (set by the launcher)
+  int32_t target_items;    // items the plan aims for with every workgroup (launcher)
+  int32_t grid_groups;     // decode workgroups launched
+  int32_t narrow_groups;   // one per compute unit, or 0 when the launch already is that
+  int32_t narrow_items;    // items the plan aims for with narrow_groups workgroups
   int32_t deal_static;     // 1: whole rounds of full chunks are dealt without the queue
   int32_t query_group;     // query vectors per work item (they share one KV head)
   int32_t query_len;       // new tokens (queries) per row: 1 for decode

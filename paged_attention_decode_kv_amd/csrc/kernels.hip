@@ -291,11 +291,28 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     if (lane == 0 && k < ncand) atomicAdd(&s_cand[k], v);
   }
   __syncthreads();
+  // Workgroups and chunk length.  A batch that gives one workgroup per compute unit
+  // enough items of more than the shortest chunk is bandwidth-bound: then one workgroup
+  // per CU (fewer concurrent streams) reads it fastest.  Otherwise every workgroup
+  // takes part, with the chunk length that gives them all enough items.
+  const int64_t per_entry = a.query_len * a.num_heads / a.query_group;
   int lp = lmin;
-  for (int k = ncand - 1; k >= 0; --k) {
-    if ((int64_t)s_cand[k] * (a.query_len * a.num_heads / a.query_group) >= a.target_items) {
-      lp = lmin + k;
-      break;
+  bool narrow = false;
+  if (a.narrow_groups > 0) {
+    for (int k = ncand - 1; k > 0; --k) {
+      if ((int64_t)s_cand[k] * per_entry >= a.narrow_items) {
+        lp = lmin + k;
+        narrow = true;
+        break;
+      }
+    }
+  }
+  if (!narrow) {
+    for (int k = ncand - 1; k >= 0; --k) {
+      if ((int64_t)s_cand[k] * per_entry >= a.target_items) {
+        lp = lmin + k;
+        break;
+      }
     }
   }
   const int P = 1 << lp;
@@ -362,6 +379,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     ws.counters[4] = total_a;
     ws.counters[5] = total_a + total_b;
     ws.counters[6] = s_irregular;
+    ws.counters[7] = narrow ? a.narrow_groups : a.grid_groups;
   }
 }
 
@@ -616,7 +634,8 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int n_static = ws.counters[4] * groups;   // section A items
   const int n_data = ws.counters[5] * groups;     // sections A and B
   const int n_items = ws.counters[0] * groups;
-  const int G = gridDim.x;
+  const int G = ws.counters[7];                  // workgroups taking part
+  if ((int)blockIdx.x >= G) return;
   const int n_dealt = a.deal_static ? n_static / G * G : 0;
   const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
@@ -944,7 +963,8 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int n_static = ws.counters[4] * groups;
   const int n_data = ws.counters[5] * groups;
   const int n_items = ws.counters[0] * groups;
-  const int G = gridDim.x;
+  const int G = ws.counters[7];                  // workgroups taking part
+  if ((int)blockIdx.x >= G) return;
   const int n_dealt = a.deal_static ? n_static / G * G : 0;
   const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
@@ -1526,7 +1546,8 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
     per_cu[dev] = n > 0 ? n : 1;
   }
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  int64_t grid = (int64_t)num_cu[dev] * per_cu[dev];
+  const int wpc = per_cu[dev] < tuning_groups_per_cu() ? per_cu[dev] : tuning_groups_per_cu();
+  int64_t grid = (int64_t)num_cu[dev] * wpc;
   const int64_t most = ws.max_entries * (a.query_len * a.num_heads / QG);
   if (grid > most) grid = most;
   AttnArgs pa = a;
@@ -1535,6 +1556,9 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   // keep the workgroups as busy (measured best at the full-width batch's lengths)
   const int per_group = MFMA ? (tuning_items_per_group() + 3) / 4 : tuning_items_per_group();
   pa.target_items = (int32_t)(grid * per_group);
+  pa.grid_groups = (int32_t)grid;
+  pa.narrow_groups = grid > num_cu[dev] ? num_cu[dev] : 0;   // the plan may keep one per CU
+  pa.narrow_items = pa.narrow_groups * per_group;
   pa.deal_static = tuning_deal_static();
   timing_begin(PKV_PHASE_PLAN, stream);
   if (write) {   // the step's scatter rides along with the plan

@@ -103,6 +103,7 @@ std::atomic<int> g_deal_static{kDefaultDealStatic};
 std::atomic<int> g_lds_stage{kDefaultLdsStage};
 std::atomic<int> g_max_query_group{kDefaultMaxQueryGroup};
 std::atomic<int> g_mfma{kDefaultMfma};
+std::atomic<int> g_groups_per_cu{kDefaultGroupsPerCu};
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 }  // namespace
@@ -115,9 +116,10 @@ int tuning_deal_static() { return g_deal_static.load(std::memory_order_relaxed);
 int tuning_lds_stage() { return g_lds_stage.load(std::memory_order_relaxed); }
 int tuning_max_query_group() { return g_max_query_group.load(std::memory_order_relaxed); }
 int tuning_mfma() { return g_mfma.load(std::memory_order_relaxed); }
+int tuning_groups_per_cu() { return g_groups_per_cu.load(std::memory_order_relaxed); }
 
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal, int staging, int max_query_group, int mfma) {
+                int deal, int staging, int max_query_group, int mfma, int groups_per_cu) {
   const int lo = chunk_min ? chunk_min : tuning_chunk_min();
   const int hi = chunk_max ? chunk_max : tuning_chunk_max();
   // validate everything before changing anything
@@ -134,6 +136,7 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
       max_query_group != 4 && max_query_group != 8 && max_query_group != 16)
     return false;
   if (mfma < 0 || mfma > 2) return false;
+  if (groups_per_cu < 0 || groups_per_cu > 16) return false;
   g_chunk_min.store(lo);
   g_chunk_max.store(hi);
   if (decode_waves != 0) g_decode_waves.store(decode_waves);
@@ -142,6 +145,7 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
   if (staging != 0) g_lds_stage.store(staging == 2 ? 1 : 0);
   if (max_query_group != 0) g_max_query_group.store(max_query_group);
   if (mfma != 0) g_mfma.store(mfma == 1 ? 1 : 0);
+  if (groups_per_cu != 0) g_groups_per_cu.store(groups_per_cu);
   return true;
 }
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
     for code, name in enumerate(_capi.STATUS_NAMES):
         assert lib.pkv_status_str(code).decode() == name
 
