@@ -262,9 +262,9 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *                         divides that count and is at most max_query_group (at most 8 on
  *                         the vector units, 4 at head_dim 256); 1 reads K/V once per
  *                         vector
- *   mfma                  1: a group of 8 or 16 vectors on a bfloat16 pool of head_dim 64
- *                         or 128 is folded on the matrix cores (default); 2: always on
- *                         the vector units
+ *   mfma                  1: a group of 4, 8 or 16 vectors on a bfloat16 pool of
+ *                         head_dim 64 or 128 is folded on the matrix cores (default);
+ *                         2: always on the vector units
  *   groups_per_cu         at most this many decode workgroups per compute unit, 1..16
  *                         (default 16: as many as fit)
  * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it

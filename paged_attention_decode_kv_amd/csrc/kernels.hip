@@ -13,8 +13,8 @@
 //                       softmax states on the vector units (Day 59, "the rectangle the
 //                       read builds, and the tile that replaces it", "What I added today"
 //                       and "What I learned" 3-4)
-//   decode_mfma_kernel  the same schedule for groups of 8 or 16 query vectors per KV
-//                       head, whose fold is a pair of small matrix products on the
+//   decode_mfma_kernel  the same schedule for groups of 4, 8 or 16 query vectors per
+//                       KV head, whose fold is a pair of small matrix products on the
 //                       matrix cores
 //   combine_kernel      merges the per-chunk (max, denominator, accumulator) partials of
 //                       rows longer than one chunk, in chunk order
@@ -31,7 +31,7 @@
 // softmax state over the tokens it loaded; the q.k partial dot is reduced inside the
 // group with DPP row operations, and the groups are merged once per item.  With one
 // query vector per KV head the work is a bandwidth-bound streaming read; the matrix
-// cores take over only where 8 or more vectors share each K/V load.
+// cores take over where 4 or more vectors share each K/V load.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -869,7 +869,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 // ------------------------------------------------------------------------- //
 // decode on the matrix cores
 // ------------------------------------------------------------------------- //
-// With 8 or 16 query vectors per KV head (grouped heads x new tokens), the fold of a
+// With 4, 8 or 16 query vectors per KV head (grouped heads x new tokens), the fold of a
 // 16-token sub-chunk is two small dense products per item:
 //   S^T[16 tokens x 16 vectors]  = K[16 x d] . Q^T[d x 16]   (v_mfma_f32_16x16x32_bf16)
 //   O^T[d x 16 vectors]         += V^T[d x 16] . P^T[16 x 16] (v_mfma_f32_16x16x16_bf16)
@@ -938,7 +938,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   constexpr int E = S::E, TPS = S::TPS, U = S::U, CH = S::CH, LPT = S::LPT;
   constexpr int ES = sizeof(T);
   static_assert(CH == 16, "one 16-token tile per sub-chunk");
-  static_assert(QG == 8 || QG == 16, "8 or 16 query vectors per item");
+  static_assert(QG == 4 || QG == 8 || QG == 16, "4, 8 or 16 query vectors per item");
   constexpr int NS = D / 32;      // score products (32 dims each)
   constexpr int NO = D / 16;      // output tiles (16 dims each)
   constexpr int ROW = D * ES;     // bytes of one token's vector in a stage
@@ -1594,13 +1594,14 @@ static int query_group_of(const AttnArgs& a) {
   return 1;
 }
 
-// query vectors per item on the matrix cores: 16 or 8 when that many share a KV head
-// (and the tuning allows it), else 0 (the vector units take the call)
+// query vectors per item on the matrix cores: 16, 8 or 4 when that many share a KV head
+// (and the tuning allows it), else 0 (the vector units take the call; with 1 or 2 they
+// measured as fast or faster)
 static int mfma_group_of(const AttnArgs& a) {
   if (!tuning_mfma() || a.g.dtype != PKV_BF16 || a.g.head_dim > 128) return 0;
   const int vpkv = a.query_len * (a.num_heads / a.g.kv_heads);
   const int cap = tuning_max_query_group();
-  for (int qg = 16; qg >= 8; qg >>= 1)
+  for (int qg = 16; qg >= 4; qg >>= 1)
     if (qg <= cap && vpkv % qg == 0) return qg;
   return 0;
 }
@@ -1612,6 +1613,7 @@ static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws, hipStr
     switch (mfma_group_of(a)) {
       case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream, combine, write);
       case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream, combine, write);
+      case 4: return launch_decode_w<T, D, 8, true, 4, true>(a, ws, stream, combine, write);
       default: break;
     }
   }

@@ -933,10 +933,12 @@ def test_config5_with_four_new_tokens_sampled():
 
 
 # --------------------------------------------------------------------------- #
-# the matrix-core fold (8 or 16 query vectors per KV head, bfloat16, d 64/128)
+# the matrix-core fold (4, 8 or 16 query vectors per KV head, bfloat16, d 64/128)
 # --------------------------------------------------------------------------- #
 MFMA_CASES = [
     # name, lens, query_len, heads, kv_heads, head_dim, layout
+    ("gqa4-d128", [9, 300, 0, 1500, 33], 1, 16, 4, 128, "HND"),
+    ("q4-mha-d64", [4, 77, 2049, 500], 4, 4, 4, 64, "NHD"),
     ("gqa8-d128", [1, 17, 0, 300, 1025, 2050, 64], 1, 32, 4, 128, "HND"),
     ("gqa16-d128-nhd", [5, 700, 129, 0, 2000], 1, 32, 2, 128, "NHD"),
     ("gqa16-d64", [33, 1, 900, 16], 1, 16, 1, 64, "HND"),
@@ -951,7 +953,7 @@ MFMA_CASES = [
 @pytest.mark.parametrize("chunk", [0, 32])
 @pytest.mark.parametrize("case", MFMA_CASES, ids=[c[0] for c in MFMA_CASES])
 def test_matrix_core_groups(case, chunk, mfma):
-    """Groups of 8 or 16 query vectors per KV head on the matrix cores (mfma=1) and on
+    """Groups of 4, 8 or 16 query vectors per KV head on the matrix cores (mfma=1) and on
     the vector units (mfma=2), default and 32-token chunks: every output against the
     oracle."""
     name, lens, n_q, heads, kvh, d, layout = case
