@@ -408,7 +408,8 @@ def main():
         if n:
             log(f"  {ph:9s} {n:5d} launches, avg {ms / n * 1e3:9.2f} us")
     dec_s = avg["decode"] * 1e-3
-    kernel, kern_s, kern_bytes = "decode_kernel", dec_s, dec_bytes
+    kernel, kern_s, kern_bytes = (binding.decode_kernel_for(k_cache, w.heads, w.query_len,
+                                                            w.layout), dec_s, dec_bytes)
     traffic = traffic_per_launch(w.name, w.layout)
     if scattered and avg.get("token_rows"):
         tok_lens = np.zeros_like(w.context_lens)

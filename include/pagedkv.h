@@ -233,6 +233,13 @@ pkv_status pkv_check_attention_slots_host(const pkv_pool_desc* pool,
                                           int64_t row_stride, const int32_t* context_lens,
                                           int64_t num_rows, int32_t num_heads);
 
+/* Which decode kernel a read with this pool, query heads and new tokens per row runs,
+ * under the current tuning, as text ("decode_kernel, 1 query vector per item",
+ * "decode_mfma_kernel, 8 query vectors per item", ...).  A static string; "" for a
+ * shape the library refuses.  For benchmarks and profiles. */
+const char* pkv_decode_kernel_for(const pkv_pool_desc* pool, int32_t num_heads,
+                                  int32_t query_len);
+
 /* Reads (and if `clear` is non-zero, resets) the current device's status word, a
  * bitwise OR of PKV_DEVERR_* raised since the last clear.  Synchronises `stream`. */
 pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);

@@ -49,6 +49,7 @@ SIGNATURES = {
     "pkv_paged_attention": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32, _f, _p,
                                    _sz, _i32, _p]),
     "pkv_device_status": (_i32, [ctypes.POINTER(ctypes.c_uint32), _i32, _p]),
+    "pkv_decode_kernel_for": (ctypes.c_char_p, [_PD, _i32, _i32]),
     "pkv_set_tuning": (_i32, [ctypes.POINTER(Tuning)]),
     "pkv_get_tuning": (_i32, [ctypes.POINTER(Tuning)]),
     "pkv_timing_enable": (_i32, [_i32]),

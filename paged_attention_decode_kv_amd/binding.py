@@ -393,6 +393,13 @@ def device_status(device=None, clear: bool = True) -> int:
     return int(flags.value)
 
 
+def decode_kernel_for(k_cache: torch.Tensor, num_heads: int, query_len: int = 1,
+                      layout: str = "HND") -> str:
+    """Which decode kernel (and query-vector group) a read of this shape runs."""
+    desc = pool_desc(k_cache, layout)
+    return _capi.lib().pkv_decode_kernel_for(ctypes.byref(desc), num_heads, query_len).decode()
+
+
 def set_tuning(chunk_min: int = 0, chunk_max: int = 0, decode_waves: int = 0,
                items_per_group: int = 0, deal: int = 0, staging: int = 0,
                max_query_group: int = 0, mfma: int = 0, groups_per_cu: int = 0) -> None:

@@ -592,6 +592,18 @@ pkv_status pkv_paged_attention_multi(const pkv_pool_desc* pool, void* out, const
   return ok();
 }
 
+const char* pkv_decode_kernel_for(const pkv_pool_desc* pool, int32_t num_heads,
+                                  int32_t query_len) {
+  if (check_pool(pool) != PKV_OK || num_heads < 1 || num_heads % pool->num_kv_heads != 0 ||
+      query_len < 1)
+    return "";
+  pkv::AttnArgs a{};
+  a.g = geom(pool);
+  a.num_heads = num_heads;
+  a.query_len = query_len;
+  return pkv::decode_kernel_name(a);
+}
+
 pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
   if (!flags) return fail(PKV_ERR_NULL, "flags is NULL");
   hipError_t e = pkv::read_device_status(flags, clear, static_cast<hipStream_t>(stream));

@@ -139,6 +139,9 @@ hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStr
 hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& s,
                                         const Workspace& ws, hipStream_t stream);
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream);
+// which decode kernel (and query-vector group) a read of this shape runs, under the
+// current tuning (uses a.g, a.num_heads, a.query_len)
+const char* decode_kernel_name(const AttnArgs& a);
 
 // Event-pair timing of kernel phases (pkv_timing_*).  begin/end bracket one launch.
 void timing_begin(int phase, hipStream_t stream);

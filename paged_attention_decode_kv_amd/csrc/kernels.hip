@@ -1745,6 +1745,28 @@ hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
   return hipGetLastError();
 }
 
+const char* decode_kernel_name(const AttnArgs& a) {
+  static const char* const kMfma[] = {"decode_mfma_kernel, 4 query vectors per item",
+                                      "decode_mfma_kernel, 8 query vectors per item",
+                                      "decode_mfma_kernel, 16 query vectors per item"};
+  static const char* const kVec[] = {"decode_kernel, 1 query vector per item",
+                                     "decode_kernel, 2 query vectors per item",
+                                     "decode_kernel, 4 query vectors per item",
+                                     "decode_kernel, 8 query vectors per item"};
+  switch (mfma_group_of(a)) {
+    case 4: return kMfma[0];
+    case 8: return kMfma[1];
+    case 16: return kMfma[2];
+    default: break;
+  }
+  switch (query_group_of(a)) {
+    case 2: return kVec[1];
+    case 4: return kVec[2];
+    case 8: return kVec[3];
+    default: return kVec[0];
+  }
+}
+
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream) {
   hipError_t err = hipMemcpyFromSymbolAsync(flags, HIP_SYMBOL(g_status), sizeof(uint32_t), 0,
                                             hipMemcpyDeviceToHost, stream);

@@ -299,3 +299,21 @@ def test_row_and_width_limits(lib):
     assert at(4, (1 << 24) // 16 + 1) == "UNSUPPORTED"
     assert lib.pkv_workspace_bytes(ctypes.byref(d), 65535, 4, 4) > 0
     assert lib.pkv_workspace_bytes(ctypes.byref(d), 65536, 4, 4) == 0
+
+
+def test_decode_kernel_choice(lib):
+    """The kernel a shape runs: query vectors per KV head (heads per KV head x new
+    tokens) decide it, bfloat16 pools of head_dim <= 128 go to the matrix cores from 4."""
+    def name(kvh, heads, d=128, dtype="bf16", q=1):
+        desc = binding.host_desc(64, 16, kvh, d, dtype, "HND")
+        return lib.pkv_decode_kernel_for(ctypes.byref(desc), heads, q).decode()
+    assert name(32, 32) == "decode_kernel, 1 query vector per item"
+    assert name(16, 32) == "decode_kernel, 2 query vectors per item"
+    assert name(8, 32) == "decode_mfma_kernel, 4 query vectors per item"
+    assert name(4, 32) == "decode_mfma_kernel, 8 query vectors per item"
+    assert name(2, 32) == "decode_mfma_kernel, 16 query vectors per item"
+    assert name(32, 32, q=4) == "decode_mfma_kernel, 4 query vectors per item"
+    assert name(32, 32, q=3) == "decode_kernel, 1 query vector per item"
+    assert name(8, 32, dtype="f32") == "decode_kernel, 4 query vectors per item"
+    assert name(4, 32, d=256) == "decode_kernel, 4 query vectors per item"
+    assert name(4, 6) == ""
