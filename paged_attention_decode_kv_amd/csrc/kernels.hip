@@ -889,6 +889,10 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
       (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
+// Bank spread of a parked vector: its column index XORed into dim bits 0-1 and 4-5
+// (a permutation of the vector's D dims for D >= 64).
+__device__ __forceinline__ int park_swizzle(int c) { return (c & 3) | ((c >> 2) << 4); }
+
 template <int D>
 struct MfmaMeta {
   int r, hg, chunk, nch, ctx;
@@ -1083,13 +1087,16 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     const Meta nxt = finish_meta_mfma<D, QG>(a, next_ent, next, lp, log2_bs, lane);
     l += __shfl_xor(l, 16);        // the four row groups' denominators
     l += __shfl_xor(l, 32);
-    // park this wave's state in its own stage (its last stage read has completed)
+    // park this wave's state in its own stage (its last stage read has completed):
+    // vector c's dim d at c * D + (d ^ park_swizzle(c)), so that the 64 lanes of one
+    // write (16 vectors x 4 row groups) fall in distinct LDS banks
     float* park = reinterpret_cast<float*>(&s_stage[wave][0][0]);
     if (col < QG) {
+      const int sw = park_swizzle(col);
 #pragma unroll
       for (int o = 0; o < NO; ++o)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) park[col * D + 16 * o + 4 * grp + e] = acc[o][e];
+        for (int e = 0; e < 4; ++e) park[col * D + ((16 * o + 4 * grp + e) ^ sw)] = acc[o][e];
       if (grp == 0) {
         s_m[buf][col][wave] = m;
         s_l[buf][col][wave] = l;
@@ -1107,13 +1114,14 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       float lj = 0.f, y[PER];
 #pragma unroll
       for (int i = 0; i < PER; ++i) y[i] = 0.f;
+      const int sw = park_swizzle(j);
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
         const float f = __builtin_amdgcn_exp2f(s_m[buf][j][w] - mu);
         lj += s_l[buf][j][w] * f;
-        const float* pw = reinterpret_cast<const float*>(&s_stage[w][0][0]) + j * D + lane * PER;
+        const float* pw = reinterpret_cast<const float*>(&s_stage[w][0][0]) + j * D;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) y[i] += pw[i] * f;
+        for (int i = 0; i < PER; ++i) y[i] += pw[(lane * PER + i) ^ sw] * f;
       }
       const int v = hg * QG + j;
       if (cur.nch == 1) {
