@@ -893,6 +893,16 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char* p) {
 // (a permutation of the vector's D dims for D >= 64).
 __device__ __forceinline__ int park_swizzle(int c) { return (c & 3) | ((c >> 2) << 4); }
 
+// XOR mask on the 16-byte piece index of token g of stage chunk u (bfloat16 head
+// vectors: 16 pieces, 4 tokens a chunk, 4 chunks at head_dim 128; 8 pieces, 8 tokens,
+// 2 chunks at 64).  At 128 the mask takes every value 0..15 once over the 16 tokens and
+// differs in bits 1..2 between the tokens of a chunk and in bit 3 between chunks 2k and
+// 2k + 1; at 64 it takes every value 0..7 once over (u, g / 2).
+template <int D>
+__device__ __forceinline__ constexpr int piece_mask(int u, int g) {
+  return D == 128 ? 2 * g + 8 * (u & 1) + (u >> 1) : 2 * (g >> 1) + u;
+}
+
 template <int D>
 struct MfmaMeta {
   int r, hg, chunk, nch, ctx;
@@ -939,23 +949,29 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using T = uint16_t;
   using S = Shape<T, D>;
   using Meta = MfmaMeta<D>;
-  constexpr int E = S::E, TPS = S::TPS, U = S::U, CH = S::CH, LPT = S::LPT;
+  constexpr int TPS = S::TPS, U = S::U, CH = S::CH, LPT = S::LPT;
   constexpr int ES = sizeof(T);
   static_assert(CH == 16, "one 16-token tile per sub-chunk");
   static_assert(QG == 4 || QG == 8 || QG == 16, "4, 8 or 16 query vectors per item");
+  static_assert(D == 64 || D == 128, "piece_mask covers head_dim 64 and 128");
   constexpr int NS = D / 32;      // score products (32 dims each)
   constexpr int NO = D / 16;      // output tiles (16 dims each)
-  constexpr int ROW = D * ES;     // bytes of one token's vector in a stage
   constexpr int PER = D / 64;     // dims per lane in the merge
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane / LPT;       // DMA: token of a wave load
-  const int sub = lane % LPT;     // DMA: 16-byte piece
   const int col = lane & 15;      // matrix cores: vector (and K row) of this lane
   const int grp = lane >> 4;      // matrix cores: row group of this lane
 
-  __shared__ __attribute__((aligned(16))) uint4 s_stage[WAVES][2 * U][64];
-  static_assert(QG * D * 4 <= 2 * U * 64 * 16, "a wave's merge state fits its stage");
+  // Stage layout.  A sub-chunk's K (then V) arrives as U chunks of 1 KB, one per
+  // buffer-to-LDS load of TPS tokens x LPT 16-byte pieces, lane i landing at byte 16 i.
+  // Lane g * LPT + j fetches piece j ^ piece_mask<D>(u, g) of token g: every quad of
+  // lanes still reads one aligned 64-byte run of the pool, and the masks spread the
+  // 16 tokens of one K read pass, and the 4 tokens x 32 bytes of one transposing V read
+  // (or two of them), over distinct LDS banks.  With plain token rows the 16 tokens of a
+  // 256-byte head vector all sit in the same 4 banks.
+  constexpr int STAGE = 2 * U * 1024;      // K chunks, then V chunks
+  __shared__ __attribute__((aligned(16))) char s_stage[WAVES][STAGE];
+  static_assert(QG * D * 4 <= STAGE, "a wave's merge state fits its stage");
   __shared__ int s_ticket[2];
   __shared__ float s_m[2][QG][WAVES], s_l[2][QG][WAVES];
 
@@ -977,15 +993,26 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int64_t head_bytes = a.g.head_stride * ES;
   uint32_t voff[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    voff[u] = (uint32_t)((u * TPS + g) * tok_bytes + sub * E * ES);
+  for (int u = 0; u < U; ++u) {
+    const int g = lane / LPT;
+    voff[u] = (uint32_t)((u * TPS + g) * tok_bytes + ((lane % LPT) ^ piece_mask<D>(u, g)) * 16);
+  }
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
-  const char* st_k = reinterpret_cast<const char*>(&s_stage[wave][0][0]);
-  const char* st_v = reinterpret_cast<const char*>(&s_stage[wave][U][0]);
-  // this lane's K row (token col, 8 dims at 8 grp) and V^T row addresses in a stage
-  const char* k_row = st_k + col * ROW + 8 * grp * ES;
-  const char* v_row = st_v + (4 * grp + (col >> 2)) * ROW + 4 * (col & 3) * ES;
+  const char* st_k = &s_stage[wave][0];
+  const char* st_v = &s_stage[wave][U * 1024];
+  // byte offset in a stage half of token t's dims d .. d + 3 (d a multiple of 4)
+  auto at = [](int t, int d) {
+    const int u = t / TPS, g = t % TPS;
+    return u * 1024 + (g * LPT + ((d / 8) ^ piece_mask<D>(u, g))) * 16 + ((d / 4) & 1) * 8;
+  };
+  // this lane's K operands (token col, dims 32 ds + 8 grp ..) and V^T operands (token
+  // 4 grp + col / 4, dims 16 o + 4 (col % 4) ..)
+  int k_off[NS], v_off[NO];
+#pragma unroll
+  for (int ds = 0; ds < NS; ++ds) k_off[ds] = at(col, 32 * ds + 8 * grp);
+#pragma unroll
+  for (int o = 0; o < NO; ++o) v_off[o] = at(4 * grp + (col >> 2), 16 * o + 4 * (col & 3));
 
   ItemOrder order{(int)blockIdx.x, G, n_dealt};
   int item, next;
@@ -1024,8 +1051,9 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       ca.describe<CH>(s, ksrc, vsrc, bad_block);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        buffer_load16_lds(ksrc, voff[u], &s_stage[wave][u][0]);
-        buffer_load16_lds(vsrc, voff[u], &s_stage[wave][U + u][0]);
+        buffer_load16_lds(ksrc, voff[u], reinterpret_cast<uint4*>(&s_stage[wave][u * 1024]));
+        buffer_load16_lds(vsrc, voff[u],
+                          reinterpret_cast<uint4*>(&s_stage[wave][(U + u) * 1024]));
       }
     };
     if (wave < n_sub) stage_in(wave);
@@ -1036,13 +1064,13 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ds = 0; ds < NS; ++ds) {
-        const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(k_row + 32 * ds * ES);
+        const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(st_k + k_off[ds]);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, __builtin_bit_cast(bf16x8_t, cur.q[ds]),
                                                      sc, 0, 0, 0);
       }
       i16x4_t vt[NO];
 #pragma unroll
-      for (int o = 0; o < NO; ++o) vt[o] = lds_read_tr16(v_row + 16 * o * ES);
+      for (int o = 0; o < NO; ++o) vt[o] = lds_read_tr16(st_v + v_off[o]);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // stage read before it is refilled
       if (s + WAVES < n_sub) stage_in(s + WAVES);
 
@@ -1090,7 +1118,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     // park this wave's state in its own stage (its last stage read has completed):
     // vector c's dim d at c * D + (d ^ park_swizzle(c)), so that the 64 lanes of one
     // write (16 vectors x 4 row groups) fall in distinct LDS banks
-    float* park = reinterpret_cast<float*>(&s_stage[wave][0][0]);
+    float* park = reinterpret_cast<float*>(&s_stage[wave][0]);
     if (col < QG) {
       const int sw = park_swizzle(col);
 #pragma unroll
@@ -1119,7 +1147,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       for (int w = 0; w < WAVES; ++w) {
         const float f = __builtin_amdgcn_exp2f(s_m[buf][j][w] - mu);
         lj += s_l[buf][j][w] * f;
-        const float* pw = reinterpret_cast<const float*>(&s_stage[w][0][0]) + j * D;
+        const float* pw = reinterpret_cast<const float*>(&s_stage[w][0]) + j * D;
 #pragma unroll
         for (int i = 0; i < PER; ++i) y[i] += pw[(lane * PER + i) ^ sw] * f;
       }
