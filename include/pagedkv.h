@@ -250,8 +250,8 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  * afterwards in chunk order.  The chunk length is chosen on the device per call: the
  * largest power of two in [chunk_min, chunk_max] that still yields items_per_group
  * items per decode workgroup (else chunk_min).  Setting chunk_min == chunk_max pins it.
- *   chunk_min, chunk_max  powers of two in [32, 2048], chunk_max/chunk_min <= 32
- *                         (defaults 128, 2048)
+ *   chunk_min, chunk_max  powers of two in [32, 8192], chunk_max/chunk_min <= 64
+ *                         (defaults 128, 8192)
  *   decode_waves          64-lane waves per workgroup: 1, 2, 4 or 8 (default 8)
  *   items_per_group       default 16 (the matrix-core fold, whose items carry 8 or 16
  *                         query vectors, aims for a quarter of it)

@@ -14,9 +14,10 @@ namespace pkv {
 // is split into cdiv(context_len, chunk) chunks; rows with more than one chunk are
 // merged by the combine kernel.  pkv_set_tuning can pin the chunk length.
 constexpr int kMinChunkTokens = 32;
-constexpr int kMaxChunkTokens = 2048;
+constexpr int kMaxChunkTokens = 8192;
 constexpr int kDefaultChunkMin = 128;
-constexpr int kDefaultChunkMax = 2048;
+constexpr int kDefaultChunkMax = 8192;
+constexpr int kMaxChunkRatio = 64;   // chunk_max / chunk_min: the plan's 7 candidates
 constexpr int kDefaultDecodeWaves = 8;
 constexpr int kDefaultItemsPerGroup = 16;
 constexpr int kDefaultDealStatic = 1;

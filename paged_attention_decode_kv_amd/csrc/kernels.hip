@@ -135,6 +135,17 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Integer sum over the wave, the same steps as group_sum<64>; every lane ends with it.
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);   // row_mirror
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -184,6 +195,12 @@ __global__ void __launch_bounds__(256) kv_write_kernel(WriteArgs a, int64_t sink
 // plan: context_lens -> work list
 // ------------------------------------------------------------------------- //
 constexpr int kPlanThreads = 1024;
+// Block-id registers of a work item (64 ids to a register).  A chunk spans at most
+// kMaxChunkTokens / 16 blocks (block sizes are at least 16): kMaxBlkRegs registers.
+// The kernels are built for NBR = 2 (chunks of up to 128 blocks) and NBR = kMaxBlkRegs;
+// the launcher takes 2 whenever no chunk of the call can be wider (the narrow variant
+// carries fewer registers and id loads per item).
+constexpr int kMaxBlkRegs = kMaxChunkTokens / 16 / 64;
 
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
   const int lane = threadIdx.x & 63;
@@ -242,21 +259,30 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 //
 // The chunk length P is the largest power of two in [chunk_min, chunk_max] whose
 // (chunk, head) item count reaches target_items (enough items per decode workgroup
-// for the queue to balance), else chunk_min.  Entries are ordered longest first so
-// that the queue's tail is short work:
+// for the queue to balance) and whose chunk holds at most a third of a workgroup's
+// share of the batch's tokens, else chunk_min.  Longer chunks split fewer rows (fewer
+// partial records to write and merge); the share bound keeps the longest item short
+// enough for the longest-first order to balance.  Entries are ordered longest first
+// so that the queue's tail is short work:
 //   A. every full chunk (P tokens) of every row, rows in order;
-//   B. every row's trailing partial chunk, by length, longest first;
+//   B. every row's trailing partial chunk, by length, longest first (in buckets of
+//      P / 1024 tokens when P > 1024);
 //   C. one zero-output entry per padding row.
 // counters[0] = entries, [1] = queue ticket (reset to 0), [2] = P, [3] = log2 P,
 // [4] = entries in section A, [5] = entries in sections A and B, [6] = rows of a slot
 // input left to the token-by-token kernel (listed in ws.irregular).  Every row's
 // clamped length goes to ws.row_ctx for the combine kernel.
 __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
-  constexpr int kMaxChunk = kMaxChunkTokens;
-  constexpr int kCand = 6;                 // chunk_max / chunk_min <= 32
+  constexpr int kCand = 7;                 // chunk_max / chunk_min <= kMaxChunkRatio
+  static_assert((1 << (kCand - 1)) == kMaxChunkRatio, "one candidate per power of two");
+  // Section B is ordered by remainder length in kBins bins (exactly when P <= kBins,
+  // else in buckets of P / kBins tokens)
+  constexpr int kBins = kPlanThreads;
+  // the longest item may take at most 1 / kBalance of a workgroup's share of the work
+  constexpr int kBalance = 3;
   __shared__ int s_wave[kPlanThreads / 64];
-  __shared__ int s_bin_start[kMaxChunk];   // first B position of each remainder length
-  __shared__ int s_bin_fill[kMaxChunk];
+  __shared__ int s_bin_start[kBins];       // first B position of each remainder bin
+  __shared__ int s_bin_fill[kBins];
   __shared__ int s_pad_fill;
   __shared__ int s_irregular;
   __shared__ int s_cand[kCand];
@@ -272,11 +298,21 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   // pass 0: chunk count of every candidate length; row lengths; irregular rows
   const int lmin = a.log2_chunk_min;
   const int ncand = a.log2_chunk_max - lmin + 1;
-  int cnt[kCand] = {0, 0, 0, 0, 0, 0};
+  int cnt[kCand];
+#pragma unroll
+  for (int k = 0; k < kCand; ++k) cnt[k] = 0;
+  // the lengths of this thread's first kKeep rows stay in registers for passes 1 and 2
+  constexpr int kKeep = 4;
+  int kept[kKeep];
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) kept[k] = 0;
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
     bool irr;
     int full_ctx;
     const int ctx = plan_ctx(a, r, true, &irr, &full_ctx);
+#pragma unroll
+    for (int k = 0; k < kKeep; ++k)
+      if (r == t + (int64_t)k * kPlanThreads) kept[k] = ctx;
     // (a row read token by token keeps its length here: its chunks are combined too)
     ws.row_ctx[r] = full_ctx;
     if (irr) ws.irregular[atomicAdd(&s_irregular, 1)] = (int)r;
@@ -285,9 +321,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   }
 #pragma unroll
   for (int k = 0; k < kCand; ++k) {
-    int v = cnt[k];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    const int v = wave_sum_i(cnt[k]);
     if (lane == 0 && k < ncand) atomicAdd(&s_cand[k], v);
   }
   __syncthreads();
@@ -296,10 +330,21 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   // per CU (fewer concurrent streams) reads it fastest.  Otherwise every workgroup
   // takes part, with the chunk length that gives them all enough items.
   const int64_t per_entry = a.query_len * a.num_heads / a.query_group;
+  // Balance: with G workgroups, the largest candidate whose chunks hold at most
+  // 1 / kBalance of a workgroup's share (tokens x items per entry / G); the work list
+  // runs longest first, so the last items to start are short ones.  The batch's tokens
+  // are taken as its chunk_min chunks x chunk_min (over by less than a chunk a row).
+  const int64_t work = ((int64_t)s_cand[0] << lmin) * per_entry;
+  auto balance_cap = [&](int64_t groups) {
+    int kc = 0;
+    for (int k = 1; k < ncand; ++k)
+      if ((int64_t{1} << (lmin + k)) * kBalance * groups <= work) kc = k;
+    return kc;
+  };
   int lp = lmin;
   bool narrow = false;
   if (a.narrow_groups > 0) {
-    for (int k = ncand - 1; k > 0; --k) {
+    for (int k = min(ncand - 1, balance_cap(a.narrow_groups)); k > 0; --k) {
       if ((int64_t)s_cand[k] * per_entry >= a.narrow_items) {
         lp = lmin + k;
         narrow = true;
@@ -308,7 +353,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     }
   }
   if (!narrow) {
-    for (int k = ncand - 1; k >= 0; --k) {
+    for (int k = min(ncand - 1, balance_cap(a.grid_groups)); k >= 0; --k) {
       if ((int64_t)s_cand[k] * per_entry >= a.target_items) {
         lp = lmin + k;
         break;
@@ -316,55 +361,58 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     }
   }
   const int P = 1 << lp;
-  for (int q = t; q < P; q += kPlanThreads) s_bin_fill[q] = 0;
+  const int bshift = lp > 10 ? lp - 10 : 0;   // remainder -> bin (kBins = 1024)
+  const int nbins = P >> bshift;
+  static_assert(kBins == 1024, "bin shift assumes 1024 bins");
+  if (t < nbins) s_bin_fill[t] = 0;
   __syncthreads();
+
+  // a row's length as pass 0 found it
+  auto row_len = [&](int64_t r) {
+    const int64_t k = (r - t) / kPlanThreads;
+    int v = 0;
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i)
+      if (k == i) v = kept[i];
+    return k < kKeep ? v : plan_ctx(a, r, false, nullptr);
+  };
 
   // pass 1: section A, remainder histogram, pad count
   int total_a = 0, n_pad = 0;
   for (int64_t base = 0; base < a.num_rows; base += kPlanThreads) {
     const int64_t r = base + t;
-    const int ctx = r < a.num_rows ? plan_ctx(a, r, false, nullptr) : 0;
+    const int ctx = r < a.num_rows ? row_len(r) : 0;
     const int full = ctx >> lp;
     const int nch = (ctx + P - 1) >> lp;
     int tile_a, tile_pad;
     const int at = total_a + block_exclusive_scan(full, s_wave, &tile_a);
     block_exclusive_scan(r < a.num_rows && ctx == 0 ? 1 : 0, s_wave, &tile_pad);
     for (int k = 0; k < full; ++k) ws.entries[at + k] = make_int4((int)r, k, nch, ctx);
-    if (r < a.num_rows && (ctx & (P - 1)) != 0) atomicAdd(&s_bin_fill[ctx & (P - 1)], 1);
+    if (r < a.num_rows && (ctx & (P - 1)) != 0)
+      atomicAdd(&s_bin_fill[(ctx & (P - 1)) >> bshift], 1);
     total_a += tile_a;
     n_pad += tile_pad;
   }
   __syncthreads();
-  // bins of section B in descending remainder order; thread t owns PER consecutive bins
+  // bins of section B in descending remainder order: thread t owns the t-th from the top
   int total_b = 0;
   {
-    constexpr int PER = kMaxChunk / kPlanThreads;
-    int local[PER];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = t * PER + i;               // q-th bin in descending order
-      local[i] = q < P ? s_bin_fill[P - 1 - q] : 0;
-      sum += local[i];
-    }
-    int start = block_exclusive_scan(sum, s_wave, &total_b);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = t * PER + i;
-      if (q < P) s_bin_start[P - 1 - q] = start;
-      start += local[i];
-    }
+    const int bin = nbins - 1 - t;
+    const int count = t < nbins ? s_bin_fill[bin] : 0;
+    const int start = block_exclusive_scan(count, s_wave, &total_b);
+    if (t < nbins) s_bin_start[bin] = start;
   }
   __syncthreads();
-  for (int q = t; q < P; q += kPlanThreads) s_bin_fill[q] = 0;
+  if (t < nbins) s_bin_fill[t] = 0;
   __syncthreads();
   // pass 2: place sections B and C
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
-    const int ctx = plan_ctx(a, r, false, nullptr);
+    const int ctx = row_len(r);
     const int rem = ctx & (P - 1);
     const int nch = (ctx + P - 1) >> lp;
     if (rem != 0) {
-      const int pos = total_a + s_bin_start[rem] + atomicAdd(&s_bin_fill[rem], 1);
+      const int pos = total_a + s_bin_start[rem >> bshift] +
+                      atomicAdd(&s_bin_fill[rem >> bshift], 1);
       ws.entries[pos] = make_int4((int)r, ctx >> lp, nch, ctx);
     } else if (ctx == 0) {
       const int pos = total_a + total_b + atomicAdd(&s_pad_fill, 1);
@@ -425,7 +473,7 @@ struct Shape {
   static constexpr int CH = TPS * U;                // tokens per sub-chunk (<= 16)
   static_assert(LPT >= 8 && LPT <= 64, "unsupported head_dim/dtype");
   static_assert(kMinChunkTokens % CH == 0 && 16 % CH == 0, "sub-chunks tile chunks and blocks");
-  static_assert(kMaxChunkTokens / 16 <= 128, "block ids of a chunk: two per lane");
+  static_assert(kMaxChunkTokens / 16 <= 64 * kMaxBlkRegs, "block ids of a chunk: 8 a lane");
 };
 
 // Query vectors.  A row has query_len x heads of them, one per (new token i, query
@@ -444,27 +492,30 @@ __device__ __forceinline__ int vec_query(const AttnArgs& a, int v) {
 
 // Everything a work item needs before its first K/V load.  An item is (row, chunk of
 // the row's history, group of QG query vectors that share one KV head).
-template <int QG>
+template <int QG, int NBR>
 struct ItemMeta {
   int r, hg, chunk, nch, ctx;   // hg: vector group; vectors hg*QG .. hg*QG + QG - 1
   uint4 q[QG];   // this lane's 16 bytes of each vector's query
   int last[QG];  // each vector's last visible position (len - query_len + i)
-  int blk;       // lane i: block id of the chunk's i-th block
-  int blk_hi;    // lane i: block id of the chunk's (64 + i)-th block
+  int blk[NBR];   // lane i: block ids i, 64 + i, 128 + i, ... of the chunk
 };
 
-// The block ids of an item's chunk, two per lane: lane i holds the chunk's i-th and
-// (64 + i)-th (a chunk spans at most kMaxChunkTokens / 16 = 128 blocks).
+// The block ids of an item's chunk, NBR per lane: lane i holds the chunk's
+// blocks i, 64 + i, ... (a chunk spans at most kMaxChunkTokens / 16 = 512 blocks).
+// Loads of ids past the chunk's last block are not issued.
+template <int NBR>
 __device__ __forceinline__ void load_chunk_blocks(const AttnArgs& a, int r, int chunk, int ctx,
-                                                  int lp, int log2_bs, int lane, int& blk,
-                                                  int& blk_hi) {
+                                                  int lp, int log2_bs, int lane,
+                                                  int (&blk)[NBR]) {
   const int t_begin = chunk << lp;
   const int t_end = min(ctx, t_begin + (1 << lp));
   const int j0 = t_begin >> log2_bs;
   const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
   const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks + j0;
-  if (lane < nblk) blk = bt[lane];
-  if (lane + 64 < nblk) blk_hi = bt[lane + 64];
+  const int nk = (nblk + 63) >> 6;   // id registers in use (uniform)
+#pragma unroll
+  for (int k = 0; k < NBR; ++k)
+    if (k < nk && lane + 64 * k < nblk) blk[k] = bt[lane + 64 * k];
 }
 
 // First half of fetching an item's metadata: the work-list entry load is issued and
@@ -475,12 +526,12 @@ __device__ __forceinline__ int4 issue_entry(const Workspace& ws, int item, int g
 
 // Second half: the entry becomes wave-uniform and the query and block-id loads are
 // issued (they complete while the current item finishes).
-template <typename T, int D, int QG>
-__device__ __forceinline__ ItemMeta<QG> finish_meta(const AttnArgs& a, int4 ent, int item,
+template <typename T, int D, int QG, int NBR>
+__device__ __forceinline__ ItemMeta<QG, NBR> finish_meta(const AttnArgs& a, int4 ent, int item,
                                                     int lp, int log2_bs, int lane, int sub) {
   constexpr int E = Elem<T>::kPerLane;
   const int groups = a.query_len * a.num_heads / QG;
-  ItemMeta<QG> m;
+  ItemMeta<QG, NBR> m;
   const int e = item / groups;
   m.hg = item - e * groups;
   m.r = __builtin_amdgcn_readfirstlane(ent.x);
@@ -492,14 +543,14 @@ __device__ __forceinline__ ItemMeta<QG> finish_meta(const AttnArgs& a, int4 ent,
     m.q[j] = make_uint4(0, 0, 0, 0);
     m.last[j] = m.ctx - a.query_len + vec_query(a, m.hg * QG + j);
   }
-  m.blk = 0;
-  m.blk_hi = 0;
+#pragma unroll
+  for (int k = 0; k < NBR; ++k) m.blk[k] = 0;
   if (m.chunk >= 0) {
 #pragma unroll
     for (int j = 0; j < QG; ++j)
       m.q[j] = load16(static_cast<const T*>(a.q) + vec_slot(a, m.r, m.hg * QG + j) * D +
                       sub * E);
-    load_chunk_blocks(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, m.blk, m.blk_hi);
+    load_chunk_blocks(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, m.blk);
   }
   return m;
 }
@@ -536,15 +587,27 @@ struct ChunkAddr {
   int64_t head_off, blk_bytes, tok_bytes;
   int t_begin, t_end, j0, log2_bs, bs_mask;
   int64_t num_blocks;
-  int blk, blk_hi;   // lane i: block ids i and 64 + i of the chunk
 
-  template <int CH>
+  // blk: the item's block ids, lane i holding ids i, 64 + i, ... of the chunk
+  template <int CH, int NBR>
   __device__ __forceinline__ int describe(int s, __amdgpu_buffer_rsrc_t& ksrc,
-                                          __amdgpu_buffer_rsrc_t& vsrc, bool& bad) const {
+                                          __amdgpu_buffer_rsrc_t& vsrc, bool& bad,
+                                          const int (&blk)[NBR]) const {
     const int t0 = t_begin + s * CH;
     const int jb = (t0 >> log2_bs) - j0;   // block of this sub-chunk within the chunk
-    const int raw = jb < 64 ? __builtin_amdgcn_readlane(blk, jb)
-                            : __builtin_amdgcn_readlane(blk_hi, jb - 64);
+    // (jb is wave-uniform: a register is read at lane jb % 64 and the scalar results are
+    // selected, so the id registers are never indexed; most chunks need only the first)
+    int raw;
+    if (jb < 64) {
+      raw = __builtin_amdgcn_readlane(blk[0], jb);
+    } else {
+      raw = __builtin_amdgcn_readlane(blk[1], jb & 63);
+#pragma unroll
+      for (int k = 2; k < NBR; ++k) {
+        const int rk = __builtin_amdgcn_readlane(blk[k], jb & 63);
+        raw = (jb >> 6) == k ? rk : raw;
+      }
+    }
     const bool blk_ok = raw >= 0 && raw < num_blocks;
     bad |= !blk_ok;
     const int id = blk_ok ? raw : 0;
@@ -603,12 +666,12 @@ struct ItemOrder {
 // counter, so the uneven tail is balanced dynamically with few atomics; padding rows
 // (section C) are zeroed round robin at the end.  The next item's metadata and the
 // ticket after it are fetched while the current item streams.
-template <typename T, int D, int WAVES, bool LDS_STAGE, int QG>
+template <typename T, int D, int WAVES, bool LDS_STAGE, int QG, int NBR>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using S = Shape<T, D>;
   using El = Elem<T>;
-  using Meta = ItemMeta<QG>;
+  using Meta = ItemMeta<QG, NBR>;
   constexpr int E = S::E, LPT = S::LPT, TPS = S::TPS, U = S::U, CH = S::CH;
   constexpr int ES = sizeof(T);
   const int lane = threadIdx.x & 63;
@@ -657,7 +720,8 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   bool bad_block = false;   // a live block id outside [0, num_blocks) was skipped
   Meta cur;
   if (item < n_data)
-    cur = finish_meta<T, D, QG>(a, issue_entry(ws, item, groups), item, lp, log2_bs, lane, sub);
+    cur = finish_meta<T, D, QG, NBR>(a, issue_entry(ws, item, groups), item, lp, log2_bs, lane,
+                                     sub);
 
   while (item < n_data) {
     // the item after next: static, or a ticket whose value is needed only at the end
@@ -692,9 +756,9 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
     const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end, j0,
-                       log2_bs, bs_mask, a.g.num_blocks, cur.blk, cur.blk_hi};
+                 log2_bs, bs_mask, a.g.num_blocks};
     auto describe = [&](int s, __amdgpu_buffer_rsrc_t& ksrc, __amdgpu_buffer_rsrc_t& vsrc) {
-      return ca.describe<CH>(s, ksrc, vsrc, bad_block);
+      return ca.describe<CH>(s, ksrc, vsrc, bad_block, cur.blk);
     };
     auto stage_in = [&](int s) {   // sub-chunk s -> this wave's LDS stage
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
@@ -761,7 +825,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     }
 
     // the next item's query and block ids load while this item's state is merged
-    const Meta nxt = finish_meta<T, D, QG>(a, next_ent, next, lp, log2_bs, lane, sub);
+    const Meta nxt = finish_meta<T, D, QG, NBR>(a, next_ent, next, lp, log2_bs, lane, sub);
 
     // merge the lane groups of this wave, head by head
 #pragma unroll
@@ -903,20 +967,20 @@ __device__ __forceinline__ constexpr int piece_mask(int u, int g) {
   return D == 128 ? 2 * g + 8 * (u & 1) + (u >> 1) : 2 * (g >> 1) + u;
 }
 
-template <int D>
+template <int D, int NBR>
 struct MfmaMeta {
   int r, hg, chunk, nch, ctx;
   int last;           // lane: last visible position of vector hg*QG + l%16 (-1: none)
   uint4 q[D / 32];    // lane: 8 dims (32 s + 8 (l/16) ..) of that vector's query
-  int blk, blk_hi;
+  int blk[NBR];
 };
 
-template <int D, int QG>
-__device__ __forceinline__ MfmaMeta<D> finish_meta_mfma(const AttnArgs& a, int4 ent, int item,
+template <int D, int QG, int NBR>
+__device__ __forceinline__ MfmaMeta<D, NBR> finish_meta_mfma(const AttnArgs& a, int4 ent, int item,
                                                         int lp, int log2_bs, int lane) {
   const int groups = a.query_len * a.num_heads / QG;
   const int col = lane & 15, grp = lane >> 4;
-  MfmaMeta<D> m;
+  MfmaMeta<D, NBR> m;
   const int e = item / groups;
   m.hg = item - e * groups;
   m.r = __builtin_amdgcn_readfirstlane(ent.x);
@@ -927,15 +991,15 @@ __device__ __forceinline__ MfmaMeta<D> finish_meta_mfma(const AttnArgs& a, int4 
   m.last = col < QG ? m.ctx - a.query_len + vec_query(a, v) : -1;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) m.q[s] = make_uint4(0, 0, 0, 0);
-  m.blk = 0;
-  m.blk_hi = 0;
+#pragma unroll
+  for (int k = 0; k < NBR; ++k) m.blk[k] = 0;
   if (m.chunk >= 0) {
     if (col < QG) {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + vec_slot(a, m.r, v) * D + 8 * grp;
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) m.q[s] = load16(qp + 32 * s);
     }
-    load_chunk_blocks(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, m.blk, m.blk_hi);
+    load_chunk_blocks(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, m.blk);
   }
   return m;
 }
@@ -943,12 +1007,12 @@ __device__ __forceinline__ MfmaMeta<D> finish_meta_mfma(const AttnArgs& a, int4 
 // Same schedule, staging and partial records as decode_kernel (bfloat16 pools, head_dim
 // 64 or 128, sub-chunks of 16 tokens).  After its last fold a wave parks its state,
 // [QG][D] floats, in its own stage, and the waves are merged from there.
-template <int D, int WAVES, int QG>
+template <int D, int WAVES, int QG, int NBR>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using T = uint16_t;
   using S = Shape<T, D>;
-  using Meta = MfmaMeta<D>;
+  using Meta = MfmaMeta<D, NBR>;
   constexpr int TPS = S::TPS, U = S::U, CH = S::CH, LPT = S::LPT;
   constexpr int ES = sizeof(T);
   static_assert(CH == 16, "one 16-token tile per sub-chunk");
@@ -1021,7 +1085,8 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   bool bad_block = false;
   Meta cur;
   if (item < n_data)
-    cur = finish_meta_mfma<D, QG>(a, issue_entry(ws, item, groups), item, lp, log2_bs, lane);
+    cur = finish_meta_mfma<D, QG, NBR>(a, issue_entry(ws, item, groups), item, lp, log2_bs,
+                                       lane);
 
   while (item < n_data) {
     int after = 0;
@@ -1045,10 +1110,10 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
     const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end, j0,
-                       log2_bs, bs_mask, a.g.num_blocks, cur.blk, cur.blk_hi};
+                 log2_bs, bs_mask, a.g.num_blocks};
     auto stage_in = [&](int s) {
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
-      ca.describe<CH>(s, ksrc, vsrc, bad_block);
+      ca.describe<CH>(s, ksrc, vsrc, bad_block, cur.blk);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         buffer_load16_lds(ksrc, voff[u], reinterpret_cast<uint4*>(&s_stage[wave][u * 1024]));
@@ -1059,7 +1124,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     if (wave < n_sub) stage_in(wave);
     for (int s = wave; s < n_sub; s += WAVES) {
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
-      const int nvalid = ca.describe<CH>(s, ksrc, vsrc, bad_block);
+      const int nvalid = ca.describe<CH>(s, ksrc, vsrc, bad_block, cur.blk);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this wave's stage has landed
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1112,7 +1177,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       m = m_new;
     }
 
-    const Meta nxt = finish_meta_mfma<D, QG>(a, next_ent, next, lp, log2_bs, lane);
+    const Meta nxt = finish_meta_mfma<D, QG, NBR>(a, next_ent, next, lp, log2_bs, lane);
     l += __shfl_xor(l, 16);        // the four row groups' denominators
     l += __shfl_xor(l, 32);
     // park this wave's state in its own stage (its last stage read has completed):
@@ -1559,12 +1624,12 @@ static void launch_combine_t(const AttnArgs& a, const Workspace& ws, hipStream_t
   timing_end(PKV_PHASE_COMBINE, stream);
 }
 
-template <typename T, int D, int WAVES, bool LDS_STAGE, int QG, bool MFMA = false>
+template <typename T, int D, int NBR, int WAVES, bool LDS_STAGE, int QG, bool MFMA = false>
 static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
                                   bool combine, const WriteArgs* write) {
   void (*kern)(AttnArgs, Workspace, float);
-  if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG>;
-  else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
+  if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG, NBR>;
+  else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG, NBR>;
   static int per_cu[64] = {0};   // occupancy per device, computed once
   static int num_cu[64] = {0};
   int dev = 0;
@@ -1642,57 +1707,73 @@ static int mfma_group_of(const AttnArgs& a) {
   return 0;
 }
 
-template <typename T, int D>
+template <typename T, int D, int NBR>
 static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
                                   bool combine, const WriteArgs* write) {
   if constexpr (sizeof(T) == 2 && D <= 128) {
     switch (mfma_group_of(a)) {
-      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream, combine, write);
-      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream, combine, write);
-      case 4: return launch_decode_w<T, D, 8, true, 4, true>(a, ws, stream, combine, write);
+      case 16: return launch_decode_w<T, D, NBR, 8, true, 16, true>(a, ws, stream, combine, write);
+      case 8: return launch_decode_w<T, D, NBR, 8, true, 8, true>(a, ws, stream, combine, write);
+      case 4: return launch_decode_w<T, D, NBR, 8, true, 4, true>(a, ws, stream, combine, write);
       default: break;
     }
   }
   switch (query_group_of(a)) {
     case 8:
-      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream, combine, write);
+      if constexpr (D < 256) return launch_decode_w<T, D, NBR, 8, true, 8>(a, ws, stream, combine, write);
       break;
-    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, stream, combine, write);
-    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, stream, combine, write);
+    case 4: return launch_decode_w<T, D, NBR, 8, true, 4>(a, ws, stream, combine, write);
+    case 2: return launch_decode_w<T, D, NBR, 8, true, 2>(a, ws, stream, combine, write);
     default: break;
   }
   if (tuning_lds_stage()) {
     switch (tuning_decode_waves()) {
-      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, stream, combine, write);
-      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, stream, combine, write);
-      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, stream, combine, write);
-      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, stream, combine, write);
+      case 1: return launch_decode_w<T, D, NBR, 1, true, 1>(a, ws, stream, combine, write);
+      case 2: return launch_decode_w<T, D, NBR, 2, true, 1>(a, ws, stream, combine, write);
+      case 8: return launch_decode_w<T, D, NBR, 8, true, 1>(a, ws, stream, combine, write);
+      default: return launch_decode_w<T, D, NBR, 4, true, 1>(a, ws, stream, combine, write);
     }
   }
   switch (tuning_decode_waves()) {
-    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, stream, combine, write);
-    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, stream, combine, write);
-    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, stream, combine, write);
-    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, stream, combine, write);
+    case 1: return launch_decode_w<T, D, NBR, 1, false, 1>(a, ws, stream, combine, write);
+    case 2: return launch_decode_w<T, D, NBR, 2, false, 1>(a, ws, stream, combine, write);
+    case 8: return launch_decode_w<T, D, NBR, 8, false, 1>(a, ws, stream, combine, write);
+    default: return launch_decode_w<T, D, NBR, 4, false, 1>(a, ws, stream, combine, write);
+  }
+}
+
+// an item of this call can span more than 128 blocks (its chunks can be longer than
+// 128 blocks and its rows can hold that many)
+static bool wide_block_ids(const AttnArgs& a) {
+  const int64_t chunk_blocks = ((int64_t)1 << a.log2_chunk_max) >> a.g.log2_bs;
+  const int64_t span = chunk_blocks < a.max_blocks ? chunk_blocks : a.max_blocks;
+  return span > 128;
+}
+
+template <int NBR>
+static hipError_t launch_paged_attention_n(const AttnArgs& a, const Workspace& ws,
+                                           hipStream_t stream, bool combine,
+                                           const WriteArgs* write) {
+  const bool f32 = a.g.dtype == PKV_F32;
+  switch (a.g.head_dim) {
+    case 64:
+      return f32 ? launch_decode_t<float, 64, NBR>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 64, NBR>(a, ws, stream, combine, write);
+    case 128:
+      return f32 ? launch_decode_t<float, 128, NBR>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 128, NBR>(a, ws, stream, combine, write);
+    case 256:
+      return f32 ? launch_decode_t<float, 256, NBR>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 256, NBR>(a, ws, stream, combine, write);
+    default:
+      return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
                                   bool combine, const WriteArgs* write) {
-  const bool f32 = a.g.dtype == PKV_F32;
-  switch (a.g.head_dim) {
-    case 64:
-      return f32 ? launch_decode_t<float, 64>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 64>(a, ws, stream, combine, write);
-    case 128:
-      return f32 ? launch_decode_t<float, 128>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 128>(a, ws, stream, combine, write);
-    case 256:
-      return f32 ? launch_decode_t<float, 256>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 256>(a, ws, stream, combine, write);
-    default:
-      return hipErrorInvalidValue;
-  }
+  if (wide_block_ids(a)) return launch_paged_attention_n<kMaxBlkRegs>(a, ws, stream, combine, write);
+  return launch_paged_attention_n<2>(a, ws, stream, combine, write);
 }
 
 static void launch_combine(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {

@@ -124,7 +124,7 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
   const int hi = chunk_max ? chunk_max : tuning_chunk_max();
   // validate everything before changing anything
   if (!pow2_in(lo, kMinChunkTokens, kMaxChunkTokens) ||
-      !pow2_in(hi, kMinChunkTokens, kMaxChunkTokens) || lo > hi || hi / lo > 32)
+      !pow2_in(hi, kMinChunkTokens, kMaxChunkTokens) || lo > hi || hi / lo > kMaxChunkRatio)
     return false;
   if (decode_waves != 0 && decode_waves != 1 && decode_waves != 2 && decode_waves != 4 &&
       decode_waves != 8)

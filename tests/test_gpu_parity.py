@@ -382,6 +382,9 @@ TUNINGS = [
     dict(chunk_min=64, chunk_max=2048, decode_waves=2, items_per_group=64, staging=2),
     dict(chunk_min=128, chunk_max=2048, decode_waves=8, items_per_group=16, staging=2),
     dict(chunk_min=256, chunk_max=256, decode_waves=8, items_per_group=1, deal=1),
+    # chunks of up to 512 blocks: an item's block ids span all eight id registers
+    dict(chunk_min=4096, chunk_max=8192, decode_waves=8, items_per_group=1),
+    dict(chunk_min=8192, chunk_max=8192, decode_waves=8, items_per_group=16, staging=2),
 ]
 
 
@@ -393,7 +396,8 @@ def test_work_split_variants(tuning):
     binding.set_tuning(**tuning)
     try:
         for dtype in ("bf16", "f32"):
-            w = wl.make_custom([4100, 0, 1, 255, 256, 257, 2049, 31, 700], heads=8, kv_heads=2,
+            w = wl.make_custom([4100, 0, 1, 255, 256, 257, 2049, 31, 700, 8192, 8177], heads=8,
+                               kv_heads=2,
                                head_dim=128, block_size=16, dtype=dtype, layout="HND",
                                seed=77)
             check_full(w)
