@@ -70,9 +70,11 @@ struct Workspace {
   int32_t* counters;    // [0] entries, [1] queue ticket, [2] chunk length, [3] its log2,
                         // [4] section-A entries, [5] section-A+B entries,
                         // [6] rows read token by token (slot input),
-                        // [7] decode workgroups that take part (the rest exit at once)
+                        // [7] decode workgroups that take part (the rest exit at once),
+                        // [8] rows split into more than one chunk
   int32_t* row_ctx;     // [rows]: each row's length as the block path reads it
   int32_t* irregular;   // [rows]: the rows read token by token, counters[6] of them
+  int2* split_rows;     // [rows]: {row, length} of the rows split into chunks, counters[8]
   float* partials;      // [rows][heads][max_chunks][head_dim + 4]: m (log2 units), l, -, -, acc
   int64_t max_entries;
   int32_t max_chunks;

@@ -270,8 +270,10 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 //   C. one zero-output entry per padding row.
 // counters[0] = entries, [1] = queue ticket (reset to 0), [2] = P, [3] = log2 P,
 // [4] = entries in section A, [5] = entries in sections A and B, [6] = rows of a slot
-// input left to the token-by-token kernel (listed in ws.irregular).  Every row's
-// clamped length goes to ws.row_ctx for the combine kernel.
+// input left to the token-by-token kernel (listed in ws.irregular), [7] = decode
+// workgroups that take part, [8] = split rows (listed with their lengths in
+// ws.split_rows for the combine kernel).  Every row's clamped length goes to
+// ws.row_ctx.
 __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   constexpr int kCand = 7;                 // chunk_max / chunk_min <= kMaxChunkRatio
   static_assert((1 << (kCand - 1)) == kMaxChunkRatio, "one candidate per power of two");
@@ -285,6 +287,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   __shared__ int s_bin_fill[kBins];
   __shared__ int s_pad_fill;
   __shared__ int s_irregular;
+  __shared__ int s_split;
   __shared__ int s_cand[kCand];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -292,6 +295,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   if (t == 0) {
     s_pad_fill = 0;
     s_irregular = 0;
+    s_split = 0;
   }
   __syncthreads();
 
@@ -405,11 +409,14 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   __syncthreads();
   if (t < nbins) s_bin_fill[t] = 0;
   __syncthreads();
-  // pass 2: place sections B and C
+  // pass 2: place sections B and C; list the split rows for the combine kernel (a row
+  // read token by token splits by its full length, which this thread wrote in pass 0)
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
     const int ctx = row_len(r);
     const int rem = ctx & (P - 1);
     const int nch = (ctx + P - 1) >> lp;
+    const int full = a.row_flags != nullptr ? ws.row_ctx[r] : ctx;
+    if (full > P) ws.split_rows[atomicAdd(&s_split, 1)] = make_int2((int)r, full);
     if (rem != 0) {
       const int pos = total_a + s_bin_start[rem >> bshift] +
                       atomicAdd(&s_bin_fill[rem >> bshift], 1);
@@ -419,6 +426,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
       ws.entries[pos] = make_int4((int)r, -1, 0, 0);
     }
   }
+  __syncthreads();
   if (t == 0) {
     ws.counters[0] = total_a + total_b + n_pad;
     ws.counters[1] = 0;
@@ -428,6 +436,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     ws.counters[5] = total_a + total_b;
     ws.counters[6] = s_irregular;
     ws.counters[7] = narrow ? a.narrow_groups : a.grid_groups;
+    ws.counters[8] = s_split;
   }
 }
 
@@ -1260,6 +1269,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 // combine
 // ------------------------------------------------------------------------- //
 constexpr int kCombineThreads = 256;
+constexpr int kCombineGroups = 1024;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -1272,8 +1282,10 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wave per (row, query vector) of a row split into several chunks, four waves to
-// a workgroup.  Chunk c of the row carries (m_c, l_c, acc_c); the result is
+// One wave per (split row, query vector) at a time, four waves to a workgroup, over
+// the plan's list of split rows (a grid of a fixed size strides over the pairs, so a
+// batch with no split row costs one load per wave).  Chunk c of the row carries
+// (m_c, l_c, acc_c); the result is
 // sum_c 2^(m_c - M) acc_c divided by sum_c 2^(m_c - M) l_c with M = max_c m_c, summed in
 // chunk order, so it does not depend on scheduling.  Lane i holds dims i * D/64 .. of
 // the vector.  A chunk wholly past a vector's causal limit carries m = -inf and l = 0
@@ -1284,42 +1296,46 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
   constexpr int W = kCombineThreads / 64;
   const int lane = threadIdx.x & 63;
   const int n_vec = a.query_len * a.num_heads;
-  const int v = blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t r = blockIdx.y;
-  if (v >= n_vec) return;
-  const int ctx = ws.row_ctx[r];
+  const int64_t pairs = (int64_t)ws.counters[8] * n_vec;
   const int lp = ws.counters[3];
-  const int nch = (ctx + (1 << lp) - 1) >> lp;
-  if (nch <= 1) return;
-  const float* rec = ws.partials + (r * n_vec + v) * ws.max_chunks * (D + 4);
+  for (int64_t pair = (int64_t)blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       pair < pairs; pair += (int64_t)gridDim.x * W) {
+    const int2 sr = ws.split_rows[pair / n_vec];
+    const int64_t r = sr.x;
+    const int v = (int)(pair % n_vec);
+    const int ctx = sr.y;
+    const int nch = (ctx + (1 << lp) - 1) >> lp;
+    if (nch <= 1) continue;
+    const float* rec = ws.partials + (r * n_vec + v) * ws.max_chunks * (D + 4);
 
-  float mx = -INFINITY;
-  for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, rec[c * (D + 4)]);
-  mx = wave_max(mx);
-  if (mx == -INFINITY) mx = 0.f;   // only a row whose length was out of bounds
-  float l = 0.f, acc[PER];
+    float mx = -INFINITY;
+    for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, rec[c * (D + 4)]);
+    mx = wave_max(mx);
+    if (mx == -INFINITY) mx = 0.f;   // only a row whose length was out of bounds
+    float l = 0.f, acc[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
 #pragma unroll 4
-  for (int c = 0; c < nch; ++c) {
-    const float* p = rec + c * (D + 4);
-    const float f = __builtin_amdgcn_exp2f(p[0] - mx);
-    l += p[1] * f;
+    for (int c = 0; c < nch; ++c) {
+      const float* p = rec + c * (D + 4);
+      const float f = __builtin_amdgcn_exp2f(p[0] - mx);
+      l += p[1] * f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += p[4 + lane * PER + i] * f;
-  }
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  T* outp = static_cast<T*>(a.out) + vec_slot(a, r, v) * D + lane * PER;
-  if constexpr (sizeof(T) == 4) {
+      for (int i = 0; i < PER; ++i) acc[i] += p[4 + lane * PER + i] * f;
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    T* outp = static_cast<T*>(a.out) + vec_slot(a, r, v) * D + lane * PER;
+    if constexpr (sizeof(T) == 4) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) outp[i] = acc[i] * inv;
-  } else if constexpr (PER == 1) {
-    outp[0] = (uint16_t)(Elem<uint16_t>::cvt2(acc[0] * inv, 0.f) & 0xffffu);
-  } else {
+      for (int i = 0; i < PER; ++i) outp[i] = acc[i] * inv;
+    } else if constexpr (PER == 1) {
+      outp[0] = (uint16_t)(Elem<uint16_t>::cvt2(acc[0] * inv, 0.f) & 0xffffu);
+    } else {
 #pragma unroll
-    for (int i = 0; i < PER; i += 2)
-      *reinterpret_cast<uint32_t*>(outp + i) = Elem<uint16_t>::cvt2(acc[i] * inv,
-                                                                    acc[i + 1] * inv);
+      for (int i = 0; i < PER; i += 2)
+        *reinterpret_cast<uint32_t*>(outp + i) = Elem<uint16_t>::cvt2(acc[i] * inv,
+                                                                      acc[i + 1] * inv);
+    }
   }
 }
 
@@ -1541,6 +1557,7 @@ size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
   int64_t bytes = align_up(entries * (int64_t)sizeof(int4), 256);
   bytes += 256;                                    // counters
   bytes += 2 * align_up(num_rows * 4, 256);        // row lengths, irregular rows
+  bytes += align_up(num_rows * 8, 256);            // split rows
   bytes += align_up(num_rows * num_heads * mc * (int64_t)(head_dim + 4) * 4, 256);
   return (size_t)bytes;
 }
@@ -1560,6 +1577,8 @@ Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads, int32
   p += align_up(num_rows * 4, 256);
   w.irregular = reinterpret_cast<int32_t*>(p);
   p += align_up(num_rows * 4, 256);
+  w.split_rows = reinterpret_cast<int2*>(p);
+  p += align_up(num_rows * 8, 256);
   w.partials = reinterpret_cast<float*>(p);
   (void)num_heads;
   (void)head_dim;
@@ -1617,10 +1636,12 @@ template <typename T, int D>
 static void launch_combine_t(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
   if (ws.max_chunks <= 1) return;
   timing_begin(PKV_PHASE_COMBINE, stream);
+  // a grid fixed by the shape (graph replays keep it): one wave per (row, vector) pair,
+  // at most kCombineGroups workgroups, striding over the split rows' pairs
   const int waves = kCombineThreads / 64;
-  hipLaunchKernelGGL((combine_kernel<T, D>),
-                     dim3((a.query_len * a.num_heads + waves - 1) / waves, (unsigned)a.num_rows),
-                     dim3(kCombineThreads), 0, stream, a, ws);
+  const int64_t most = ((int64_t)a.num_rows * a.query_len * a.num_heads + waves - 1) / waves;
+  const unsigned grid = (unsigned)(most < kCombineGroups ? most : kCombineGroups);
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(grid), dim3(kCombineThreads), 0, stream, a, ws);
   timing_end(PKV_PHASE_COMBINE, stream);
 }
 
