@@ -153,6 +153,19 @@ __device__ __forceinline__ void store16(void* p, const uint4& v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
 
+// A step's attention outputs are written once and not read again by this library:
+// non-temporal stores (measured: the 16-new-token step 1.261 -> 1.245 ms).  Partial
+// records keep ordinary stores, as the combine kernel reads them back.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_out(void* p, const uint4& v) {
+  const u32x4_nt x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4_nt*>(p));
+}
+template <typename X>
+__device__ __forceinline__ void store_out(X* p, X v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 // ------------------------------------------------------------------------- //
 // slot scatter
 // ------------------------------------------------------------------------- //
@@ -901,7 +914,8 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
           const float inv = lj > 0.f ? 1.0f / lj : 0.f;
 #pragma unroll
           for (int i = 0; i < E; ++i) aj[i] *= inv;
-          store16(static_cast<T*>(a.out) + vec_slot(a, cur.r, v) * D + sub * E, El::pack(aj));
+          store16_out(static_cast<T*>(a.out) + vec_slot(a, cur.r, v) * D + sub * E,
+                      El::pack(aj));
         } else {
           const int64_t rv = (int64_t)cur.r * n_vec + v;
           float* rec = ws.partials + (rv * ws.max_chunks + chunk) * (D + 4);
@@ -1230,11 +1244,12 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
         const float inv = lj > 0.f ? 1.0f / lj : 0.f;
         T* op = static_cast<T*>(a.out) + vec_slot(a, cur.r, v) * D + lane * PER;
         if constexpr (PER == 1) {
-          op[0] = (uint16_t)(Elem<uint16_t>::cvt2(y[0] * inv, 0.f) & 0xffffu);
+          store_out(op, (uint16_t)(Elem<uint16_t>::cvt2(y[0] * inv, 0.f) & 0xffffu));
         } else {
 #pragma unroll
           for (int i = 0; i < PER; i += 2)
-            *reinterpret_cast<uint32_t*>(op + i) = Elem<uint16_t>::cvt2(y[i] * inv, y[i + 1] * inv);
+            store_out(reinterpret_cast<uint32_t*>(op + i),
+                      Elem<uint16_t>::cvt2(y[i] * inv, y[i + 1] * inv));
         }
       } else {
         float* rec = ws.partials + (((int64_t)cur.r * n_vec + v) * ws.max_chunks + chunk) * (D + 4);
@@ -1327,14 +1342,14 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
     T* outp = static_cast<T*>(a.out) + vec_slot(a, r, v) * D + lane * PER;
     if constexpr (sizeof(T) == 4) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) outp[i] = acc[i] * inv;
+      for (int i = 0; i < PER; ++i) store_out(outp + i, (T)(acc[i] * inv));
     } else if constexpr (PER == 1) {
-      outp[0] = (uint16_t)(Elem<uint16_t>::cvt2(acc[0] * inv, 0.f) & 0xffffu);
+      store_out(outp, (uint16_t)(Elem<uint16_t>::cvt2(acc[0] * inv, 0.f) & 0xffffu));
     } else {
 #pragma unroll
       for (int i = 0; i < PER; i += 2)
-        *reinterpret_cast<uint32_t*>(outp + i) = Elem<uint16_t>::cvt2(acc[i] * inv,
-                                                                      acc[i + 1] * inv);
+        store_out(reinterpret_cast<uint32_t*>(outp + i),
+                  Elem<uint16_t>::cvt2(acc[i] * inv, acc[i + 1] * inv));
     }
   }
 }
@@ -1521,7 +1536,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;   // every live slot skipped: zeros
 #pragma unroll
         for (int i = 0; i < E; ++i) y[i] *= inv;
-        store16(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(y));
+        store16_out(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(y));
       } else {
         float* rec = ws.partials + (rh * ws.max_chunks + chunk) * (D + 4);
         if (sub == 0) {
