@@ -88,6 +88,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="read a buffer of this many MB before each event-timed step, so that "
+                         "the per-kernel times see no K/V left in the 256 MB MALL by the step "
+                         "before (a read leaves no dirty lines to write back during the step; "
+                         "the step-time loops are unchanged)")
     return ap.parse_args()
 
 
@@ -348,18 +353,24 @@ def main():
     # the same K steps again with a HIP event pair around every kernel, on the stream it
     # runs on: the per-kernel averages (the events add ~10 us of idle time per kernel
     # boundary, so this loop's wall clock is reported but is not the step time)
+    flush = (torch.ones(args.flush_mb << 18, dtype=torch.float32, device=dev)
+             if args.flush_mb > 0 else None)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
     binding.timing_enable(True)
     for ph in _capi.PHASES:
         binding.timing_read(ph, reset=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if flush is not None:
+            torch.sum(flush, dim=0, out=sink)   # outside the library's event pairs
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     phases = {ph: binding.timing_read(ph, reset=True) for ph in _capi.PHASES}
     binding.timing_enable(False)
     event_s = (t1 - t0) / args.steps
+    del flush, sink
 
     # the same step recorded once into a HIP graph over the same tensors, then replayed:
     # identical kernels and arguments, without a host launch per kernel
@@ -480,6 +491,7 @@ def main():
         },
         "eager_ms_per_step": round(eager_s * 1e3, 4),
         "event_timed_ms_per_step": round(event_s * 1e3, 4),
+        "flush_mb_before_event_timed_steps": args.flush_mb,
         "graph_ms_per_step": round(graph_s * 1e3, 4) if graph_s else None,
         "hbm_frac": round(b["total"] / step_s / 1e9 / HBM_PEAK_GBPS, 4),
         "total_algorithmic_GBps": round(b["total"] / step_s / 1e9, 2),
