@@ -215,13 +215,17 @@ constexpr int kPlanThreads = 1024;
 // carries fewer registers and id loads per item).
 constexpr int kMaxBlkRegs = kMaxChunkTokens / 16 / 64;
 
+// Inclusive prefix sum over the wave with DPP: within each 16-lane row shift-and-add by
+// 1, 2, 4 and 8 lanes (lanes with no source add 0), then add row 0's total to row 1 and
+// row 2's to row 3 (row_bcast:15), then the first two rows' total to rows 2 and 3
+// (row_bcast:31).  Checked against a host prefix sum on the GPU before use.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
 
