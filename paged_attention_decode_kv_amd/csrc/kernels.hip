@@ -1454,28 +1454,52 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
     float m = -INFINITY, l = 0.f, acc[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) acc[i] = 0.f;
-    for (int t0 = t_begin + wave * TPS * U; t0 < t_end; t0 += STEP) {
-      uint4 kr[U], vr[U];
-      bool ok[U];
+    // Software pipeline over this wave's steps of TPS * U tokens: the slots two steps
+    // ahead and the K/V one step ahead are in flight while a step is folded (a slot
+    // is needed before its K/V can be addressed).  A slot outside the allocatable
+    // slots (or a position past the chunk) loads nothing and scores -inf.
+    auto slots_of = [&](int t0, int64_t (&sl)[U]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = t0 + u * TPS + g;
-        ok[u] = false;
+        sl[u] = t < t_end ? row[t] : -1;
+      }
+    };
+    auto kv_of = [&](const int64_t (&sl)[U], uint4 (&kr)[U], uint4 (&vr)[U], bool (&ok)[U],
+                     int t0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * TPS + g;
+        const int64_t slot = sl[u];
+        ok[u] = t < t_end && slot >= 0 && slot < n_slots;
+        bad |= t < t_end && !ok[u];
         kr[u] = make_uint4(0, 0, 0, 0);
         vr[u] = make_uint4(0, 0, 0, 0);
-        if (t < t_end) {
-          const int64_t slot = row[t];
-          if (slot >= 0 && slot < n_slots) {
-            ok[u] = true;
-            const int64_t off = (slot >> log2_bs) * blk_bytes + (slot & bs_mask) * tok_bytes +
-                                lane_off;
-            kr[u] = load16_stream(kpool + off);
-            vr[u] = load16_stream(vpool + off);
-          } else {
-            bad = true;
-          }
+        if (ok[u]) {
+          const int64_t off = (slot >> log2_bs) * blk_bytes + (slot & bs_mask) * tok_bytes +
+                              lane_off;
+          kr[u] = load16_stream(kpool + off);
+          vr[u] = load16_stream(vpool + off);
         }
       }
+    };
+    const int t_first = t_begin + wave * TPS * U;
+    int64_t sl_next[U];
+    uint4 kr[U], vr[U];
+    bool ok[U];
+    {
+      int64_t sl[U];
+      slots_of(t_first, sl);
+      kv_of(sl, kr, vr, ok, t_first);
+      slots_of(t_first + STEP, sl_next);
+    }
+    for (int t0 = t_first; t0 < t_end; t0 += STEP) {
+      // the next step's K/V (its slots have landed) and the slots of the one after
+      uint4 kr_n[U], vr_n[U];
+      bool ok_n[U];
+      kv_of(sl_next, kr_n, vr_n, ok_n, t0 + STEP);
+      slots_of(t0 + 2 * STEP, sl_next);
+
       float sc[U];
       float smax = -INFINITY;
 #pragma unroll
@@ -1497,6 +1521,12 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
         El::axpy(p, vr[u], acc);
       }
       m = m_new;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kr[u] = kr_n[u];
+        vr[u] = vr_n[u];
+        ok[u] = ok_n[u];
+      }
     }
     // merge the lane groups, then the waves
 #pragma unroll
