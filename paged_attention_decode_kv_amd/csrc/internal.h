@@ -71,7 +71,8 @@ struct Workspace {
                         // [4] section-A entries, [5] section-A+B entries,
                         // [6] rows read token by token (slot input),
                         // [7] decode workgroups that take part (the rest exit at once),
-                        // [8] rows split into more than one chunk
+                        // [8] rows split into more than one chunk,
+                        // [9] most chunks of a row read token by token (slot input)
   int32_t* row_ctx;     // [rows]: each row's length as the block path reads it
   int32_t* irregular;   // [rows]: the rows read token by token, counters[6] of them
   int2* split_rows;     // [rows]: {row, length} of the rows split into chunks, counters[8]

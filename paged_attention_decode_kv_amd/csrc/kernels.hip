@@ -289,8 +289,8 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 // [4] = entries in section A, [5] = entries in sections A and B, [6] = rows of a slot
 // input left to the token-by-token kernel (listed in ws.irregular), [7] = decode
 // workgroups that take part, [8] = split rows (listed with their lengths in
-// ws.split_rows for the combine kernel).  Every row's clamped length goes to
-// ws.row_ctx.
+// ws.split_rows for the combine kernel), [9] = most chunks of a row read token by
+// token.  Every row's clamped length goes to ws.row_ctx.
 __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   constexpr int kCand = 7;                 // chunk_max / chunk_min <= kMaxChunkRatio
   static_assert((1 << (kCand - 1)) == kMaxChunkRatio, "one candidate per power of two");
@@ -305,6 +305,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   __shared__ int s_pad_fill;
   __shared__ int s_irregular;
   __shared__ int s_split;
+  __shared__ int s_irr_chunks;
   __shared__ int s_cand[kCand];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -313,6 +314,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     s_pad_fill = 0;
     s_irregular = 0;
     s_split = 0;
+    s_irr_chunks = 0;
   }
   __syncthreads();
 
@@ -434,6 +436,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     const int nch = (ctx + P - 1) >> lp;
     const int full = a.row_flags != nullptr ? ws.row_ctx[r] : ctx;
     if (full > P) ws.split_rows[atomicAdd(&s_split, 1)] = make_int2((int)r, full);
+    if (full != ctx) atomicMax(&s_irr_chunks, (full + P - 1) >> lp);   // a token-by-token row
     if (rem != 0) {
       const int pos = total_a + s_bin_start[rem >> bshift] +
                       atomicAdd(&s_bin_fill[rem >> bshift], 1);
@@ -454,6 +457,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     ws.counters[6] = s_irregular;
     ws.counters[7] = narrow ? a.narrow_groups : a.grid_groups;
     ws.counters[8] = s_split;
+    ws.counters[9] = s_irr_chunks;
   }
 }
 
@@ -1423,7 +1427,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
   const int heads = a.num_heads;
   const int qpkv = heads / a.g.kv_heads;
   const int lp = ws.counters[3];
-  const int mch = ws.max_chunks;
+  const int mch = ws.counters[9];      // most chunks of a token-by-token row
   const int64_t n_items = (int64_t)ws.counters[6] * heads * mch;
   const int64_t n_slots = a.g.num_blocks * a.g.block_size;
   const int log2_bs = a.g.log2_bs;
