@@ -208,12 +208,14 @@ __global__ void __launch_bounds__(256) kv_write_kernel(WriteArgs a, int64_t sink
 // plan: context_lens -> work list
 // ------------------------------------------------------------------------- //
 constexpr int kPlanThreads = 1024;
-// Block-id registers of a work item (64 ids to a register).  A chunk spans at most
-// kMaxChunkTokens / 16 blocks (block sizes are at least 16): kMaxBlkRegs registers.
-// The kernels are built for NBR = 2 (chunks of up to 128 blocks) and NBR = kMaxBlkRegs;
-// the launcher takes 2 whenever no chunk of the call can be wider (the narrow variant
-// carries fewer registers and id loads per item).
-constexpr int kMaxBlkRegs = kMaxChunkTokens / 16 / 64;
+// Block ids of a work item.  Wave w of a workgroup streams sub-chunks w, w + WAVES,
+// w + 2 WAVES, ... of the item's chunk, so lane i of wave w holds the block id of the
+// wave's i-th sub-chunk (and of its 64 + i-th, ... in further registers): a chunk of
+// kMaxChunkTokens tokens in sub-chunks of CH tokens needs id_regs(CH, WAVES) registers
+// a lane (one for 16-token sub-chunks and 8 waves), loaded with one load a lane each.
+__host__ __device__ constexpr int id_regs(int ch, int waves) {
+  return (kMaxChunkTokens / ch / waves + 63) / 64;
+}
 
 // Inclusive prefix sum over the wave with DPP: within each 16-lane row shift-and-add by
 // 1, 2, 4 and 8 lanes (lanes with no source add 0), then add row 0's total to row 1 and
@@ -503,7 +505,6 @@ struct Shape {
   static constexpr int CH = TPS * U;                // tokens per sub-chunk (<= 16)
   static_assert(LPT >= 8 && LPT <= 64, "unsupported head_dim/dtype");
   static_assert(kMinChunkTokens % CH == 0 && 16 % CH == 0, "sub-chunks tile chunks and blocks");
-  static_assert(kMaxChunkTokens / 16 <= 64 * kMaxBlkRegs, "block ids of a chunk: 8 a lane");
 };
 
 // Query vectors.  A row has query_len x heads of them, one per (new token i, query
@@ -522,30 +523,30 @@ __device__ __forceinline__ int vec_query(const AttnArgs& a, int v) {
 
 // Everything a work item needs before its first K/V load.  An item is (row, chunk of
 // the row's history, group of QG query vectors that share one KV head).
-template <int QG, int NBR>
+template <int QG, int NR>
 struct ItemMeta {
   int r, hg, chunk, nch, ctx;   // hg: vector group; vectors hg*QG .. hg*QG + QG - 1
   uint4 q[QG];   // this lane's 16 bytes of each vector's query
   int last[QG];  // each vector's last visible position (len - query_len + i)
-  int blk[NBR];   // lane i: block ids i, 64 + i, 128 + i, ... of the chunk
+  int blk[NR];   // lane i: block id of this wave's sub-chunks i, 64 + i, ...
 };
 
-// The block ids of an item's chunk, NBR per lane: lane i holds the chunk's
-// blocks i, 64 + i, ... (a chunk spans at most kMaxChunkTokens / 16 = 512 blocks).
-// Loads of ids past the chunk's last block are not issued.
-template <int NBR>
+// The block ids of this wave's sub-chunks of an item's chunk (see id_regs): lane i of
+// register k holds the id of sub-chunk wave + WAVES (64 k + i).  Loads past the chunk's
+// last sub-chunk are not issued.
+template <int NR, int CH, int WAVES>
 __device__ __forceinline__ void load_chunk_blocks(const AttnArgs& a, int r, int chunk, int ctx,
-                                                  int lp, int log2_bs, int lane,
-                                                  int (&blk)[NBR]) {
+                                                  int lp, int log2_bs, int lane, int wave,
+                                                  int (&blk)[NR]) {
   const int t_begin = chunk << lp;
-  const int t_end = min(ctx, t_begin + (1 << lp));
-  const int j0 = t_begin >> log2_bs;
-  const int nblk = ((t_end - 1) >> log2_bs) - j0 + 1;
-  const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks + j0;
-  const int nk = (nblk + 63) >> 6;   // id registers in use (uniform)
+  const int n_sub = (min(ctx, t_begin + (1 << lp)) - t_begin + CH - 1) / CH;
+  const int32_t* bt = a.block_tables + (int64_t)r * a.max_blocks;
 #pragma unroll
-  for (int k = 0; k < NBR; ++k)
-    if (k < nk && lane + 64 * k < nblk) blk[k] = bt[lane + 64 * k];
+  for (int k = 0; k < NR; ++k) {
+    if (wave + WAVES * 64 * k >= n_sub) break;   // uniform
+    const int s = wave + WAVES * (64 * k + lane);
+    if (s < n_sub) blk[k] = bt[(t_begin + s * CH) >> log2_bs];
+  }
 }
 
 // First half of fetching an item's metadata: the work-list entry load is issued and
@@ -556,12 +557,13 @@ __device__ __forceinline__ int4 issue_entry(const Workspace& ws, int item, int g
 
 // Second half: the entry becomes wave-uniform and the query and block-id loads are
 // issued (they complete while the current item finishes).
-template <typename T, int D, int QG, int NBR>
-__device__ __forceinline__ ItemMeta<QG, NBR> finish_meta(const AttnArgs& a, int4 ent, int item,
-                                                    int lp, int log2_bs, int lane, int sub) {
+template <typename T, int D, int QG, int NR, int CH, int WAVES>
+__device__ __forceinline__ ItemMeta<QG, NR> finish_meta(const AttnArgs& a, int4 ent, int item,
+                                                   int lp, int log2_bs, int lane, int sub,
+                                                   int wave) {
   constexpr int E = Elem<T>::kPerLane;
   const int groups = a.query_len * a.num_heads / QG;
-  ItemMeta<QG, NBR> m;
+  ItemMeta<QG, NR> m;
   const int e = item / groups;
   m.hg = item - e * groups;
   m.r = __builtin_amdgcn_readfirstlane(ent.x);
@@ -574,13 +576,13 @@ __device__ __forceinline__ ItemMeta<QG, NBR> finish_meta(const AttnArgs& a, int4
     m.last[j] = m.ctx - a.query_len + vec_query(a, m.hg * QG + j);
   }
 #pragma unroll
-  for (int k = 0; k < NBR; ++k) m.blk[k] = 0;
+  for (int k = 0; k < NR; ++k) m.blk[k] = 0;
   if (m.chunk >= 0) {
 #pragma unroll
     for (int j = 0; j < QG; ++j)
       m.q[j] = load16(static_cast<const T*>(a.q) + vec_slot(a, m.r, m.hg * QG + j) * D +
                       sub * E);
-    load_chunk_blocks(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, m.blk);
+    load_chunk_blocks<NR, CH, WAVES>(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, wave, m.blk);
   }
   return m;
 }
@@ -615,28 +617,22 @@ struct ChunkAddr {
   const char* kpool;
   const char* vpool;
   int64_t head_off, blk_bytes, tok_bytes;
-  int t_begin, t_end, j0, log2_bs, bs_mask;
+  int t_begin, t_end, bs_mask;
   int64_t num_blocks;
 
-  // blk: the item's block ids, lane i holding ids i, 64 + i, ... of the chunk
-  template <int CH, int NBR>
-  __device__ __forceinline__ int describe(int s, __amdgpu_buffer_rsrc_t& ksrc,
+  // sub-chunk s is the calling wave's i-th; blk: the wave's ids (load_chunk_blocks)
+  template <int CH, int NR>
+  __device__ __forceinline__ int describe(int s, int i, __amdgpu_buffer_rsrc_t& ksrc,
                                           __amdgpu_buffer_rsrc_t& vsrc, bool& bad,
-                                          const int (&blk)[NBR]) const {
+                                          const int (&blk)[NR]) const {
     const int t0 = t_begin + s * CH;
-    const int jb = (t0 >> log2_bs) - j0;   // block of this sub-chunk within the chunk
-    // (jb is wave-uniform: a register is read at lane jb % 64 and the scalar results are
-    // selected, so the id registers are never indexed; most chunks need only the first)
-    int raw;
-    if (jb < 64) {
-      raw = __builtin_amdgcn_readlane(blk[0], jb);
-    } else {
-      raw = __builtin_amdgcn_readlane(blk[1], jb & 63);
+    // (i is wave-uniform: each register is read at lane i % 64 and the scalar results
+    // are selected, so the id registers are never indexed)
+    int raw = __builtin_amdgcn_readlane(blk[0], i & 63);
 #pragma unroll
-      for (int k = 2; k < NBR; ++k) {
-        const int rk = __builtin_amdgcn_readlane(blk[k], jb & 63);
-        raw = (jb >> 6) == k ? rk : raw;
-      }
+    for (int k = 1; k < NR; ++k) {
+      const int rk = __builtin_amdgcn_readlane(blk[k], i & 63);
+      raw = (i >> 6) == k ? rk : raw;
     }
     const bool blk_ok = raw >= 0 && raw < num_blocks;
     bad |= !blk_ok;
@@ -696,13 +692,14 @@ struct ItemOrder {
 // counter, so the uneven tail is balanced dynamically with few atomics; padding rows
 // (section C) are zeroed round robin at the end.  The next item's metadata and the
 // ticket after it are fetched while the current item streams.
-template <typename T, int D, int WAVES, bool LDS_STAGE, int QG, int NBR>
+template <typename T, int D, int WAVES, bool LDS_STAGE, int QG>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using S = Shape<T, D>;
   using El = Elem<T>;
-  using Meta = ItemMeta<QG, NBR>;
   constexpr int E = S::E, LPT = S::LPT, TPS = S::TPS, U = S::U, CH = S::CH;
+  constexpr int NR = id_regs(CH, WAVES);
+  using Meta = ItemMeta<QG, NR>;
   constexpr int ES = sizeof(T);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -750,8 +747,8 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   bool bad_block = false;   // a live block id outside [0, num_blocks) was skipped
   Meta cur;
   if (item < n_data)
-    cur = finish_meta<T, D, QG, NBR>(a, issue_entry(ws, item, groups), item, lp, log2_bs, lane,
-                                     sub);
+    cur = finish_meta<T, D, QG, NR, CH, WAVES>(a, issue_entry(ws, item, groups), item, lp,
+                                               log2_bs, lane, sub, wave);
 
   while (item < n_data) {
     // the item after next: static, or a ticket whose value is needed only at the end
@@ -766,7 +763,6 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     const int hg = __builtin_amdgcn_readfirstlane(cur.hg);
     const int t_begin = chunk * P;
     const int t_end = min(__builtin_amdgcn_readfirstlane(cur.ctx), t_begin + P);
-    const int j0 = t_begin >> log2_bs;
     const int64_t head_off = (int64_t)(hg * QG / vpkv) * head_bytes;
 
     float m[QG], l[QG], acc[QG][E];
@@ -785,10 +781,10 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       last_rel[j] = __builtin_amdgcn_readfirstlane(cur.last[j]) - t_begin;
 
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
-    const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end, j0,
-                 log2_bs, bs_mask, a.g.num_blocks};
+    const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end,
+                 bs_mask, a.g.num_blocks};
     auto describe = [&](int s, __amdgpu_buffer_rsrc_t& ksrc, __amdgpu_buffer_rsrc_t& vsrc) {
-      return ca.describe<CH>(s, ksrc, vsrc, bad_block, cur.blk);
+      return ca.describe<CH>(s, (s - wave) / WAVES, ksrc, vsrc, bad_block, cur.blk);
     };
     auto stage_in = [&](int s) {   // sub-chunk s -> this wave's LDS stage
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
@@ -855,7 +851,8 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     }
 
     // the next item's query and block ids load while this item's state is merged
-    const Meta nxt = finish_meta<T, D, QG, NBR>(a, next_ent, next, lp, log2_bs, lane, sub);
+    const Meta nxt = finish_meta<T, D, QG, NR, CH, WAVES>(a, next_ent, next, lp, log2_bs, lane,
+                                                          sub, wave);
 
     // merge the lane groups of this wave, head by head
 #pragma unroll
@@ -998,20 +995,20 @@ __device__ __forceinline__ constexpr int piece_mask(int u, int g) {
   return D == 128 ? 2 * g + 8 * (u & 1) + (u >> 1) : 2 * (g >> 1) + u;
 }
 
-template <int D, int NBR>
+template <int D, int NR>
 struct MfmaMeta {
   int r, hg, chunk, nch, ctx;
   int last;           // lane: last visible position of vector hg*QG + l%16 (-1: none)
   uint4 q[D / 32];    // lane: 8 dims (32 s + 8 (l/16) ..) of that vector's query
-  int blk[NBR];
+  int blk[NR];   // lane i: block id of this wave's sub-chunks i, 64 + i, ...
 };
 
-template <int D, int QG, int NBR>
-__device__ __forceinline__ MfmaMeta<D, NBR> finish_meta_mfma(const AttnArgs& a, int4 ent, int item,
-                                                        int lp, int log2_bs, int lane) {
+template <int D, int QG, int NR, int WAVES>
+__device__ __forceinline__ MfmaMeta<D, NR> finish_meta_mfma(const AttnArgs& a, int4 ent, int item,
+                                                        int lp, int log2_bs, int lane, int wave) {
   const int groups = a.query_len * a.num_heads / QG;
   const int col = lane & 15, grp = lane >> 4;
-  MfmaMeta<D, NBR> m;
+  MfmaMeta<D, NR> m;
   const int e = item / groups;
   m.hg = item - e * groups;
   m.r = __builtin_amdgcn_readfirstlane(ent.x);
@@ -1023,14 +1020,14 @@ __device__ __forceinline__ MfmaMeta<D, NBR> finish_meta_mfma(const AttnArgs& a, 
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) m.q[s] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-  for (int k = 0; k < NBR; ++k) m.blk[k] = 0;
+  for (int k = 0; k < NR; ++k) m.blk[k] = 0;
   if (m.chunk >= 0) {
     if (col < QG) {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + vec_slot(a, m.r, v) * D + 8 * grp;
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) m.q[s] = load16(qp + 32 * s);
     }
-    load_chunk_blocks(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, m.blk);
+    load_chunk_blocks<NR, 16, WAVES>(a, m.r, m.chunk, m.ctx, lp, log2_bs, lane, wave, m.blk);
   }
   return m;
 }
@@ -1038,12 +1035,13 @@ __device__ __forceinline__ MfmaMeta<D, NBR> finish_meta_mfma(const AttnArgs& a, 
 // Same schedule, staging and partial records as decode_kernel (bfloat16 pools, head_dim
 // 64 or 128, sub-chunks of 16 tokens).  After its last fold a wave parks its state,
 // [QG][D] floats, in its own stage, and the waves are merged from there.
-template <int D, int WAVES, int QG, int NBR>
+template <int D, int WAVES, int QG>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using T = uint16_t;
   using S = Shape<T, D>;
-  using Meta = MfmaMeta<D, NBR>;
+  constexpr int NR = id_regs(16, WAVES);
+  using Meta = MfmaMeta<D, NR>;
   constexpr int TPS = S::TPS, U = S::U, CH = S::CH, LPT = S::LPT;
   constexpr int ES = sizeof(T);
   static_assert(CH == 16, "one 16-token tile per sub-chunk");
@@ -1116,8 +1114,8 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   bool bad_block = false;
   Meta cur;
   if (item < n_data)
-    cur = finish_meta_mfma<D, QG, NBR>(a, issue_entry(ws, item, groups), item, lp, log2_bs,
-                                       lane);
+    cur = finish_meta_mfma<D, QG, NR, WAVES>(a, issue_entry(ws, item, groups), item, lp,
+                                             log2_bs, lane, wave);
 
   while (item < n_data) {
     int after = 0;
@@ -1130,7 +1128,6 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     const int hg = __builtin_amdgcn_readfirstlane(cur.hg);
     const int t_begin = chunk * P;
     const int t_end = min(__builtin_amdgcn_readfirstlane(cur.ctx), t_begin + P);
-    const int j0 = t_begin >> log2_bs;
     const int64_t head_off = (int64_t)(hg * QG / vpkv) * head_bytes;
     const int last_rel = cur.last - t_begin;      // this lane's vector
 
@@ -1140,11 +1137,11 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     float m = -INFINITY, l = 0.f;
 
     const int n_sub = (t_end - t_begin + CH - 1) / CH;
-    const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end, j0,
-                 log2_bs, bs_mask, a.g.num_blocks};
+    const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end,
+                 bs_mask, a.g.num_blocks};
     auto stage_in = [&](int s) {
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
-      ca.describe<CH>(s, ksrc, vsrc, bad_block, cur.blk);
+      ca.describe<CH>(s, (s - wave) / WAVES, ksrc, vsrc, bad_block, cur.blk);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         buffer_load16_lds(ksrc, voff[u], reinterpret_cast<uint4*>(&s_stage[wave][u * 1024]));
@@ -1155,7 +1152,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     if (wave < n_sub) stage_in(wave);
     for (int s = wave; s < n_sub; s += WAVES) {
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
-      const int nvalid = ca.describe<CH>(s, ksrc, vsrc, bad_block, cur.blk);
+      const int nvalid = ca.describe<CH>(s, (s - wave) / WAVES, ksrc, vsrc, bad_block, cur.blk);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this wave's stage has landed
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1208,7 +1205,8 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       m = m_new;
     }
 
-    const Meta nxt = finish_meta_mfma<D, QG, NBR>(a, next_ent, next, lp, log2_bs, lane);
+    const Meta nxt = finish_meta_mfma<D, QG, NR, WAVES>(a, next_ent, next, lp, log2_bs, lane,
+                                                        wave);
     l += __shfl_xor(l, 16);        // the four row groups' denominators
     l += __shfl_xor(l, 32);
     // park this wave's state in its own stage (its last stage read has completed):
@@ -1698,12 +1696,12 @@ static void launch_combine_t(const AttnArgs& a, const Workspace& ws, hipStream_t
   timing_end(PKV_PHASE_COMBINE, stream);
 }
 
-template <typename T, int D, int NBR, int WAVES, bool LDS_STAGE, int QG, bool MFMA = false>
+template <typename T, int D, int WAVES, bool LDS_STAGE, int QG, bool MFMA = false>
 static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
                                   bool combine, const WriteArgs* write) {
   void (*kern)(AttnArgs, Workspace, float);
-  if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG, NBR>;
-  else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG, NBR>;
+  if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG>;
+  else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
   static int per_cu[64] = {0};   // occupancy per device, computed once
   static int num_cu[64] = {0};
   int dev = 0;
@@ -1781,74 +1779,59 @@ static int mfma_group_of(const AttnArgs& a) {
   return 0;
 }
 
-template <typename T, int D, int NBR>
+template <typename T, int D>
 static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
                                   bool combine, const WriteArgs* write) {
   if constexpr (sizeof(T) == 2 && D <= 128) {
     switch (mfma_group_of(a)) {
-      case 16: return launch_decode_w<T, D, NBR, 8, true, 16, true>(a, ws, stream, combine, write);
-      case 8: return launch_decode_w<T, D, NBR, 8, true, 8, true>(a, ws, stream, combine, write);
-      case 4: return launch_decode_w<T, D, NBR, 8, true, 4, true>(a, ws, stream, combine, write);
+      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream, combine, write);
+      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream, combine, write);
+      case 4: return launch_decode_w<T, D, 8, true, 4, true>(a, ws, stream, combine, write);
       default: break;
     }
   }
   switch (query_group_of(a)) {
     case 8:
-      if constexpr (D < 256) return launch_decode_w<T, D, NBR, 8, true, 8>(a, ws, stream, combine, write);
+      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream, combine, write);
       break;
-    case 4: return launch_decode_w<T, D, NBR, 8, true, 4>(a, ws, stream, combine, write);
-    case 2: return launch_decode_w<T, D, NBR, 8, true, 2>(a, ws, stream, combine, write);
+    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, stream, combine, write);
+    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, stream, combine, write);
     default: break;
   }
   if (tuning_lds_stage()) {
     switch (tuning_decode_waves()) {
-      case 1: return launch_decode_w<T, D, NBR, 1, true, 1>(a, ws, stream, combine, write);
-      case 2: return launch_decode_w<T, D, NBR, 2, true, 1>(a, ws, stream, combine, write);
-      case 8: return launch_decode_w<T, D, NBR, 8, true, 1>(a, ws, stream, combine, write);
-      default: return launch_decode_w<T, D, NBR, 4, true, 1>(a, ws, stream, combine, write);
+      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, stream, combine, write);
+      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, stream, combine, write);
+      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, stream, combine, write);
+      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, stream, combine, write);
     }
   }
   switch (tuning_decode_waves()) {
-    case 1: return launch_decode_w<T, D, NBR, 1, false, 1>(a, ws, stream, combine, write);
-    case 2: return launch_decode_w<T, D, NBR, 2, false, 1>(a, ws, stream, combine, write);
-    case 8: return launch_decode_w<T, D, NBR, 8, false, 1>(a, ws, stream, combine, write);
-    default: return launch_decode_w<T, D, NBR, 4, false, 1>(a, ws, stream, combine, write);
-  }
-}
-
-// an item of this call can span more than 128 blocks (its chunks can be longer than
-// 128 blocks and its rows can hold that many)
-static bool wide_block_ids(const AttnArgs& a) {
-  const int64_t chunk_blocks = ((int64_t)1 << a.log2_chunk_max) >> a.g.log2_bs;
-  const int64_t span = chunk_blocks < a.max_blocks ? chunk_blocks : a.max_blocks;
-  return span > 128;
-}
-
-template <int NBR>
-static hipError_t launch_paged_attention_n(const AttnArgs& a, const Workspace& ws,
-                                           hipStream_t stream, bool combine,
-                                           const WriteArgs* write) {
-  const bool f32 = a.g.dtype == PKV_F32;
-  switch (a.g.head_dim) {
-    case 64:
-      return f32 ? launch_decode_t<float, 64, NBR>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 64, NBR>(a, ws, stream, combine, write);
-    case 128:
-      return f32 ? launch_decode_t<float, 128, NBR>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 128, NBR>(a, ws, stream, combine, write);
-    case 256:
-      return f32 ? launch_decode_t<float, 256, NBR>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 256, NBR>(a, ws, stream, combine, write);
-    default:
-      return hipErrorInvalidValue;
+    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, stream, combine, write);
+    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, stream, combine, write);
+    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, stream, combine, write);
+    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, stream, combine, write);
   }
 }
 
 hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
                                   bool combine, const WriteArgs* write) {
-  if (wide_block_ids(a)) return launch_paged_attention_n<kMaxBlkRegs>(a, ws, stream, combine, write);
-  return launch_paged_attention_n<2>(a, ws, stream, combine, write);
+  const bool f32 = a.g.dtype == PKV_F32;
+  switch (a.g.head_dim) {
+    case 64:
+      return f32 ? launch_decode_t<float, 64>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 64>(a, ws, stream, combine, write);
+    case 128:
+      return f32 ? launch_decode_t<float, 128>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 128>(a, ws, stream, combine, write);
+    case 256:
+      return f32 ? launch_decode_t<float, 256>(a, ws, stream, combine, write)
+                 : launch_decode_t<uint16_t, 256>(a, ws, stream, combine, write);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
+
 
 static void launch_combine(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
   const bool f32 = a.g.dtype == PKV_F32;
