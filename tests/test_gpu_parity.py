@@ -405,6 +405,36 @@ def test_work_split_variants(tuning):
         binding.set_tuning(**before)
 
 
+LONG_CHUNKS = [
+    # lens, heads, kv_heads, head_dim, block_size, dtype, layout, chunk, waves: chunks of
+    # thousands of tokens, so a wave's block ids fill one or more id registers; block
+    # sizes above 16 put several sub-chunks in a block, and float32 (and head_dim 256)
+    # has sub-chunks of 8 (4) tokens
+    ([8000, 4097, 31], 4, 4, 128, 32, "bf16", "HND", 8192, 8),
+    ([8192, 5000], 4, 4, 128, 256, "bf16", "NHD", 8192, 8),
+    ([6000, 100], 4, 4, 128, 16, "f32", "HND", 8192, 8),
+    ([4100, 2], 2, 2, 256, 64, "f32", "HND", 4096, 8),
+    ([7000, 300], 8, 2, 128, 64, "bf16", "HND", 8192, 8),
+    ([8192, 1500, 0], 4, 4, 128, 16, "bf16", "HND", 8192, 1),
+]
+
+
+@pytest.mark.parametrize("case", LONG_CHUNKS,
+                         ids=lambda c: f"{c[5]}-d{c[3]}-bs{c[4]}-h{c[1]}/{c[2]}-c{c[7]}-w{c[8]}")
+def test_long_chunks_across_block_sizes(case):
+    """Pinned chunks of 4096-8192 tokens over long rows give oracle parity for every
+    block size and sub-chunk width (each wave's block ids span 64+ sub-chunks)."""
+    lens, h, hkv, d, bs, dtype, layout, chunk, waves = case
+    before = binding.get_tuning()
+    binding.set_tuning(chunk_min=chunk, chunk_max=chunk, decode_waves=waves)
+    try:
+        w = wl.make_custom(lens, heads=h, kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype,
+                           layout=layout, seed=sum(lens) + bs + chunk)
+        check_full(w)
+    finally:
+        binding.set_tuning(**before)
+
+
 GQA_CASES = [
     # lens, heads, kv_heads, head_dim, dtype, layout: query groups 8, 4, 2 and 16 (two items)
     ([700, 1, 0, 2049, 31], 16, 2, 128, "bf16", "HND"),
