@@ -249,7 +249,8 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  * shared by the waves of one workgroup, and rows longer than one chunk are merged
  * afterwards in chunk order.  The chunk length is chosen on the device per call: the
  * largest power of two in [chunk_min, chunk_max] that still yields items_per_group
- * items per decode workgroup (else chunk_min).  Setting chunk_min == chunk_max pins it.
+ * items per decode workgroup (else the largest that yields a quarter of that, else
+ * chunk_min).  Setting chunk_min == chunk_max pins it.
  *   chunk_min, chunk_max  powers of two in [32, 8192], chunk_max/chunk_min <= 64
  *                         (defaults 128, 8192)
  *   decode_waves          64-lane waves per workgroup: 1, 2, 4 or 8 (default 8)

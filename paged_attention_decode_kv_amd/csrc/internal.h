@@ -98,7 +98,7 @@ struct AttnArgs {
   int32_t log2_chunk_max;
   int32_t target_items;    // items the plan aims for with every workgroup (launcher)
   int32_t grid_groups;     // decode workgroups launched
-  int32_t narrow_groups;   // one per compute unit, or 0 when the launch already is that
+  int32_t narrow_groups;   // 8 waves per compute unit, or 0 when the launch already is that
   int32_t narrow_items;    // items the plan aims for with narrow_groups workgroups
   int32_t deal_static;     // 1: whole rounds of full chunks are dealt without the queue
   int32_t query_group;     // query vectors per work item (they share one KV head)

@@ -350,9 +350,9 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     if (lane == 0 && k < ncand) atomicAdd(&s_cand[k], v);
   }
   __syncthreads();
-  // Workgroups and chunk length.  A batch that gives one workgroup per compute unit
-  // enough items of more than the shortest chunk is bandwidth-bound: then one workgroup
-  // per CU (fewer concurrent streams) reads it fastest.  Otherwise every workgroup
+  // Workgroups and chunk length.  A batch that gives 8 waves per compute unit enough
+  // items of more than the shortest chunk is bandwidth-bound: then 8 waves per CU
+  // (fewer concurrent streams) read it fastest.  Otherwise every workgroup
   // takes part, with the chunk length that gives them all enough items.
   const int64_t per_entry = a.query_len * a.num_heads / a.query_group;
   // Balance: with G workgroups, the largest candidate whose chunks hold at most
@@ -378,12 +378,16 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     }
   }
   if (!narrow) {
-    for (int k = min(ncand - 1, balance_cap(a.grid_groups)); k >= 0; --k) {
-      if ((int64_t)s_cand[k] * per_entry >= a.target_items) {
-        lp = lmin + k;
-        break;
-      }
-    }
+    // A batch too small to give every workgroup its share even at the shortest chunk
+    // takes the longest that gives a quarter of it: each extra split of a row costs a
+    // float32 partial record per vector, and the shortest chunk splits the most.
+    const int kc = min(ncand - 1, balance_cap(a.grid_groups));
+    int found = -1;
+    for (int k = kc; k >= 0 && found < 0; --k)
+      if ((int64_t)s_cand[k] * per_entry >= a.target_items) found = k;
+    for (int k = kc; k >= 0 && found < 0; --k)
+      if ((int64_t)s_cand[k] * per_entry >= a.target_items / 4) found = k;
+    lp = lmin + (found > 0 ? found : 0);
   }
   const int P = 1 << lp;
   const int bshift = lp > 10 ? lp - 10 : 0;   // remainder -> bin (kBins = 1024)
@@ -1730,7 +1734,9 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   const int per_group = MFMA ? (tuning_items_per_group() + 3) / 4 : tuning_items_per_group();
   pa.target_items = (int32_t)(grid * per_group);
   pa.grid_groups = (int32_t)grid;
-  pa.narrow_groups = grid > num_cu[dev] ? num_cu[dev] : 0;   // the plan may keep one per CU
+  // the plan may keep 8 waves per CU (one workgroup of 8, two of 4, ...)
+  const int64_t narrow = (int64_t)num_cu[dev] * (WAVES < 8 ? 8 / WAVES : 1);
+  pa.narrow_groups = grid > narrow ? (int32_t)narrow : 0;
   pa.narrow_items = pa.narrow_groups * per_group;
   pa.deal_static = tuning_deal_static();
   timing_begin(PKV_PHASE_PLAN, stream);
