@@ -68,6 +68,8 @@ def parse():
                          "cores (library default), 2: always on the vector units")
     ap.add_argument("--groups-per-cu", type=int, default=0,
                     help="at most this many decode workgroups per compute unit")
+    ap.add_argument("--solo-tokens", type=int, default=0,
+                    help="chunks shorter than this are read by one wave each (1: none)")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="override the workload's KV heads (grouped-query variant)")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
@@ -255,7 +257,7 @@ def main():
     torch.cuda.set_device(dev)
     binding.set_tuning(args.chunk_min, args.chunk_max, args.decode_waves,
                        args.items_per_group, args.deal, args.staging, args.max_query_group,
-                       args.mfma, args.groups_per_cu)
+                       args.mfma, args.groups_per_cu, args.solo_tokens)
     tuning = binding.get_tuning()
     if args.query_len > 1 and args.address != "blocks":
         raise SystemExit("--query-len > 1 reads through block tables only")

@@ -275,6 +275,11 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *                         2: always on the vector units
  *   groups_per_cu         at most this many decode workgroups per compute unit, 1..16
  *                         (default 16: as many as fit)
+ *   solo_tokens           chunks of fewer than this many tokens are read first, by one
+ *                         wave each, with no merge across the waves of a workgroup,
+ *                         when there is at least one such chunk per decode wave: a power
+ *                         of two in [32, 1024], or 1 for none (default 512; the
+ *                         vector-unit kernel only)
  * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it
  * before sizing workspaces.  Results do not depend on these values beyond float32
  * rounding order.  Returns UNSUPPORTED for other values. */
@@ -288,6 +293,7 @@ typedef struct pkv_tuning {
   int32_t max_query_group;
   int32_t mfma;
   int32_t groups_per_cu;
+  int32_t solo_tokens;
 } pkv_tuning;
 
 pkv_status pkv_set_tuning(const pkv_tuning* tuning);

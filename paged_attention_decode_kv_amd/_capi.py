@@ -31,7 +31,7 @@ class Tuning(ctypes.Structure):
                 ("decode_waves", ctypes.c_int32), ("items_per_group", ctypes.c_int32),
                 ("deal", ctypes.c_int32), ("staging", ctypes.c_int32),
                 ("max_query_group", ctypes.c_int32), ("mfma", ctypes.c_int32),
-                ("groups_per_cu", ctypes.c_int32)]
+                ("groups_per_cu", ctypes.c_int32), ("solo_tokens", ctypes.c_int32)]
 
 
 _PD = ctypes.POINTER(PoolDesc)

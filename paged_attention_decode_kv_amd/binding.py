@@ -402,10 +402,11 @@ def decode_kernel_for(k_cache: torch.Tensor, num_heads: int, query_len: int = 1,
 
 def set_tuning(chunk_min: int = 0, chunk_max: int = 0, decode_waves: int = 0,
                items_per_group: int = 0, deal: int = 0, staging: int = 0,
-               max_query_group: int = 0, mfma: int = 0, groups_per_cu: int = 0) -> None:
+               max_query_group: int = 0, mfma: int = 0, groups_per_cu: int = 0,
+               solo_tokens: int = 0) -> None:
     """Set the decode work split (0 keeps a value); see pkv_set_tuning."""
     t = _capi.Tuning(chunk_min, chunk_max, decode_waves, items_per_group, deal, staging,
-                     max_query_group, mfma, groups_per_cu)
+                     max_query_group, mfma, groups_per_cu, solo_tokens)
     _check(_capi.lib().pkv_set_tuning(ctypes.byref(t)))
 
 

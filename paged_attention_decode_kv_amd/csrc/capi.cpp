@@ -187,7 +187,7 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
                             const int32_t* context_lens, int64_t num_rows, int32_t num_heads,
                             float scale, void* workspace, hipStream_t st,
                             int32_t query_len = 1, const pkv::WriteArgs* write = nullptr) {
-  pkv::AttnArgs a;
+  pkv::AttnArgs a{};
   a.g = geom(pool);
   a.out = out;
   a.q = q;
@@ -270,7 +270,7 @@ hipError_t launch_attention_slots(const pkv_pool_desc* pool, void* out, const vo
                                   int64_t row_stride, const int32_t* context_lens,
                                   int64_t num_rows, int32_t num_heads, float scale,
                                   void* workspace, hipStream_t st) {
-  pkv::AttnArgs a;
+  pkv::AttnArgs a{};
   a.g = geom(pool);
   a.out = out;
   a.q = q;
@@ -614,11 +614,13 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
 pkv_status pkv_set_tuning(const pkv_tuning* t) {
   if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
   if (!pkv::set_tuning(t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group,
-                       t->deal, t->staging, t->max_query_group, t->mfma, t->groups_per_cu))
+                       t->deal, t->staging, t->max_query_group, t->mfma, t->groups_per_cu,
+                       t->solo_tokens))
     return fail(PKV_ERR_UNSUPPORTED, "tuning chunk [%d, %d], waves %d, items/group %d, "
-                "deal %d, staging %d, query group %d, mfma %d, groups/CU %d not supported",
+                "deal %d, staging %d, query group %d, mfma %d, groups/CU %d, solo tokens %d "
+                "not supported",
                 t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group, t->deal,
-                t->staging, t->max_query_group, t->mfma, t->groups_per_cu);
+                t->staging, t->max_query_group, t->mfma, t->groups_per_cu, t->solo_tokens);
   return ok();
 }
 
@@ -633,6 +635,7 @@ pkv_status pkv_get_tuning(pkv_tuning* t) {
   t->max_query_group = pkv::tuning_max_query_group();
   t->mfma = pkv::tuning_mfma() ? 1 : 2;
   t->groups_per_cu = pkv::tuning_groups_per_cu();
+  t->solo_tokens = pkv::tuning_solo_tokens();
   return ok();
 }
 

@@ -25,6 +25,12 @@ constexpr int kDefaultLdsStage = 1;
 constexpr int kDefaultMaxQueryGroup = 16;
 constexpr int kDefaultMfma = 1;
 constexpr int kDefaultGroupsPerCu = 16;   // i.e. as many as fit
+// Chunks shorter than this many tokens are read by one wave alone (the plan puts them
+// last); at most kMaxSoloTokens.  1: none.
+constexpr int kDefaultSoloTokens = 512;
+constexpr int kMaxSoloTokens = 1024;
+// ... and only when there are at least this many of them per decode wave
+constexpr int kSoloPerWave = 1;
 
 // Slot input: tokens of one row that one workgroup of the translation pass checks.
 constexpr int kTranslateTokens = 1024;
@@ -38,8 +44,10 @@ int tuning_lds_stage();
 int tuning_max_query_group();
 int tuning_mfma();
 int tuning_groups_per_cu();
+int tuning_solo_tokens();
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal, int staging, int max_query_group, int mfma, int groups_per_cu);
+                int deal, int staging, int max_query_group, int mfma, int groups_per_cu,
+                int solo_tokens);
 
 // Pool geometry in elements, derived from the descriptor.
 struct PoolGeom {
@@ -72,7 +80,9 @@ struct Workspace {
                         // [6] rows read token by token (slot input),
                         // [7] decode workgroups that take part (the rest exit at once),
                         // [8] rows split into more than one chunk,
-                        // [9] most chunks of a row read token by token (slot input)
+                        // [9] most chunks of a row read token by token (slot input),
+                        // [10] entries before the single-wave items (chunks shorter
+                        // than AttnArgs::solo_tokens)
   int32_t* row_ctx;     // [rows]: each row's length as the block path reads it
   int32_t* irregular;   // [rows]: the rows read token by token, counters[6] of them
   int2* split_rows;     // [rows]: {row, length} of the rows split into chunks, counters[8]
@@ -103,6 +113,8 @@ struct AttnArgs {
   int32_t deal_static;     // 1: whole rounds of full chunks are dealt without the queue
   int32_t query_group;     // query vectors per work item (they share one KV head)
   int32_t query_len;       // new tokens (queries) per row: 1 for decode
+  int32_t solo_tokens;     // chunks shorter than this go last, one wave each (0: none)
+  int32_t group_waves;     // waves per decode workgroup
   float scale;
   // slot input only (else null / 0): [rows][flag_stride], nonzero where a row's live
   // slots are not block structured; such rows are left to the token-by-token kernel

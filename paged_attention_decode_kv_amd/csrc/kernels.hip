@@ -292,7 +292,9 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 // input left to the token-by-token kernel (listed in ws.irregular), [7] = decode
 // workgroups that take part, [8] = split rows (listed with their lengths in
 // ws.split_rows for the combine kernel), [9] = most chunks of a row read token by
-// token.  Every row's clamped length goes to ws.row_ctx.
+// token, [10] = entries before the single-wave items (those of fewer than
+// a.solo_tokens tokens, the tail of the longest-first order).  Every row's clamped
+// length goes to ws.row_ctx.
 __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   constexpr int kCand = 7;                 // chunk_max / chunk_min <= kMaxChunkRatio
   static_assert((1 << (kCand - 1)) == kMaxChunkRatio, "one candidate per power of two");
@@ -454,6 +456,22 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   }
   __syncthreads();
   if (t == 0) {
+    // entries before the single-wave items: section A if its chunks are not short, and
+    // the B bins of remainders >= solo_tokens (bin b holds [b, b + 1) << bshift, and
+    // solo_tokens is a multiple of 1 << bshift: a power of two >= 32 against <= 8)
+    int n_wide = total_a + total_b;
+    if (a.solo_tokens > 1) {
+      if (P < a.solo_tokens) {
+        n_wide = 0;
+      } else {
+        const int tb = a.solo_tokens >> bshift;   // first bin of the long remainders
+        n_wide = total_a + (tb >= nbins ? 0 : s_bin_start[tb - 1]);
+      }
+      // too few to keep every wave streaming: all items go wide
+      const int64_t waves = (int64_t)(narrow ? a.narrow_groups : a.grid_groups) * a.group_waves;
+      if ((int64_t)(total_a + total_b - n_wide) * per_entry < kSoloPerWave * waves)
+        n_wide = total_a + total_b;
+    }
     ws.counters[0] = total_a + total_b + n_pad;
     ws.counters[1] = 0;
     ws.counters[2] = P;
@@ -464,6 +482,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     ws.counters[7] = narrow ? a.narrow_groups : a.grid_groups;
     ws.counters[8] = s_split;
     ws.counters[9] = s_irr_chunks;
+    ws.counters[10] = n_wide;
   }
 }
 
@@ -684,26 +703,139 @@ struct ItemOrder {
   }
 };
 
+// Fold one sub-chunk (this lane's 16 bytes of U wave loads of K and of V) into the
+// online-softmax state of every vector of a group.  `nvalid` of its tokens are live;
+// vector j sees positions up to last_rel[j] (relative to the chunk start): the causal
+// limit of several new tokens.  Scores are in log2 units (scale_log2 = scale * log2 e).
+template <typename T, int D, int QG>
+__device__ __forceinline__ void fold_sub_chunk(const uint4 (&kr)[Shape<T, D>::U],
+                                               const uint4 (&vr)[Shape<T, D>::U], int nvalid,
+                                               int s, int g, const int (&last_rel)[QG],
+                                               const uint4 (&q)[QG], float scale_log2,
+                                               float (&m)[QG], float (&l)[QG],
+                                               float (&acc)[QG][Shape<T, D>::E]) {
+  using S = Shape<T, D>;
+  using El = Elem<T>;
+  constexpr int E = S::E, LPT = S::LPT, TPS = S::TPS, U = S::U, CH = S::CH;
+#pragma unroll
+  for (int j = 0; j < QG; ++j) {
+    const int nv = min(nvalid, last_rel[j] - s * CH + 1);
+    float sc[U];
+    float smax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float d = group_sum<LPT>(El::dot(q[j], kr[u], 0.f));
+      sc[u] = u * TPS + g < nv ? d * scale_log2 : -INFINITY;
+      smax = fmaxf(smax, sc[u]);
+    }
+    const float m_new = fmaxf(m[j], smax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m[j] - m_use);
+    l[j] *= alpha;
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[j][i] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = __builtin_amdgcn_exp2f(sc[u] - m_use);
+      l[j] += p;
+      El::axpy(p, vr[u], acc[j]);
+    }
+    m[j] = m_new;
+  }
+}
+
+// Merge the online-softmax states of the lane groups of one wave (groups of LPT lanes
+// that loaded different tokens), vector by vector; every group ends with the merge.
+template <int LPT, int QG, int E>
+__device__ __forceinline__ void merge_lane_groups(float (&m)[QG], float (&l)[QG],
+                                                  float (&acc)[QG][E]) {
+#pragma unroll
+  for (int j = 0; j < QG; ++j) {
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      const float m_o = __shfl_xor(m[j], off);
+      const float l_o = __shfl_xor(l[j], off);
+      const float mx = fmaxf(m[j], m_o);
+      const float mu = mx == -INFINITY ? 0.f : mx;
+      const float fa = __builtin_amdgcn_exp2f(m[j] - mu);
+      const float fb = __builtin_amdgcn_exp2f(m_o - mu);
+      l[j] = l[j] * fa + l_o * fb;
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[j][i] = acc[j][i] * fa + __shfl_xor(acc[j][i], off) * fb;
+      m[j] = mx;
+    }
+  }
+}
+
+// The finished state of query vector v of row r over one chunk, written by the LPT
+// lanes of one lane group (this lane's piece `sub`): the output (a row of one chunk:
+// acc / l, zeros where nothing was visible) or the chunk's partial record (m, l, acc)
+// for the combine kernel.
+template <typename T, int D>
+__device__ __forceinline__ void write_item_result(const AttnArgs& a, const Workspace& ws,
+                                                  int r, int v, int chunk, int nch, int n_vec,
+                                                  int sub, float mj, float lj,
+                                                  float (&aj)[Elem<T>::kPerLane]) {
+  constexpr int E = Elem<T>::kPerLane;
+  if (nch == 1) {
+    const float inv = lj > 0.f ? 1.0f / lj : 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) aj[i] *= inv;
+    store16_out(static_cast<T*>(a.out) + vec_slot(a, r, v) * D + sub * E, Elem<T>::pack(aj));
+  } else {
+    const int64_t rv = (int64_t)r * n_vec + v;
+    float* rec = ws.partials + (rv * ws.max_chunks + chunk) * (D + 4);
+    if (sub == 0) {
+      rec[0] = mj;
+      rec[1] = lj;
+    }
+#pragma unroll
+    for (int i = 0; i < E; i += 4)
+      store16(rec + 4 + sub * E + i, make_uint4(__float_as_uint(aj[i]), __float_as_uint(aj[i + 1]),
+                                                __float_as_uint(aj[i + 2]),
+                                                __float_as_uint(aj[i + 3])));
+  }
+}
+
+// Block-id registers of a single-wave item (its chunk has fewer than kMaxSoloTokens
+// tokens, all of its sub-chunks read by one wave).
+__host__ __device__ constexpr int solo_id_regs(int ch) {
+  return (kMaxSoloTokens / ch + 63) / 64;
+}
+
 // The decode read.  Persistent workgroups process work items; an item is (chunk of a
-// row's history, group of QG query heads sharing one KV head), and the waves of a
-// workgroup share it, wave w folding sub-chunks w, w + WAVES, ... into its own
-// online-softmax state of every head of the group before the waves are merged through
-// LDS.  With grouped-query attention one K/V load serves QG query heads.
+// row's history, group of QG query heads sharing one KV head).
 //
-// Schedule: whole rounds of the full chunks (section A, all the same length) are
-// dealt round robin, workgroup g taking items g, g + G, g + 2G, ...; the rest of A and
-// the trailing partial chunks (section B, longest first) come from one shared ticket
-// counter, so the uneven tail is balanced dynamically with few atomics; padding rows
-// (section C) are zeroed round robin at the end.  The next item's metadata and the
-// ticket after it are fetched while the current item streams.
+// Wide items: the waves of a workgroup share the item, wave w folding sub-chunks w,
+// w + WAVES, ... into its own online-softmax state of every head of the group before
+// the waves are merged through LDS.  With grouped-query attention one K/V load serves
+// QG query heads.  Whole rounds of the full chunks (section A, all the same length)
+// are dealt round robin, workgroup g taking items g, g + G, g + 2G, ...; the rest of A
+// and the trailing partial chunks (section B, longest first) come from one shared
+// ticket counter, so the uneven tail is balanced dynamically with few atomics.  The
+// next item's metadata and the ticket after it are fetched while the current item
+// streams.
+//
+// Single-wave items: chunks shorter than a.solo_tokens (the end of section B; the plan
+// keeps them only when there are at least kSoloPerWave for every wave) are read first,
+// by one wave each, dealt round robin over every wave of the launch.  A short chunk
+// shared by 8 waves leaves most of them idle at its last round and pays a workgroup
+// merge and barrier per few sub-chunks; alone, a wave streams its items back to back:
+// the next item's metadata loads while the current one streams, and its first
+// sub-chunk is staged while the current item's last one is folded.  A single wave
+// takes ~8x as long over one item, so these go before the wide items, whose shared
+// queue evens out the workgroups' finishing times.
+//
+// Padding rows (section C) are zeroed round robin at the end.
 template <typename T, int D, int WAVES, bool LDS_STAGE, int QG>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   using S = Shape<T, D>;
-  using El = Elem<T>;
   constexpr int E = S::E, LPT = S::LPT, TPS = S::TPS, U = S::U, CH = S::CH;
   constexpr int NR = id_regs(CH, WAVES);
+  constexpr int NRS = solo_id_regs(CH);
   using Meta = ItemMeta<QG, NR>;
+  using MetaS = ItemMeta<QG, NRS>;
   constexpr int ES = sizeof(T);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -725,11 +857,12 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int vpkv = n_vec / a.g.kv_heads;         // query vectors per KV head
   const int lp = ws.counters[3];
   const int P = 1 << lp;
-  const int n_static = ws.counters[4] * groups;   // section A items
+  const int n_wide = ws.counters[10] * groups;    // items before the single-wave ones
   const int n_data = ws.counters[5] * groups;     // sections A and B
   const int n_items = ws.counters[0] * groups;
   const int G = ws.counters[7];                  // workgroups taking part
   if ((int)blockIdx.x >= G) return;
+  const int n_static = min(ws.counters[4] * groups, n_wide);   // section A items
   const int n_dealt = a.deal_static ? n_static / G * G : 0;
   const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
@@ -743,31 +876,141 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     voff[u] = (uint32_t)((u * TPS + g) * tok_bytes + sub * E * ES);
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
+  bool bad_block = false;   // a live block id outside [0, num_blocks) was skipped
 
+  // addressing of an item's sub-chunks (its fields are wave-uniform; saying so keeps the
+  // load descriptors scalar)
+  auto chunk_addr = [&](int chunk, int hg, int ctx) {
+    const int t_begin = chunk * P;
+    return ChunkAddr{kpool, vpool, (int64_t)(hg * QG / vpkv) * head_bytes, blk_bytes,
+                     tok_bytes, t_begin, min(ctx, t_begin + P), bs_mask, a.g.num_blocks};
+  };
+  // this wave's LDS stage <- sub-chunk s of an item
+  auto stage_from = [&](const ChunkAddr& ca, int s, int i, auto& blk) {
+    __amdgpu_buffer_rsrc_t ksrc, vsrc;
+    ca.describe<CH>(s, i, ksrc, vsrc, bad_block, blk);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      buffer_load16_lds(ksrc, voff[u], &s_stage[wave][u][0]);
+      buffer_load16_lds(vsrc, voff[u], &s_stage[wave][U + u][0]);
+    }
+  };
+  // sub-chunk s of an item into registers: from the stage (then the stage is free), or
+  // straight from memory; returns its live tokens
+  auto fetch = [&](const ChunkAddr& ca, int s, int i, auto& blk, uint4 (&kr)[U],
+                   uint4 (&vr)[U]) {
+    __amdgpu_buffer_rsrc_t ksrc, vsrc;
+    const int nvalid = ca.describe<CH>(s, i, ksrc, vsrc, bad_block, blk);
+    if constexpr (LDS_STAGE) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this wave's stage has landed
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kr[u] = s_stage[wave][u][lane];
+        vr[u] = s_stage[wave][U + u][lane];
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // stage read before it is refilled
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kr[u] = buffer_load16(ksrc, voff[u]);
+        vr[u] = buffer_load16(vsrc, voff[u]);
+      }
+    }
+    return nvalid;
+  };
+
+  // ---- single-wave items first: [n_wide, n_data), wave k of the launch takes n_wide + k,
+  // n_wide + k + G * WAVES, ...; the wide items' shared queue then evens out the
+  // workgroups' finishing times ----
+  {
+    const int stride = G * WAVES;
+    int it = n_wide + (int)blockIdx.x * WAVES + wave;
+    MetaS sc;
+    int4 ent_nx = make_int4(0, -1, 0, 0);
+    if (it < n_data) {
+      sc = finish_meta<T, D, QG, NRS, CH, 1>(a, issue_entry(ws, it, groups), it, lp, log2_bs,
+                                             lane, sub, 0);
+      if (it + stride < n_data) ent_nx = issue_entry(ws, it + stride, groups);
+    }
+    bool staged = false;   // the item's first sub-chunk is already in the stage
+    while (it < n_data) {
+      const int nx = it + stride;
+      // the next item's query and block ids, and the entry after it, load while this
+      // item streams
+      MetaS sn = finish_meta<T, D, QG, NRS, CH, 1>(a, ent_nx, nx, lp, log2_bs, lane, sub, 0);
+      ent_nx = nx + stride < n_data ? issue_entry(ws, nx + stride, groups)
+                                    : make_int4(0, -1, 0, 0);
+
+      const int chunk = __builtin_amdgcn_readfirstlane(sc.chunk);
+      const int hg = __builtin_amdgcn_readfirstlane(sc.hg);
+      const ChunkAddr ca = chunk_addr(chunk, hg, __builtin_amdgcn_readfirstlane(sc.ctx));
+      float m[QG], l[QG], acc[QG][E];
+#pragma unroll
+      for (int j = 0; j < QG; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[j][i] = 0.f;
+      }
+      int last_rel[QG];
+#pragma unroll
+      for (int j = 0; j < QG; ++j)
+        last_rel[j] = __builtin_amdgcn_readfirstlane(sc.last[j]) - ca.t_begin;
+
+      const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
+      if constexpr (LDS_STAGE) {
+        if (!staged) stage_from(ca, 0, 0, sc.blk);
+      }
+      staged = false;
+      for (int s = 0; s < n_sub; ++s) {
+        uint4 kr[U], vr[U];
+        const int nvalid = fetch(ca, s, s, sc.blk, kr, vr);
+        if constexpr (LDS_STAGE) {
+          if (s + 1 < n_sub) {
+            stage_from(ca, s + 1, s + 1, sc.blk);
+          } else if (nx < n_data) {   // the next item's first sub-chunk
+            const ChunkAddr cn = chunk_addr(__builtin_amdgcn_readfirstlane(sn.chunk),
+                                            __builtin_amdgcn_readfirstlane(sn.hg),
+                                            __builtin_amdgcn_readfirstlane(sn.ctx));
+            stage_from(cn, 0, 0, sn.blk);
+            staged = true;
+          }
+        }
+        fold_sub_chunk<T, D, QG>(kr, vr, nvalid, s, g, last_rel, sc.q, scale_log2, m, l, acc);
+      }
+      merge_lane_groups<LPT, QG, E>(m, l, acc);
+      if (g == 0) {
+#pragma unroll
+        for (int j = 0; j < QG; ++j)
+          write_item_result<T, D>(a, ws, sc.r, hg * QG + j, chunk, sc.nch, n_vec, sub, m[j],
+                                  l[j], acc[j]);
+      }
+      it = nx;
+      sc = sn;
+    }
+  }
+
+  // ---- wide items: the workgroup's waves share each one ----
   ItemOrder order{(int)blockIdx.x, G, n_dealt};
   int item, next;
   order.first_two(item, next, &ws.counters[1], s_ticket);
   int buf = 0;
-  bool bad_block = false;   // a live block id outside [0, num_blocks) was skipped
   Meta cur;
-  if (item < n_data)
+  if (item < n_wide)
     cur = finish_meta<T, D, QG, NR, CH, WAVES>(a, issue_entry(ws, item, groups), item, lp,
                                                log2_bs, lane, sub, wave);
 
-  while (item < n_data) {
+  while (item < n_wide) {
     // the item after next: static, or a ticket whose value is needed only at the end
     int after = 0;
     const bool after_static = order.take(after);
     if (!after_static && threadIdx.x == 0) after = atomicAdd(&ws.counters[1], 1);
     int4 next_ent = make_int4(0, -1, 0, 0);
-    if (next < n_data) next_ent = issue_entry(ws, next, groups);
+    if (next < n_wide) next_ent = issue_entry(ws, next, groups);
 
-    // (the item's fields are wave-uniform; saying so keeps the load descriptors scalar)
     const int chunk = __builtin_amdgcn_readfirstlane(cur.chunk);
     const int hg = __builtin_amdgcn_readfirstlane(cur.hg);
-    const int t_begin = chunk * P;
-    const int t_end = min(__builtin_amdgcn_readfirstlane(cur.ctx), t_begin + P);
-    const int64_t head_off = (int64_t)(hg * QG / vpkv) * head_bytes;
+    const ChunkAddr ca = chunk_addr(chunk, hg, __builtin_amdgcn_readfirstlane(cur.ctx));
 
     float m[QG], l[QG], acc[QG][E];
 #pragma unroll
@@ -777,104 +1020,29 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 #pragma unroll
       for (int i = 0; i < E; ++i) acc[j][i] = 0.f;
     }
-
-    // each vector's last visible position, relative to the chunk start
     int last_rel[QG];
 #pragma unroll
     for (int j = 0; j < QG; ++j)
-      last_rel[j] = __builtin_amdgcn_readfirstlane(cur.last[j]) - t_begin;
+      last_rel[j] = __builtin_amdgcn_readfirstlane(cur.last[j]) - ca.t_begin;
 
-    const int n_sub = (t_end - t_begin + CH - 1) / CH;
-    const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end,
-                 bs_mask, a.g.num_blocks};
-    auto describe = [&](int s, __amdgpu_buffer_rsrc_t& ksrc, __amdgpu_buffer_rsrc_t& vsrc) {
-      return ca.describe<CH>(s, (s - wave) / WAVES, ksrc, vsrc, bad_block, cur.blk);
-    };
-    auto stage_in = [&](int s) {   // sub-chunk s -> this wave's LDS stage
-      __amdgpu_buffer_rsrc_t ksrc, vsrc;
-      describe(s, ksrc, vsrc);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        buffer_load16_lds(ksrc, voff[u], &s_stage[wave][u][0]);
-        buffer_load16_lds(vsrc, voff[u], &s_stage[wave][U + u][0]);
-      }
-    };
+    const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
     if constexpr (LDS_STAGE) {
-      if (wave < n_sub) stage_in(wave);
+      if (wave < n_sub) stage_from(ca, wave, 0, cur.blk);
     }
     for (int s = wave; s < n_sub; s += WAVES) {
       uint4 kr[U], vr[U];
-      int nvalid;
+      const int i = (s - wave) / WAVES;   // the wave's i-th sub-chunk of the item
+      const int nvalid = fetch(ca, s, i, cur.blk, kr, vr);
       if constexpr (LDS_STAGE) {
-        __amdgpu_buffer_rsrc_t ksrc, vsrc;
-        nvalid = describe(s, ksrc, vsrc);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this wave's stage has landed
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          kr[u] = s_stage[wave][u][lane];
-          vr[u] = s_stage[wave][U + u][lane];
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // stage read before it is refilled
-        if (s + WAVES < n_sub) stage_in(s + WAVES);
-      } else {
-        __amdgpu_buffer_rsrc_t ksrc, vsrc;
-        nvalid = describe(s, ksrc, vsrc);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          kr[u] = buffer_load16(ksrc, voff[u]);
-          vr[u] = buffer_load16(vsrc, voff[u]);
-        }
+        if (s + WAVES < n_sub) stage_from(ca, s + WAVES, i + 1, cur.blk);
       }
-      // fold the sub-chunk into every vector of the group: one K/V load, QG vectors,
-      // each seeing the positions up to its own (the causal limit of several new tokens)
-#pragma unroll
-      for (int j = 0; j < QG; ++j) {
-        const int nv = min(nvalid, last_rel[j] - s * CH + 1);
-        float sc[U];
-        float smax = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float d = group_sum<LPT>(El::dot(cur.q[j], kr[u], 0.f));
-          sc[u] = u * TPS + g < nv ? d * scale_log2 : -INFINITY;
-          smax = fmaxf(smax, sc[u]);
-        }
-        const float m_new = fmaxf(m[j], smax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m[j] - m_use);
-        l[j] *= alpha;
-#pragma unroll
-        for (int i = 0; i < E; ++i) acc[j][i] *= alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float p = __builtin_amdgcn_exp2f(sc[u] - m_use);
-          l[j] += p;
-          El::axpy(p, vr[u], acc[j]);
-        }
-        m[j] = m_new;
-      }
+      fold_sub_chunk<T, D, QG>(kr, vr, nvalid, s, g, last_rel, cur.q, scale_log2, m, l, acc);
     }
 
     // the next item's query and block ids load while this item's state is merged
     const Meta nxt = finish_meta<T, D, QG, NR, CH, WAVES>(a, next_ent, next, lp, log2_bs, lane,
                                                           sub, wave);
-
-    // merge the lane groups of this wave, head by head
-#pragma unroll
-    for (int j = 0; j < QG; ++j) {
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) {
-        const float m_o = __shfl_xor(m[j], off);
-        const float l_o = __shfl_xor(l[j], off);
-        const float mx = fmaxf(m[j], m_o);
-        const float mu = mx == -INFINITY ? 0.f : mx;
-        const float fa = __builtin_amdgcn_exp2f(m[j] - mu);
-        const float fb = __builtin_amdgcn_exp2f(m_o - mu);
-        l[j] = l[j] * fa + l_o * fb;
-#pragma unroll
-        for (int i = 0; i < E; ++i) acc[j][i] = acc[j][i] * fa + __shfl_xor(acc[j][i], off) * fb;
-        m[j] = mx;
-      }
-    }
+    merge_lane_groups<LPT, QG, E>(m, l, acc);
     // merge the waves (LDS double-buffered by item parity: one barrier); wave w merges
     // and writes heads w, w + WAVES, ... of the group
     if constexpr (WAVES > 1) {
@@ -918,27 +1086,8 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
           }
           mj = mx;
         }
-        const int v = hg * QG + j;
-        if (cur.nch == 1) {
-          const float inv = lj > 0.f ? 1.0f / lj : 0.f;
-#pragma unroll
-          for (int i = 0; i < E; ++i) aj[i] *= inv;
-          store16_out(static_cast<T*>(a.out) + vec_slot(a, cur.r, v) * D + sub * E,
-                      El::pack(aj));
-        } else {
-          const int64_t rv = (int64_t)cur.r * n_vec + v;
-          float* rec = ws.partials + (rv * ws.max_chunks + chunk) * (D + 4);
-          if (sub == 0) {
-            rec[0] = mj;
-            rec[1] = lj;
-          }
-#pragma unroll
-          for (int i = 0; i < E; i += 4)
-            store16(rec + 4 + sub * E + i, make_uint4(__float_as_uint(aj[i]),
-                                                      __float_as_uint(aj[i + 1]),
-                                                      __float_as_uint(aj[i + 2]),
-                                                      __float_as_uint(aj[i + 3])));
-        }
+        write_item_result<T, D>(a, ws, cur.r, hg * QG + j, chunk, cur.nch, n_vec, sub, mj, lj,
+                                aj);
       }
     }
     buf ^= 1;
@@ -946,6 +1095,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     cur = nxt;
     next = after;
   }
+
   if (bad_block && lane == 0) atomicOr(&g_status, PKV_DEVERR_BLOCK_ID);
   // padding rows: zero output, nothing read
   for (int it = n_data + (int)blockIdx.x; it < n_items; it += G) {
@@ -1739,6 +1889,8 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   pa.narrow_groups = grid > narrow ? (int32_t)narrow : 0;
   pa.narrow_items = pa.narrow_groups * per_group;
   pa.deal_static = tuning_deal_static();
+  pa.solo_tokens = MFMA ? 0 : tuning_solo_tokens();   // the matrix-core kernel has no solo phase
+  pa.group_waves = WAVES;
   timing_begin(PKV_PHASE_PLAN, stream);
   if (write) {   // the step's scatter rides along with the plan
     const int64_t pieces = write->num_tokens * write->g.kv_heads *

@@ -104,6 +104,7 @@ std::atomic<int> g_lds_stage{kDefaultLdsStage};
 std::atomic<int> g_max_query_group{kDefaultMaxQueryGroup};
 std::atomic<int> g_mfma{kDefaultMfma};
 std::atomic<int> g_groups_per_cu{kDefaultGroupsPerCu};
+std::atomic<int> g_solo_tokens{kDefaultSoloTokens};
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 }  // namespace
@@ -117,9 +118,11 @@ int tuning_lds_stage() { return g_lds_stage.load(std::memory_order_relaxed); }
 int tuning_max_query_group() { return g_max_query_group.load(std::memory_order_relaxed); }
 int tuning_mfma() { return g_mfma.load(std::memory_order_relaxed); }
 int tuning_groups_per_cu() { return g_groups_per_cu.load(std::memory_order_relaxed); }
+int tuning_solo_tokens() { return g_solo_tokens.load(std::memory_order_relaxed); }
 
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
-                int deal, int staging, int max_query_group, int mfma, int groups_per_cu) {
+                int deal, int staging, int max_query_group, int mfma, int groups_per_cu,
+                int solo_tokens) {
   const int lo = chunk_min ? chunk_min : tuning_chunk_min();
   const int hi = chunk_max ? chunk_max : tuning_chunk_max();
   // validate everything before changing anything
@@ -137,6 +140,9 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
     return false;
   if (mfma < 0 || mfma > 2) return false;
   if (groups_per_cu < 0 || groups_per_cu > 16) return false;
+  if (solo_tokens != 0 && solo_tokens != 1 &&
+      !pow2_in(solo_tokens, kMinChunkTokens, kMaxSoloTokens))
+    return false;
   g_chunk_min.store(lo);
   g_chunk_max.store(hi);
   if (decode_waves != 0) g_decode_waves.store(decode_waves);
@@ -146,6 +152,7 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
   if (max_query_group != 0) g_max_query_group.store(max_query_group);
   if (mfma != 0) g_mfma.store(mfma == 1 ? 1 : 0);
   if (groups_per_cu != 0) g_groups_per_cu.store(groups_per_cu);
+  if (solo_tokens != 0) g_solo_tokens.store(solo_tokens);
   return true;
 }
 

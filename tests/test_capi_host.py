@@ -317,3 +317,24 @@ def test_decode_kernel_choice(lib):
     assert name(8, 32, dtype="f32") == "decode_kernel, 4 query vectors per item"
     assert name(4, 32, d=256) == "decode_kernel, 4 query vectors per item"
     assert name(4, 6) == ""
+
+
+def test_tuning_is_validated_before_it_changes(lib):
+    """A refused tuning changes nothing; solo_tokens takes 1 (none) or a power of two in
+    [32, 1024], and the chunk range must be powers of two within a ratio of 64."""
+    before = binding.get_tuning()
+    try:
+        for bad in (dict(solo_tokens=16), dict(solo_tokens=2048), dict(solo_tokens=300),
+                    dict(chunk_min=64, chunk_max=8192), dict(chunk_min=96),
+                    dict(decode_waves=3), dict(groups_per_cu=17), dict(solo_tokens=-1)):
+            with pytest.raises(binding.PagedKVError, match="UNSUPPORTED"):
+                binding.set_tuning(**bad)
+            assert binding.get_tuning() == before
+        binding.set_tuning(solo_tokens=1)
+        assert binding.get_tuning()["solo_tokens"] == 1
+        binding.set_tuning(solo_tokens=1024, chunk_min=32, chunk_max=2048)
+        t = binding.get_tuning()
+        assert (t["solo_tokens"], t["chunk_min"], t["chunk_max"]) == (1024, 32, 2048)
+    finally:
+        binding.set_tuning(**before)
+    assert binding.get_tuning() == before

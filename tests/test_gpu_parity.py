@@ -435,6 +435,54 @@ def test_long_chunks_across_block_sizes(case):
         binding.set_tuning(**before)
 
 
+MIXED = [1, 31, 255, 256, 257, 600, 1023, 1025, 0, 4100]
+SOLO_CASES = [
+    # lens, query_len, heads, kv_heads, head_dim, block_size, dtype, layout, tuning: chunks
+    # above and below solo_tokens, so both phases of the vector-unit decode run (the
+    # short ones one wave each, back to back)
+    (MIXED, 1, 8, 8, 128, 16, "bf16", "HND", dict(solo_tokens=256)),
+    # 128-token chunks under a 1024 bound: every item single-wave, split rows included
+    (MIXED, 1, 8, 8, 128, 16, "bf16", "HND", dict(solo_tokens=1024, chunk_min=128,
+                                                  chunk_max=128)),
+    # four query heads per item on the vector units, float32
+    (MIXED, 1, 8, 2, 128, 16, "f32", "NHD", dict(solo_tokens=512, mfma=2)),
+    # 4-token sub-chunks: a 1023-token item spans four id registers of one wave
+    (MIXED, 1, 4, 4, 256, 32, "f32", "HND", dict(solo_tokens=1024)),
+    (MIXED, 1, 4, 4, 64, 16, "bf16", "HND", dict(solo_tokens=128, staging=1)),
+    (MIXED, 1, 8, 8, 128, 64, "bf16", "HND", dict(solo_tokens=256, decode_waves=1)),
+    (MIXED, 1, 8, 8, 128, 16, "bf16", "HND", dict(solo_tokens=32, decode_waves=4)),
+    (MIXED, 1, 8, 8, 128, 16, "bf16", "HND", dict(solo_tokens=1)),
+    # several new tokens: causal limits inside single-wave items
+    ([4, 40, 300, 700, 0], 4, 4, 4, 128, 16, "bf16", "HND", dict(solo_tokens=1024, mfma=2)),
+    ([2, 33, 129, 1000], 2, 8, 8, 128, 16, "f32", "HND", dict(solo_tokens=256,
+                                                             chunk_min=64, chunk_max=64)),
+]
+
+
+@pytest.mark.parametrize("case", SOLO_CASES,
+                         ids=lambda c: f"{c[6]}-d{c[4]}-bs{c[5]}-h{c[2]}/{c[3]}-q{c[1]}-" +
+                         "-".join(f"{k}{v}" for k, v in c[8].items()))
+def test_single_wave_items(case):
+    """Chunks shorter than solo_tokens are read one wave each; every output against the
+    oracle for every bound, sub-chunk width, staging path and query group."""
+    lens, n_q, h, hkv, d, bs, dtype, layout, tuning = case
+    w = wl.make_custom(lens, heads=h, kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype,
+                       layout=layout, query_len=n_q, seed=sum(lens) + d + bs + n_q)
+    before = binding.get_tuning()
+    binding.set_tuning(**tuning)
+    try:
+        if n_q == 1:
+            check_full(w)
+        else:
+            st = Step(w, host_history=True)
+            got = _multi_run(w, st)
+            ref = _multi_oracle(w, st.k_host, st.v_host)
+            assert_close(to_host(got, dtype), ref, dtype, w.name)
+    finally:
+        binding.set_tuning(**before)
+    assert binding.device_status(DEV, clear=True) == 0
+
+
 GQA_CASES = [
     # lens, heads, kv_heads, head_dim, dtype, layout: query groups 8, 4, 2 and 16 (two items)
     ([700, 1, 0, 2049, 31], 16, 2, 128, "bf16", "HND"),
