@@ -25,8 +25,8 @@ constexpr int kDefaultLdsStage = 1;
 constexpr int kDefaultMaxQueryGroup = 16;
 constexpr int kDefaultMfma = 1;
 constexpr int kDefaultGroupsPerCu = 16;   // i.e. as many as fit
-// Chunks shorter than this many tokens are read by one wave alone (the plan puts them
-// last); at most kMaxSoloTokens.  1: none.
+// Chunks shorter than this many tokens are read by one wave alone (they end the work
+// list, and the decode kernel reads them first); at most kMaxSoloTokens.  1: none.
 constexpr int kDefaultSoloTokens = 512;
 constexpr int kMaxSoloTokens = 1024;
 // ... and only when there are at least this many of them per decode wave
@@ -113,7 +113,7 @@ struct AttnArgs {
   int32_t deal_static;     // 1: whole rounds of full chunks are dealt without the queue
   int32_t query_group;     // query vectors per work item (they share one KV head)
   int32_t query_len;       // new tokens (queries) per row: 1 for decode
-  int32_t solo_tokens;     // chunks shorter than this go last, one wave each (0: none)
+  int32_t solo_tokens;     // chunks shorter than this are read one wave each (0, 1: none)
   int32_t group_waves;     // waves per decode workgroup
   float scale;
   // slot input only (else null / 0): [rows][flag_stride], nonzero where a row's live

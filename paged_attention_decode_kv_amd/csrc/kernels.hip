@@ -12,7 +12,7 @@
 //                       block table in 16-token sub-chunks and folds them into online
 //                       softmax states on the vector units (Day 59, "the rectangle the
 //                       read builds, and the tile that replaces it", "What I added today"
-//                       and "What I learned" 3-4)
+//                       and "What I learned" 3-4); short chunks go one wave each
 //   decode_mfma_kernel  the same schedule for groups of 4, 8 or 16 query vectors per
 //                       KV head, whose fold is a pair of small matrix products on the
 //                       matrix cores
@@ -816,15 +816,16 @@ __host__ __device__ constexpr int solo_id_regs(int ch) {
 // next item's metadata and the ticket after it are fetched while the current item
 // streams.
 //
-// Single-wave items: chunks shorter than a.solo_tokens (the end of section B; the plan
-// keeps them only when there are at least kSoloPerWave for every wave) are read first,
-// by one wave each, dealt round robin over every wave of the launch.  A short chunk
-// shared by 8 waves leaves most of them idle at its last round and pays a workgroup
-// merge and barrier per few sub-chunks; alone, a wave streams its items back to back:
-// the next item's metadata loads while the current one streams, and its first
-// sub-chunk is staged while the current item's last one is folded.  A single wave
-// takes ~8x as long over one item, so these go before the wide items, whose shared
-// queue evens out the workgroups' finishing times.
+// Single-wave items: chunks shorter than a.solo_tokens (the tail of section B, or every
+// item when the chunk length itself is shorter; the plan keeps them only when there are
+// at least kSoloPerWave for every wave) are read first, by one wave each, dealt round
+// robin over every wave of the launch.  A short chunk shared by 8 waves leaves most of
+// them idle at its last round and pays a workgroup merge and barrier per few
+// sub-chunks; alone, a wave streams its items back to back: the next item's metadata
+// loads while the current one streams, and its first sub-chunk is staged while the
+// current item's last one is folded.  A single wave takes ~8x as long over one item, so
+// these go before the wide items, whose shared queue evens out the workgroups'
+// finishing times.
 //
 // Padding rows (section C) are zeroed round robin at the end.
 template <typename T, int D, int WAVES, bool LDS_STAGE, int QG>
@@ -1889,7 +1890,7 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   pa.narrow_groups = grid > narrow ? (int32_t)narrow : 0;
   pa.narrow_items = pa.narrow_groups * per_group;
   pa.deal_static = tuning_deal_static();
-  pa.solo_tokens = MFMA ? 0 : tuning_solo_tokens();   // the matrix-core kernel has no solo phase
+  pa.solo_tokens = MFMA ? 0 : tuning_solo_tokens();   // no single-wave phase on the matrix cores
   pa.group_waves = WAVES;
   timing_begin(PKV_PHASE_PLAN, stream);
   if (write) {   // the step's scatter rides along with the plan
