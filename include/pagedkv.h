@@ -278,8 +278,7 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *   solo_tokens           chunks of fewer than this many tokens are read first, by one
  *                         wave each, with no merge across the waves of a workgroup,
  *                         when there is at least one such chunk per decode wave: a power
- *                         of two in [32, 1024], or 1 for none (default 512; the
- *                         vector-unit kernel only)
+ *                         of two in [32, 1024], or 1 for none (default 512)
  * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it
  * before sizing workspaces.  Results do not depend on these values beyond float32
  * rounding order.  Returns UNSUPPORTED for other values. */

@@ -1187,9 +1187,79 @@ __device__ __forceinline__ MfmaMeta<D, NR> finish_meta_mfma(const AttnArgs& a, i
   return m;
 }
 
+// Scores of one staged 16-token tile for the lane's vector (S^T = K . Q^T: lane
+// (col, grp) gets tokens 4 grp .. 4 grp + 3 of vector col) and the tile's V^T operands,
+// both read from a wave's stage.
+template <int D>
+__device__ __forceinline__ f32x4_t mfma_tile_scores(const char* st_k, const char* st_v,
+                                                    const int (&k_off)[D / 32],
+                                                    const int (&v_off)[D / 16],
+                                                    const uint4 (&q)[D / 32],
+                                                    i16x4_t (&vt)[D / 16]) {
+  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+    const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(st_k + k_off[ds]);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, __builtin_bit_cast(bf16x8_t, q[ds]), sc,
+                                                 0, 0, 0);
+  }
+#pragma unroll
+  for (int o = 0; o < D / 16; ++o) vt[o] = lds_read_tr16(st_v + v_off[o]);
+  return sc;
+}
+
+// Online-softmax fold of one tile into the lane's vector state: `vis` of the tile's
+// tokens are visible to it; the row groups share the tile's maximum, and each keeps its
+// own share of the denominator.  P goes in as two bfloat16 parts (hi + the rounding
+// residue).
+template <int NO>
+__device__ __forceinline__ void mfma_tile_fold(f32x4_t sc, const i16x4_t (&vt)[NO], int vis,
+                                               int grp, float scale_log2, float& m, float& l,
+                                               f32x4_t (&acc)[NO]) {
+  float x[4], tmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = 4 * grp + e < vis ? sc[e] * scale_log2 : -INFINITY;
+    tmax = fmaxf(tmax, x[e]);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(m, tmax);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+  l *= alpha;
+#pragma unroll
+  for (int o = 0; o < NO; ++o) acc[o] *= alpha;
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+    l += p[e];
+  }
+  const uint32_t h01 = Elem<uint16_t>::cvt2(p[0], p[1]);
+  const uint32_t h23 = Elem<uint16_t>::cvt2(p[2], p[3]);
+  const uint32_t l01 = Elem<uint16_t>::cvt2(p[0] - __uint_as_float(h01 << 16),
+                                            p[1] - __uint_as_float(h01 & 0xffff0000u));
+  const uint32_t l23 = Elem<uint16_t>::cvt2(p[2] - __uint_as_float(h23 << 16),
+                                            p[3] - __uint_as_float(h23 & 0xffff0000u));
+  const i16x4_t ph = __builtin_bit_cast(i16x4_t, make_uint2(h01, h23));
+  const i16x4_t pl = __builtin_bit_cast(i16x4_t, make_uint2(l01, l23));
+#pragma unroll
+  for (int o = 0; o < NO; ++o) {
+    acc[o] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[o], ph, acc[o], 0, 0, 0);
+    acc[o] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[o], pl, acc[o], 0, 0, 0);
+  }
+  m = m_new;
+}
+
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
+
 // Same schedule, staging and partial records as decode_kernel (bfloat16 pools, head_dim
-// 64 or 128, sub-chunks of 16 tokens).  After its last fold a wave parks its state,
-// [QG][D] floats, in its own stage, and the waves are merged from there.
+// 64 or 128, sub-chunks of 16 tokens), single-wave items first.  A single wave's tiles
+// hold whole vectors (lane (col, grp): dims 16 o + 4 grp .. + 3 of vector col), so it
+// writes its item's result from registers.  After its last fold of a wide item a wave
+// parks its state, [QG][D] floats, in its own stage, and the waves are merged from
+// there.
 template <int D, int WAVES, int QG>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
@@ -1228,11 +1298,12 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int vpkv = n_vec / a.g.kv_heads;
   const int lp = ws.counters[3];
   const int P = 1 << lp;
-  const int n_static = ws.counters[4] * groups;
+  const int n_wide = ws.counters[10] * groups;    // items before the single-wave ones
   const int n_data = ws.counters[5] * groups;
   const int n_items = ws.counters[0] * groups;
   const int G = ws.counters[7];                  // workgroups taking part
   if ((int)blockIdx.x >= G) return;
+  const int n_static = min(ws.counters[4] * groups, n_wide);
   const int n_dealt = a.deal_static ? n_static / G * G : 0;
   const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
@@ -1262,102 +1333,146 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 #pragma unroll
   for (int o = 0; o < NO; ++o) v_off[o] = at(4 * grp + (col >> 2), 16 * o + 4 * (col & 3));
 
+  bool bad_block = false;
+  // addressing of an item's sub-chunks (fields wave-uniform: scalar descriptors)
+  auto chunk_addr = [&](int chunk, int hg, int ctx) {
+    const int t_begin = chunk * P;
+    return ChunkAddr{kpool, vpool, (int64_t)(hg * QG / vpkv) * head_bytes, blk_bytes,
+                     tok_bytes, t_begin, min(ctx, t_begin + P), bs_mask, a.g.num_blocks};
+  };
+  // this wave's stage <- sub-chunk s (the wave's i-th) of an item
+  auto stage_in = [&](const ChunkAddr& c, int s, int i, const auto& blk) {
+    __amdgpu_buffer_rsrc_t ksrc, vsrc;
+    c.describe<CH>(s, i, ksrc, vsrc, bad_block, blk);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      buffer_load16_lds(ksrc, voff[u], reinterpret_cast<uint4*>(&s_stage[wave][u * 1024]));
+      buffer_load16_lds(vsrc, voff[u], reinterpret_cast<uint4*>(&s_stage[wave][(U + u) * 1024]));
+    }
+  };
+
+  // ---- single-wave items first (see decode_kernel) ----
+  {
+    constexpr int NRS = solo_id_regs(16);
+    using MetaS = MfmaMeta<D, NRS>;
+    const int stride = G * WAVES;
+    int it = n_wide + (int)blockIdx.x * WAVES + wave;
+    MetaS sc_m;
+    int4 ent_nx = make_int4(0, -1, 0, 0);
+    if (it < n_data) {
+      sc_m = finish_meta_mfma<D, QG, NRS, 1>(a, issue_entry(ws, it, groups), it, lp, log2_bs,
+                                             lane, 0);
+      if (it + stride < n_data) ent_nx = issue_entry(ws, it + stride, groups);
+    }
+    bool staged = false;   // the item's first sub-chunk is already in the stage
+    while (it < n_data) {
+      const int nx = it + stride;
+      // the next item's query and block ids, and the entry after it, load while this
+      // item streams
+      MetaS sn = finish_meta_mfma<D, QG, NRS, 1>(a, ent_nx, nx, lp, log2_bs, lane, 0);
+      ent_nx = nx + stride < n_data ? issue_entry(ws, nx + stride, groups)
+                                    : make_int4(0, -1, 0, 0);
+      const int chunk = __builtin_amdgcn_readfirstlane(sc_m.chunk);
+      const int hg = __builtin_amdgcn_readfirstlane(sc_m.hg);
+      const ChunkAddr ca = chunk_addr(chunk, hg, __builtin_amdgcn_readfirstlane(sc_m.ctx));
+      const int last_rel = sc_m.last - ca.t_begin;
+      f32x4_t acc[NO];
+#pragma unroll
+      for (int o = 0; o < NO; ++o) acc[o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      float m = -INFINITY, l = 0.f;
+      const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
+      if (!staged) stage_in(ca, 0, 0, sc_m.blk);
+      staged = false;
+      for (int s = 0; s < n_sub; ++s) {
+        __amdgpu_buffer_rsrc_t ksrc, vsrc;
+        const int nvalid = ca.describe<CH>(s, s, ksrc, vsrc, bad_block, sc_m.blk);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);          // the stage has landed
+        i16x4_t vt[NO];
+        const f32x4_t sc = mfma_tile_scores<D>(st_k, st_v, k_off, v_off, sc_m.q, vt);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // stage read before it is refilled
+        if (s + 1 < n_sub) {
+          stage_in(ca, s + 1, s + 1, sc_m.blk);
+        } else if (nx < n_data) {   // the next item's first sub-chunk
+          stage_in(chunk_addr(__builtin_amdgcn_readfirstlane(sn.chunk),
+                              __builtin_amdgcn_readfirstlane(sn.hg),
+                              __builtin_amdgcn_readfirstlane(sn.ctx)),
+                   0, 0, sn.blk);
+          staged = true;
+        }
+        mfma_tile_fold<NO>(sc, vt, min(nvalid, last_rel - s * CH + 1), grp, scale_log2, m, l,
+                           acc);
+      }
+      l += __shfl_xor(l, 16);        // the four row groups' denominators
+      l += __shfl_xor(l, 32);
+      if (col < QG) {
+        const int v = hg * QG + col;
+        if (sc_m.nch == 1) {
+          const float inv = l > 0.f ? 1.0f / l : 0.f;
+          T* op = static_cast<T*>(a.out) + vec_slot(a, sc_m.r, v) * D + 4 * grp;
+#pragma unroll
+          for (int o = 0; o < NO; ++o)
+            store_out(reinterpret_cast<u32x2_nt*>(op + 16 * o),
+                      u32x2_nt{Elem<uint16_t>::cvt2(acc[o][0] * inv, acc[o][1] * inv),
+                               Elem<uint16_t>::cvt2(acc[o][2] * inv, acc[o][3] * inv)});
+        } else {
+          float* rec = ws.partials +
+                       (((int64_t)sc_m.r * n_vec + v) * ws.max_chunks + chunk) * (D + 4);
+          if (grp == 0) {
+            rec[0] = m;
+            rec[1] = l;
+          }
+#pragma unroll
+          for (int o = 0; o < NO; ++o)
+            store16(rec + 4 + 16 * o + 4 * grp,
+                    make_uint4(__float_as_uint(acc[o][0]), __float_as_uint(acc[o][1]),
+                               __float_as_uint(acc[o][2]), __float_as_uint(acc[o][3])));
+        }
+      }
+      it = nx;
+      sc_m = sn;
+    }
+  }
+
+  // ---- wide items: the workgroup's waves share each one ----
   ItemOrder order{(int)blockIdx.x, G, n_dealt};
   int item, next;
   order.first_two(item, next, &ws.counters[1], s_ticket);
   int buf = 0;
-  bool bad_block = false;
   Meta cur;
-  if (item < n_data)
+  if (item < n_wide)
     cur = finish_meta_mfma<D, QG, NR, WAVES>(a, issue_entry(ws, item, groups), item, lp,
                                              log2_bs, lane, wave);
 
-  while (item < n_data) {
+  while (item < n_wide) {
     int after = 0;
     const bool after_static = order.take(after);
     if (!after_static && threadIdx.x == 0) after = atomicAdd(&ws.counters[1], 1);
     int4 next_ent = make_int4(0, -1, 0, 0);
-    if (next < n_data) next_ent = issue_entry(ws, next, groups);
+    if (next < n_wide) next_ent = issue_entry(ws, next, groups);
 
     const int chunk = __builtin_amdgcn_readfirstlane(cur.chunk);
     const int hg = __builtin_amdgcn_readfirstlane(cur.hg);
-    const int t_begin = chunk * P;
-    const int t_end = min(__builtin_amdgcn_readfirstlane(cur.ctx), t_begin + P);
-    const int64_t head_off = (int64_t)(hg * QG / vpkv) * head_bytes;
-    const int last_rel = cur.last - t_begin;      // this lane's vector
+    const ChunkAddr ca = chunk_addr(chunk, hg, __builtin_amdgcn_readfirstlane(cur.ctx));
+    const int last_rel = cur.last - ca.t_begin;      // this lane's vector
 
     f32x4_t acc[NO];
 #pragma unroll
     for (int o = 0; o < NO; ++o) acc[o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
-    const int n_sub = (t_end - t_begin + CH - 1) / CH;
-    const ChunkAddr ca{kpool, vpool, head_off, blk_bytes, tok_bytes, t_begin, t_end,
-                 bs_mask, a.g.num_blocks};
-    auto stage_in = [&](int s) {
-      __amdgpu_buffer_rsrc_t ksrc, vsrc;
-      ca.describe<CH>(s, (s - wave) / WAVES, ksrc, vsrc, bad_block, cur.blk);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        buffer_load16_lds(ksrc, voff[u], reinterpret_cast<uint4*>(&s_stage[wave][u * 1024]));
-        buffer_load16_lds(vsrc, voff[u],
-                          reinterpret_cast<uint4*>(&s_stage[wave][(U + u) * 1024]));
-      }
-    };
-    if (wave < n_sub) stage_in(wave);
+    const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
+    if (wave < n_sub) stage_in(ca, wave, 0, cur.blk);
     for (int s = wave; s < n_sub; s += WAVES) {
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
-      const int nvalid = ca.describe<CH>(s, (s - wave) / WAVES, ksrc, vsrc, bad_block, cur.blk);
+      const int i = (s - wave) / WAVES;
+      const int nvalid = ca.describe<CH>(s, i, ksrc, vsrc, bad_block, cur.blk);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);          // this wave's stage has landed
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < NS; ++ds) {
-        const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(st_k + k_off[ds]);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, __builtin_bit_cast(bf16x8_t, cur.q[ds]),
-                                                     sc, 0, 0, 0);
-      }
       i16x4_t vt[NO];
-#pragma unroll
-      for (int o = 0; o < NO; ++o) vt[o] = lds_read_tr16(st_v + v_off[o]);
+      const f32x4_t sc = mfma_tile_scores<D>(st_k, st_v, k_off, v_off, cur.q, vt);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);        // stage read before it is refilled
-      if (s + WAVES < n_sub) stage_in(s + WAVES);
-
-      // online softmax of this tile for the lane's vector (tokens 4 grp .. 4 grp + 3)
-      const int vis = min(nvalid, last_rel - s * CH + 1);
-      float x[4], tmax = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = 4 * grp + e < vis ? sc[e] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[e]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      l *= alpha;
-#pragma unroll
-      for (int o = 0; o < NO; ++o) acc[o] *= alpha;
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
-        l += p[e];
-      }
-      const uint32_t h01 = Elem<uint16_t>::cvt2(p[0], p[1]);
-      const uint32_t h23 = Elem<uint16_t>::cvt2(p[2], p[3]);
-      const uint32_t l01 = Elem<uint16_t>::cvt2(p[0] - __uint_as_float(h01 << 16),
-                                                p[1] - __uint_as_float(h01 & 0xffff0000u));
-      const uint32_t l23 = Elem<uint16_t>::cvt2(p[2] - __uint_as_float(h23 << 16),
-                                                p[3] - __uint_as_float(h23 & 0xffff0000u));
-      const i16x4_t ph = __builtin_bit_cast(i16x4_t, make_uint2(h01, h23));
-      const i16x4_t pl = __builtin_bit_cast(i16x4_t, make_uint2(l01, l23));
-#pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        acc[o] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[o], ph, acc[o], 0, 0, 0);
-        acc[o] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[o], pl, acc[o], 0, 0, 0);
-      }
-      m = m_new;
+      if (s + WAVES < n_sub) stage_in(ca, s + WAVES, i + 1, cur.blk);
+      mfma_tile_fold<NO>(sc, vt, min(nvalid, last_rel - s * CH + 1), grp, scale_log2, m, l,
+                         acc);
     }
 
     const Meta nxt = finish_meta_mfma<D, QG, NR, WAVES>(a, next_ent, next, lp, log2_bs, lane,
@@ -1890,7 +2005,7 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   pa.narrow_groups = grid > narrow ? (int32_t)narrow : 0;
   pa.narrow_items = pa.narrow_groups * per_group;
   pa.deal_static = tuning_deal_static();
-  pa.solo_tokens = MFMA ? 0 : tuning_solo_tokens();   // no single-wave phase on the matrix cores
+  pa.solo_tokens = tuning_solo_tokens();
   pa.group_waves = WAVES;
   timing_begin(PKV_PHASE_PLAN, stream);
   if (write) {   // the step's scatter rides along with the plan

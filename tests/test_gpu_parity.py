@@ -435,52 +435,103 @@ def test_long_chunks_across_block_sizes(case):
         binding.set_tuning(**before)
 
 
-MIXED = [1, 31, 255, 256, 257, 600, 1023, 1025, 0, 4100]
+def _solo_lens(n_short, n_long, seed, short_max=300, low=1):
+    """Many short rows (below the single-wave bound), a few long ones and two pad rows."""
+    rng = np.random.default_rng(seed)
+    lens = np.concatenate([rng.integers(low, short_max, n_short),
+                           rng.integers(600, 1600, n_long), [0, 0]])
+    rng.shuffle(lens)
+    return [int(x) for x in lens]
+
+
 SOLO_CASES = [
-    # lens, query_len, heads, kv_heads, head_dim, block_size, dtype, layout, tuning: chunks
-    # above and below solo_tokens, so both phases of the vector-unit decode run (the
-    # short ones one wave each, back to back)
-    (MIXED, 1, 8, 8, 128, 16, "bf16", "HND", dict(solo_tokens=256)),
+    # name, lens, query_len, heads, kv_heads, head_dim, block_size, dtype, layout, tuning.
+    # The test pins 256 workgroups (groups_per_cu 1), and every case has at least one
+    # short chunk per wave (>= 2048 for 8-wave workgroups), so the plan keeps the
+    # single-wave phase; the long rows still go through the shared 8-wave items.
+    ("vec-bf16", _solo_lens(560, 8, 1), 1, 4, 4, 128, 16, "bf16", "HND",
+     dict(solo_tokens=512)),
     # 128-token chunks under a 1024 bound: every item single-wave, split rows included
-    (MIXED, 1, 8, 8, 128, 16, "bf16", "HND", dict(solo_tokens=1024, chunk_min=128,
-                                                  chunk_max=128)),
+    ("vec-bf16-all", _solo_lens(100, 40, 2), 1, 4, 4, 128, 16, "bf16", "HND",
+     dict(solo_tokens=1024, chunk_min=128, chunk_max=128)),
     # four query heads per item on the vector units, float32
-    (MIXED, 1, 8, 2, 128, 16, "f32", "NHD", dict(solo_tokens=512, mfma=2)),
-    # 4-token sub-chunks: a 1023-token item spans four id registers of one wave
-    (MIXED, 1, 4, 4, 256, 32, "f32", "HND", dict(solo_tokens=1024)),
-    (MIXED, 1, 4, 4, 64, 16, "bf16", "HND", dict(solo_tokens=128, staging=1)),
-    (MIXED, 1, 8, 8, 128, 64, "bf16", "HND", dict(solo_tokens=256, decode_waves=1)),
-    (MIXED, 1, 8, 8, 128, 16, "bf16", "HND", dict(solo_tokens=32, decode_waves=4)),
-    (MIXED, 1, 8, 8, 128, 16, "bf16", "HND", dict(solo_tokens=1)),
+    ("vec-f32-gqa4", _solo_lens(1100, 8, 3), 1, 8, 2, 128, 16, "f32", "NHD",
+     dict(solo_tokens=512, mfma=2)),
+    # 4-token sub-chunks: items of up to 1023 tokens span four id registers of one wave
+    ("vec-f32-d256", _solo_lens(140, 2, 4, short_max=1024), 1, 2, 2, 256, 32, "f32", "HND",
+     dict(solo_tokens=1024, decode_waves=1)),
+    ("vec-d64-registers", _solo_lens(560, 8, 5, short_max=128), 1, 4, 4, 64, 16, "bf16",
+     "HND", dict(solo_tokens=128, staging=1)),
+    ("vec-one-wave", _solo_lens(300, 4, 6, short_max=256), 1, 4, 4, 128, 64, "bf16", "HND",
+     dict(solo_tokens=256, decode_waves=1)),
+    ("vec-four-waves", _solo_lens(300, 4, 7, short_max=64), 1, 4, 4, 128, 16, "bf16", "HND",
+     dict(solo_tokens=64, decode_waves=4)),
+    ("vec-off", _solo_lens(560, 8, 1), 1, 4, 4, 128, 16, "bf16", "HND", dict(solo_tokens=1)),
     # several new tokens: causal limits inside single-wave items
-    ([4, 40, 300, 700, 0], 4, 4, 4, 128, 16, "bf16", "HND", dict(solo_tokens=1024, mfma=2)),
-    ([2, 33, 129, 1000], 2, 8, 8, 128, 16, "f32", "HND", dict(solo_tokens=256,
-                                                             chunk_min=64, chunk_max=64)),
+    ("vec-q2-f32", _solo_lens(300, 4, 8, low=2), 2, 4, 4, 128, 16, "f32", "HND",
+     dict(solo_tokens=256, chunk_min=64, chunk_max=64)),
+    ("vec-q4", _solo_lens(560, 4, 9, low=4), 4, 4, 4, 128, 16, "bf16", "HND",
+     dict(solo_tokens=1024, mfma=2)),
+    # the matrix cores: 4, 8 and 16 vectors per item, written from one wave's tiles
+    ("mfma-gqa4", _solo_lens(560, 8, 10), 1, 16, 4, 128, 16, "bf16", "HND",
+     dict(solo_tokens=512)),
+    ("mfma-gqa16-d64", _solo_lens(1100, 4, 11), 1, 32, 2, 64, 16, "bf16", "NHD",
+     dict(solo_tokens=512)),
+    ("mfma-q4", _solo_lens(560, 4, 12, low=4), 4, 4, 4, 128, 16, "bf16", "HND",
+     dict(solo_tokens=1024)),
+    ("mfma-gqa4-split", _solo_lens(200, 30, 13), 1, 16, 4, 128, 32, "bf16", "HND",
+     dict(solo_tokens=1024, chunk_min=128, chunk_max=128)),
 ]
 
 
-@pytest.mark.parametrize("case", SOLO_CASES,
-                         ids=lambda c: f"{c[6]}-d{c[4]}-bs{c[5]}-h{c[2]}/{c[3]}-q{c[1]}-" +
-                         "-".join(f"{k}{v}" for k, v in c[8].items()))
+def _oracle_by_rows(w, k_host, v_host, cells=1 << 23):
+    """The oracle's step over a large batch: one scatter, then the read a few rows at a
+    time (a row's output depends on that row alone), rows of similar length together so
+    that each call's rectangle stays narrow."""
+    kw, vw = k_host.copy(), v_host.copy()
+    oracle.kv_write(kw, vw, w.k_new, w.v_new, w.slot_mapping, num_blocks=w.num_blocks,
+                    block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+    read = oracle.paged_attention if w.query_len == 1 else oracle.paged_attention_multi
+    per_row = w.heads * w.head_dim * w.query_len
+    out = np.zeros(w.q.shape)
+    order = np.argsort(w.context_lens, kind="stable")
+    at = 0
+    while at < w.rows:
+        end = at + 1
+        while end < w.rows and (end + 1 - at) * max(1, int(w.context_lens[order[end]])) * \
+                per_row <= cells:
+            end += 1
+        part = order[at:end]
+        out[part] = read(w.q[part], kw, vw, w.block_tables[part], w.context_lens[part],
+                         w.scale, num_blocks=w.num_blocks, block_size=w.block_size,
+                         layout=w.layout, dtype=w.dtype)
+        at = end
+    return out, kw, vw
+
+
+@pytest.mark.parametrize("case", SOLO_CASES, ids=[c[0] for c in SOLO_CASES])
 def test_single_wave_items(case):
-    """Chunks shorter than solo_tokens are read one wave each; every output against the
-    oracle for every bound, sub-chunk width, staging path and query group."""
-    lens, n_q, h, hkv, d, bs, dtype, layout, tuning = case
+    """Chunks shorter than solo_tokens are read one wave each, before the shared items;
+    every output against the oracle for every bound, sub-chunk width, staging path,
+    query group and kernel."""
+    name, lens, n_q, h, hkv, d, bs, dtype, layout, tuning = case
     w = wl.make_custom(lens, heads=h, kv_heads=hkv, head_dim=d, block_size=bs, dtype=dtype,
-                       layout=layout, query_len=n_q, seed=sum(lens) + d + bs + n_q)
+                       layout=layout, query_len=n_q, seed=zlib.crc32(name.encode()))
+    say(f"{name}: rows {w.rows} heads {h}/{hkv} d {d} q {n_q} {dtype} {layout} {tuning}")
     before = binding.get_tuning()
-    binding.set_tuning(**tuning)
+    binding.set_tuning(groups_per_cu=1, **tuning)
     try:
-        if n_q == 1:
-            check_full(w)
-        else:
-            st = Step(w, host_history=True)
-            got = _multi_run(w, st)
-            ref = _multi_oracle(w, st.k_host, st.v_host)
-            assert_close(to_host(got, dtype), ref, dtype, w.name)
+        st = Step(w, host_history=True)
+        got = st.run() if n_q == 1 else _multi_run(w, st)
     finally:
         binding.set_tuning(**before)
     assert binding.device_status(DEV, clear=True) == 0
+    ref, kw, vw = _oracle_by_rows(w, st.k_host, st.v_host)
+    assert_close(to_host(got, dtype), ref, dtype, name)
+    ints = np.uint16 if dtype == "bf16" else np.uint32
+    for dev_pool, want in ((st.k_cache, kw), (st.v_cache, vw)):
+        got_pool = to_host(dev_pool, dtype)
+        assert np.array_equal(got_pool[:w.num_blocks].view(ints), want[:w.num_blocks].view(ints))
 
 
 GQA_CASES = [
