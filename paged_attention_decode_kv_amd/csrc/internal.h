@@ -80,12 +80,14 @@ struct Workspace {
                         // [6] rows read token by token (slot input),
                         // [7] decode workgroups that take part (the rest exit at once),
                         // [8] rows split into more than one chunk,
-                        // [9] most chunks of a row read token by token (slot input),
+                        // [9] entries of the rows read token by token (slot input),
                         // [10] entries before the single-wave items (chunks shorter
-                        // than AttnArgs::solo_tokens)
+                        // than AttnArgs::solo_tokens), [11] token queue ticket
   int32_t* row_ctx;     // [rows]: each row's length as the block path reads it
   int32_t* irregular;   // [rows]: the rows read token by token, counters[6] of them
   int2* split_rows;     // [rows]: {row, length} of the rows split into chunks, counters[8]
+  int2* token_entries;  // slot input only (else null): [rows * max_chunks] {row, chunk} of
+                        // the rows read token by token, longest chunk first, counters[9]
   float* partials;      // [rows][heads][max_chunks][head_dim + 4]: m (log2 units), l, -, -, acc
   int64_t max_entries;
   int32_t max_chunks;

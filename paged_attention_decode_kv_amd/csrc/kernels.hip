@@ -291,10 +291,10 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 // [4] = entries in section A, [5] = entries in sections A and B, [6] = rows of a slot
 // input left to the token-by-token kernel (listed in ws.irregular), [7] = decode
 // workgroups that take part, [8] = split rows (listed with their lengths in
-// ws.split_rows for the combine kernel), [9] = most chunks of a row read token by
-// token, [10] = entries before the single-wave items (those of fewer than
-// a.solo_tokens tokens, the tail of the longest-first order).  Every row's clamped
-// length goes to ws.row_ctx.
+// ws.split_rows for the combine kernel), [9] = entries of the rows read token by token
+// (ws.token_entries), [10] = entries before the single-wave items (those of fewer than
+// a.solo_tokens tokens, the tail of the longest-first order), [11] = the token kernel's
+// queue ticket (reset to 0).  Every row's clamped length goes to ws.row_ctx.
 __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   constexpr int kCand = 7;                 // chunk_max / chunk_min <= kMaxChunkRatio
   static_assert((1 << (kCand - 1)) == kMaxChunkRatio, "one candidate per power of two");
@@ -309,7 +309,6 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   __shared__ int s_pad_fill;
   __shared__ int s_irregular;
   __shared__ int s_split;
-  __shared__ int s_irr_chunks;
   __shared__ int s_cand[kCand];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -318,7 +317,6 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     s_pad_fill = 0;
     s_irregular = 0;
     s_split = 0;
-    s_irr_chunks = 0;
   }
   __syncthreads();
 
@@ -444,7 +442,6 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     const int nch = (ctx + P - 1) >> lp;
     const int full = a.row_flags != nullptr ? ws.row_ctx[r] : ctx;
     if (full > P) ws.split_rows[atomicAdd(&s_split, 1)] = make_int2((int)r, full);
-    if (full != ctx) atomicMax(&s_irr_chunks, (full + P - 1) >> lp);   // a token-by-token row
     if (rem != 0) {
       const int pos = total_a + s_bin_start[rem >> bshift] +
                       atomicAdd(&s_bin_fill[rem >> bshift], 1);
@@ -455,23 +452,63 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     }
   }
   __syncthreads();
-  if (t == 0) {
-    // entries before the single-wave items: section A if its chunks are not short, and
-    // the B bins of remainders >= solo_tokens (bin b holds [b, b + 1) << bshift, and
-    // solo_tokens is a multiple of 1 << bshift: a power of two >= 32 against <= 8)
-    int n_wide = total_a + total_b;
-    if (a.solo_tokens > 1) {
-      if (P < a.solo_tokens) {
-        n_wide = 0;
-      } else {
-        const int tb = a.solo_tokens >> bshift;   // first bin of the long remainders
-        n_wide = total_a + (tb >= nbins ? 0 : s_bin_start[tb - 1]);
-      }
-      // too few to keep every wave streaming: all items go wide
-      const int64_t waves = (int64_t)(narrow ? a.narrow_groups : a.grid_groups) * a.group_waves;
-      if ((int64_t)(total_a + total_b - n_wide) * per_entry < kSoloPerWave * waves)
-        n_wide = total_a + total_b;
+  // Entries before the single-wave items: section A if its chunks are not short, and
+  // the B bins of remainders >= solo_tokens (bin b holds [b, b + 1) << bshift, and
+  // solo_tokens is a multiple of 1 << bshift: a power of two >= 32 against <= 8).  Read
+  // from the bins before the token rows below reuse them.
+  int n_wide = total_a + total_b;
+  if (a.solo_tokens > 1) {
+    if (P < a.solo_tokens) {
+      n_wide = 0;
+    } else {
+      const int tb = a.solo_tokens >> bshift;   // first bin of the long remainders
+      n_wide = total_a + (tb >= nbins ? 0 : s_bin_start[tb - 1]);
     }
+    // too few to keep every wave streaming: all items go wide
+    const int64_t waves = (int64_t)(narrow ? a.narrow_groups : a.grid_groups) * a.group_waves;
+    if ((int64_t)(total_a + total_b - n_wide) * per_entry < kSoloPerWave * waves)
+      n_wide = total_a + total_b;
+  }
+  // The rows read token by token (slot input): their chunks, longest first, for the
+  // token kernel's shared queue, as sections A and B are for the block path: every full
+  // chunk, then the trailing partial chunks by length, descending (bins as for B).
+  int total_ta = 0, total_tb = 0;
+  const int n_irr = s_irregular;
+  if (n_irr > 0 && ws.token_entries != nullptr) {
+    if (t < nbins) s_bin_fill[t] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_irr; base += kPlanThreads) {
+      const int i = base + t;
+      const int r = i < n_irr ? ws.irregular[i] : 0;
+      const int full = i < n_irr ? ws.row_ctx[r] : 0;
+      const int nfull = full >> lp;
+      int tile;
+      const int at = total_ta + block_exclusive_scan(nfull, s_wave, &tile);
+      for (int k = 0; k < nfull; ++k) ws.token_entries[at + k] = make_int2(r, k);
+      if ((full & (P - 1)) != 0) atomicAdd(&s_bin_fill[(full & (P - 1)) >> bshift], 1);
+      total_ta += tile;
+    }
+    __syncthreads();
+    {
+      const int bin = nbins - 1 - t;
+      const int count = t < nbins ? s_bin_fill[bin] : 0;
+      const int start = block_exclusive_scan(count, s_wave, &total_tb);
+      if (t < nbins) s_bin_start[bin] = start;
+    }
+    __syncthreads();
+    if (t < nbins) s_bin_fill[t] = 0;
+    __syncthreads();
+    for (int i = t; i < n_irr; i += kPlanThreads) {
+      const int r = ws.irregular[i];
+      const int full = ws.row_ctx[r];
+      const int rem = full & (P - 1);
+      if (rem != 0)
+        ws.token_entries[total_ta + s_bin_start[rem >> bshift] +
+                         atomicAdd(&s_bin_fill[rem >> bshift], 1)] = make_int2(r, full >> lp);
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
     ws.counters[0] = total_a + total_b + n_pad;
     ws.counters[1] = 0;
     ws.counters[2] = P;
@@ -481,8 +518,9 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     ws.counters[6] = s_irregular;
     ws.counters[7] = narrow ? a.narrow_groups : a.grid_groups;
     ws.counters[8] = s_split;
-    ws.counters[9] = s_irr_chunks;
+    ws.counters[9] = total_ta + total_tb;
     ws.counters[10] = n_wide;
+    ws.counters[11] = 0;
   }
 }
 
@@ -1668,8 +1706,10 @@ __global__ void __launch_bounds__(kTranslateThreads) translate_slots_kernel(Attn
 }
 
 // The rows of a slot input that are not block structured.  An item is (chunk of a row,
-// row, query head), chunk index slowest: chunks have the decode kernel's length, and a split row
-// leaves partial records for the combine kernel just as the decode kernel does.  Each
+// query head): the plan lists these rows' chunks longest first (the decode kernel's
+// chunk length; a split row leaves partial records for the combine kernel just as the
+// decode kernel does); each workgroup takes the item of its own index first, then items
+// from one shared ticket counter, so the short ones even out the finishing times.  Each
 // 16-lane group (bf16 x 128) takes one token, loads its slot, then the token's K and V
 // through that slot, and folds it into its own online softmax; the groups and the waves
 // are merged at the end of the item.  A live slot outside the allocatable slots is
@@ -1688,6 +1728,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
   constexpr int STEP = WAVES * TPS * U;
   __shared__ float s_m[WAVES], s_l[WAVES];
   __shared__ float s_acc[WAVES][D];
+  __shared__ int s_item[2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane / LPT;
@@ -1695,8 +1736,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
   const int heads = a.num_heads;
   const int qpkv = heads / a.g.kv_heads;
   const int lp = ws.counters[3];
-  const int mch = ws.counters[9];      // most chunks of a token-by-token row
-  const int64_t n_items = (int64_t)ws.counters[6] * heads * mch;
+  const int n_items = ws.counters[9] * heads;   // (token entry, query head)
   const int64_t n_slots = a.g.num_blocks * a.g.block_size;
   const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
@@ -1706,17 +1746,21 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
   const char* kpool = static_cast<const char*>(a.k_cache);
   const char* vpool = static_cast<const char*>(a.v_cache);
   bool bad = false;
-  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    // chunk slowest: every row's first chunk comes first, so the items that exist are
-    // spread over the grid rather than bunched by the grid stride
-    const int64_t per_chunk = (int64_t)ws.counters[6] * heads;
-    const int chunk = (int)(item / per_chunk);
-    const int64_t rest = item - chunk * per_chunk;
-    const int h = (int)(rest % heads);
-    const int r = __builtin_amdgcn_readfirstlane(ws.irregular[rest / heads]);
+  // workgroup b's first item is b (one a workgroup across the grid), later ones come
+  // from the ticket counter, past the first round
+  int item = blockIdx.x;
+  int buf = 0;
+  while (item < n_items) {
+    // the next ticket, whose value is needed only at the end of this item
+    int next = 0;
+    if (threadIdx.x == 0) next = (int)gridDim.x + atomicAdd(&ws.counters[11], 1);
+    const int e = item / heads;
+    const int h = item - e * heads;
+    const int2 ent = ws.token_entries[e];
+    const int r = __builtin_amdgcn_readfirstlane(ent.x);
+    const int chunk = __builtin_amdgcn_readfirstlane(ent.y);
     const int ctx = __builtin_amdgcn_readfirstlane(ws.row_ctx[r]);
     const int nch = (ctx + (1 << lp) - 1) >> lp;
-    if (chunk >= nch) continue;            // uniform over the workgroup
     const int t_begin = chunk << lp;
     const int t_end = min(ctx, t_begin + (1 << lp));
     const int64_t rh = (int64_t)r * heads + h;
@@ -1822,6 +1866,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
         s_l[wave] = l;
       }
     }
+    if (threadIdx.x == 0) s_item[buf] = next;
     __syncthreads();
     if (wave == 0 && g == 0) {
       float mx = s_m[0];
@@ -1857,6 +1902,8 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
       }
     }
     __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item[buf]);
+    buf ^= 1;
   }
   if (bad) atomicOr(&g_status, PKV_DEVERR_SLOT);
 }
@@ -1900,6 +1947,7 @@ Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads, int32
   p += align_up(num_rows * 4, 256);
   w.split_rows = reinterpret_cast<int2*>(p);
   p += align_up(num_rows * 8, 256);
+  w.token_entries = nullptr;
   w.partials = reinterpret_cast<float*>(p);
   (void)num_heads;
   (void)head_dim;
@@ -1913,11 +1961,18 @@ static int32_t slot_flag_stride(int32_t width) {
   return (int32_t)(((int64_t)width + kTranslateTokens - 1) / kTranslateTokens);
 }
 
+// token entries of a slot input: at most every row's chunks
+static int64_t token_entry_bytes(int64_t num_rows, int32_t mb, int32_t block_size) {
+  const int64_t mc = max_chunks_for(mb, block_size, tuning_chunk_min());
+  return align_up(num_rows * (mc > 1 ? mc : 1) * 8, 256);
+}
+
 size_t slot_workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
                             int32_t width, int32_t block_size) {
   const int32_t mb = slot_table_blocks(width, block_size);
   int64_t bytes = align_up(num_rows * mb * 4, 256);
   bytes += align_up(num_rows * slot_flag_stride(width) * 4, 256);
+  bytes += token_entry_bytes(num_rows, mb, block_size);
   return (size_t)bytes + workspace_bytes(num_rows, num_heads, head_dim, mb, block_size);
 }
 
@@ -1932,7 +1987,11 @@ Workspace carve_slot_workspace(void* base, int64_t num_rows, int32_t num_heads,
   p += align_up(num_rows * mb * 4, 256);
   sa->row_flags = reinterpret_cast<int32_t*>(p);
   p += align_up(num_rows * sa->flag_stride * 4, 256);
-  return carve_workspace(p, num_rows, num_heads, head_dim, mb, block_size);
+  int2* token_entries = reinterpret_cast<int2*>(p);
+  p += token_entry_bytes(num_rows, mb, block_size);
+  Workspace w = carve_workspace(p, num_rows, num_heads, head_dim, mb, block_size);
+  w.token_entries = token_entries;
+  return w;
 }
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {

@@ -484,14 +484,20 @@ SOLO_CASES = [
 ]
 
 
-def _oracle_by_rows(w, k_host, v_host, cells=1 << 23):
+def _oracle_by_rows(w, k_host, v_host, cells=1 << 23, slot_rect=None):
     """The oracle's step over a large batch: one scatter, then the read a few rows at a
     time (a row's output depends on that row alone), rows of similar length together so
-    that each call's rectangle stays narrow."""
+    that each call's rectangle stays narrow.  With slot_rect, the read through that slot
+    window instead of the block tables."""
     kw, vw = k_host.copy(), v_host.copy()
     oracle.kv_write(kw, vw, w.k_new, w.v_new, w.slot_mapping, num_blocks=w.num_blocks,
                     block_size=w.block_size, layout=w.layout, dtype=w.dtype)
-    read = oracle.paged_attention if w.query_len == 1 else oracle.paged_attention_multi
+    if slot_rect is not None:
+        read, addr = oracle.paged_attention_slots, slot_rect
+    elif w.query_len == 1:
+        read, addr = oracle.paged_attention, w.block_tables
+    else:
+        read, addr = oracle.paged_attention_multi, w.block_tables
     per_row = w.heads * w.head_dim * w.query_len
     out = np.zeros(w.q.shape)
     order = np.argsort(w.context_lens, kind="stable")
@@ -502,9 +508,9 @@ def _oracle_by_rows(w, k_host, v_host, cells=1 << 23):
                 per_row <= cells:
             end += 1
         part = order[at:end]
-        out[part] = read(w.q[part], kw, vw, w.block_tables[part], w.context_lens[part],
-                         w.scale, num_blocks=w.num_blocks, block_size=w.block_size,
-                         layout=w.layout, dtype=w.dtype)
+        out[part] = read(w.q[part], kw, vw, addr[part], w.context_lens[part], w.scale,
+                         num_blocks=w.num_blocks, block_size=w.block_size, layout=w.layout,
+                         dtype=w.dtype)
         at = end
     return out, kw, vw
 
@@ -800,6 +806,59 @@ def test_scattered_slots_are_read_token_by_token(case, chunk):
     ref = _slot_oracle(w, st.k_host, st.v_host, table, width)
     assert_close(to_host(got, dtype), ref, dtype, name)
     assert binding.device_status(DEV, clear=True) == 0
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_many_token_rows_share_one_queue(chunk):
+    """Every live row of a 1500-row batch scattered: more token-by-token rows than one
+    pass of the plan's threads, their chunks (full ones, then remainders by length) in
+    one shared queue; chunk=64 splits most rows.  Against the oracle."""
+    rows = 1500
+    rng = np.random.default_rng(31)
+    lens = rng.integers(0, 300, rows)
+    lens[::50] = rng.integers(600, 2500, len(lens[::50]))
+    w = wl.make_custom(lens.tolist(), heads=2, kv_heads=2, head_dim=64, dtype="bf16", seed=31)
+    width = w.max_blocks * w.block_size
+    live = [r for r in range(rows) if lens[r] > 0]
+    table = _scatter_rows(w, _block_table_rect(w, width, width), live, rng)
+    st = Step(w, host_history=True)
+    saved = binding.get_tuning()
+    if chunk:
+        binding.set_tuning(chunk_min=chunk, chunk_max=chunk)
+    try:
+        got = _slot_run(st, table, width)
+    finally:
+        binding.set_tuning(**saved)
+    assert binding.device_status(DEV, clear=True) == 0
+    ref = _oracle_by_rows(w, st.k_host, st.v_host, slot_rect=table[:, :width])[0]
+    assert_close(to_host(got, "bf16"), ref, "bf16", f"1500 token rows, chunk {chunk}")
+
+
+def test_token_rows_beside_single_wave_items():
+    """A slot window with both kinds of rows while the single-wave phase runs: 600 short
+    block-structured rows (2400 short chunks, more than one per wave of 256 workgroups),
+    long block rows whose 2048-token chunks and remainders stay shared, and scattered
+    rows for the token kernel, whose list the plan builds in the same bins after it has
+    placed the block rows' chunks.  Against the oracle."""
+    rng = np.random.default_rng(41)
+    lens = np.concatenate([rng.integers(1, 300, 600), rng.integers(2500, 4000, 20),
+                           rng.integers(700, 3000, 20), [0]])
+    rng.shuffle(lens)
+    w = wl.make_custom(lens.tolist(), heads=4, kv_heads=4, head_dim=64, dtype="bf16", seed=41)
+    width = w.max_blocks * w.block_size
+    scattered = [r for r in range(w.rows) if 700 <= lens[r] < 3000 and lens[r] > 300]
+    scattered = [r for r in scattered if not 2500 <= lens[r] < 4000][:20]
+    table = _scatter_rows(w, _block_table_rect(w, width, width), scattered, rng)
+    st = Step(w, host_history=True)
+    saved = binding.get_tuning()
+    binding.set_tuning(groups_per_cu=1, chunk_min=2048, chunk_max=2048, solo_tokens=512)
+    try:
+        got = _slot_run(st, table, width)
+    finally:
+        binding.set_tuning(**saved)
+    assert binding.device_status(DEV, clear=True) == 0
+    ref = _oracle_by_rows(w, st.k_host, st.v_host, slot_rect=table[:, :width])[0]
+    assert_close(to_host(got, "bf16"), ref, "bf16", "token rows beside single-wave items")
 
 
 def test_one_moved_token_past_the_first_translation_chunk():
