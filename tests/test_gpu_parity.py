@@ -344,6 +344,53 @@ def test_runs_are_bit_deterministic():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("kind", ["vector", "vector-single-wave", "matrix-cores",
+                                  "matrix-cores-single-wave"])
+def test_bad_block_ids_without_validation_are_skipped_and_reported(kind):
+    """validate=False on every decode path: a live block id outside [0, num_blocks) (the
+    sink block, -1, far past the pool) is never read, its 16 tokens drop out of the
+    row's softmax, and the BLOCK_ID status bit is raised.  The decode read has no
+    positional term, so such a row equals the oracle over its table without that entry;
+    the other rows are untouched."""
+    solo = kind.endswith("single-wave")
+    heads, kvh = (16, 4) if kind.startswith("matrix") else (4, 4)
+    lens = _solo_lens(560, 8, 17) if solo else [700, 40, 1500, 0, 33, 260, 2100]
+    w = wl.make_custom(lens, heads=heads, kv_heads=kvh, head_dim=128, dtype="bf16", seed=17)
+    bs = w.block_size
+    # rows of at least three blocks; a bad id goes in a block before the last (the last
+    # holds the step's own token)
+    cand = [r for r in range(w.rows) if w.context_lens[r] >= 3 * bs]
+    long_row = int(np.argmax(w.context_lens))
+    short_rows = [r for r in cand if w.context_lens[r] < 300][:2]
+    bad = {long_row: (1, w.num_blocks)}
+    for r, v in zip(short_rows, (-1, w.num_blocks + 1000)):
+        bad[r] = (wl.cdiv(int(w.context_lens[r]), bs) - 2, v)
+    tables = w.block_tables.copy()
+    for r, (j, v) in bad.items():
+        tables[r, j] = v
+    st = Step(w, host_history=True)
+    st.tables = to_dev(tables)
+    saved = binding.get_tuning()
+    binding.set_tuning(groups_per_cu=1, solo_tokens=512 if solo else 1)
+    try:
+        binding.device_status(DEV, clear=True)
+        got = to_host(st.run(validate=False), "bf16")
+        assert binding.device_status(DEV, clear=True) & _capi.DEVERR_BLOCK_ID
+    finally:
+        binding.set_tuning(**saved)
+    ref, kw, vw = _oracle_by_rows(w, st.k_host, st.v_host)
+    for r, (j, _) in bad.items():
+        n = int(w.context_lens[r])
+        row = np.delete(w.block_tables[r], j)
+        bt = np.full((1, w.max_blocks), -1, dtype=np.int32)
+        bt[0, :len(row)] = row
+        ref[r] = oracle.paged_attention(w.q[[r]], kw, vw, bt, np.array([n - bs], np.int32),
+                                        w.scale, num_blocks=w.num_blocks, block_size=bs,
+                                        layout=w.layout, dtype="bf16")[0]
+    say(f"{kind}: bad ids in rows {sorted(bad)} of {w.rows}")
+    assert_close(got, ref, "bf16", kind)
+
+
 def test_refusals_touch_nothing():
     w = wl.make_custom([37, 5, 16], heads=4, head_dim=128, dtype="bf16", seed=9)
     st = Step(w, host_history=True)
