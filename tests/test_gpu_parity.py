@@ -1244,3 +1244,61 @@ def test_many_rows_through_a_slot_window():
     got = _slot_run(st, table, width)
     ref = _slot_oracle(w, st.k_host, st.v_host, table, width)
     assert_close(to_host(got, "bf16"), ref, "bf16", "3000-row slot window")
+
+
+# --------------------------------------------------------------------------- #
+# seeded random configurations: shapes and work splits drawn together
+# --------------------------------------------------------------------------- #
+def _random_case(seed):
+    """One drawn configuration: a workload and a tuning, both seeded."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "f32"][int(rng.integers(2))]
+    d = [64, 128, 256][int(rng.integers(3))]
+    bs = [16, 32, 64][int(rng.integers(3))]
+    kvh = [1, 2, 4][int(rng.integers(3))]
+    group = [1, 2, 4, 8][int(rng.integers(4))]
+    n_q = [1, 1, 2, 4][int(rng.integers(4))]
+    many = bool(rng.integers(4) == 0)     # enough short rows for the single-wave phase
+    if many:
+        lens = rng.integers(n_q, 200, 520 if group * n_q >= 4 else 560).tolist()
+        kvh, group = 4, 1
+    else:
+        lens = rng.integers(0, 900, int(rng.integers(1, 12))).tolist()
+        lens = [0 if x < n_q and x > 0 else x for x in lens]
+    chunk_min = [32, 64, 128, 256][int(rng.integers(4))]
+    tuning = dict(chunk_min=chunk_min,
+                  chunk_max=min(8192, chunk_min * [1, 4, 16, 64][int(rng.integers(4))]),
+                  decode_waves=[1, 2, 4, 8][int(rng.integers(4))],
+                  staging=[1, 2][int(rng.integers(2))],
+                  mfma=[1, 2][int(rng.integers(2))],
+                  solo_tokens=[1, 64, 256, 1024][int(rng.integers(4))],
+                  groups_per_cu=1 if many else [1, 2, 16][int(rng.integers(3))])
+    return dict(context_lens=lens, heads=kvh * group, kv_heads=kvh, head_dim=d, block_size=bs,
+                dtype=dtype, layout=["HND", "NHD"][int(rng.integers(2))], query_len=n_q,
+                seed=seed), tuning
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configurations(seed):
+    """Drawn shapes (dtype, head_dim, block size, head grouping, new tokens per row,
+    layout, lengths) under drawn work splits (chunk range, waves, staging, matrix cores,
+    single-wave bound, workgroups per CU): every output against the oracle, the
+    scatter bit-exact."""
+    kw, tuning = _random_case(seed)
+    w = wl.make_custom(**kw)
+    say(f"random {seed}: rows {w.rows} heads {w.heads}/{w.kv_heads} d {w.head_dim} "
+        f"bs {w.block_size} {w.dtype} {w.layout} q {w.query_len} {tuning}")
+    before = binding.get_tuning()
+    binding.set_tuning(**tuning)
+    try:
+        st = Step(w, host_history=True)
+        got = st.run() if w.query_len == 1 else _multi_run(w, st)
+    finally:
+        binding.set_tuning(**before)
+    assert binding.device_status(DEV, clear=True) == 0
+    ref, kwp, vwp = _oracle_by_rows(w, st.k_host, st.v_host)
+    assert_close(to_host(got, w.dtype), ref, w.dtype, f"random {seed}")
+    ints = np.uint16 if w.dtype == "bf16" else np.uint32
+    for dev_pool, want in ((st.k_cache, kwp), (st.v_cache, vwp)):
+        assert np.array_equal(to_host(dev_pool, w.dtype)[:w.num_blocks].view(ints),
+                              want[:w.num_blocks].view(ints))
