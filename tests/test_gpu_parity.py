@@ -1302,3 +1302,35 @@ def test_random_configurations(seed):
     for dev_pool, want in ((st.k_cache, kwp), (st.v_cache, vwp)):
         assert np.array_equal(to_host(dev_pool, w.dtype)[:w.num_blocks].view(ints),
                               want[:w.num_blocks].view(ints))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_slot_windows(seed):
+    """Drawn shapes and work splits read through a slot window in which a drawn share of
+    the live rows is scattered (token by token) and the rest block-structured: every
+    output against the oracle."""
+    kw, tuning = _random_case(500 + seed)
+    kw["query_len"] = 1
+    kw["context_lens"] = [max(x, 1) if x else 0 for x in kw["context_lens"]]
+    rng = np.random.default_rng(600 + seed)
+    w = wl.make_custom(num_blocks=sum(wl.cdiv(c, kw["block_size"])
+                                      for c in kw["context_lens"]) + 40, **kw)
+    width = w.max_blocks * w.block_size
+    live = [r for r in range(w.rows) if w.context_lens[r] > 1]
+    share = [0.3, 0.6, 1.0][seed % 3]
+    scattered = sorted(rng.choice(live, int(round(share * len(live))), replace=False).tolist()) \
+        if live else []
+    table = _scatter_rows(w, _block_table_rect(w, width, width + 5), scattered, rng)
+    say(f"random slots {seed}: rows {w.rows} scattered {len(scattered)} heads "
+        f"{w.heads}/{w.kv_heads} d {w.head_dim} bs {w.block_size} {w.dtype} {w.layout} "
+        f"{tuning}")
+    st = Step(w, host_history=True)
+    before = binding.get_tuning()
+    binding.set_tuning(**tuning)
+    try:
+        got = _slot_run(st, table, width)
+    finally:
+        binding.set_tuning(**before)
+    assert binding.device_status(DEV, clear=True) == 0
+    ref = _oracle_by_rows(w, st.k_host, st.v_host, slot_rect=table[:, :width])[0]
+    assert_close(to_host(got, w.dtype), ref, w.dtype, f"random slots {seed}")
