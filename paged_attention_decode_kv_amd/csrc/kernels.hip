@@ -709,6 +709,17 @@ struct ChunkAddr {
   }
 };
 
+// The workgroup's place in the item order.  Workgroups are dispatched to the 8 XCDs
+// round robin (workgroup b on XCD b % 8), each XCD with its own L2; numbering them XCD
+// by XCD gives consecutive items, the query heads of one row chunk, to one XCD, which
+// then fetches that chunk's block ids and queries once.  Measured 0.2-1.1 % faster on
+// the long-gather batches; any permutation is correct.
+__device__ __forceinline__ int xcd_order(int G) {
+  const int b = blockIdx.x;
+  if (G % 8 != 0) return b;
+  return (b % 8) * (G / 8) + b / 8;
+}
+
 // Item order of the persistent decode kernels: whole rounds of the full chunks
 // (section A) are dealt round robin, workgroup g taking items g, g + G, ...; the rest
 // come from one shared ticket counter (n_dealt + ticket; anything at or past the data
@@ -963,7 +974,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   // workgroups' finishing times ----
   {
     const int stride = G * WAVES;
-    int it = n_wide + (int)blockIdx.x * WAVES + wave;
+    int it = n_wide + xcd_order(G) * WAVES + wave;
     MetaS sc;
     int4 ent_nx = make_int4(0, -1, 0, 0);
     if (it < n_data) {
@@ -1030,7 +1041,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   }
 
   // ---- wide items: the workgroup's waves share each one ----
-  ItemOrder order{(int)blockIdx.x, G, n_dealt};
+  ItemOrder order{xcd_order(G), G, n_dealt};
   int item, next;
   order.first_two(item, next, &ws.counters[1], s_ticket);
   int buf = 0;
@@ -1394,7 +1405,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     constexpr int NRS = solo_id_regs(16);
     using MetaS = MfmaMeta<D, NRS>;
     const int stride = G * WAVES;
-    int it = n_wide + (int)blockIdx.x * WAVES + wave;
+    int it = n_wide + xcd_order(G) * WAVES + wave;
     MetaS sc_m;
     int4 ent_nx = make_int4(0, -1, 0, 0);
     if (it < n_data) {
@@ -1472,7 +1483,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   }
 
   // ---- wide items: the workgroup's waves share each one ----
-  ItemOrder order{(int)blockIdx.x, G, n_dealt};
+  ItemOrder order{xcd_order(G), G, n_dealt};
   int item, next;
   order.first_two(item, next, &ws.counters[1], s_ticket);
   int buf = 0;
