@@ -686,6 +686,50 @@ def test_bucketed_graphs_replay_real_steps(heads, kv_heads):
     graphs.close()
 
 
+def test_graph_replays_switch_the_single_wave_phase():
+    """One recorded 640-row step, 256 workgroups pinned at capture, replayed on batches
+    that do and do not keep the single-wave phase (the plan decides it on the device per
+    replay): mostly short rows, long rows, a mix, and a few rows.  Every replay against
+    the oracle on the evolving pool."""
+    from paged_attention_decode_kv_amd.graphs import DecodeGraphs
+    heads, kvh, d, mb = 4, 4, 64, 80
+    nb = 640 * mb + 8
+    saved = binding.get_tuning()
+    binding.set_tuning(groups_per_cu=1, solo_tokens=512)
+    try:
+        def batch(n_short, n_long, seed):
+            rng = np.random.default_rng(seed)
+            lens = np.concatenate([rng.integers(1, 300, n_short),
+                                   rng.integers(600, mb * 16 - 16, n_long)])
+            rng.shuffle(lens)
+            return wl.make_custom(lens.tolist(), heads=heads, kv_heads=kvh, head_dim=d,
+                                  block_size=16, dtype="bf16", layout="HND",
+                                  num_blocks=nb, max_blocks=mb, seed=seed)
+        first = batch(4, 4, 900)
+        k_host, v_host = wl.history_host(first)
+        k_cache, v_cache = to_dev(k_host, "bf16"), to_dev(v_host, "bf16")
+        graphs = DecodeGraphs(k_cache, v_cache, num_heads=heads, max_blocks=mb,
+                              scale=first.scale, buckets=[640])
+        torch.cuda.synchronize()
+        kh, vh = k_host.copy(), v_host.copy()
+        for i, (n_short, n_long) in enumerate([(600, 0), (0, 600), (560, 40), (3, 2),
+                                               (600, 20)]):
+            w = batch(n_short, n_long, 910 + i)
+            say(f"  replay {i}: {n_short} short rows, {n_long} long")
+            got = graphs.step(to_dev(w.q, "bf16"), to_dev(w.k_new, "bf16"),
+                              to_dev(w.v_new, "bf16"), to_dev(w.slot_mapping),
+                              to_dev(w.block_tables), to_dev(w.context_lens))
+            torch.cuda.synchronize()
+            ref, kh, vh = _oracle_by_rows(w, kh, vh)
+            assert_close(to_host(got, "bf16"), ref, "bf16", f"replay {i}")
+            assert np.array_equal(to_host(k_cache, "bf16")[:nb], kh[:nb])
+            assert torch.count_nonzero(graphs.out[w.rows:]).item() == 0
+        assert binding.device_status(DEV, clear=True) == 0
+        graphs.close()
+    finally:
+        binding.set_tuning(**saved)
+
+
 def test_caller_stream_capture_of_the_step():
     """The two entry points with validate=0 are capturable by a caller's own stream
     capture: recorded over padding, replayed several times on real batches written into
