@@ -82,7 +82,8 @@ struct Workspace {
                         // [8] rows split into more than one chunk,
                         // [9] entries of the rows read token by token (slot input),
                         // [10] entries before the single-wave items (chunks shorter
-                        // than AttnArgs::solo_tokens), [11] token queue ticket
+                        // than AttnArgs::solo_tokens), [11] token queue ticket,
+                        // [12] token entries before the short ones
   int32_t* row_ctx;     // [rows]: each row's length as the block path reads it
   int32_t* irregular;   // [rows]: the rows read token by token, counters[6] of them
   int2* split_rows;     // [rows]: {row, length} of the rows split into chunks, counters[8]
@@ -122,6 +123,7 @@ struct AttnArgs {
   // slots are not block structured; such rows are left to the token-by-token kernel
   const int32_t* row_flags;
   int32_t flag_stride;
+  int32_t token_waves;   // slot input only: waves of the token kernels' grid
 };
 
 // The slot rectangle of a read addressed per token, and what the translation pass

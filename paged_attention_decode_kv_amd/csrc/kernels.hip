@@ -294,7 +294,8 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 // ws.split_rows for the combine kernel), [9] = entries of the rows read token by token
 // (ws.token_entries), [10] = entries before the single-wave items (those of fewer than
 // a.solo_tokens tokens, the tail of the longest-first order), [11] = the token kernel's
-// queue ticket (reset to 0).  Every row's clamped length goes to ws.row_ctx.
+// queue ticket (reset to 0), [12] = token entries before the short ones.  Every row's
+// clamped length goes to ws.row_ctx.
 __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   constexpr int kCand = 7;                 // chunk_max / chunk_min <= kMaxChunkRatio
   static_assert((1 << (kCand - 1)) == kMaxChunkRatio, "one candidate per power of two");
@@ -472,7 +473,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   // The rows read token by token (slot input): their chunks, longest first, for the
   // token kernel's shared queue, as sections A and B are for the block path: every full
   // chunk, then the trailing partial chunks by length, descending (bins as for B).
-  int total_ta = 0, total_tb = 0;
+  int total_ta = 0, total_tb = 0, n_tok_wide = 0;
   const int n_irr = s_irregular;
   if (n_irr > 0 && ws.token_entries != nullptr) {
     if (t < nbins) s_bin_fill[t] = 0;
@@ -506,6 +507,16 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
         ws.token_entries[total_ta + s_bin_start[rem >> bshift] +
                          atomicAdd(&s_bin_fill[rem >> bshift], 1)] = make_int2(r, full >> lp);
     }
+    // entries before the chunks shorter than solo_tokens, which token_rows_short_kernel
+    // reads one wave each, if there are at least kSoloPerWave for each of its waves
+    n_tok_wide = total_ta + total_tb;
+    if (a.solo_tokens > 1) {
+      const int tb = a.solo_tokens >> bshift;
+      n_tok_wide = P < a.solo_tokens ? 0 : total_ta + (tb >= nbins ? 0 : s_bin_start[tb - 1]);
+      if ((int64_t)(total_ta + total_tb - n_tok_wide) * a.num_heads <
+          (int64_t)kSoloPerWave * a.token_waves)
+        n_tok_wide = total_ta + total_tb;
+    }
     __syncthreads();
   }
   if (t == 0) {
@@ -521,6 +532,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     ws.counters[9] = total_ta + total_tb;
     ws.counters[10] = n_wide;
     ws.counters[11] = 0;
+    ws.counters[12] = n_tok_wide;
   }
 }
 
@@ -1719,8 +1731,9 @@ __global__ void __launch_bounds__(kTranslateThreads) translate_slots_kernel(Attn
 // The rows of a slot input that are not block structured.  An item is (chunk of a row,
 // query head): the plan lists these rows' chunks longest first (the decode kernel's
 // chunk length; a split row leaves partial records for the combine kernel just as the
-// decode kernel does); each workgroup takes the item of its own index first, then items
-// from one shared ticket counter, so the short ones even out the finishing times.  Each
+// decode kernel does).  This kernel reads the chunks of at least a.solo_tokens tokens:
+// each workgroup takes the item of its own index first, then items from one shared
+// ticket counter; token_rows_short_kernel reads the rest.  Each
 // 16-lane group (bf16 x 128) takes one token, loads its slot, then the token's K and V
 // through that slot, and folds it into its own online softmax; the groups and the waves
 // are merged at the end of the item.  A live slot outside the allocatable slots is
@@ -1747,7 +1760,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
   const int heads = a.num_heads;
   const int qpkv = heads / a.g.kv_heads;
   const int lp = ws.counters[3];
-  const int n_items = ws.counters[9] * heads;   // (token entry, query head)
+  const int n_items = ws.counters[12] * heads;  // (token entry, query head), long ones
   const int64_t n_slots = a.g.num_blocks * a.g.block_size;
   const int log2_bs = a.g.log2_bs;
   const int bs_mask = a.g.block_size - 1;
@@ -1915,6 +1928,130 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
     __syncthreads();
     item = __builtin_amdgcn_readfirstlane(s_item[buf]);
     buf ^= 1;
+  }
+  if (bad) atomicOr(&g_status, PKV_DEVERR_SLOT);
+}
+
+// The token rows' chunks shorter than a.solo_tokens (the end of their list), one wave
+// each, dealt round robin over every wave of the grid (the list runs longest first; a
+// shared ticket counter cost ~50 us of serialized atomics over 4096 waves), with no
+// merge across waves: a wave streams all of an item's steps through the same pipeline
+// as token_rows_kernel (slots two steps ahead, K/V one).  A kernel of its own: the same
+// loop inside token_rows_kernel slowed that kernel's shared items.  Runs right after it.
+template <typename T, int D>
+__global__ void __launch_bounds__(kTokenRowThreads)
+token_rows_short_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
+  using Sh = Shape<T, D>;
+  using El = Elem<T>;
+  constexpr int E = Sh::E, LPT = Sh::LPT, TPS = Sh::TPS, U = Sh::U;
+  constexpr int ES = sizeof(T);
+  constexpr int WSTEP = TPS * U;
+  const int lane = threadIdx.x & 63;
+  const int g = lane / LPT;
+  const int sub = lane % LPT;
+  const int heads = a.num_heads;
+  const int qpkv = heads / a.g.kv_heads;
+  const int lp = ws.counters[3];
+  const int n_items = ws.counters[9] * heads;
+  const int n_wide = ws.counters[12] * heads;
+  const int64_t n_slots = a.g.num_blocks * a.g.block_size;
+  const int log2_bs = a.g.log2_bs;
+  const int bs_mask = a.g.block_size - 1;
+  const int64_t tok_bytes = a.g.tok_stride * ES;
+  const int64_t blk_bytes = a.g.blk_stride * ES;
+  const int64_t head_bytes = a.g.head_stride * ES;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+  bool bad = false;
+  const int waves = gridDim.x * (kTokenRowThreads / 64);
+  for (int item = n_wide + blockIdx.x * (kTokenRowThreads / 64) +
+                  __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       item < n_items; item += waves) {
+    const int e = item / heads;
+    const int h = item - e * heads;
+    const int2 ent = ws.token_entries[e];
+    const int r = __builtin_amdgcn_readfirstlane(ent.x);
+    const int chunk = __builtin_amdgcn_readfirstlane(ent.y);
+    const int ctx = __builtin_amdgcn_readfirstlane(ws.row_ctx[r]);
+    const int nch = (ctx + (1 << lp) - 1) >> lp;
+    const int t_begin = chunk << lp;
+    const int t_end = min(ctx, t_begin + (1 << lp));
+    const uint4 qv = load16(static_cast<const T*>(a.q) + ((int64_t)r * heads + h) * D + sub * E);
+    const int64_t lane_off = (int64_t)(h / qpkv) * head_bytes + sub * E * ES;
+    const int64_t* row = sa.slots + (int64_t)r * sa.row_stride;
+    float m[1] = {-INFINITY}, l[1] = {0.f}, acc[1][E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[0][i] = 0.f;
+    // step 0's slots and K/V, step 1's slots
+    int64_t sl_next[U];
+    uint4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t_begin + u * TPS + g;
+      const int64_t slot = t < t_end ? row[t] : -1;
+      sl_next[u] = t + WSTEP < t_end ? row[t + WSTEP] : -1;
+      ok[u] = t < t_end && slot >= 0 && slot < n_slots;
+      bad |= t < t_end && !ok[u];
+      kr[u] = make_uint4(0, 0, 0, 0);
+      vr[u] = make_uint4(0, 0, 0, 0);
+      if (ok[u]) {
+        const int64_t off = (slot >> log2_bs) * blk_bytes + (slot & bs_mask) * tok_bytes +
+                            lane_off;
+        kr[u] = load16_stream(kpool + off);
+        vr[u] = load16_stream(vpool + off);
+      }
+    }
+    for (int t0 = t_begin; t0 < t_end; t0 += WSTEP) {
+      // the next step's K/V (its slots have landed) and the slots of the one after
+      uint4 kr_n[U], vr_n[U];
+      bool ok_n[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + WSTEP + u * TPS + g;
+        ok_n[u] = t < t_end && sl_next[u] >= 0 && sl_next[u] < n_slots;
+        bad |= t < t_end && !ok_n[u];
+        kr_n[u] = make_uint4(0, 0, 0, 0);
+        vr_n[u] = make_uint4(0, 0, 0, 0);
+        if (ok_n[u]) {
+          const int64_t off = (sl_next[u] >> log2_bs) * blk_bytes +
+                              (sl_next[u] & bs_mask) * tok_bytes + lane_off;
+          kr_n[u] = load16_stream(kpool + off);
+          vr_n[u] = load16_stream(vpool + off);
+        }
+        sl_next[u] = t + WSTEP < t_end ? row[t + WSTEP] : -1;
+      }
+      float sc[U];
+      float smax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float d = group_sum<LPT>(El::dot(qv, kr[u], 0.f));
+        sc[u] = ok[u] ? d * scale_log2 : -INFINITY;
+        smax = fmaxf(smax, sc[u]);
+      }
+      const float m_new = fmaxf(m[0], smax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[0] - m_use);
+      l[0] *= alpha;
+#pragma unroll
+      for (int i = 0; i < E; ++i) acc[0][i] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = __builtin_amdgcn_exp2f(sc[u] - m_use);
+        l[0] += p;
+        El::axpy(p, vr[u], acc[0]);
+      }
+      m[0] = m_new;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kr[u] = kr_n[u];
+        vr[u] = vr_n[u];
+        ok[u] = ok_n[u];
+      }
+    }
+    merge_lane_groups<LPT, 1, E>(m, l, acc);
+    if (g == 0)
+      write_item_result<T, D>(a, ws, r, h, chunk, nch, heads, sub, m[0], l[0], acc[0]);
   }
   if (bad) atomicOr(&g_status, PKV_DEVERR_SLOT);
 }
@@ -2213,45 +2350,50 @@ static hipError_t device_cus(int* cus) {
 template <typename T, int D>
 static void launch_token_rows(const AttnArgs& a, const SlotArgs& sa, const Workspace& ws,
                               int grid, hipStream_t stream) {
+  const float scale_log2 = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((token_rows_kernel<T, D>), dim3(grid), dim3(kTokenRowThreads), 0,
-                     stream, a, sa, ws, a.scale * 1.4426950408889634f);
+                     stream, a, sa, ws, scale_log2);
+  hipLaunchKernelGGL((token_rows_short_kernel<T, D>), dim3(grid), dim3(kTokenRowThreads), 0,
+                     stream, a, sa, ws, scale_log2);
 }
 
 hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
                                         const Workspace& ws, hipStream_t stream) {
+  // the token kernels: four 4-wave workgroups per CU
+  int cus = 0;
+  hipError_t err = device_cus(&cus);
+  if (err != hipSuccess) return err;
+  const int token_groups = cus * 4;
   AttnArgs b = a;
   b.block_tables = sa.block_tables;
   b.max_blocks = sa.max_blocks;
   b.row_flags = sa.row_flags;
   b.flag_stride = sa.flag_stride;
+  b.token_waves = token_groups * (kTokenRowThreads / 64);
   timing_begin(PKV_PHASE_TRANSLATE, stream);
   hipLaunchKernelGGL(translate_slots_kernel, dim3((unsigned)sa.flag_stride, (unsigned)a.num_rows),
                      dim3(kTranslateThreads), 0, stream, b, sa);
   timing_end(PKV_PHASE_TRANSLATE, stream);
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_paged_attention(b, ws, stream, /*combine=*/false);
   if (err != hipSuccess) return err;
   // the rows the block path could not take, then the merge of every split row: the
   // count is on the device, and with none every workgroup exits at once
-  int cus = 0;
-  err = device_cus(&cus);
-  if (err != hipSuccess) return err;
-  cus *= 4;
   timing_begin(PKV_PHASE_TOKEN_ROWS, stream);
   const bool f32 = a.g.dtype == PKV_F32;
   switch (a.g.head_dim) {
     case 64:
-      f32 ? launch_token_rows<float, 64>(b, sa, ws, cus, stream)
-          : launch_token_rows<uint16_t, 64>(b, sa, ws, cus, stream);
+      f32 ? launch_token_rows<float, 64>(b, sa, ws, token_groups, stream)
+          : launch_token_rows<uint16_t, 64>(b, sa, ws, token_groups, stream);
       break;
     case 128:
-      f32 ? launch_token_rows<float, 128>(b, sa, ws, cus, stream)
-          : launch_token_rows<uint16_t, 128>(b, sa, ws, cus, stream);
+      f32 ? launch_token_rows<float, 128>(b, sa, ws, token_groups, stream)
+          : launch_token_rows<uint16_t, 128>(b, sa, ws, token_groups, stream);
       break;
     case 256:
-      f32 ? launch_token_rows<float, 256>(b, sa, ws, cus, stream)
-          : launch_token_rows<uint16_t, 256>(b, sa, ws, cus, stream);
+      f32 ? launch_token_rows<float, 256>(b, sa, ws, token_groups, stream)
+          : launch_token_rows<uint16_t, 256>(b, sa, ws, token_groups, stream);
       break;
     default:
       return hipErrorInvalidValue;

@@ -925,6 +925,33 @@ def test_many_token_rows_share_one_queue(chunk):
     assert_close(to_host(got, "bf16"), ref, "bf16", f"1500 token rows, chunk {chunk}")
 
 
+@pytest.mark.parametrize("chunk", [0, 128])
+def test_short_token_rows_one_wave_each(chunk):
+    """Every live row of a 1200-row batch scattered, mostly shorter than solo_tokens:
+    more short chunks than the token kernels have waves, so token_rows_short_kernel
+    reads them one wave each after the shared ones; a few long rows stay shared
+    (chunk=128 splits everything into short chunks).  Against the oracle."""
+    rng = np.random.default_rng(51)
+    lens = np.concatenate([rng.integers(1, 400, 1150), rng.integers(600, 3000, 50), [0]])
+    rng.shuffle(lens)
+    w = wl.make_custom(lens.tolist(), heads=4, kv_heads=2, head_dim=128, dtype="bf16",
+                       layout="NHD", seed=51)
+    width = w.max_blocks * w.block_size
+    live = [r for r in range(w.rows) if lens[r] > 0]
+    table = _scatter_rows(w, _block_table_rect(w, width, width), live, rng)
+    st = Step(w, host_history=True)
+    saved = binding.get_tuning()
+    if chunk:
+        binding.set_tuning(chunk_min=chunk, chunk_max=chunk)
+    try:
+        got = _slot_run(st, table, width)
+    finally:
+        binding.set_tuning(**saved)
+    assert binding.device_status(DEV, clear=True) == 0
+    ref = _oracle_by_rows(w, st.k_host, st.v_host, slot_rect=table[:, :width])[0]
+    assert_close(to_host(got, "bf16"), ref, "bf16", f"short token rows, chunk {chunk}")
+
+
 def test_token_rows_beside_single_wave_items():
     """A slot window with both kinds of rows while the single-wave phase runs: 600 short
     block-structured rows (2400 short chunks, more than one per wave of 256 workgroups),
