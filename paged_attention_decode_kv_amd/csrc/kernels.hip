@@ -342,8 +342,11 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     // (a row read token by token keeps its length here: its chunks are combined too)
     ws.row_ctx[r] = full_ctx;
     if (irr) ws.irregular[atomicAdd(&s_irregular, 1)] = (int)r;
+    // (the chunk length serves the rows read token by token too: counted by their full
+    // length, so that a batch of them is not cut into the shortest chunks)
 #pragma unroll
-    for (int k = 0; k < kCand; ++k) cnt[k] += (ctx + (1 << (lmin + k)) - 1) >> (lmin + k);
+    for (int k = 0; k < kCand; ++k)
+      cnt[k] += (full_ctx + (1 << (lmin + k)) - 1) >> (lmin + k);
   }
 #pragma unroll
   for (int k = 0; k < kCand; ++k) {
