@@ -2362,11 +2362,11 @@ static void launch_token_rows(const AttnArgs& a, const SlotArgs& sa, const Works
 
 hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
                                         const Workspace& ws, hipStream_t stream) {
-  // the token kernels: four 4-wave workgroups per CU
+  // the token kernels: two 4-wave workgroups per CU (measured against one and four)
   int cus = 0;
   hipError_t err = device_cus(&cus);
   if (err != hipSuccess) return err;
-  const int token_groups = cus * 4;
+  const int token_groups = cus * 2;
   AttnArgs b = a;
   b.block_tables = sa.block_tables;
   b.max_blocks = sa.max_blocks;
