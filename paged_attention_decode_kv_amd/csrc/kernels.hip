@@ -356,8 +356,10 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   __syncthreads();
   // Workgroups and chunk length.  A batch that gives 8 waves per compute unit enough
   // items of more than the shortest chunk is bandwidth-bound: then 8 waves per CU
-  // (fewer concurrent streams) read it fastest.  Otherwise every workgroup
-  // takes part, with the chunk length that gives them all enough items.
+  // (fewer concurrent streams) read it fastest.  Enough is narrow_items, or one item
+  // per wave when the chunk makes every item a single-wave one (then each wave is one
+  // stream).  Otherwise every workgroup takes part, with the chunk length that gives
+  // them all enough items.
   const int64_t per_entry = a.query_len * a.num_heads / a.query_group;
   // Balance: with G workgroups, the largest candidate whose chunks hold at most
   // 1 / kBalance of a workgroup's share (tokens x items per entry / G); the work list
@@ -374,7 +376,12 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   bool narrow = false;
   if (a.narrow_groups > 0) {
     for (int k = min(ncand - 1, balance_cap(a.narrow_groups)); k > 0; --k) {
-      if ((int64_t)s_cand[k] * per_entry >= a.narrow_items) {
+      const int64_t items = (int64_t)s_cand[k] * per_entry;
+      // chunks shorter than solo_tokens are all single-wave items, which need only
+      // kSoloPerWave of them for each wave, not narrow_items for the workgroups
+      const bool solo = a.solo_tokens > 1 && (1 << (lmin + k)) < a.solo_tokens &&
+                        items >= (int64_t)kSoloPerWave * a.narrow_groups * a.group_waves;
+      if (items >= a.narrow_items || solo) {
         lp = lmin + k;
         narrow = true;
         break;
