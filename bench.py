@@ -238,7 +238,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the decode step is built and timed on a "
-              "single MI355X (see DESIGN.md for how it would shard); run with --gpus 1.",
+              "single MI355X; run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
