@@ -587,6 +587,37 @@ def test_single_wave_items(case):
         assert np.array_equal(got_pool[:w.num_blocks].view(ints), want[:w.num_blocks].view(ints))
 
 
+NARROW_SOLO_CASES = [
+    # name, lens, query_len, dtype, layout (32 heads, head_dim 128, block 16).  Small,
+    # near-uniform batches whose 256-token chunks give about one item per wave at 8
+    # waves per CU but not 16 items per workgroup: on a 256-CU MI355X the plan takes
+    # 256-token single-wave chunks at 8 waves per CU, by the single-wave branch alone
+    ("16x1024-bf16", [1024] * 16, 1, "bf16", "HND"),
+    ("ragged8-bf16-nhd", [2135, 2202, 1811, 2203, 2034, 2057, 2115, 1942], 1, "bf16", "NHD"),
+    ("16x1024-f32", [1024] * 16, 1, "f32", "HND"),
+    ("16x1024-q2", [1024] * 16, 2, "bf16", "HND"),
+]
+
+
+@pytest.mark.parametrize("case", NARROW_SOLO_CASES, ids=[c[0] for c in NARROW_SOLO_CASES])
+def test_single_wave_chunks_at_eight_waves_per_cu(case):
+    """Default tuning on batches whose chunks are all single-wave items, one per wave of
+    an 8-waves-per-CU launch: every output against the oracle, the scatter bit-exact."""
+    name, lens, n_q, dtype, layout = case
+    w = wl.make_custom(lens, heads=32, kv_heads=32, head_dim=128, block_size=16, dtype=dtype,
+                       layout=layout, query_len=n_q, seed=zlib.crc32(name.encode()))
+    say(f"{name}: rows {w.rows} lens {lens[:4]}.. q {n_q} {dtype} {layout}")
+    st = Step(w, host_history=True)
+    got = st.run() if n_q == 1 else _multi_run(w, st)
+    assert binding.device_status(DEV, clear=True) == 0
+    ref, kw, vw = _oracle_by_rows(w, st.k_host, st.v_host)
+    assert_close(to_host(got, dtype), ref, dtype, name)
+    ints = np.uint16 if dtype == "bf16" else np.uint32
+    for dev_pool, want in ((st.k_cache, kw), (st.v_cache, vw)):
+        got_pool = to_host(dev_pool, dtype)
+        assert np.array_equal(got_pool[:w.num_blocks].view(ints), want[:w.num_blocks].view(ints))
+
+
 GQA_CASES = [
     # lens, heads, kv_heads, head_dim, dtype, layout: query groups 8, 4, 2 and 16 (two items)
     ([700, 1, 0, 2049, 31], 16, 2, 128, "bf16", "HND"),
