@@ -352,6 +352,32 @@ def main():
     t1 = time.perf_counter()
     eager_s = (t1 - t0) / args.steps
 
+    # the same step recorded once into a HIP graph over the same tensors, then replayed:
+    # identical kernels and arguments, without a host launch per kernel.  Timed before
+    # the event-timed loop: for a few ms after hundreds of event pairs, replays of a
+    # small step run up to 1.5x slower
+    graph_s = None
+    if args.launch == "graph":
+        if slot_win is not None:
+            graph = binding.capture_step_slots(k_new, v_new, slots, q, k_cache, v_cache,
+                                               slot_win, lens, w.scale, out, ws,
+                                               layout=w.layout)
+        elif w.query_len > 1:
+            graph = _CallerGraph(step, torch)     # the calls captured on a side stream
+        else:
+            graph = binding.capture_step(k_new, v_new, slots, q, k_cache, v_cache, tables,
+                                         lens, w.scale, out, ws, layout=w.layout)
+        for _ in range(args.warmup):
+            graph.launch()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.launch()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        graph_s = (t1 - t0) / args.steps
+        graph.destroy()
+
     # the same K steps again with a HIP event pair around every kernel, on the stream it
     # runs on: the per-kernel averages (the events add ~10 us of idle time per kernel
     # boundary, so this loop's wall clock is reported but is not the step time)
@@ -374,29 +400,6 @@ def main():
     event_s = (t1 - t0) / args.steps
     del flush, sink
 
-    # the same step recorded once into a HIP graph over the same tensors, then replayed:
-    # identical kernels and arguments, without a host launch per kernel
-    graph_s = None
-    if args.launch == "graph":
-        if slot_win is not None:
-            graph = binding.capture_step_slots(k_new, v_new, slots, q, k_cache, v_cache,
-                                               slot_win, lens, w.scale, out, ws,
-                                               layout=w.layout)
-        elif w.query_len > 1:
-            graph = _CallerGraph(step, torch)     # the calls captured on a side stream
-        else:
-            graph = binding.capture_step(k_new, v_new, slots, q, k_cache, v_cache, tables,
-                                         lens, w.scale, out, ws, layout=w.layout)
-        for _ in range(args.warmup):
-            graph.launch()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.launch()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        graph_s = (t1 - t0) / args.steps
-        graph.destroy()
     flags = binding.device_status(dev, clear=True)
     if flags:
         raise SystemExit(f"kernels clamped or skipped inputs (status bits {flags}); "
