@@ -302,7 +302,10 @@ pkv_status pkv_get_tuning(pkv_tuning* tuning);
  * phases below is bracketed by a pair of HIP events recorded on the launch stream;
  * pkv_timing_read synchronises on the recorded events and returns the summed elapsed
  * milliseconds and the number of launches of one phase.  Disabled by default; costs
- * two event records per launch when on.  Not thread-safe against concurrent calls. */
+ * two event records per launch when on (~10 us of device idle at each kernel boundary).
+ * On this runtime the device also runs slower for a few milliseconds after hundreds of
+ * event pairs: time steps before a timed loop, not after it.  Not thread-safe against
+ * concurrent calls. */
 typedef enum pkv_phase {
   PKV_PHASE_KV_WRITE = 0,  /* the slot scatter kernel */
   PKV_PHASE_PLAN = 1,      /* the work-list kernel of pkv_paged_attention */
