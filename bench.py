@@ -13,8 +13,8 @@ must stream (every live (row, KV head, position) once) divided by the wall-clock
 per step.  The step is timed twice over the same tensors: as the two library calls
 per step (eager), and as replays of one HIP graph recorded from those calls (graph, the
 default ``value``; ``--launch eager`` reports the other).  ``roofline`` reports the
-decode kernel alone, timed with HIP events on its launch stream over the eager steps,
-against MI355X's 8 TB/s HBM peak.
+decode kernel alone, timed with HIP events on its launch stream over a third pass of
+the same library-call steps, against MI355X's 8 TB/s HBM peak.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
 """
 
