@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "internal.h"
 #include "pagedkv.h"
 
@@ -2189,25 +2191,30 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   void (*kern)(AttnArgs, Workspace, float);
   if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG>;
   else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
-  static int per_cu[64] = {0};   // occupancy per device, computed once
-  static int num_cu[64] = {0};
+  // occupancy and compute units per device, computed once (host threads that race to
+  // fill them store the same values; the occupancy is published last)
+  static std::atomic<int> per_cu[64];
+  static std::atomic<int> num_cu[64];
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev >= 64) return hipErrorInvalidDevice;
-  if (per_cu[dev] == 0) {
+  int occ = per_cu[dev].load(std::memory_order_acquire);
+  if (occ == 0) {
     int n = 0;
     err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, WAVES * 64, 0);
     if (err != hipSuccess) return err;
     int cus = 0;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    num_cu[dev] = cus;
-    per_cu[dev] = n > 0 ? n : 1;
+    occ = n > 0 ? n : 1;
+    num_cu[dev].store(cus, std::memory_order_relaxed);
+    per_cu[dev].store(occ, std::memory_order_release);
   }
+  const int cus = num_cu[dev].load(std::memory_order_relaxed);
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  const int wpc = per_cu[dev] < tuning_groups_per_cu() ? per_cu[dev] : tuning_groups_per_cu();
-  int64_t grid = (int64_t)num_cu[dev] * wpc;
+  const int wpc = occ < tuning_groups_per_cu() ? occ : tuning_groups_per_cu();
+  int64_t grid = (int64_t)cus * wpc;
   const int64_t most = ws.max_entries * (a.query_len * a.num_heads / QG);
   if (grid > most) grid = most;
   AttnArgs pa = a;
@@ -2218,7 +2225,7 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   pa.target_items = (int32_t)(grid * per_group);
   pa.grid_groups = (int32_t)grid;
   // the plan may keep 8 waves per CU (one workgroup of 8, two of 4, ...)
-  const int64_t narrow = (int64_t)num_cu[dev] * (WAVES < 8 ? 8 / WAVES : 1);
+  const int64_t narrow = (int64_t)cus * (WAVES < 8 ? 8 / WAVES : 1);
   pa.narrow_groups = grid > narrow ? (int32_t)narrow : 0;
   pa.narrow_items = pa.narrow_groups * per_group;
   pa.deal_static = tuning_deal_static();
@@ -2342,18 +2349,20 @@ static void launch_combine(const AttnArgs& a, const Workspace& ws, hipStream_t s
 }
 
 static hipError_t device_cus(int* cus) {
-  static int count[64] = {0};
+  static std::atomic<int> count[64];   // per device, computed once
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev >= 64) return hipErrorInvalidDevice;
-  if (count[dev] == 0) {
+  int c = count[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
     err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    count[dev] = n > 0 ? n : 1;
+    c = n > 0 ? n : 1;
+    count[dev].store(c, std::memory_order_relaxed);
   }
-  *cus = count[dev];
+  *cus = c;
   return hipSuccess;
 }
 
