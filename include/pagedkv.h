@@ -76,7 +76,8 @@ typedef enum pkv_status {
   PKV_ERR_UNSUPPORTED = 7,    /* legal, but not a shape this library was built for */
   PKV_ERR_WORKSPACE = 8,      /* workspace missing or smaller than pkv_workspace_bytes */
   PKV_ERR_NULL = 9,           /* a required pointer is NULL */
-  PKV_ERR_HIP = 10            /* the HIP runtime reported an error */
+  PKV_ERR_HIP = 10            /* the HIP runtime reported an error, or host memory to
+                                 validate with could not be allocated (out of memory) */
 } pkv_status;
 
 /* The pool both caches share.  num_blocks counts the blocks a block table may name;

@@ -5,6 +5,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <exception>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -83,6 +85,18 @@ pkv::PoolGeom geom(const pkv_pool_desc* p) {
 
 pkv_status hip_fail(hipError_t e, const char* what) {
   return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A host buffer of a validating call.  An allocation failure is returned as a status,
+// since no exception may cross the C ABI.
+template <typename T>
+bool host_buffer(std::vector<T>& v, size_t n) {
+  try {
+    v.resize(n);
+    return true;
+  } catch (const std::exception&) {
+    return false;
+  }
 }
 
 int64_t ctx_limit_of(const pkv_pool_desc* p, int32_t max_blocks) {
@@ -326,7 +340,11 @@ pkv_status record_graph(F&& record, pkv_step_graph** graph) {
   if (g) (void)hipGraphDestroy(g);
   (void)hipStreamDestroy(cs);
   if (e != hipSuccess) return hip_fail(e, "capturing the decode step");
-  *graph = new pkv_step_graph{exec};
+  *graph = new (std::nothrow) pkv_step_graph{exec};
+  if (*graph == nullptr) {   // no exception crosses the C ABI
+    (void)hipGraphExecDestroy(exec);
+    return hip_fail(hipErrorOutOfMemory, "allocating the graph handle");
+  }
   return ok();
 }
 
@@ -403,7 +421,9 @@ pkv_status pkv_kv_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
     return fail(PKV_ERR_NULL, "a required pointer is NULL");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (validate) {
-    std::vector<int64_t> host((size_t)num_tokens);
+    std::vector<int64_t> host;
+    if (!host_buffer(host, (size_t)num_tokens))
+      return hip_fail(hipErrorOutOfMemory, "allocating host memory to validate");
     hipError_t e = hipMemcpyAsync(host.data(), slot_mapping, host.size() * sizeof(int64_t),
                                   hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -441,8 +461,12 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
   if (s != PKV_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (validate) {
-    std::vector<int32_t> ctx((size_t)num_rows);
-    std::vector<int32_t> bt((size_t)(num_rows * max_blocks_per_row));
+    std::vector<int32_t> ctx;
+    if (!host_buffer(ctx, (size_t)num_rows))
+      return hip_fail(hipErrorOutOfMemory, "allocating host memory to validate");
+    std::vector<int32_t> bt;
+    if (!host_buffer(bt, (size_t)(num_rows * max_blocks_per_row)))
+      return hip_fail(hipErrorOutOfMemory, "allocating host memory to validate");
     hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * sizeof(int32_t),
                                   hipMemcpyDeviceToHost, st);
     if (e == hipSuccess)
@@ -499,8 +523,12 @@ pkv_status pkv_paged_attention_slots(const pkv_pool_desc* pool, void* out, const
   if (s != PKV_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (validate) {
-    std::vector<int32_t> ctx((size_t)num_rows);
-    std::vector<int64_t> rect((size_t)(num_rows * width));
+    std::vector<int32_t> ctx;
+    if (!host_buffer(ctx, (size_t)num_rows))
+      return hip_fail(hipErrorOutOfMemory, "allocating host memory to validate");
+    std::vector<int64_t> rect;
+    if (!host_buffer(rect, (size_t)(num_rows * width)))
+      return hip_fail(hipErrorOutOfMemory, "allocating host memory to validate");
     hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * sizeof(int32_t),
                                   hipMemcpyDeviceToHost, st);
     if (e == hipSuccess)
@@ -572,8 +600,12 @@ pkv_status pkv_paged_attention_multi(const pkv_pool_desc* pool, void* out, const
   if (s != PKV_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (validate) {
-    std::vector<int32_t> ctx((size_t)num_rows);
-    std::vector<int32_t> bt((size_t)(num_rows * max_blocks_per_row));
+    std::vector<int32_t> ctx;
+    if (!host_buffer(ctx, (size_t)num_rows))
+      return hip_fail(hipErrorOutOfMemory, "allocating host memory to validate");
+    std::vector<int32_t> bt;
+    if (!host_buffer(bt, (size_t)(num_rows * max_blocks_per_row)))
+      return hip_fail(hipErrorOutOfMemory, "allocating host memory to validate");
     hipError_t e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * sizeof(int32_t),
                                   hipMemcpyDeviceToHost, st);
     if (e == hipSuccess)
