@@ -36,6 +36,16 @@ hipEvent_t take(PhaseLog& p) {
   return e;
 }
 
+// Returns an event to the phase's spares; if that cannot grow, the event is destroyed
+// (these run inside C-ABI calls, which no exception may leave).
+void keep_spare(PhaseLog& p, hipEvent_t e) noexcept {
+  try {
+    p.spare.push_back(e);
+  } catch (...) {
+    (void)hipEventDestroy(e);
+  }
+}
+
 }  // namespace
 
 void timing_enable(bool on) {
@@ -65,24 +75,38 @@ void timing_end(int phase, hipStream_t stream) {
   if (!p.open) return;
   hipEvent_t stop = take(p);
   if (!stop) return;
-  if (hipEventRecord(stop, stream) != hipSuccess) { p.spare.push_back(p.open); p.spare.push_back(stop); p.open = nullptr; return; }
-  p.pending.emplace_back(p.open, stop);
+  if (hipEventRecord(stop, stream) != hipSuccess) {
+    keep_spare(p, p.open);
+    keep_spare(p, stop);
+    p.open = nullptr;
+    return;
+  }
+  try {
+    p.pending.emplace_back(p.open, stop);
+  } catch (...) {   // the sample is dropped
+    keep_spare(p, p.open);
+    keep_spare(p, stop);
+  }
   p.open = nullptr;
 }
 
 hipError_t timing_read(int phase, double* total_ms, int64_t* launches, bool reset) {
   std::lock_guard<std::mutex> lock(g_mu);
   PhaseLog& p = g_log[phase];
-  for (auto& pr : p.pending) {
+  size_t done = 0;
+  for (; done < p.pending.size(); ++done) {
+    const auto& pr = p.pending[done];
     hipError_t e = hipEventSynchronize(pr.second);
-    if (e != hipSuccess) return e;
     float ms = 0.f;
-    e = hipEventElapsedTime(&ms, pr.first, pr.second);
-    if (e != hipSuccess) return e;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) {   // the samples already summed leave the list
+      p.pending.erase(p.pending.begin(), p.pending.begin() + done);
+      return e;
+    }
     p.total_ms += ms;
     p.launches += 1;
-    p.spare.push_back(pr.first);
-    p.spare.push_back(pr.second);
+    keep_spare(p, pr.first);
+    keep_spare(p, pr.second);
   }
   p.pending.clear();
   *total_ms = p.total_ms;
