@@ -7,7 +7,6 @@
 #include <cstring>
 #include <exception>
 #include <new>
-#include <string>
 #include <vector>
 
 #include "internal.h"
@@ -19,20 +18,19 @@ struct pkv_step_graph {
 
 namespace {
 
-thread_local std::string g_detail;
+// the calling thread's last refusal, in a fixed buffer (nothing here allocates)
+thread_local char g_detail[512];
 
 pkv_status fail(pkv_status s, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
   va_end(ap);
-  g_detail = buf;
   return s;
 }
 
 pkv_status ok() {
-  g_detail.clear();
+  g_detail[0] = '\0';
   return PKV_OK;
 }
 
@@ -371,7 +369,7 @@ const char* pkv_status_str(pkv_status s) {
   return "UNKNOWN";
 }
 
-const char* pkv_last_error_detail(void) { return g_detail.c_str(); }
+const char* pkv_last_error_detail(void) { return g_detail; }
 
 int64_t pkv_sink_slot(const pkv_pool_desc* pool) {
   if (check_pool(pool) != PKV_OK) return -1;
