@@ -33,7 +33,13 @@
  *     outside the pool: a context_len is clamped to [0, max_blocks_per_row *
  *     block_size], a live block id outside [0, num_blocks) is skipped and a write
  *     slot outside [0, sink] is skipped.  Such inputs give unspecified output values
- *     (not a fault) and raise a bit in the device status word (pkv_device_status).
+ *     (not a fault) and raise a bit in the call's own status word, kept in its
+ *     workspace (pkv_workspace_status), and in the device-wide word
+ *     (pkv_device_status).
+ *   - Tuning: every call reads the process-wide work split (pkv_set_tuning) once and
+ *     sizes, checks and launches everything from that one copy; a concurrent
+ *     pkv_set_tuning affects later calls only.  A workspace sized under one tuning can
+ *     be too small under another: the call then refuses with WORKSPACE.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -45,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 /* Element type of q, out, the new K/V and both pools. */
 typedef enum pkv_dtype {
@@ -137,8 +143,12 @@ pkv_status pkv_kv_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
                         const void* k, const void* v, const int64_t* slot_mapping,
                         int64_t num_tokens, int32_t validate, void* stream);
 
-/* Device workspace bytes pkv_paged_attention needs for this batch shape (may be 0).
- * Depends only on the arguments, never on the lengths. */
+/* Device workspace bytes pkv_paged_attention needs for this batch shape under the
+ * current tuning (0 for a shape the call would refuse).  Depends on the arguments and
+ * the tuning's chunk range, never on the lengths.  Layout: a 256-byte counters block
+ * at offset 0 (pkv_plan_info_read), the work list, and float32 partial records of the
+ * rows split into several chunks, at most 16 MiB of them unless the longest chunk
+ * itself splits rows into more. */
 size_t pkv_workspace_bytes(const pkv_pool_desc* pool, int64_t num_rows, int32_t num_heads,
                            int32_t max_blocks_per_row);
 
@@ -150,8 +160,10 @@ size_t pkv_workspace_bytes(const pkv_pool_desc* pool, int64_t num_rows, int32_t 
  *   context_lens  [num_rows] int32; 0 marks a padding row (output zero, nothing read)
  *   scale         multiplies q.k before the softmax
  *   workspace     device scratch of at least pkv_workspace_bytes(...) bytes, owned by
- *                 the caller; its contents on entry do not matter and are undefined
- *                 on return.  Two calls in flight at once need two workspaces.
+ *                 the caller; its contents on entry do not matter.  On return it holds
+ *                 the call's plan and status (pkv_plan_info_read, pkv_workspace_status)
+ *                 until the next call that uses it.  Two calls in flight at once need
+ *                 two workspaces.
  * out[r,h,:] = sum_t softmax_t(scale * q[r,h,:].K[t]) V[t] over t < context_lens[r],
  * accumulated in float32, rounded once to the pool dtype.
  * validate != 0 copies context_lens and block_tables to the host first (synchronising
@@ -242,8 +254,47 @@ const char* pkv_decode_kernel_for(const pkv_pool_desc* pool, int32_t num_heads,
                                   int32_t query_len);
 
 /* Reads (and if `clear` is non-zero, resets) the current device's status word, a
- * bitwise OR of PKV_DEVERR_* raised since the last clear.  Synchronises `stream`. */
+ * bitwise OR of PKV_DEVERR_* raised since the last clear by every call on the device,
+ * from any thread (pkv_kv_write reports its skipped slots here only).  Synchronises
+ * `stream`.  A clear races with concurrent calls; for one attention call's own bits
+ * use pkv_workspace_status. */
 pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
+
+/* The PKV_DEVERR_* bits raised by the kernels of the last attention call
+ * (pkv_paged_attention, _multi, _slots, or a captured step's read) that used this
+ * workspace, and by no other call: the call's plan kernel starts the word afresh.
+ * workspace_bytes must cover the 256-byte counters block.  Synchronises `stream`,
+ * which must be ordered after that call. */
+pkv_status pkv_workspace_status(const void* workspace, size_t workspace_bytes,
+                                uint32_t* flags, void* stream);
+
+/* What the last attention call that used a workspace did, read back from the
+ * counters at the workspace's start: the plan's choices and the decode kernel's own
+ * count of the tiles it streamed (Day 59, "What I learned" 5: the host's count of
+ * walked tiles and the kernel's loop are held to the same lengths).  For tests and
+ * profiling.  Synchronises `stream`, which must be ordered after that call. */
+typedef struct pkv_plan_info {
+  int32_t chunk_tokens;     /* P: tokens per work-list chunk, chosen on the device */
+  int32_t entries;          /* work-list entries: live chunks + one per padding row */
+  int32_t full_chunks;      /* entries of chunks of exactly P tokens */
+  int32_t live_entries;     /* entries of live chunks: sum over rows of cdiv(len, P) */
+  int32_t wide_entries;     /* live entries read by a whole workgroup; the rest (chunks
+                               shorter than solo_tokens) were read by one wave each */
+  int32_t split_rows;       /* rows longer than P, merged over their chunks */
+  int32_t records;          /* their chunks: one float32 partial record per vector */
+  int32_t record_capacity;  /* chunk records the workspace holds */
+  int32_t decode_groups;    /* decode workgroups that took part */
+  int32_t vector_groups;    /* work items per entry: query-vector groups of a row */
+  int32_t tile_tokens;      /* tokens per sub-chunk (tile) of the decode kernel that ran */
+  int32_t token_rows;       /* slot input: rows read token by token */
+  int64_t tiles_walked;     /* tiles the decode kernel streamed, summed over its items:
+                               vector_groups x sum over block-path rows of
+                               cdiv(len, tile_tokens) when every item ran once */
+  int32_t token_entries;    /* slot input: the chunk entries of the token rows */
+  uint32_t status;          /* PKV_DEVERR_* bits of the call (pkv_workspace_status) */
+} pkv_plan_info;
+pkv_status pkv_plan_info_read(const void* workspace, size_t workspace_bytes,
+                              pkv_plan_info* info, void* stream);
 
 /* Work split of the decode read (process-wide).  Each call cuts every row's history
  * into chunks; one (chunk, query head) is a work item of the persistent decode kernel,
@@ -280,9 +331,11 @@ pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream);
  *                         wave each, with no merge across the waves of a workgroup,
  *                         when there is at least one such chunk per decode wave: a power
  *                         of two in [32, 1024], or 1 for none (default 512)
- * A field of 0 leaves that value unchanged.  chunk_min sets pkv_workspace_bytes: set it
- * before sizing workspaces.  Results do not depend on these values beyond float32
- * rounding order.  Returns UNSUPPORTED for other values. */
+ * A field of 0 leaves that value unchanged.  chunk_min and chunk_max set
+ * pkv_workspace_bytes: set them before sizing workspaces.  Results do not depend on
+ * these values beyond float32 rounding order.  Returns UNSUPPORTED for other values,
+ * changing nothing.  Safe to call while other threads run calls (each call uses the
+ * values in force when it starts). */
 typedef struct pkv_tuning {
   int32_t chunk_min;
   int32_t chunk_max;

@@ -34,6 +34,17 @@ class Tuning(ctypes.Structure):
                 ("groups_per_cu", ctypes.c_int32), ("solo_tokens", ctypes.c_int32)]
 
 
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("chunk_tokens", ctypes.c_int32), ("entries", ctypes.c_int32),
+                ("full_chunks", ctypes.c_int32), ("live_entries", ctypes.c_int32),
+                ("wide_entries", ctypes.c_int32), ("split_rows", ctypes.c_int32),
+                ("records", ctypes.c_int32), ("record_capacity", ctypes.c_int32),
+                ("decode_groups", ctypes.c_int32), ("vector_groups", ctypes.c_int32),
+                ("tile_tokens", ctypes.c_int32), ("token_rows", ctypes.c_int32),
+                ("tiles_walked", ctypes.c_int64), ("token_entries", ctypes.c_int32),
+                ("status", ctypes.c_uint32)]
+
+
 _PD = ctypes.POINTER(PoolDesc)
 SIGNATURES = {
     "pkv_abi_version": (_i32, []),
@@ -49,6 +60,8 @@ SIGNATURES = {
     "pkv_paged_attention": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32, _f, _p,
                                    _sz, _i32, _p]),
     "pkv_device_status": (_i32, [ctypes.POINTER(ctypes.c_uint32), _i32, _p]),
+    "pkv_workspace_status": (_i32, [_p, _sz, ctypes.POINTER(ctypes.c_uint32), _p]),
+    "pkv_plan_info_read": (_i32, [_p, _sz, ctypes.POINTER(PlanInfo), _p]),
     "pkv_decode_kernel_for": (ctypes.c_char_p, [_PD, _i32, _i32]),
     "pkv_set_tuning": (_i32, [ctypes.POINTER(Tuning)]),
     "pkv_get_tuning": (_i32, [ctypes.POINTER(Tuning)]),

@@ -393,6 +393,34 @@ def device_status(device=None, clear: bool = True) -> int:
     return int(flags.value)
 
 
+def _workspace_args(workspace: torch.Tensor):
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        _raise("WORKSPACE", "workspace must be a contiguous device tensor")
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def workspace_status(workspace: torch.Tensor) -> int:
+    """PKV_DEVERR_* bits raised by the last attention call that used this workspace
+    (and by no other call); synchronises the current stream."""
+    flags = ctypes.c_uint32(0)
+    ptr, nbytes = _workspace_args(workspace)
+    with torch.cuda.device(workspace.device):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(workspace.device).cuda_stream)
+        _check(_capi.lib().pkv_workspace_status(ptr, nbytes, ctypes.byref(flags), stream))
+    return int(flags.value)
+
+
+def plan_info(workspace: torch.Tensor) -> dict:
+    """The plan and the decode kernel's walk count of the last attention call that used
+    this workspace (pkv_plan_info_read); synchronises the current stream."""
+    info = _capi.PlanInfo()
+    ptr, nbytes = _workspace_args(workspace)
+    with torch.cuda.device(workspace.device):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(workspace.device).cuda_stream)
+        _check(_capi.lib().pkv_plan_info_read(ptr, nbytes, ctypes.byref(info), stream))
+    return {f: int(getattr(info, f)) for f, _ in _capi.PlanInfo._fields_}
+
+
 def decode_kernel_for(k_cache: torch.Tensor, num_heads: int, query_len: int = 1,
                       layout: str = "HND") -> str:
     """Which decode kernel (and query-vector group) a read of this shape runs."""

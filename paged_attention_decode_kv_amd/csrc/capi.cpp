@@ -163,10 +163,11 @@ pkv_status check_write_data(const pkv_pool_desc* pool, const int64_t* slots, int
 
 
 // Work items of one call at the shortest chunk; the plan indexes them in 32 bits.
+// `vectors` is query vectors per row (query_len x heads).
 pkv_status check_attention_items(const pkv_pool_desc* pool, int32_t max_blocks,
-                                 int64_t num_rows, int32_t num_heads) {
+                                 int64_t num_rows, int32_t vectors, const pkv::Tuning& t) {
   const int64_t most_items = num_rows * ((int64_t)max_blocks * pool->block_size /
-                                         pkv::tuning_chunk_min() + 1) * num_heads;
+                                         t.chunk_min + 1) * vectors;
   if (most_items > (int64_t{1} << 30))
     return fail(PKV_ERR_UNSUPPORTED, "rows x heads x chunks too large for one call");
   return PKV_OK;
@@ -197,8 +198,9 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
                             const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int32_t max_blocks,
                             const int32_t* context_lens, int64_t num_rows, int32_t num_heads,
-                            float scale, void* workspace, hipStream_t st,
-                            int32_t query_len = 1, const pkv::WriteArgs* write = nullptr) {
+                            float scale, void* workspace, const pkv::Tuning& t,
+                            hipStream_t st, int32_t query_len = 1,
+                            const pkv::WriteArgs* write = nullptr) {
   pkv::AttnArgs a{};
   a.g = geom(pool);
   a.out = out;
@@ -211,8 +213,8 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
   a.num_heads = num_heads;
   a.max_blocks = max_blocks;
   a.ctx_limit = (int32_t)ctx_limit_of(pool, max_blocks);
-  a.log2_chunk_min = log2i(pkv::tuning_chunk_min());
-  a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
+  a.log2_chunk_min = log2i(t.chunk_min);
+  a.log2_chunk_max = log2i(t.chunk_max);
   a.target_items = 0;
   a.grid_groups = 0;
   a.narrow_groups = 0;
@@ -224,8 +226,9 @@ hipError_t launch_attention(const pkv_pool_desc* pool, void* out, const void* q,
   a.row_flags = nullptr;
   a.flag_stride = 0;
   const pkv::Workspace ws = pkv::carve_workspace(workspace, num_rows, num_heads * query_len,
-                                                 pool->head_dim, max_blocks, pool->block_size);
-  return pkv::launch_paged_attention(a, ws, st, true, write);
+                                                 pool->head_dim, max_blocks, pool->block_size,
+                                                 t);
+  return pkv::launch_paged_attention(a, ws, t, st, true, write);
 }
 
 // ---- slot input ----
@@ -281,7 +284,7 @@ hipError_t launch_attention_slots(const pkv_pool_desc* pool, void* out, const vo
                                   const int64_t* slot_table, int32_t width,
                                   int64_t row_stride, const int32_t* context_lens,
                                   int64_t num_rows, int32_t num_heads, float scale,
-                                  void* workspace, hipStream_t st) {
+                                  void* workspace, const pkv::Tuning& t, hipStream_t st) {
   pkv::AttnArgs a{};
   a.g = geom(pool);
   a.out = out;
@@ -294,8 +297,8 @@ hipError_t launch_attention_slots(const pkv_pool_desc* pool, void* out, const vo
   a.num_heads = num_heads;
   a.max_blocks = (int32_t)(((int64_t)width + pool->block_size - 1) / pool->block_size);
   a.ctx_limit = (int32_t)slot_ctx_limit(pool, width);
-  a.log2_chunk_min = log2i(pkv::tuning_chunk_min());
-  a.log2_chunk_max = log2i(pkv::tuning_chunk_max());
+  a.log2_chunk_min = log2i(t.chunk_min);
+  a.log2_chunk_max = log2i(t.chunk_max);
   a.target_items = 0;
   a.grid_groups = 0;
   a.narrow_groups = 0;
@@ -312,8 +315,8 @@ hipError_t launch_attention_slots(const pkv_pool_desc* pool, void* out, const vo
   sa.width = width;
   const pkv::Workspace ws = pkv::carve_slot_workspace(workspace, num_rows, num_heads,
                                                       pool->head_dim, width,
-                                                      pool->block_size, &sa);
-  return pkv::launch_paged_attention_slots(a, sa, ws, st);
+                                                      pool->block_size, t, &sa);
+  return pkv::launch_paged_attention_slots(a, sa, ws, t, st);
 }
 
 // Records what `record` enqueues on a private stream into an instantiated graph.  The
@@ -436,9 +439,12 @@ pkv_status pkv_kv_write(const pkv_pool_desc* pool, void* k_cache, void* v_cache,
 
 size_t pkv_workspace_bytes(const pkv_pool_desc* pool, int64_t num_rows, int32_t num_heads,
                            int32_t max_blocks_per_row) {
-  if (check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads) != PKV_OK) return 0;
+  const pkv::Tuning t = pkv::tuning_snapshot();
+  if (check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads) != PKV_OK ||
+      check_attention_items(pool, max_blocks_per_row, num_rows, num_heads, t) != PKV_OK)
+    return 0;
   return pkv::workspace_bytes(num_rows, num_heads, pool->head_dim, max_blocks_per_row,
-                              pool->block_size);
+                              pool->block_size, t);
 }
 
 pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void* q,
@@ -447,16 +453,17 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
                                const int32_t* context_lens, int64_t num_rows,
                                int32_t num_heads, float scale, void* workspace,
                                size_t workspace_bytes, int32_t validate, void* stream) {
+  const pkv::Tuning t = pkv::tuning_snapshot();   // this call's one view of the tuning
   pkv_status s = check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads);
   if (s != PKV_OK) return s;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_NULL, "a required pointer is NULL");
-  const size_t need = pkv::workspace_bytes(num_rows, num_heads, pool->head_dim,
-                                           max_blocks_per_row, pool->block_size);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads);
+  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads, t);
   if (s != PKV_OK) return s;
+  const size_t need = pkv::workspace_bytes(num_rows, num_heads, pool->head_dim,
+                                           max_blocks_per_row, pool->block_size, t);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (validate) {
     std::vector<int32_t> ctx;
@@ -477,16 +484,20 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
   }
   hipError_t e = launch_attention(pool, out, q, k_cache, v_cache, block_tables,
                                   max_blocks_per_row, context_lens, num_rows, num_heads, scale,
-                                  workspace, st);
+                                  workspace, t, st);
   if (e != hipSuccess) return hip_fail(e, "launching paged_attention");
   return ok();
 }
 
 size_t pkv_workspace_bytes_slots(const pkv_pool_desc* pool, int64_t num_rows,
                                  int32_t num_heads, int32_t width) {
+  const pkv::Tuning t = pkv::tuning_snapshot();
   if (check_slots_shape(pool, width, width, num_rows, num_heads) != PKV_OK) return 0;
+  const int32_t max_blocks = (int32_t)(((int64_t)width + pool->block_size - 1) /
+                                       pool->block_size);
+  if (check_attention_items(pool, max_blocks, num_rows, num_heads, t) != PKV_OK) return 0;
   return pkv::slot_workspace_bytes(num_rows, num_heads, pool->head_dim, width,
-                                   pool->block_size);
+                                   pool->block_size, t);
 }
 
 pkv_status pkv_check_attention_slots_host(const pkv_pool_desc* pool,
@@ -507,18 +518,19 @@ pkv_status pkv_paged_attention_slots(const pkv_pool_desc* pool, void* out, const
                                      int64_t num_rows, int32_t num_heads, float scale,
                                      void* workspace, size_t workspace_bytes,
                                      int32_t validate, void* stream) {
+  const pkv::Tuning t = pkv::tuning_snapshot();   // this call's one view of the tuning
   pkv_status s = check_slots_shape(pool, width, row_stride, num_rows, num_heads);
   if (s != PKV_OK) return s;
   if (!out || !q || !k_cache || !v_cache || !slot_table || !context_lens)
     return fail(PKV_ERR_NULL, "a required pointer is NULL");
-  const size_t need = pkv::slot_workspace_bytes(num_rows, num_heads, pool->head_dim, width,
-                                                pool->block_size);
-  if (!workspace || workspace_bytes < need)
-    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   const int32_t max_blocks = (int32_t)(((int64_t)width + pool->block_size - 1) /
                                        pool->block_size);
-  s = check_attention_items(pool, max_blocks, num_rows, num_heads);
+  s = check_attention_items(pool, max_blocks, num_rows, num_heads, t);
   if (s != PKV_OK) return s;
+  const size_t need = pkv::slot_workspace_bytes(num_rows, num_heads, pool->head_dim, width,
+                                                pool->block_size, t);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (validate) {
     std::vector<int32_t> ctx;
@@ -541,7 +553,7 @@ pkv_status pkv_paged_attention_slots(const pkv_pool_desc* pool, void* out, const
   }
   hipError_t e = launch_attention_slots(pool, out, q, k_cache, v_cache, slot_table, width,
                                         row_stride, context_lens, num_rows, num_heads, scale,
-                                        workspace, st);
+                                        workspace, t, st);
   if (e != hipSuccess) return hip_fail(e, "launching paged_attention_slots");
   return ok();
 }
@@ -560,10 +572,13 @@ static pkv_status check_multi_shape(const pkv_pool_desc* pool, int32_t max_block
 size_t pkv_workspace_bytes_multi(const pkv_pool_desc* pool, int64_t num_rows,
                                  int32_t query_len, int32_t num_heads,
                                  int32_t max_blocks_per_row) {
-  if (check_multi_shape(pool, max_blocks_per_row, num_rows, query_len, num_heads) != PKV_OK)
+  const pkv::Tuning t = pkv::tuning_snapshot();
+  if (check_multi_shape(pool, max_blocks_per_row, num_rows, query_len, num_heads) != PKV_OK ||
+      check_attention_items(pool, max_blocks_per_row, num_rows, num_heads * query_len, t) !=
+          PKV_OK)
     return 0;
   return pkv::workspace_bytes(num_rows, num_heads * query_len, pool->head_dim,
-                              max_blocks_per_row, pool->block_size);
+                              max_blocks_per_row, pool->block_size, t);
 }
 
 pkv_status pkv_check_attention_multi_host(const pkv_pool_desc* pool,
@@ -586,16 +601,17 @@ pkv_status pkv_paged_attention_multi(const pkv_pool_desc* pool, void* out, const
                                      int32_t query_len, int32_t num_heads, float scale,
                                      void* workspace, size_t workspace_bytes,
                                      int32_t validate, void* stream) {
+  const pkv::Tuning t = pkv::tuning_snapshot();   // this call's one view of the tuning
   pkv_status s = check_multi_shape(pool, max_blocks_per_row, num_rows, query_len, num_heads);
   if (s != PKV_OK) return s;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_NULL, "a required pointer is NULL");
-  const size_t need = pkv::workspace_bytes(num_rows, num_heads * query_len, pool->head_dim,
-                                           max_blocks_per_row, pool->block_size);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads * query_len);
+  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads * query_len, t);
   if (s != PKV_OK) return s;
+  const size_t need = pkv::workspace_bytes(num_rows, num_heads * query_len, pool->head_dim,
+                                           max_blocks_per_row, pool->block_size, t);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (validate) {
     std::vector<int32_t> ctx;
@@ -617,7 +633,7 @@ pkv_status pkv_paged_attention_multi(const pkv_pool_desc* pool, void* out, const
   }
   hipError_t e = launch_attention(pool, out, q, k_cache, v_cache, block_tables,
                                   max_blocks_per_row, context_lens, num_rows, num_heads, scale,
-                                  workspace, st, query_len);
+                                  workspace, t, st, query_len);
   if (e != hipSuccess) return hip_fail(e, "launching paged_attention_multi");
   return ok();
 }
@@ -631,13 +647,64 @@ const char* pkv_decode_kernel_for(const pkv_pool_desc* pool, int32_t num_heads,
   a.g = geom(pool);
   a.num_heads = num_heads;
   a.query_len = query_len;
-  return pkv::decode_kernel_name(a);
+  return pkv::decode_kernel_name(a, pkv::tuning_snapshot());
 }
 
 pkv_status pkv_device_status(uint32_t* flags, int32_t clear, void* stream) {
   if (!flags) return fail(PKV_ERR_NULL, "flags is NULL");
   hipError_t e = pkv::read_device_status(flags, clear, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "reading the device status word");
+  return ok();
+}
+
+// The counters block every attention call keeps at the start of its workspace.
+static pkv_status read_counters(const void* workspace, size_t workspace_bytes, int32_t* c,
+                                void* stream) {
+  if (!workspace) return fail(PKV_ERR_NULL, "workspace is NULL");
+  if (workspace_bytes < (size_t)pkv::kCounterBytes)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes holds no counters (%d bytes)",
+                workspace_bytes, pkv::kCounterBytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(c, workspace, pkv::kNumCounters * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "reading the workspace counters");
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_info_read(const void* workspace, size_t workspace_bytes,
+                              pkv_plan_info* info, void* stream) {
+  if (!info) return fail(PKV_ERR_NULL, "info is NULL");
+  int32_t c[pkv::kNumCounters];
+  const pkv_status s = read_counters(workspace, workspace_bytes, c, stream);
+  if (s != PKV_OK) return s;
+  info->chunk_tokens = c[pkv::kCtrChunk];
+  info->entries = c[pkv::kCtrEntries];
+  info->full_chunks = c[pkv::kCtrSectionA];
+  info->live_entries = c[pkv::kCtrData];
+  info->wide_entries = c[pkv::kCtrWide];
+  info->split_rows = c[pkv::kCtrSplitRows];
+  info->records = c[pkv::kCtrRecords];
+  info->record_capacity = c[pkv::kCtrRecordCap];
+  info->decode_groups = c[pkv::kCtrGroups];
+  info->vector_groups = c[pkv::kCtrVectorGroups];
+  info->tile_tokens = c[pkv::kCtrTileTokens];
+  uint64_t walked = 0;
+  std::memcpy(&walked, &c[pkv::kCtrWalked], sizeof walked);
+  info->tiles_walked = (int64_t)walked;
+  info->token_rows = c[pkv::kCtrTokenRows];
+  info->token_entries = c[pkv::kCtrTokenEntries];
+  info->status = (uint32_t)c[pkv::kCtrStatus];
+  return ok();
+}
+
+pkv_status pkv_workspace_status(const void* workspace, size_t workspace_bytes,
+                                uint32_t* flags, void* stream) {
+  if (!flags) return fail(PKV_ERR_NULL, "flags is NULL");
+  int32_t c[pkv::kNumCounters];
+  const pkv_status s = read_counters(workspace, workspace_bytes, c, stream);
+  if (s != PKV_OK) return s;
+  *flags = (uint32_t)c[pkv::kCtrStatus];
   return ok();
 }
 
@@ -656,16 +723,17 @@ pkv_status pkv_set_tuning(const pkv_tuning* t) {
 
 pkv_status pkv_get_tuning(pkv_tuning* t) {
   if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
-  t->chunk_min = pkv::tuning_chunk_min();
-  t->chunk_max = pkv::tuning_chunk_max();
-  t->decode_waves = pkv::tuning_decode_waves();
-  t->items_per_group = pkv::tuning_items_per_group();
-  t->deal = pkv::tuning_deal_static() ? 1 : 2;
-  t->staging = pkv::tuning_lds_stage() ? 2 : 1;
-  t->max_query_group = pkv::tuning_max_query_group();
-  t->mfma = pkv::tuning_mfma() ? 1 : 2;
-  t->groups_per_cu = pkv::tuning_groups_per_cu();
-  t->solo_tokens = pkv::tuning_solo_tokens();
+  const pkv::Tuning c = pkv::tuning_snapshot();
+  t->chunk_min = c.chunk_min;
+  t->chunk_max = c.chunk_max;
+  t->decode_waves = c.decode_waves;
+  t->items_per_group = c.items_per_group;
+  t->deal = c.deal_static ? 1 : 2;
+  t->staging = c.lds_stage ? 2 : 1;
+  t->max_query_group = c.max_query_group;
+  t->mfma = c.mfma ? 1 : 2;
+  t->groups_per_cu = c.groups_per_cu;
+  t->solo_tokens = c.solo_tokens;
   return ok();
 }
 
@@ -696,23 +764,24 @@ pkv_status pkv_graph_capture(const pkv_pool_desc* pool, void* k_cache, void* v_c
                              pkv_step_graph** graph) {
   if (!graph) return fail(PKV_ERR_NULL, "graph is NULL");
   *graph = nullptr;
+  const pkv::Tuning t = pkv::tuning_snapshot();   // frozen into the graph
   pkv_status s = check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads);
   if (s != PKV_OK) return s;
   if (!k_cache || !v_cache || !k || !v || !slot_mapping || !out || !q || !block_tables ||
       !context_lens)
     return fail(PKV_ERR_NULL, "a required pointer is NULL");
-  const size_t need = pkv::workspace_bytes(num_rows, num_heads, pool->head_dim,
-                                           max_blocks_per_row, pool->block_size);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads);
+  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads, t);
   if (s != PKV_OK) return s;
+  const size_t need = pkv::workspace_bytes(num_rows, num_heads, pool->head_dim,
+                                           max_blocks_per_row, pool->block_size, t);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
 
   // the slot scatter rides in the plan kernel's launch: one kernel fewer per replay
   const pkv::WriteArgs wa = write_args(pool, k_cache, v_cache, k, v, slot_mapping, num_rows);
   return record_graph([&](hipStream_t cs) {
     return launch_attention(pool, out, q, k_cache, v_cache, block_tables, max_blocks_per_row,
-                            context_lens, num_rows, num_heads, scale, workspace, cs, 1, &wa);
+                            context_lens, num_rows, num_heads, scale, workspace, t, cs, 1, &wa);
   }, graph);
 }
 
@@ -725,25 +794,26 @@ pkv_status pkv_graph_capture_slots(const pkv_pool_desc* pool, void* k_cache, voi
                                    size_t workspace_bytes, pkv_step_graph** graph) {
   if (!graph) return fail(PKV_ERR_NULL, "graph is NULL");
   *graph = nullptr;
+  const pkv::Tuning t = pkv::tuning_snapshot();   // frozen into the graph
   pkv_status s = check_slots_shape(pool, width, row_stride, num_rows, num_heads);
   if (s != PKV_OK) return s;
   if (!k_cache || !v_cache || !k || !v || !slot_mapping || !out || !q || !slot_table ||
       !context_lens)
     return fail(PKV_ERR_NULL, "a required pointer is NULL");
-  const size_t need = pkv::slot_workspace_bytes(num_rows, num_heads, pool->head_dim, width,
-                                                pool->block_size);
-  if (!workspace || workspace_bytes < need)
-    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   const int32_t max_blocks = (int32_t)(((int64_t)width + pool->block_size - 1) /
                                        pool->block_size);
-  s = check_attention_items(pool, max_blocks, num_rows, num_heads);
+  s = check_attention_items(pool, max_blocks, num_rows, num_heads, t);
   if (s != PKV_OK) return s;
+  const size_t need = pkv::slot_workspace_bytes(num_rows, num_heads, pool->head_dim, width,
+                                                pool->block_size, t);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   return record_graph([&](hipStream_t cs) {
     hipError_t e = launch_write(pool, k_cache, v_cache, k, v, slot_mapping, num_rows, cs);
     if (e != hipSuccess) return e;
     return launch_attention_slots(pool, out, q, k_cache, v_cache, slot_table, width,
                                   row_stride, context_lens, num_rows, num_heads, scale,
-                                  workspace, cs);
+                                  workspace, t, cs);
   }, graph);
 }
 

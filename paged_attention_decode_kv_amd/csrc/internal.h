@@ -35,19 +35,60 @@ constexpr int kSoloPerWave = 1;
 // Slot input: tokens of one row that one workgroup of the translation pass checks.
 constexpr int kTranslateTokens = 1024;
 
-int tuning_chunk_min();
-int tuning_chunk_max();
-int tuning_decode_waves();
-int tuning_items_per_group();
-int tuning_deal_static();
-int tuning_lds_stage();
-int tuning_max_query_group();
-int tuning_mfma();
-int tuning_groups_per_cu();
-int tuning_solo_tokens();
+// The work-split settings (pkv_set_tuning), process-wide.  Every library call reads
+// them once, as one snapshot, and derives its workspace size, its workspace carve-up,
+// its plan arguments and its kernel choice from that one copy, so a concurrent
+// pkv_set_tuning can change the next call but never split one call's view.
+struct Tuning {
+  int32_t chunk_min;
+  int32_t chunk_max;
+  int32_t decode_waves;
+  int32_t items_per_group;
+  int32_t deal_static;       // 1: whole rounds of full chunks dealt without the queue
+  int32_t lds_stage;         // 1: K/V staged through LDS
+  int32_t max_query_group;
+  int32_t mfma;              // 1: groups of 4-16 vectors on the matrix cores
+  int32_t groups_per_cu;
+  int32_t solo_tokens;
+};
+Tuning tuning_snapshot() noexcept;
+// Raw pkv_tuning values (0 keeps a field); false, changing nothing, for unsupported ones.
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
                 int deal, int staging, int max_query_group, int mfma, int groups_per_cu,
-                int solo_tokens);
+                int solo_tokens) noexcept;
+
+// Partial records (float32 m, l and acc[head_dim] per chunk of a split row and query
+// vector) are kept within this many bytes unless the longest chunk itself splits rows
+// into more: the plan lengthens its chunk until the records fit (record_chunks below).
+constexpr int64_t kPartialBudgetBytes = int64_t{16} << 20;
+
+// The counters block at offset 0 of every workspace (kCounterBytes).  The plan kernel
+// writes every field it uses at each call, so the workspace needs no clearing.
+enum Counter : int {
+  kCtrEntries = 0,       // work-list entries (sections A, B and C)
+  kCtrTicket = 1,        // the decode kernels' queue ticket
+  kCtrChunk = 2,         // chunk length P (tokens)
+  kCtrLog2Chunk = 3,     // log2 P
+  kCtrSectionA = 4,      // entries of full chunks
+  kCtrData = 5,          // entries of sections A and B (live chunks)
+  kCtrTokenRows = 6,     // slot input: rows read token by token
+  kCtrGroups = 7,        // decode workgroups that take part (the rest exit at once)
+  kCtrSplitRows = 8,     // rows split into more than one chunk
+  kCtrTokenEntries = 9,  // slot input: entries of the rows read token by token
+  kCtrWide = 10,         // entries before the single-wave items
+  kCtrTokenTicket = 11,  // slot input: the token kernel's queue ticket
+  kCtrTokenWide = 12,    // slot input: token entries before the short ones
+  kCtrStatus = 13,       // PKV_DEVERR_* bits raised by this call's kernels
+  kCtrWalked = 14,       // 64 bits (14, 15): sub-chunks the decode kernel streamed,
+                         // summed over its items
+  kCtrTileTokens = 16,   // tokens per sub-chunk of the decode kernel that ran
+  kCtrVectorGroups = 17, // work items per entry (query-vector groups) of that kernel
+  kCtrRecords = 18,      // chunk records the plan assigned to split rows
+  kCtrRecordCap = 19,    // chunk records the workspace holds
+  kNumCounters = 20
+};
+constexpr int kCounterBytes = 256;
+static_assert(kNumCounters * 4 <= kCounterBytes, "counters fit their block");
 
 // Pool geometry in elements, derived from the descriptor.
 struct PoolGeom {
@@ -74,24 +115,21 @@ struct WriteArgs {
 
 // Workspace carve-up of one pkv_paged_attention call.
 struct Workspace {
-  int4* entries;        // [max_entries]: {row, chunk (-1: pad row), chunks in row, context_len}
-  int32_t* counters;    // [0] entries, [1] queue ticket, [2] chunk length, [3] its log2,
-                        // [4] section-A entries, [5] section-A+B entries,
-                        // [6] rows read token by token (slot input),
-                        // [7] decode workgroups that take part (the rest exit at once),
-                        // [8] rows split into more than one chunk,
-                        // [9] entries of the rows read token by token (slot input),
-                        // [10] entries before the single-wave items (chunks shorter
-                        // than AttnArgs::solo_tokens), [11] token queue ticket,
-                        // [12] token entries before the short ones
+  int32_t* counters;    // [kNumCounters] at offset 0 (enum Counter)
+  int4* entries;        // [max_entries]: {row, chunk (-1: pad row), record (-1: the row is
+                        // one chunk, its output is written directly), context_len}
   int32_t* row_ctx;     // [rows]: each row's length as the block path reads it
-  int32_t* irregular;   // [rows]: the rows read token by token, counters[6] of them
-  int2* split_rows;     // [rows]: {row, length} of the rows split into chunks, counters[8]
+  int32_t* row_rec;     // [rows]: first chunk record of a split row (slot input's token
+                        // rows read it; only split rows' values are meaningful)
+  int32_t* irregular;   // [rows]: the rows read token by token, counters[kCtrTokenRows]
+  int4* split_rows;     // [rows]: {row, length, first record, 0} of the split rows, in row
+                        // order, counters[kCtrSplitRows] of them
   int2* token_entries;  // slot input only (else null): [rows * max_chunks] {row, chunk} of
-                        // the rows read token by token, longest chunk first, counters[9]
-  float* partials;      // [rows][heads][max_chunks][head_dim + 4]: m (log2 units), l, -, -, acc
+                        // the rows read token by token, longest chunk first
+  float* partials;      // [record_chunks][vectors per row][head_dim + 4]: m (log2 units),
+                        // l, -, -, acc; chunk c of a split row is record first + c
   int64_t max_entries;
-  int32_t max_chunks;
+  int32_t record_chunks;
 };
 
 struct AttnArgs {
@@ -124,6 +162,8 @@ struct AttnArgs {
   const int32_t* row_flags;
   int32_t flag_stride;
   int32_t token_waves;   // slot input only: waves of the token kernels' grid
+  int32_t record_chunks; // chunk records the workspace holds: the plan lengthens its chunk
+                         // until the split rows' chunks fit
 };
 
 // The slot rectangle of a read addressed per token, and what the translation pass
@@ -138,30 +178,36 @@ struct SlotArgs {
   int32_t* row_flags;      // out: [rows][flag_stride]
 };
 
-size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
-                       int32_t max_blocks, int32_t block_size);
-Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads,
-                          int32_t head_dim, int32_t max_blocks, int32_t block_size);
+// Sizes and carve-ups follow one tuning snapshot; `vectors` is query vectors per row
+// (query_len x heads).
+int32_t record_chunks_for(int64_t num_rows, int32_t vectors, int32_t head_dim,
+                          int32_t max_blocks, int32_t block_size, const Tuning& t);
+size_t workspace_bytes(int64_t num_rows, int32_t vectors, int32_t head_dim,
+                       int32_t max_blocks, int32_t block_size, const Tuning& t);
+Workspace carve_workspace(void* base, int64_t num_rows, int32_t vectors, int32_t head_dim,
+                          int32_t max_blocks, int32_t block_size, const Tuning& t);
 
-// Slot input: the derived table and flags, then the block-path workspace.
+// Slot input: the block-path workspace, then the derived table, flags and token entries.
 size_t slot_workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
-                            int32_t width, int32_t block_size);
+                            int32_t width, int32_t block_size, const Tuning& t);
 Workspace carve_slot_workspace(void* base, int64_t num_rows, int32_t num_heads,
                                int32_t head_dim, int32_t width, int32_t block_size,
-                               SlotArgs* s);
+                               const Tuning& t, SlotArgs* s);
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 // combine = false leaves split rows' partials for a later launch_combine (slot input);
 // `write`, if given, is the step's slot scatter, run inside the plan kernel's launch
 // (a captured step)
-hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
-                                  bool combine = true, const WriteArgs* write = nullptr);
+hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, const Tuning& t,
+                                  hipStream_t stream, bool combine = true,
+                                  const WriteArgs* write = nullptr);
 hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& s,
-                                        const Workspace& ws, hipStream_t stream);
+                                        const Workspace& ws, const Tuning& t,
+                                        hipStream_t stream);
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream);
-// which decode kernel (and query-vector group) a read of this shape runs, under the
-// current tuning (uses a.g, a.num_heads, a.query_len)
-const char* decode_kernel_name(const AttnArgs& a);
+// which decode kernel (and query-vector group) a read of this shape runs under tuning t
+// (uses a.g, a.num_heads, a.query_len)
+const char* decode_kernel_name(const AttnArgs& a, const Tuning& t);
 
 // Event-pair timing of kernel phases (pkv_timing_*).  begin/end bracket one launch.
 void timing_begin(int phase, hipStream_t stream);

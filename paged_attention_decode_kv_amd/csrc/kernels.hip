@@ -43,7 +43,9 @@
 
 namespace pkv {
 
-__device__ unsigned int g_status;   // PKV_DEVERR_* bits, see pkv_device_status
+// PKV_DEVERR_* bits raised since the last clear by any call on this device (see
+// pkv_device_status); each call also keeps its own bits in its workspace's counters.
+__device__ unsigned int g_status;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
@@ -168,6 +170,13 @@ __device__ __forceinline__ void store_out(X* p, X v) {
   __builtin_nontemporal_store(v, p);
 }
 
+// A bad input skipped by a kernel of an attention call: the bit goes to the call's own
+// status word (in its workspace) and to the device-wide one.
+__device__ __forceinline__ void raise_status(const Workspace& ws, unsigned bits) {
+  atomicOr(&g_status, bits);
+  atomicOr(reinterpret_cast<unsigned*>(ws.counters + kCtrStatus), bits);
+}
+
 // ------------------------------------------------------------------------- //
 // slot scatter
 // ------------------------------------------------------------------------- //
@@ -253,18 +262,51 @@ __device__ int block_exclusive_scan(int x, int* s_wave, int* total) {
   return prefix;
 }
 
+// The same for N values per thread at once (one set of barriers): each x[k] becomes the
+// thread's exclusive prefix of value k, and total[k] the workgroup's sum of it.
+template <int N>
+__device__ void block_exclusive_scan_n(int (&x)[N], int (*s_wave)[N], int (&total)[N]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kPlanThreads / 64;
+  int incl[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) incl[k] = wave_inclusive_scan(x[k]);
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) s_wave[wave][k] = incl[k];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int v = lane < kWaves ? s_wave[lane][k] : 0;
+      const int vi = wave_inclusive_scan(v);
+      if (lane < kWaves) s_wave[lane][k] = vi;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int prefix = (wave > 0 ? s_wave[wave - 1][k] : 0) + incl[k] - x[k];
+    total[k] = s_wave[kWaves - 1][k];
+    x[k] = prefix;
+  }
+  __syncthreads();
+}
+
 // A row's length as the block path reads it: clamped to what the table addresses (the
 // first pass reports a bad length), and 0 for a row of a slot input whose live slots
 // are not block structured, which the token-by-token kernel reads instead.
-__device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool report,
+// `status` (the plan's LDS word, or null) collects the bits of bad lengths.
+__device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, int* status,
                                         bool* irregular, int* clamped = nullptr) {
   int ctx = a.context_lens[r];
   if (ctx < 0 || ctx > a.ctx_limit) {
-    if (report) atomicOr(&g_status, PKV_DEVERR_CONTEXT_BOUNDS);
+    if (status) atomicOr(status, (int)PKV_DEVERR_CONTEXT_BOUNDS);
     ctx = ctx < 0 ? 0 : a.ctx_limit;
   }
   // a live row shorter than its new tokens: its earliest queries see nothing (zeros)
-  if (report && ctx > 0 && ctx < a.query_len) atomicOr(&g_status, PKV_DEVERR_CONTEXT_BOUNDS);
+  if (status && ctx > 0 && ctx < a.query_len) atomicOr(status, (int)PKV_DEVERR_CONTEXT_BOUNDS);
   bool irr = false;
   if (a.row_flags != nullptr && ctx > 0) {
     const int32_t* f = a.row_flags + r * a.flag_stride;
@@ -281,22 +323,18 @@ __device__ __forceinline__ int plan_ctx(const AttnArgs& a, int64_t r, bool repor
 // The chunk length P is the largest power of two in [chunk_min, chunk_max] whose
 // (chunk, head) item count reaches target_items (enough items per decode workgroup
 // for the queue to balance) and whose chunk holds at most a third of a workgroup's
-// share of the batch's tokens, else chunk_min.  Longer chunks split fewer rows (fewer
-// partial records to write and merge); the share bound keeps the longest item short
-// enough for the longest-first order to balance.  Entries are ordered longest first
-// so that the queue's tail is short work:
+// share of the batch's tokens, else chunk_min; then the shortest at least that long
+// whose split rows' chunks fit the workspace's a.record_chunks partial records.
+// Longer chunks split fewer rows (fewer partial records to write and merge); the share
+// bound keeps the longest item short enough for the longest-first order to balance.
+// Entries are ordered longest first so that the queue's tail is short work:
 //   A. every full chunk (P tokens) of every row, rows in order;
 //   B. every row's trailing partial chunk, by length, longest first (in buckets of
 //      P / 1024 tokens when P > 1024);
 //   C. one zero-output entry per padding row.
-// counters[0] = entries, [1] = queue ticket (reset to 0), [2] = P, [3] = log2 P,
-// [4] = entries in section A, [5] = entries in sections A and B, [6] = rows of a slot
-// input left to the token-by-token kernel (listed in ws.irregular), [7] = decode
-// workgroups that take part, [8] = split rows (listed with their lengths in
-// ws.split_rows for the combine kernel), [9] = entries of the rows read token by token
-// (ws.token_entries), [10] = entries before the single-wave items (those of fewer than
-// a.solo_tokens tokens, the tail of the longest-first order), [11] = the token kernel's
-// queue ticket (reset to 0), [12] = token entries before the short ones.  Every row's
+// A row longer than P is split: its chunks c = 0, 1, ... own partial records first + c,
+// the rows' records laid out in row order (ws.row_rec, ws.split_rows).  The counters
+// (enum Counter) are all written here, so the workspace needs no clearing; every row's
 // clamped length goes to ws.row_ctx.
 __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   constexpr int kCand = 7;                 // chunk_max / chunk_min <= kMaxChunkRatio
@@ -307,28 +345,34 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   // the longest item may take at most 1 / kBalance of a workgroup's share of the work
   constexpr int kBalance = 3;
   __shared__ int s_wave[kPlanThreads / 64];
+  __shared__ int s_scan[kPlanThreads / 64][4];
   __shared__ int s_bin_start[kBins];       // first B position of each remainder bin
   __shared__ int s_bin_fill[kBins];
   __shared__ int s_pad_fill;
   __shared__ int s_irregular;
-  __shared__ int s_split;
+  __shared__ int s_status;
   __shared__ int s_cand[kCand];
+  __shared__ int s_spl[kCand];
   const int t = threadIdx.x;
   const int lane = t & 63;
-  if (t < kCand) s_cand[t] = 0;
+  if (t < kCand) {
+    s_cand[t] = 0;
+    s_spl[t] = 0;
+  }
   if (t == 0) {
     s_pad_fill = 0;
     s_irregular = 0;
-    s_split = 0;
+    s_status = 0;
   }
   __syncthreads();
 
-  // pass 0: chunk count of every candidate length; row lengths; irregular rows
+  // pass 0: chunk count and split rows' chunk count of every candidate length; row
+  // lengths; irregular rows
   const int lmin = a.log2_chunk_min;
   const int ncand = a.log2_chunk_max - lmin + 1;
-  int cnt[kCand];
+  int cnt[kCand], spl[kCand];
 #pragma unroll
-  for (int k = 0; k < kCand; ++k) cnt[k] = 0;
+  for (int k = 0; k < kCand; ++k) cnt[k] = spl[k] = 0;
   // the lengths of this thread's first kKeep rows stay in registers for passes 1 and 2
   constexpr int kKeep = 4;
   int kept[kKeep];
@@ -337,7 +381,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
     bool irr;
     int full_ctx;
-    const int ctx = plan_ctx(a, r, true, &irr, &full_ctx);
+    const int ctx = plan_ctx(a, r, &s_status, &irr, &full_ctx);
 #pragma unroll
     for (int k = 0; k < kKeep; ++k)
       if (r == t + (int64_t)k * kPlanThreads) kept[k] = ctx;
@@ -347,13 +391,20 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     // (the chunk length serves the rows read token by token too: counted by their full
     // length, so that a batch of them is not cut into the shortest chunks)
 #pragma unroll
-    for (int k = 0; k < kCand; ++k)
-      cnt[k] += (full_ctx + (1 << (lmin + k)) - 1) >> (lmin + k);
+    for (int k = 0; k < kCand; ++k) {
+      const int n = (full_ctx + (1 << (lmin + k)) - 1) >> (lmin + k);
+      cnt[k] += n;
+      spl[k] += n > 1 ? n : 0;
+    }
   }
 #pragma unroll
   for (int k = 0; k < kCand; ++k) {
     const int v = wave_sum_i(cnt[k]);
-    if (lane == 0 && k < ncand) atomicAdd(&s_cand[k], v);
+    const int vs = wave_sum_i(spl[k]);
+    if (lane == 0 && k < ncand) {
+      atomicAdd(&s_cand[k], v);
+      atomicAdd(&s_spl[k], vs);
+    }
   }
   __syncthreads();
   // Workgroups and chunk length.  A batch that gives 8 waves per compute unit enough
@@ -402,6 +453,9 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
       if ((int64_t)s_cand[k] * per_entry >= a.target_items / 4) found = k;
     lp = lmin + (found > 0 ? found : 0);
   }
+  // the split rows' partial records must fit the workspace (they always do at the
+  // longest candidate, which the workspace is sized for)
+  while (lp < lmin + ncand - 1 && s_spl[lp - lmin] > a.record_chunks) ++lp;
   const int P = 1 << lp;
   const int bshift = lp > 10 ? lp - 10 : 0;   // remainder -> bin (kBins = 1024)
   const int nbins = P >> bshift;
@@ -416,24 +470,43 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
 #pragma unroll
     for (int i = 0; i < kKeep; ++i)
       if (k == i) v = kept[i];
-    return k < kKeep ? v : plan_ctx(a, r, false, nullptr);
+    return k < kKeep ? v : plan_ctx(a, r, nullptr, nullptr);
   };
 
-  // pass 1: section A, remainder histogram, pad count
-  int total_a = 0, n_pad = 0;
+  // pass 1: section A; the split rows in row order, with their first partial records;
+  // remainder histogram; pad count
+  int total_a = 0, n_pad = 0, total_rec = 0, n_split = 0;
+  int kept_rec[kKeep];
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) kept_rec[k] = -1;
   for (int64_t base = 0; base < a.num_rows; base += kPlanThreads) {
     const int64_t r = base + t;
-    const int ctx = r < a.num_rows ? row_len(r) : 0;
+    const bool in = r < a.num_rows;
+    const int ctx = in ? row_len(r) : 0;
+    // a row read token by token (slot input) splits by its full length
+    const int fl = in ? (a.row_flags != nullptr ? ws.row_ctx[r] : ctx) : 0;
+    const int fnch = (fl + P - 1) >> lp;
+    const bool split = fnch > 1;
     const int full = ctx >> lp;
-    const int nch = (ctx + P - 1) >> lp;
-    int tile_a, tile_pad;
-    const int at = total_a + block_exclusive_scan(full, s_wave, &tile_a);
-    block_exclusive_scan(r < a.num_rows && ctx == 0 ? 1 : 0, s_wave, &tile_pad);
-    for (int k = 0; k < full; ++k) ws.entries[at + k] = make_int4((int)r, k, nch, ctx);
-    if (r < a.num_rows && (ctx & (P - 1)) != 0)
-      atomicAdd(&s_bin_fill[(ctx & (P - 1)) >> bshift], 1);
-    total_a += tile_a;
-    n_pad += tile_pad;
+    int v[4] = {full, in && ctx == 0 ? 1 : 0, split ? fnch : 0, split ? 1 : 0};
+    int tot[4];
+    block_exclusive_scan_n<4>(v, s_scan, tot);
+    const int rec0 = split ? total_rec + v[2] : -1;
+    for (int k = 0; k < full; ++k)
+      ws.entries[total_a + v[0] + k] = make_int4((int)r, k, split ? rec0 + k : -1, ctx);
+    if (in) {
+      ws.row_rec[r] = rec0;
+      const int64_t kk = base / kPlanThreads;
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i)
+        if (kk == i) kept_rec[i] = rec0;
+    }
+    if (split) ws.split_rows[n_split + v[3]] = make_int4((int)r, fl, rec0, 0);
+    if (in && (ctx & (P - 1)) != 0) atomicAdd(&s_bin_fill[(ctx & (P - 1)) >> bshift], 1);
+    total_a += tot[0];
+    n_pad += tot[1];
+    total_rec += tot[2];
+    n_split += tot[3];
   }
   __syncthreads();
   // bins of section B in descending remainder order: thread t owns the t-th from the top
@@ -447,21 +520,24 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   __syncthreads();
   if (t < nbins) s_bin_fill[t] = 0;
   __syncthreads();
-  // pass 2: place sections B and C; list the split rows for the combine kernel (a row
-  // read token by token splits by its full length, which this thread wrote in pass 0)
+  // pass 2: place sections B and C
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
     const int ctx = row_len(r);
     const int rem = ctx & (P - 1);
-    const int nch = (ctx + P - 1) >> lp;
-    const int full = a.row_flags != nullptr ? ws.row_ctx[r] : ctx;
-    if (full > P) ws.split_rows[atomicAdd(&s_split, 1)] = make_int2((int)r, full);
     if (rem != 0) {
+      const int64_t k = (r - t) / kPlanThreads;
+      int rec0 = 0;
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i)
+        if (k == i) rec0 = kept_rec[i];
+      if (k >= kKeep) rec0 = ws.row_rec[r];   // written by this thread in pass 1
+      const int chunk = ctx >> lp;
       const int pos = total_a + s_bin_start[rem >> bshift] +
                       atomicAdd(&s_bin_fill[rem >> bshift], 1);
-      ws.entries[pos] = make_int4((int)r, ctx >> lp, nch, ctx);
+      ws.entries[pos] = make_int4((int)r, chunk, rec0 >= 0 ? rec0 + chunk : -1, ctx);
     } else if (ctx == 0) {
       const int pos = total_a + total_b + atomicAdd(&s_pad_fill, 1);
-      ws.entries[pos] = make_int4((int)r, -1, 0, 0);
+      ws.entries[pos] = make_int4((int)r, -1, -1, 0);
     }
   }
   __syncthreads();
@@ -532,19 +608,29 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     __syncthreads();
   }
   if (t == 0) {
-    ws.counters[0] = total_a + total_b + n_pad;
-    ws.counters[1] = 0;
-    ws.counters[2] = P;
-    ws.counters[3] = lp;
-    ws.counters[4] = total_a;
-    ws.counters[5] = total_a + total_b;
-    ws.counters[6] = s_irregular;
-    ws.counters[7] = narrow ? a.narrow_groups : a.grid_groups;
-    ws.counters[8] = s_split;
-    ws.counters[9] = total_ta + total_tb;
-    ws.counters[10] = n_wide;
-    ws.counters[11] = 0;
-    ws.counters[12] = n_tok_wide;
+    int* c = ws.counters;
+    c[kCtrEntries] = total_a + total_b + n_pad;
+    c[kCtrTicket] = 0;
+    c[kCtrChunk] = P;
+    c[kCtrLog2Chunk] = lp;
+    c[kCtrSectionA] = total_a;
+    c[kCtrData] = total_a + total_b;
+    c[kCtrTokenRows] = s_irregular;
+    c[kCtrGroups] = narrow ? a.narrow_groups : a.grid_groups;
+    c[kCtrSplitRows] = n_split;
+    c[kCtrTokenEntries] = total_ta + total_tb;
+    c[kCtrWide] = n_wide;
+    c[kCtrTokenTicket] = 0;
+    c[kCtrTokenWide] = n_tok_wide;
+    // this call's status starts with the plan's own findings
+    c[kCtrStatus] = s_status;
+    c[kCtrWalked] = 0;
+    c[kCtrWalked + 1] = 0;
+    c[kCtrTileTokens] = 0;
+    c[kCtrVectorGroups] = 0;
+    c[kCtrRecords] = total_rec;
+    c[kCtrRecordCap] = a.record_chunks;
+    if (s_status != 0) atomicOr(&g_status, (unsigned)s_status);
   }
 }
 
@@ -610,7 +696,9 @@ __device__ __forceinline__ int vec_query(const AttnArgs& a, int v) {
 // the row's history, group of QG query vectors that share one KV head).
 template <int QG, int NR>
 struct ItemMeta {
-  int r, hg, chunk, nch, ctx;   // hg: vector group; vectors hg*QG .. hg*QG + QG - 1
+  // hg: vector group (vectors hg*QG .. hg*QG + QG - 1); rec: the chunk's partial record
+  // (-1: the row is one chunk)
+  int r, hg, chunk, rec, ctx;
   uint4 q[QG];   // this lane's 16 bytes of each vector's query
   int last[QG];  // each vector's last visible position (len - query_len + i)
   int blk[NR];   // lane i: block id of this wave's sub-chunks i, 64 + i, ...
@@ -653,7 +741,7 @@ __device__ __forceinline__ ItemMeta<QG, NR> finish_meta(const AttnArgs& a, int4 
   m.hg = item - e * groups;
   m.r = __builtin_amdgcn_readfirstlane(ent.x);
   m.chunk = __builtin_amdgcn_readfirstlane(ent.y);
-  m.nch = __builtin_amdgcn_readfirstlane(ent.z);
+  m.rec = __builtin_amdgcn_readfirstlane(ent.z);
   m.ctx = __builtin_amdgcn_readfirstlane(ent.w);
 #pragma unroll
   for (int j = 0; j < QG; ++j) {
@@ -840,33 +928,56 @@ __device__ __forceinline__ void merge_lane_groups(float (&m)[QG], float (&l)[QG]
   }
 }
 
+// Float offset of query vector v's partial record of chunk record `rec` (records of
+// one chunk hold every vector of the row).
+template <int D>
+__device__ __forceinline__ int64_t record_offset(int rec, int n_vec, int v) {
+  return ((int64_t)rec * n_vec + v) * (D + 4);
+}
+
 // The finished state of query vector v of row r over one chunk, written by the LPT
-// lanes of one lane group (this lane's piece `sub`): the output (a row of one chunk:
-// acc / l, zeros where nothing was visible) or the chunk's partial record (m, l, acc)
-// for the combine kernel.
+// lanes of one lane group (this lane's piece `sub`): the output (a row of one chunk,
+// rec < 0: acc / l, zeros where nothing was visible) or the chunk's partial record
+// (m, l, acc) for the combine kernel.
 template <typename T, int D>
 __device__ __forceinline__ void write_item_result(const AttnArgs& a, const Workspace& ws,
-                                                  int r, int v, int chunk, int nch, int n_vec,
+                                                  int r, int v, int rec, int n_vec,
                                                   int sub, float mj, float lj,
                                                   float (&aj)[Elem<T>::kPerLane]) {
   constexpr int E = Elem<T>::kPerLane;
-  if (nch == 1) {
+  if (rec < 0) {
     const float inv = lj > 0.f ? 1.0f / lj : 0.f;
 #pragma unroll
     for (int i = 0; i < E; ++i) aj[i] *= inv;
     store16_out(static_cast<T*>(a.out) + vec_slot(a, r, v) * D + sub * E, Elem<T>::pack(aj));
   } else {
-    const int64_t rv = (int64_t)r * n_vec + v;
-    float* rec = ws.partials + (rv * ws.max_chunks + chunk) * (D + 4);
+    float* p = ws.partials + record_offset<D>(rec, n_vec, v);
     if (sub == 0) {
-      rec[0] = mj;
-      rec[1] = lj;
+      p[0] = mj;
+      p[1] = lj;
     }
 #pragma unroll
     for (int i = 0; i < E; i += 4)
-      store16(rec + 4 + sub * E + i, make_uint4(__float_as_uint(aj[i]), __float_as_uint(aj[i + 1]),
-                                                __float_as_uint(aj[i + 2]),
-                                                __float_as_uint(aj[i + 3])));
+      store16(p + 4 + sub * E + i, make_uint4(__float_as_uint(aj[i]), __float_as_uint(aj[i + 1]),
+                                              __float_as_uint(aj[i + 2]),
+                                              __float_as_uint(aj[i + 3])));
+  }
+}
+
+// The sub-chunks a workgroup streamed (each wave's count in s_walk[wave]), added to the
+// call's counter once per workgroup: the kernel's own loop count, which the tests hold
+// against the host's tile accounting.  All waves of the workgroup call this.
+template <int WAVES>
+__device__ __forceinline__ void report_walked(const Workspace& ws, int* s_walk, int walked) {
+  if ((threadIdx.x & 63) == 0) s_walk[threadIdx.x >> 6] = walked;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += s_walk[w];
+    if (sum != 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(ws.counters + kCtrWalked),
+                (unsigned long long)sum);
   }
 }
 
@@ -925,6 +1036,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   __shared__ int s_ticket[2];
   __shared__ float s_m[2][QG][WAVES], s_l[2][QG][WAVES];
   __shared__ float s_acc[2][QG][WAVES][D];
+  __shared__ int s_walk[WAVES];
 
   const int n_vec = a.query_len * a.num_heads;   // query vectors per row
   const int groups = n_vec / QG;                 // items per work-list entry
@@ -936,6 +1048,10 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int n_items = ws.counters[0] * groups;
   const int G = ws.counters[7];                  // workgroups taking part
   if ((int)blockIdx.x >= G) return;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {     // what the walk count is counted in
+    ws.counters[kCtrTileTokens] = CH;
+    ws.counters[kCtrVectorGroups] = groups;
+  }
   const int n_static = min(ws.counters[4] * groups, n_wide);   // section A items
   const int n_dealt = a.deal_static ? n_static / G * G : 0;
   const int log2_bs = a.g.log2_bs;
@@ -943,6 +1059,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int64_t tok_bytes = a.g.tok_stride * ES;
   const int64_t blk_bytes = a.g.blk_stride * ES;
   const int64_t head_bytes = a.g.head_stride * ES;
+  int walked = 0;   // sub-chunks this wave streamed (wide items: wave 0 counts each once)
   // byte offset of this lane's 16 bytes in the u-th wave load of a sub-chunk
   uint32_t voff[U];
 #pragma unroll
@@ -1032,6 +1149,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
         last_rel[j] = __builtin_amdgcn_readfirstlane(sc.last[j]) - ca.t_begin;
 
       const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
+      walked += n_sub;
       if constexpr (LDS_STAGE) {
         if (!staged) stage_from(ca, 0, 0, sc.blk);
       }
@@ -1056,8 +1174,8 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       if (g == 0) {
 #pragma unroll
         for (int j = 0; j < QG; ++j)
-          write_item_result<T, D>(a, ws, sc.r, hg * QG + j, chunk, sc.nch, n_vec, sub, m[j],
-                                  l[j], acc[j]);
+          write_item_result<T, D>(a, ws, sc.r, hg * QG + j, sc.rec, n_vec, sub, m[j], l[j],
+                                  acc[j]);
       }
       it = nx;
       sc = sn;
@@ -1100,6 +1218,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       last_rel[j] = __builtin_amdgcn_readfirstlane(cur.last[j]) - ca.t_begin;
 
     const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
+    if (wave == 0) walked += n_sub;
     if constexpr (LDS_STAGE) {
       if (wave < n_sub) stage_from(ca, wave, 0, cur.blk);
     }
@@ -1160,8 +1279,7 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
           }
           mj = mx;
         }
-        write_item_result<T, D>(a, ws, cur.r, hg * QG + j, chunk, cur.nch, n_vec, sub, mj, lj,
-                                aj);
+        write_item_result<T, D>(a, ws, cur.r, hg * QG + j, cur.rec, n_vec, sub, mj, lj, aj);
       }
     }
     buf ^= 1;
@@ -1170,7 +1288,8 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     next = after;
   }
 
-  if (bad_block && lane == 0) atomicOr(&g_status, PKV_DEVERR_BLOCK_ID);
+  if (bad_block && lane == 0) raise_status(ws, PKV_DEVERR_BLOCK_ID);
+  report_walked<WAVES>(ws, s_walk, walked);
   // padding rows: zero output, nothing read
   for (int it = n_data + (int)blockIdx.x; it < n_items; it += G) {
     const int e = it / groups;
@@ -1225,7 +1344,7 @@ __device__ __forceinline__ constexpr int piece_mask(int u, int g) {
 
 template <int D, int NR>
 struct MfmaMeta {
-  int r, hg, chunk, nch, ctx;
+  int r, hg, chunk, rec, ctx;   // rec: the chunk's partial record (-1: one-chunk row)
   int last;           // lane: last visible position of vector hg*QG + l%16 (-1: none)
   uint4 q[D / 32];    // lane: 8 dims (32 s + 8 (l/16) ..) of that vector's query
   int blk[NR];   // lane i: block id of this wave's sub-chunks i, 64 + i, ...
@@ -1241,7 +1360,7 @@ __device__ __forceinline__ MfmaMeta<D, NR> finish_meta_mfma(const AttnArgs& a, i
   m.hg = item - e * groups;
   m.r = __builtin_amdgcn_readfirstlane(ent.x);
   m.chunk = __builtin_amdgcn_readfirstlane(ent.y);
-  m.nch = __builtin_amdgcn_readfirstlane(ent.z);
+  m.rec = __builtin_amdgcn_readfirstlane(ent.z);
   m.ctx = __builtin_amdgcn_readfirstlane(ent.w);
   const int v = m.hg * QG + col;
   m.last = col < QG ? m.ctx - a.query_len + vec_query(a, v) : -1;
@@ -1365,6 +1484,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   static_assert(QG * D * 4 <= STAGE, "a wave's merge state fits its stage");
   __shared__ int s_ticket[2];
   __shared__ float s_m[2][QG][WAVES], s_l[2][QG][WAVES];
+  __shared__ int s_walk[WAVES];
 
   const int n_vec = a.query_len * a.num_heads;
   const int groups = n_vec / QG;
@@ -1376,6 +1496,11 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   const int n_items = ws.counters[0] * groups;
   const int G = ws.counters[7];                  // workgroups taking part
   if ((int)blockIdx.x >= G) return;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {     // what the walk count is counted in
+    ws.counters[kCtrTileTokens] = CH;
+    ws.counters[kCtrVectorGroups] = groups;
+  }
+  int walked = 0;   // sub-chunks this wave streamed (wide items: wave 0 counts each once)
   const int n_static = min(ws.counters[4] * groups, n_wide);
   const int n_dealt = a.deal_static ? n_static / G * G : 0;
   const int log2_bs = a.g.log2_bs;
@@ -1454,6 +1579,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       for (int o = 0; o < NO; ++o) acc[o] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       float m = -INFINITY, l = 0.f;
       const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
+      walked += n_sub;
       if (!staged) stage_in(ca, 0, 0, sc_m.blk);
       staged = false;
       for (int s = 0; s < n_sub; ++s) {
@@ -1479,7 +1605,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       l += __shfl_xor(l, 32);
       if (col < QG) {
         const int v = hg * QG + col;
-        if (sc_m.nch == 1) {
+        if (sc_m.rec < 0) {
           const float inv = l > 0.f ? 1.0f / l : 0.f;
           T* op = static_cast<T*>(a.out) + vec_slot(a, sc_m.r, v) * D + 4 * grp;
 #pragma unroll
@@ -1488,8 +1614,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
                       u32x2_nt{Elem<uint16_t>::cvt2(acc[o][0] * inv, acc[o][1] * inv),
                                Elem<uint16_t>::cvt2(acc[o][2] * inv, acc[o][3] * inv)});
         } else {
-          float* rec = ws.partials +
-                       (((int64_t)sc_m.r * n_vec + v) * ws.max_chunks + chunk) * (D + 4);
+          float* rec = ws.partials + record_offset<D>(sc_m.rec, n_vec, v);
           if (grp == 0) {
             rec[0] = m;
             rec[1] = l;
@@ -1534,6 +1659,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     float m = -INFINITY, l = 0.f;
 
     const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
+    if (wave == 0) walked += n_sub;
     if (wave < n_sub) stage_in(ca, wave, 0, cur.blk);
     for (int s = wave; s < n_sub; s += WAVES) {
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
@@ -1589,7 +1715,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
         for (int i = 0; i < PER; ++i) y[i] += pw[(lane * PER + i) ^ sw] * f;
       }
       const int v = hg * QG + j;
-      if (cur.nch == 1) {
+      if (cur.rec < 0) {
         const float inv = lj > 0.f ? 1.0f / lj : 0.f;
         T* op = static_cast<T*>(a.out) + vec_slot(a, cur.r, v) * D + lane * PER;
         if constexpr (PER == 1) {
@@ -1601,7 +1727,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
                       Elem<uint16_t>::cvt2(y[i] * inv, y[i + 1] * inv));
         }
       } else {
-        float* rec = ws.partials + (((int64_t)cur.r * n_vec + v) * ws.max_chunks + chunk) * (D + 4);
+        float* rec = ws.partials + record_offset<D>(cur.rec, n_vec, v);
         if (lane == 0) {
           rec[0] = mx;
           rec[1] = lj;
@@ -1616,7 +1742,8 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
     cur = nxt;
     next = after;
   }
-  if (bad_block && lane == 0) atomicOr(&g_status, PKV_DEVERR_BLOCK_ID);
+  if (bad_block && lane == 0) raise_status(ws, PKV_DEVERR_BLOCK_ID);
+  report_walked<WAVES>(ws, s_walk, walked);
   for (int it = n_data + (int)blockIdx.x; it < n_items; it += G) {
     const int e = it / groups;
     const int hgp = it - e * groups;
@@ -1664,16 +1791,18 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
   const int lp = ws.counters[3];
   for (int64_t pair = (int64_t)blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
        pair < pairs; pair += (int64_t)gridDim.x * W) {
-    const int2 sr = ws.split_rows[pair / n_vec];
+    const int4 sr = ws.split_rows[pair / n_vec];
     const int64_t r = sr.x;
     const int v = (int)(pair % n_vec);
     const int ctx = sr.y;
     const int nch = (ctx + (1 << lp) - 1) >> lp;
     if (nch <= 1) continue;
-    const float* rec = ws.partials + (r * n_vec + v) * ws.max_chunks * (D + 4);
+    // chunk c's record of vector v, c = 0 .. nch - 1
+    const float* rec = ws.partials + record_offset<D>(sr.z, n_vec, v);
+    const int64_t stride = (int64_t)n_vec * (D + 4);
 
     float mx = -INFINITY;
-    for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, rec[c * (D + 4)]);
+    for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, rec[c * stride]);
     mx = wave_max(mx);
     if (mx == -INFINITY) mx = 0.f;   // only a row whose length was out of bounds
     float l = 0.f, acc[PER];
@@ -1681,7 +1810,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
 #pragma unroll 4
     for (int c = 0; c < nch; ++c) {
-      const float* p = rec + c * (D + 4);
+      const float* p = rec + c * stride;
       const float f = __builtin_amdgcn_exp2f(p[0] - mx);
       l += p[1] * f;
 #pragma unroll
@@ -1925,7 +2054,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
         for (int i = 0; i < E; ++i) y[i] *= inv;
         store16_out(static_cast<T*>(a.out) + rh * D + sub * E, El::pack(y));
       } else {
-        float* rec = ws.partials + (rh * ws.max_chunks + chunk) * (D + 4);
+        float* rec = ws.partials + record_offset<D>(ws.row_rec[r] + chunk, heads, h);
         if (sub == 0) {
           rec[0] = mx;
           rec[1] = lt;
@@ -1941,7 +2070,7 @@ token_rows_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2) {
     item = __builtin_amdgcn_readfirstlane(s_item[buf]);
     buf ^= 1;
   }
-  if (bad) atomicOr(&g_status, PKV_DEVERR_SLOT);
+  if (bad) raise_status(ws, PKV_DEVERR_SLOT);
 }
 
 // The token rows' chunks shorter than a.solo_tokens (the end of their list), one wave
@@ -2063,9 +2192,10 @@ token_rows_short_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2)
     }
     merge_lane_groups<LPT, 1, E>(m, l, acc);
     if (g == 0)
-      write_item_result<T, D>(a, ws, r, h, chunk, nch, heads, sub, m[0], l[0], acc[0]);
+      write_item_result<T, D>(a, ws, r, h, nch > 1 ? ws.row_rec[r] + chunk : -1, heads, sub,
+                              m[0], l[0], acc[0]);
   }
-  if (bad) atomicOr(&g_status, PKV_DEVERR_SLOT);
+  if (bad) raise_status(ws, PKV_DEVERR_SLOT);
 }
 
 // ------------------------------------------------------------------------- //
@@ -2073,44 +2203,66 @@ token_rows_short_kernel(AttnArgs a, SlotArgs sa, Workspace ws, float scale_log2)
 // ------------------------------------------------------------------------- //
 static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-static int max_chunks_for(int32_t max_blocks, int32_t block_size, int32_t chunk) {
+static int64_t cdiv64(int64_t x, int64_t y) { return (x + y - 1) / y; }
+
+// Chunk records (each one record of head_dim + 4 floats per query vector) the partials
+// area holds.  The plan splits a row into cdiv(length, P) chunks only when that is
+// more than one, so at P = chunk_max at most rows x cdiv(width, chunk_max) chunks have
+// records (none when a chunk covers the table), and at P = chunk_min at most rows x
+// cdiv(width, chunk_min).  Between the two the area is kPartialBudgetBytes: the plan
+// lengthens P until its split rows' chunks fit.
+int32_t record_chunks_for(int64_t num_rows, int32_t vectors, int32_t head_dim,
+                          int32_t max_blocks, int32_t block_size, const Tuning& t) {
   const int64_t width = (int64_t)max_blocks * block_size;
-  return (int)((width + chunk - 1) / chunk);
+  const int64_t mc_min = cdiv64(width, t.chunk_min);
+  const int64_t mc_max = cdiv64(width, t.chunk_max);
+  const int64_t at_min = mc_min > 1 ? num_rows * mc_min : 0;
+  const int64_t at_max = mc_max > 1 ? num_rows * mc_max : 0;
+  const int64_t budget = kPartialBudgetBytes / ((int64_t)(head_dim + 4) * 4 * vectors);
+  const int64_t chunks = at_min < (at_max > budget ? at_max : budget)
+                             ? at_min
+                             : (at_max > budget ? at_max : budget);
+  return (int32_t)chunks;   // <= rows x cdiv(width, chunk_min), bounded by the item check
 }
 
-size_t workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
-                       int32_t max_blocks, int32_t block_size) {
-  const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_min());
-  const int64_t entries = num_rows * (mc > 1 ? mc : 1);
-  int64_t bytes = align_up(entries * (int64_t)sizeof(int4), 256);
-  bytes += 256;                                    // counters
-  bytes += 2 * align_up(num_rows * 4, 256);        // row lengths, irregular rows
-  bytes += align_up(num_rows * 8, 256);            // split rows
-  bytes += align_up(num_rows * num_heads * mc * (int64_t)(head_dim + 4) * 4, 256);
+// Work-list entries: at most every row's chunks at the shortest chunk (pad rows: one).
+static int64_t max_entries_for(int64_t num_rows, int32_t max_blocks, int32_t block_size,
+                               const Tuning& t) {
+  const int64_t mc = cdiv64((int64_t)max_blocks * block_size, t.chunk_min);
+  return num_rows * (mc > 1 ? mc : 1);
+}
+
+size_t workspace_bytes(int64_t num_rows, int32_t vectors, int32_t head_dim,
+                       int32_t max_blocks, int32_t block_size, const Tuning& t) {
+  const int64_t recs = record_chunks_for(num_rows, vectors, head_dim, max_blocks, block_size, t);
+  int64_t bytes = kCounterBytes;
+  bytes += align_up(max_entries_for(num_rows, max_blocks, block_size, t) * 16, 256);
+  bytes += 3 * align_up(num_rows * 4, 256);        // row lengths, first records, irregular
+  bytes += align_up(num_rows * 16, 256);           // split rows
+  bytes += align_up(recs * vectors * (int64_t)(head_dim + 4) * 4, 256);
   return (size_t)bytes;
 }
 
-Workspace carve_workspace(void* base, int64_t num_rows, int32_t num_heads, int32_t head_dim,
-                          int32_t max_blocks, int32_t block_size) {
+Workspace carve_workspace(void* base, int64_t num_rows, int32_t vectors, int32_t head_dim,
+                          int32_t max_blocks, int32_t block_size, const Tuning& t) {
   Workspace w;
-  const int64_t mc = max_chunks_for(max_blocks, block_size, tuning_chunk_min());
-  w.max_chunks = (int32_t)mc;
-  w.max_entries = num_rows * (mc > 1 ? mc : 1);
+  w.record_chunks = record_chunks_for(num_rows, vectors, head_dim, max_blocks, block_size, t);
+  w.max_entries = max_entries_for(num_rows, max_blocks, block_size, t);
   char* p = static_cast<char*>(base);
-  w.entries = reinterpret_cast<int4*>(p);
-  p += align_up(w.max_entries * (int64_t)sizeof(int4), 256);
   w.counters = reinterpret_cast<int32_t*>(p);
-  p += 256;
+  p += kCounterBytes;
+  w.entries = reinterpret_cast<int4*>(p);
+  p += align_up(w.max_entries * 16, 256);
   w.row_ctx = reinterpret_cast<int32_t*>(p);
+  p += align_up(num_rows * 4, 256);
+  w.row_rec = reinterpret_cast<int32_t*>(p);
   p += align_up(num_rows * 4, 256);
   w.irregular = reinterpret_cast<int32_t*>(p);
   p += align_up(num_rows * 4, 256);
-  w.split_rows = reinterpret_cast<int2*>(p);
-  p += align_up(num_rows * 8, 256);
+  w.split_rows = reinterpret_cast<int4*>(p);
+  p += align_up(num_rows * 16, 256);
   w.token_entries = nullptr;
   w.partials = reinterpret_cast<float*>(p);
-  (void)num_heads;
-  (void)head_dim;
   return w;
 }
 
@@ -2122,35 +2274,35 @@ static int32_t slot_flag_stride(int32_t width) {
 }
 
 // token entries of a slot input: at most every row's chunks
-static int64_t token_entry_bytes(int64_t num_rows, int32_t mb, int32_t block_size) {
-  const int64_t mc = max_chunks_for(mb, block_size, tuning_chunk_min());
-  return align_up(num_rows * (mc > 1 ? mc : 1) * 8, 256);
+static int64_t token_entry_bytes(int64_t num_rows, int32_t mb, int32_t block_size,
+                                 const Tuning& t) {
+  return align_up(max_entries_for(num_rows, mb, block_size, t) * 8, 256);
 }
 
 size_t slot_workspace_bytes(int64_t num_rows, int32_t num_heads, int32_t head_dim,
-                            int32_t width, int32_t block_size) {
+                            int32_t width, int32_t block_size, const Tuning& t) {
   const int32_t mb = slot_table_blocks(width, block_size);
-  int64_t bytes = align_up(num_rows * mb * 4, 256);
+  int64_t bytes = (int64_t)workspace_bytes(num_rows, num_heads, head_dim, mb, block_size, t);
+  bytes += align_up(num_rows * mb * 4, 256);
   bytes += align_up(num_rows * slot_flag_stride(width) * 4, 256);
-  bytes += token_entry_bytes(num_rows, mb, block_size);
-  return (size_t)bytes + workspace_bytes(num_rows, num_heads, head_dim, mb, block_size);
+  bytes += token_entry_bytes(num_rows, mb, block_size, t);
+  return (size_t)bytes;
 }
 
 Workspace carve_slot_workspace(void* base, int64_t num_rows, int32_t num_heads,
                                int32_t head_dim, int32_t width, int32_t block_size,
-                               SlotArgs* sa) {
+                               const Tuning& t, SlotArgs* sa) {
   const int32_t mb = slot_table_blocks(width, block_size);
+  Workspace w = carve_workspace(base, num_rows, num_heads, head_dim, mb, block_size, t);
   sa->max_blocks = mb;
   sa->flag_stride = slot_flag_stride(width);
-  char* p = static_cast<char*>(base);
+  char* p = static_cast<char*>(base) +
+            workspace_bytes(num_rows, num_heads, head_dim, mb, block_size, t);
   sa->block_tables = reinterpret_cast<int32_t*>(p);
   p += align_up(num_rows * mb * 4, 256);
   sa->row_flags = reinterpret_cast<int32_t*>(p);
   p += align_up(num_rows * sa->flag_stride * 4, 256);
-  int2* token_entries = reinterpret_cast<int2*>(p);
-  p += token_entry_bytes(num_rows, mb, block_size);
-  Workspace w = carve_workspace(p, num_rows, num_heads, head_dim, mb, block_size);
-  w.token_entries = token_entries;
+  w.token_entries = reinterpret_cast<int2*>(p);
   return w;
 }
 
@@ -2174,7 +2326,7 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream) {
 // the merge of split rows (nothing to do when no row can split)
 template <typename T, int D>
 static void launch_combine_t(const AttnArgs& a, const Workspace& ws, hipStream_t stream) {
-  if (ws.max_chunks <= 1) return;
+  if (ws.record_chunks <= 0) return;
   timing_begin(PKV_PHASE_COMBINE, stream);
   // a grid fixed by the shape (graph replays keep it): one wave per (row, vector) pair,
   // at most kCombineGroups workgroups, striding over the split rows' pairs
@@ -2186,8 +2338,8 @@ static void launch_combine_t(const AttnArgs& a, const Workspace& ws, hipStream_t
 }
 
 template <typename T, int D, int WAVES, bool LDS_STAGE, int QG, bool MFMA = false>
-static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
-                                  bool combine, const WriteArgs* write) {
+static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, const Tuning& t,
+                                  hipStream_t stream, bool combine, const WriteArgs* write) {
   void (*kern)(AttnArgs, Workspace, float);
   if constexpr (MFMA) kern = decode_mfma_kernel<D, WAVES, QG>;
   else kern = decode_kernel<T, D, WAVES, LDS_STAGE, QG>;
@@ -2213,7 +2365,7 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   }
   const int cus = num_cu[dev].load(std::memory_order_relaxed);
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  const int wpc = occ < tuning_groups_per_cu() ? occ : tuning_groups_per_cu();
+  const int wpc = occ < t.groups_per_cu ? occ : t.groups_per_cu;
   int64_t grid = (int64_t)cus * wpc;
   const int64_t most = ws.max_entries * (a.query_len * a.num_heads / QG);
   if (grid > most) grid = most;
@@ -2221,16 +2373,17 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
   pa.query_group = QG;
   // an item on the matrix cores carries 8 or 16 query vectors: a quarter as many items
   // keep the workgroups as busy (measured best at the full-width batch's lengths)
-  const int per_group = MFMA ? (tuning_items_per_group() + 3) / 4 : tuning_items_per_group();
+  const int per_group = MFMA ? (t.items_per_group + 3) / 4 : t.items_per_group;
   pa.target_items = (int32_t)(grid * per_group);
   pa.grid_groups = (int32_t)grid;
   // the plan may keep 8 waves per CU (one workgroup of 8, two of 4, ...)
   const int64_t narrow = (int64_t)cus * (WAVES < 8 ? 8 / WAVES : 1);
   pa.narrow_groups = grid > narrow ? (int32_t)narrow : 0;
   pa.narrow_items = pa.narrow_groups * per_group;
-  pa.deal_static = tuning_deal_static();
-  pa.solo_tokens = tuning_solo_tokens();
+  pa.deal_static = t.deal_static;
+  pa.solo_tokens = t.solo_tokens;
   pa.group_waves = WAVES;
+  pa.record_chunks = ws.record_chunks;
   timing_begin(PKV_PHASE_PLAN, stream);
   if (write) {   // the step's scatter rides along with the plan
     const int64_t pieces = write->num_tokens * write->g.kv_heads *
@@ -2255,9 +2408,9 @@ static hipError_t launch_decode_w(const AttnArgs& a, const Workspace& ws, hipStr
 // query vectors per KV head (query heads per KV head x new tokens per row) and is at
 // most the tuning cap (4 for head_dim 256, whose per-vector merge buffers would not fit
 // in LDS beside the K/V stages at 8)
-static int query_group_of(const AttnArgs& a) {
+static int query_group_of(const AttnArgs& a, const Tuning& t) {
   const int vpkv = a.query_len * (a.num_heads / a.g.kv_heads);
-  int cap = tuning_max_query_group();
+  int cap = t.max_query_group;
   if (cap > 8) cap = 8;
   if (a.g.head_dim >= 256 && cap > 4) cap = 4;
   for (int qg = 8; qg > 1; qg >>= 1)
@@ -2268,63 +2421,63 @@ static int query_group_of(const AttnArgs& a) {
 // query vectors per item on the matrix cores: 16, 8 or 4 when that many share a KV head
 // (and the tuning allows it), else 0 (the vector units take the call; with 1 or 2 they
 // measured as fast or faster)
-static int mfma_group_of(const AttnArgs& a) {
-  if (!tuning_mfma() || a.g.dtype != PKV_BF16 || a.g.head_dim > 128) return 0;
+static int mfma_group_of(const AttnArgs& a, const Tuning& t) {
+  if (!t.mfma || a.g.dtype != PKV_BF16 || a.g.head_dim > 128) return 0;
   const int vpkv = a.query_len * (a.num_heads / a.g.kv_heads);
-  const int cap = tuning_max_query_group();
+  const int cap = t.max_query_group;
   for (int qg = 16; qg >= 4; qg >>= 1)
     if (qg <= cap && vpkv % qg == 0) return qg;
   return 0;
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
-                                  bool combine, const WriteArgs* write) {
+static hipError_t launch_decode_t(const AttnArgs& a, const Workspace& ws, const Tuning& t,
+                                  hipStream_t stream, bool combine, const WriteArgs* write) {
   if constexpr (sizeof(T) == 2 && D <= 128) {
-    switch (mfma_group_of(a)) {
-      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, stream, combine, write);
-      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, stream, combine, write);
-      case 4: return launch_decode_w<T, D, 8, true, 4, true>(a, ws, stream, combine, write);
+    switch (mfma_group_of(a, t)) {
+      case 16: return launch_decode_w<T, D, 8, true, 16, true>(a, ws, t, stream, combine, write);
+      case 8: return launch_decode_w<T, D, 8, true, 8, true>(a, ws, t, stream, combine, write);
+      case 4: return launch_decode_w<T, D, 8, true, 4, true>(a, ws, t, stream, combine, write);
       default: break;
     }
   }
-  switch (query_group_of(a)) {
+  switch (query_group_of(a, t)) {
     case 8:
-      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, stream, combine, write);
+      if constexpr (D < 256) return launch_decode_w<T, D, 8, true, 8>(a, ws, t, stream, combine, write);
       break;
-    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, stream, combine, write);
-    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, stream, combine, write);
+    case 4: return launch_decode_w<T, D, 8, true, 4>(a, ws, t, stream, combine, write);
+    case 2: return launch_decode_w<T, D, 8, true, 2>(a, ws, t, stream, combine, write);
     default: break;
   }
-  if (tuning_lds_stage()) {
-    switch (tuning_decode_waves()) {
-      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, stream, combine, write);
-      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, stream, combine, write);
-      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, stream, combine, write);
-      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, stream, combine, write);
+  if (t.lds_stage) {
+    switch (t.decode_waves) {
+      case 1: return launch_decode_w<T, D, 1, true, 1>(a, ws, t, stream, combine, write);
+      case 2: return launch_decode_w<T, D, 2, true, 1>(a, ws, t, stream, combine, write);
+      case 8: return launch_decode_w<T, D, 8, true, 1>(a, ws, t, stream, combine, write);
+      default: return launch_decode_w<T, D, 4, true, 1>(a, ws, t, stream, combine, write);
     }
   }
-  switch (tuning_decode_waves()) {
-    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, stream, combine, write);
-    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, stream, combine, write);
-    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, stream, combine, write);
-    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, stream, combine, write);
+  switch (t.decode_waves) {
+    case 1: return launch_decode_w<T, D, 1, false, 1>(a, ws, t, stream, combine, write);
+    case 2: return launch_decode_w<T, D, 2, false, 1>(a, ws, t, stream, combine, write);
+    case 8: return launch_decode_w<T, D, 8, false, 1>(a, ws, t, stream, combine, write);
+    default: return launch_decode_w<T, D, 4, false, 1>(a, ws, t, stream, combine, write);
   }
 }
 
-hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, hipStream_t stream,
-                                  bool combine, const WriteArgs* write) {
+hipError_t launch_paged_attention(const AttnArgs& a, const Workspace& ws, const Tuning& t,
+                                  hipStream_t stream, bool combine, const WriteArgs* write) {
   const bool f32 = a.g.dtype == PKV_F32;
   switch (a.g.head_dim) {
     case 64:
-      return f32 ? launch_decode_t<float, 64>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 64>(a, ws, stream, combine, write);
+      return f32 ? launch_decode_t<float, 64>(a, ws, t, stream, combine, write)
+                 : launch_decode_t<uint16_t, 64>(a, ws, t, stream, combine, write);
     case 128:
-      return f32 ? launch_decode_t<float, 128>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 128>(a, ws, stream, combine, write);
+      return f32 ? launch_decode_t<float, 128>(a, ws, t, stream, combine, write)
+                 : launch_decode_t<uint16_t, 128>(a, ws, t, stream, combine, write);
     case 256:
-      return f32 ? launch_decode_t<float, 256>(a, ws, stream, combine, write)
-                 : launch_decode_t<uint16_t, 256>(a, ws, stream, combine, write);
+      return f32 ? launch_decode_t<float, 256>(a, ws, t, stream, combine, write)
+                 : launch_decode_t<uint16_t, 256>(a, ws, t, stream, combine, write);
     default:
       return hipErrorInvalidValue;
   }
@@ -2377,7 +2530,8 @@ static void launch_token_rows(const AttnArgs& a, const SlotArgs& sa, const Works
 }
 
 hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
-                                        const Workspace& ws, hipStream_t stream) {
+                                        const Workspace& ws, const Tuning& t,
+                                        hipStream_t stream) {
   // the token kernels: two 4-wave workgroups per CU (measured against one and four)
   int cus = 0;
   hipError_t err = device_cus(&cus);
@@ -2395,7 +2549,7 @@ hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
   timing_end(PKV_PHASE_TRANSLATE, stream);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_paged_attention(b, ws, stream, /*combine=*/false);
+  err = launch_paged_attention(b, ws, t, stream, /*combine=*/false);
   if (err != hipSuccess) return err;
   // the rows the block path could not take, then the merge of every split row: the
   // count is on the device, and with none every workgroup exits at once
@@ -2424,7 +2578,7 @@ hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& sa,
   return hipGetLastError();
 }
 
-const char* decode_kernel_name(const AttnArgs& a) {
+const char* decode_kernel_name(const AttnArgs& a, const Tuning& t) {
   static const char* const kMfma[] = {"decode_mfma_kernel, 4 query vectors per item",
                                       "decode_mfma_kernel, 8 query vectors per item",
                                       "decode_mfma_kernel, 16 query vectors per item"};
@@ -2432,13 +2586,13 @@ const char* decode_kernel_name(const AttnArgs& a) {
                                      "decode_kernel, 2 query vectors per item",
                                      "decode_kernel, 4 query vectors per item",
                                      "decode_kernel, 8 query vectors per item"};
-  switch (mfma_group_of(a)) {
+  switch (mfma_group_of(a, t)) {
     case 4: return kMfma[0];
     case 8: return kMfma[1];
     case 16: return kMfma[2];
     default: break;
   }
-  switch (query_group_of(a)) {
+  switch (query_group_of(a, t)) {
     case 2: return kVec[1];
     case 4: return kVec[2];
     case 8: return kVec[3];

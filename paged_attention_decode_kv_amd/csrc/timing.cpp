@@ -1,8 +1,9 @@
-// Event-pair timing of the library's kernel phases (pkv_timing_enable / _read).
+// Event-pair timing of the library's kernel phases (pkv_timing_enable / _read), and the
+// process-wide work-split settings (pkv_set_tuning / pkv_get_tuning).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
-#include <mutex>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -11,21 +12,47 @@
 namespace pkv {
 namespace {
 
+// A lock whose lock() cannot throw (std::mutex::lock may throw std::system_error, and
+// these functions run inside C-ABI calls that no exception may leave).
+class SpinLock {
+ public:
+  void lock() noexcept {
+    while (flag_.test_and_set(std::memory_order_acquire)) std::this_thread::yield();
+  }
+  void unlock() noexcept { flag_.clear(std::memory_order_release); }
+
+ private:
+  std::atomic_flag flag_ = ATOMIC_FLAG_INIT;
+};
+
+class Guard {
+ public:
+  explicit Guard(SpinLock& l) noexcept : l_(l) { l_.lock(); }
+  ~Guard() { l_.unlock(); }
+  Guard(const Guard&) = delete;
+  Guard& operator=(const Guard&) = delete;
+
+ private:
+  SpinLock& l_;
+};
+
 constexpr int kPhases = 6;
 
 struct PhaseLog {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;  // recorded, not yet read
   std::vector<hipEvent_t> spare;                           // reusable events
-  hipEvent_t open = nullptr;                               // start of the current launch
+  // the start event of the launch in progress on each stream: a phase timed from two
+  // host threads on two streams pairs each stream's start with its own stop
+  std::vector<std::pair<hipStream_t, hipEvent_t>> open;
   double total_ms = 0.0;
   int64_t launches = 0;
 };
 
-std::mutex g_mu;
+SpinLock g_mu;
 std::atomic<bool> g_on{false};
 PhaseLog g_log[kPhases];
 
-hipEvent_t take(PhaseLog& p) {
+hipEvent_t take(PhaseLog& p) noexcept {
   if (!p.spare.empty()) {
     hipEvent_t e = p.spare.back();
     p.spare.pop_back();
@@ -36,8 +63,7 @@ hipEvent_t take(PhaseLog& p) {
   return e;
 }
 
-// Returns an event to the phase's spares; if that cannot grow, the event is destroyed
-// (these run inside C-ABI calls, which no exception may leave).
+// Returns an event to the phase's spares; if that cannot grow, the event is destroyed.
 void keep_spare(PhaseLog& p, hipEvent_t e) noexcept {
   try {
     p.spare.push_back(e);
@@ -46,10 +72,23 @@ void keep_spare(PhaseLog& p, hipEvent_t e) noexcept {
   }
 }
 
+// Removes and returns the open start event of `stream` (nullptr if none).
+hipEvent_t take_open(PhaseLog& p, hipStream_t stream) noexcept {
+  for (size_t i = 0; i < p.open.size(); ++i) {
+    if (p.open[i].first == stream) {
+      hipEvent_t e = p.open[i].second;
+      p.open[i] = p.open.back();
+      p.open.pop_back();
+      return e;
+    }
+  }
+  return nullptr;
+}
+
 }  // namespace
 
 void timing_enable(bool on) {
-  std::lock_guard<std::mutex> lock(g_mu);
+  Guard lock(g_mu);
   g_on = on;
 }
 
@@ -62,46 +101,63 @@ static bool capturing(hipStream_t stream) {
 
 void timing_begin(int phase, hipStream_t stream) {
   if (!g_on || capturing(stream)) return;
-  std::lock_guard<std::mutex> lock(g_mu);
+  Guard lock(g_mu);
   PhaseLog& p = g_log[phase];
-  p.open = take(p);
-  if (p.open && hipEventRecord(p.open, stream) != hipSuccess) p.open = nullptr;
+  // a start left open on this stream (a launch that failed before its stop) is dropped
+  if (hipEvent_t stale = take_open(p, stream)) keep_spare(p, stale);
+  hipEvent_t e = take(p);
+  if (!e) return;
+  if (hipEventRecord(e, stream) != hipSuccess) {
+    keep_spare(p, e);
+    return;
+  }
+  try {
+    p.open.emplace_back(stream, e);
+  } catch (...) {   // this launch goes untimed
+    keep_spare(p, e);
+  }
 }
 
 void timing_end(int phase, hipStream_t stream) {
   if (!g_on || capturing(stream)) return;
-  std::lock_guard<std::mutex> lock(g_mu);
+  Guard lock(g_mu);
   PhaseLog& p = g_log[phase];
-  if (!p.open) return;
+  hipEvent_t start = take_open(p, stream);
+  if (!start) return;
   hipEvent_t stop = take(p);
-  if (!stop) return;
+  if (!stop) {
+    keep_spare(p, start);
+    return;
+  }
   if (hipEventRecord(stop, stream) != hipSuccess) {
-    keep_spare(p, p.open);
+    keep_spare(p, start);
     keep_spare(p, stop);
-    p.open = nullptr;
     return;
   }
   try {
-    p.pending.emplace_back(p.open, stop);
+    p.pending.emplace_back(start, stop);
   } catch (...) {   // the sample is dropped
-    keep_spare(p, p.open);
+    keep_spare(p, start);
     keep_spare(p, stop);
   }
-  p.open = nullptr;
 }
 
+// Sums the recorded pairs of one phase.  A pair whose events fail is dropped with its
+// events destroyed, so a persistent error is reported once, not on every later read;
+// the pairs summed before it stay summed.
 hipError_t timing_read(int phase, double* total_ms, int64_t* launches, bool reset) {
-  std::lock_guard<std::mutex> lock(g_mu);
+  Guard lock(g_mu);
   PhaseLog& p = g_log[phase];
-  size_t done = 0;
-  for (; done < p.pending.size(); ++done) {
-    const auto& pr = p.pending[done];
+  hipError_t first_error = hipSuccess;
+  for (const auto& pr : p.pending) {
     hipError_t e = hipEventSynchronize(pr.second);
     float ms = 0.f;
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
-    if (e != hipSuccess) {   // the samples already summed leave the list
-      p.pending.erase(p.pending.begin(), p.pending.begin() + done);
-      return e;
+    if (e != hipSuccess) {
+      if (first_error == hipSuccess) first_error = e;
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+      continue;
     }
     p.total_ms += ms;
     p.launches += 1;
@@ -109,6 +165,7 @@ hipError_t timing_read(int phase, double* total_ms, int64_t* launches, bool rese
     keep_spare(p, pr.second);
   }
   p.pending.clear();
+  if (first_error != hipSuccess) return first_error;
   *total_ms = p.total_ms;
   *launches = p.launches;
   if (reset) {
@@ -118,37 +175,31 @@ hipError_t timing_read(int phase, double* total_ms, int64_t* launches, bool rese
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------------------------
+// work-split settings
+// ---------------------------------------------------------------------------------
 namespace {
-std::atomic<int> g_chunk_min{kDefaultChunkMin};
-std::atomic<int> g_chunk_max{kDefaultChunkMax};
-std::atomic<int> g_decode_waves{kDefaultDecodeWaves};
-std::atomic<int> g_items_per_group{kDefaultItemsPerGroup};
-std::atomic<int> g_deal_static{kDefaultDealStatic};
-std::atomic<int> g_lds_stage{kDefaultLdsStage};
-std::atomic<int> g_max_query_group{kDefaultMaxQueryGroup};
-std::atomic<int> g_mfma{kDefaultMfma};
-std::atomic<int> g_groups_per_cu{kDefaultGroupsPerCu};
-std::atomic<int> g_solo_tokens{kDefaultSoloTokens};
+SpinLock g_tuning_mu;
+Tuning g_tuning = {kDefaultChunkMin,      kDefaultChunkMax,   kDefaultDecodeWaves,
+                   kDefaultItemsPerGroup, kDefaultDealStatic, kDefaultLdsStage,
+                   kDefaultMaxQueryGroup, kDefaultMfma,       kDefaultGroupsPerCu,
+                   kDefaultSoloTokens};
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 }  // namespace
 
-int tuning_chunk_min() { return g_chunk_min.load(std::memory_order_relaxed); }
-int tuning_chunk_max() { return g_chunk_max.load(std::memory_order_relaxed); }
-int tuning_decode_waves() { return g_decode_waves.load(std::memory_order_relaxed); }
-int tuning_items_per_group() { return g_items_per_group.load(std::memory_order_relaxed); }
-int tuning_deal_static() { return g_deal_static.load(std::memory_order_relaxed); }
-int tuning_lds_stage() { return g_lds_stage.load(std::memory_order_relaxed); }
-int tuning_max_query_group() { return g_max_query_group.load(std::memory_order_relaxed); }
-int tuning_mfma() { return g_mfma.load(std::memory_order_relaxed); }
-int tuning_groups_per_cu() { return g_groups_per_cu.load(std::memory_order_relaxed); }
-int tuning_solo_tokens() { return g_solo_tokens.load(std::memory_order_relaxed); }
+Tuning tuning_snapshot() noexcept {
+  Guard lock(g_tuning_mu);
+  return g_tuning;
+}
 
 bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_group,
                 int deal, int staging, int max_query_group, int mfma, int groups_per_cu,
-                int solo_tokens) {
-  const int lo = chunk_min ? chunk_min : tuning_chunk_min();
-  const int hi = chunk_max ? chunk_max : tuning_chunk_max();
+                int solo_tokens) noexcept {
+  Guard lock(g_tuning_mu);
+  Tuning t = g_tuning;
+  const int lo = chunk_min ? chunk_min : t.chunk_min;
+  const int hi = chunk_max ? chunk_max : t.chunk_max;
   // validate everything before changing anything
   if (!pow2_in(lo, kMinChunkTokens, kMaxChunkTokens) ||
       !pow2_in(hi, kMinChunkTokens, kMaxChunkTokens) || lo > hi || hi / lo > kMaxChunkRatio)
@@ -167,16 +218,17 @@ bool set_tuning(int chunk_min, int chunk_max, int decode_waves, int items_per_gr
   if (solo_tokens != 0 && solo_tokens != 1 &&
       !pow2_in(solo_tokens, kMinChunkTokens, kMaxSoloTokens))
     return false;
-  g_chunk_min.store(lo);
-  g_chunk_max.store(hi);
-  if (decode_waves != 0) g_decode_waves.store(decode_waves);
-  if (items_per_group != 0) g_items_per_group.store(items_per_group);
-  if (deal != 0) g_deal_static.store(deal == 1 ? 1 : 0);
-  if (staging != 0) g_lds_stage.store(staging == 2 ? 1 : 0);
-  if (max_query_group != 0) g_max_query_group.store(max_query_group);
-  if (mfma != 0) g_mfma.store(mfma == 1 ? 1 : 0);
-  if (groups_per_cu != 0) g_groups_per_cu.store(groups_per_cu);
-  if (solo_tokens != 0) g_solo_tokens.store(solo_tokens);
+  t.chunk_min = lo;
+  t.chunk_max = hi;
+  if (decode_waves != 0) t.decode_waves = decode_waves;
+  if (items_per_group != 0) t.items_per_group = items_per_group;
+  if (deal != 0) t.deal_static = deal == 1 ? 1 : 0;
+  if (staging != 0) t.lds_stage = staging == 2 ? 1 : 0;
+  if (max_query_group != 0) t.max_query_group = max_query_group;
+  if (mfma != 0) t.mfma = mfma == 1 ? 1 : 0;
+  if (groups_per_cu != 0) t.groups_per_cu = groups_per_cu;
+  if (solo_tokens != 0) t.solo_tokens = solo_tokens;
+  g_tuning = t;
   return true;
 }
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_and_status_strings(lib):
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
     for code, name in enumerate(_capi.STATUS_NAMES):
         assert lib.pkv_status_str(code).decode() == name
 
@@ -64,6 +64,115 @@ def test_workspace_size_depends_on_shape_only(lib):
     big = lib.pkv_workspace_bytes(ctypes.byref(d), 256, 32, 512)
     assert 0 < small < big
     assert lib.pkv_workspace_bytes(ctypes.byref(d), 0, 32, 128) == 0
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+def _expected_workspace(rows, vectors, head_dim, max_blocks, block_size, cmin, cmax):
+    """The documented layout: counters, work list, four row arrays, split-row records
+    (at most 16 MiB between the shortest and longest chunk's needs)."""
+    width = max_blocks * block_size
+    mc_min, mc_max = -(-width // cmin), -(-width // cmax)
+    at_min = rows * mc_min if mc_min > 1 else 0
+    at_max = rows * mc_max if mc_max > 1 else 0
+    budget = (16 << 20) // ((head_dim + 4) * 4 * vectors)
+    recs = min(at_min, max(at_max, budget))
+    return (256 + _align(rows * max(mc_min, 1) * 16) + 3 * _align(rows * 4) +
+            _align(rows * 16) + _align(recs * vectors * (head_dim + 4) * 4))
+
+
+@pytest.mark.parametrize("rows,heads,d,mb,bs,qlen", [
+    (256, 32, 128, 512, 16, 1),    # the full-width batch: ~17 MB, not 138 MB
+    (8, 32, 128, 128, 16, 1),      # small: every row may split into the shortest chunks
+    (34, 32, 128, 512, 16, 1),
+    (4, 8, 64, 8, 16, 1),          # a table narrower than the shortest chunk: no records
+    (64, 16, 256, 4096, 16, 4),    # multi-token
+])
+def test_workspace_layout_and_record_budget(lib, rows, heads, d, mb, bs, qlen):
+    desc = binding.host_desc(1 << 20, bs, heads, d)
+    binding.set_tuning(chunk_min=128, chunk_max=8192)
+    got = lib.pkv_workspace_bytes_multi(ctypes.byref(desc), rows, qlen, heads, mb)
+    assert got == _expected_workspace(rows, qlen * heads, d, mb, bs, 128, 8192)
+    if (rows, mb) == (256, 512):
+        assert got < 20 << 20
+    # pinning the chunk leaves the plan no room: every row's chunks get records
+    binding.set_tuning(chunk_min=256, chunk_max=256)
+    try:
+        pinned = lib.pkv_workspace_bytes_multi(ctypes.byref(desc), rows, qlen, heads, mb)
+        assert pinned == _expected_workspace(rows, qlen * heads, d, mb, bs, 256, 256)
+    finally:
+        binding.set_tuning(chunk_min=128, chunk_max=8192)
+
+
+def test_tuning_reads_are_one_snapshot_under_concurrent_sets(lib):
+    """A thread flips the chunk range between two settings while this one sizes
+    workspaces and reads the tuning: every read sees one setting or the other, never
+    one field of each (the pair (32, 8192) would even be an illegal range)."""
+    import threading
+    desc = binding.host_desc(131072, 16, 32, 128)
+    a, b = (128, 8192), (32, 2048)
+    sizes = set()
+    for lo, hi in (a, b):
+        binding.set_tuning(chunk_min=lo, chunk_max=hi)
+        sizes.add(lib.pkv_workspace_bytes(ctypes.byref(desc), 256, 32, 512))
+    assert len(sizes) == 2
+    stop = threading.Event()
+
+    def flip():
+        t = [_capi.Tuning(*a, 0, 0, 0, 0, 0, 0, 0, 0), _capi.Tuning(*b, 0, 0, 0, 0, 0, 0, 0, 0)]
+        i = 0
+        while not stop.is_set():
+            assert lib.pkv_set_tuning(ctypes.byref(t[i & 1])) == 0
+            i += 1
+
+    th = threading.Thread(target=flip)
+    th.start()
+    try:
+        seen = set()
+        for _ in range(20000):
+            sz = lib.pkv_workspace_bytes(ctypes.byref(desc), 256, 32, 512)
+            assert sz in sizes, sz
+            tu = _capi.Tuning()
+            assert lib.pkv_get_tuning(ctypes.byref(tu)) == 0
+            assert (tu.chunk_min, tu.chunk_max) in (a, b), (tu.chunk_min, tu.chunk_max)
+            seen.add(sz)
+    finally:
+        stop.set()
+        th.join()
+        binding.set_tuning(chunk_min=128, chunk_max=8192)
+
+
+def test_error_detail_is_per_thread(lib):
+    """Two threads make refused host checks with different bad entries at the same time;
+    each reads back the detail naming its own entry."""
+    import threading
+    w, _ = _attention_cases()
+    d = binding.host_desc(w.num_blocks, w.block_size, w.kv_heads, w.head_dim, w.dtype,
+                          w.layout)
+    errors = []
+
+    def worker(row, n):
+        ctx = w.context_lens.copy()
+        ctx[row] = -1 - row
+        bt = np.ascontiguousarray(w.block_tables, dtype=np.int32)
+        for _ in range(n):
+            st = lib.pkv_check_attention_host(
+                ctypes.byref(d), bt.ctypes.data_as(ctypes.c_void_p), bt.shape[1],
+                ctx.ctypes.data_as(ctypes.c_void_p), ctx.shape[0], w.heads)
+            detail = lib.pkv_last_error_detail().decode()
+            if _capi.STATUS_NAMES[st] != "CONTEXT_BOUNDS" or \
+                    f"context_lens[{row}] = {-1 - row}" not in detail:
+                errors.append((row, st, detail))
+                return
+
+    threads = [threading.Thread(target=worker, args=(r, 5000)) for r in (0, 3)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
 
 
 def _oracle_code(fn):
@@ -285,7 +394,11 @@ def test_multi_query_len_limits(lib):
     assert binding.check_attention_multi_host(d, bt[:0], ctx[:0], 4, w.heads) == "EMPTY"
     one = lib.pkv_workspace_bytes(ctypes.byref(d), 4, 4, 4)
     assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 1, 4, 4) == one
-    assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 4, 4, 4) > one
+    # a table narrower than the shortest chunk splits no row: no records either way
+    assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 4, 4, 4) == one
+    # a wider one holds a record per query vector of every chunk of a split row
+    wide = lib.pkv_workspace_bytes(ctypes.byref(d), 4, 4, 64)
+    assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 4, 4, 64) > wide
     assert lib.pkv_workspace_bytes_multi(ctypes.byref(d), 4, 0, 4, 4) == 0
 
 

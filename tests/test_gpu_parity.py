@@ -6,19 +6,22 @@ Tolerances (written here, derived from the arithmetic):
   |gpu - oracle| <= 2^-8 |oracle| + 2e-5: the kernel accumulates in float32 (relative
   error ~1e-6 on these sizes) and rounds once to bfloat16 (half an ulp, 2^-9 relative);
 * the slot scatter: bit-exact.
-Small cases compare every output; the large configurations (pools of 2-34 GB) compare
-sampled rows, each recomputed by the oracle from a host copy of just the blocks those
-rows name (block relabelling leaves the oracle's result unchanged, a pinned invariant).
+Every case compares every output row.  The large configurations (pools of 2-34 GB)
+recompute each row with the oracle from a host copy of just the blocks that row group
+names (block relabelling leaves the oracle's result unchanged, a pinned invariant), on
+a pool of host threads.
 """
 
+import os
 import zlib
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from paged_attention_decode_kv_amd import _capi, binding
+from paged_attention_decode_kv_amd import _capi, accounting, binding
 from paged_attention_decode_kv_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -91,20 +94,33 @@ class Step:
         self.tables = to_dev(w.block_tables)
         self.lens = to_dev(w.context_lens)
 
-    def run(self, validate=True, out=None):
+    def run(self, validate=True, out=None, workspace=None):
+        """kv_write then the read (the multi-token read when the workload has several
+        new tokens per row), in the given workspace if any."""
         w = self.w
         binding.kv_write(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache,
                          layout=w.layout, validate=validate)
-        out = binding.paged_attention(self.q, self.k_cache, self.v_cache, self.tables,
-                                      self.lens, w.scale, layout=w.layout, out=out,
-                                      validate=validate)
+        read = binding.paged_attention if w.query_len == 1 else binding.paged_attention_multi
+        out = read(self.q, self.k_cache, self.v_cache, self.tables, self.lens, w.scale,
+                   layout=w.layout, out=out, workspace=workspace, validate=validate)
         torch.cuda.synchronize()
         return out
 
+    def workspace(self):
+        w = self.w
+        if w.query_len == 1:
+            n = binding.workspace_bytes(self.k_cache, w.rows, w.heads, w.max_blocks, w.layout)
+        else:
+            n = binding.workspace_bytes_multi(self.k_cache, w.rows, w.query_len, w.heads,
+                                              w.max_blocks, w.layout)
+        return torch.empty(n, dtype=torch.uint8, device=DEV)
+
     def host_pools_for(self, rows):
         """Host copies of the pre-step blocks the given rows name, relabelled 0..n-1,
-        with the tables and write slots of those rows remapped to match."""
+        with the tables and write slots (query_len per row) of those rows remapped to
+        match."""
         w = self.w
+        nq = w.query_len
         blocks = wl.live_blocks(w, rows)
         remap = {int(b): i for i, b in enumerate(blocks)}
         n = len(blocks)
@@ -112,15 +128,16 @@ class Step:
         k = to_host(self.k_cache.index_select(0, idx), w.dtype)
         v = to_host(self.v_cache.index_select(0, idx), w.dtype)
         bt = np.full((len(rows), w.max_blocks), -1, dtype=np.int32)
-        sm = np.empty(len(rows), dtype=np.int64)
+        sm = np.empty(len(rows) * nq, dtype=np.int64)
         for i, r in enumerate(rows):
             live = wl.cdiv(w.context_lens[r], w.block_size)
             bt[i, :live] = [remap[int(b)] for b in w.block_tables[r, :live]]
-            s = int(w.slot_mapping[r])
-            if w.context_lens[r] == 0:
-                sm[i] = n * w.block_size
-            else:
-                sm[i] = remap[s // w.block_size] * w.block_size + s % w.block_size
+            for j in range(nq):
+                s = int(w.slot_mapping[r * nq + j])
+                if w.context_lens[r] == 0:
+                    sm[i * nq + j] = n * w.block_size
+                else:
+                    sm[i * nq + j] = remap[s // w.block_size] * w.block_size + s % w.block_size
         return k, v, bt, sm, n
 
 
@@ -134,19 +151,80 @@ def oracle_full(w, k_host, v_host):
     return out, kw, vw
 
 
-def oracle_rows(step, rows, chunk=4):
-    """Oracle outputs of the given rows, a few rows per oracle call."""
+# host threads for the oracle (numpy releases the interpreter lock in its gathers,
+# products and elementwise loops); a few, so that the float64 rectangles in flight
+# stay within a few GB of host memory
+ORACLE_THREADS = max(1, min(8, len(os.sched_getaffinity(0))))
+
+
+def _row_groups(lens, rows, per_row, cells):
+    """Rows sorted by length, cut into groups whose oracle rectangle (rows x longest
+    length x per_row elements) stays within `cells` (a longer row goes alone)."""
+    order = sorted(range(len(rows)), key=lambda i: int(lens[rows[i]]))
+    groups, at = [], 0
+    while at < len(order):
+        end = at + 1
+        while end < len(order) and \
+                (end + 1 - at) * max(1, int(lens[rows[order[end]]])) * per_row <= cells:
+            end += 1
+        groups.append(order[at:end])
+        at = end
+    return groups
+
+
+def oracle_rows(step, rows, cells=1 << 23):
+    """Oracle outputs of the given rows (all of a full-size batch's rows, as the tests
+    ask): groups of rows of similar length, each from a host copy of just the blocks it
+    names (copied in this thread), computed on ORACLE_THREADS host threads."""
     w = step.w
-    out = np.zeros((len(rows), w.heads, w.head_dim))
-    for at in range(0, len(rows), chunk):
-        part = rows[at:at + chunk]
-        k, v, bt, sm, n = step.host_pools_for(part)
-        oracle.kv_write(k, v, w.k_new[part], w.v_new[part], sm, num_blocks=n,
-                        block_size=w.block_size, layout=w.layout, dtype=w.dtype)
-        out[at:at + len(part)] = oracle.paged_attention(
-            w.q[part], k, v, bt, w.context_lens[part], w.scale, num_blocks=n,
-            block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+    rows = [int(r) for r in rows]
+    nq = w.query_len
+    out = np.zeros((len(rows),) + w.q.shape[1:])
+    kv_shape = (w.rows, nq, w.kv_heads, w.head_dim)
+    read = oracle.paged_attention if nq == 1 else oracle.paged_attention_multi
+
+    def compute(part, k, v, bt, sm, n):
+        k_new = w.k_new.reshape(kv_shape)[part].reshape(-1, w.kv_heads, w.head_dim)
+        v_new = w.v_new.reshape(kv_shape)[part].reshape(-1, w.kv_heads, w.head_dim)
+        oracle.kv_write(k, v, k_new, v_new, sm, num_blocks=n, block_size=w.block_size,
+                        layout=w.layout, dtype=w.dtype)
+        return read(w.q[part], k, v, bt, w.context_lens[part], w.scale, num_blocks=n,
+                    block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+
+    groups = _row_groups(w.context_lens, rows, w.heads * w.head_dim * nq, cells)
+    with ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        pending = []
+        for g in groups:
+            part = [rows[i] for i in g]
+            pending.append((g, ex.submit(compute, part, *step.host_pools_for(part))))
+            while len(pending) >= 2 * ORACLE_THREADS:   # bound the host copies in flight
+                g0, f0 = pending.pop(0)
+                out[g0] = f0.result()
+        for g0, f0 in pending:
+            out[g0] = f0.result()
     return out
+
+
+def check_plan(w, info):
+    """The plan and the decode kernel's own walk count against the host's accounting
+    of the same lengths (Day 59, "What I learned" 5: the helper's tile count and the
+    kernel's loop are held to the same lengths)."""
+    lens = w.context_lens.astype(np.int64)
+    P = info["chunk_tokens"]
+    assert P > 0 and P & (P - 1) == 0, info
+    live = lens[lens > 0]
+    assert info["live_entries"] == accounting.tiles_walked(live, P), info
+    assert info["entries"] == info["live_entries"] + int(np.count_nonzero(lens == 0)), info
+    assert info["full_chunks"] == int(np.sum(live // P)), info
+    split = live[live > P]
+    assert info["split_rows"] == len(split), info
+    assert info["records"] == accounting.tiles_walked(split, P), info
+    assert info["records"] <= info["record_capacity"], info
+    T = info["tile_tokens"]
+    assert T in (4, 8, 16), info
+    assert info["vector_groups"] >= 1, info
+    assert info["tiles_walked"] == info["vector_groups"] * accounting.tiles_walked(live, T), info
+    assert info["status"] == 0, info
 
 
 def check_full(w):
@@ -179,69 +257,113 @@ def test_config2_uniform_bf16():
     say(f"uniform bf16: max err {err:.3e}")
 
 
-def _sampled(idx, rows_pick):
-    w = wl.make_config(idx)
-    say(f"{w.name}: building {w.pool_bytes / 1e9:.1f} GB of pools on the device")
+def _full_size(idx, kv_heads=None, query_len=1):
+    """A full-size configuration (or its grouped or multi-token variant): every live
+    row against the oracle, pad rows zero, the scatter bit-exact at every written slot
+    with the rest of the pool untouched, and the plan's counts and the kernel's own
+    walk count against the host accounting."""
+    w = wl.make_config(idx, kv_heads=kv_heads, query_len=query_len)
+    say(f"{w.name} kv_heads={w.kv_heads} query_len={w.query_len}: building "
+        f"{w.pool_bytes / 1e9:.1f} GB of pools on the device")
     st = Step(w, host_history=False)
     k_before = st.k_cache.clone()
     v_before = st.v_cache.clone()
-    out = st.run()
-    rows = rows_pick(w)
-    say(f"{w.name}: oracle on rows {rows}")
-    ref = oracle_rows(st, rows)
-    got = to_host(out, w.dtype)[rows]
-    err = assert_close(got, ref, w.dtype, w.name)
-    # scatter: every live row's slot holds its new K/V bit-exactly, nothing else moved
+    ws = st.workspace()
+    out = st.run(workspace=ws)
+    info = binding.plan_info(ws)
+    say(f"{w.name}: plan {info}")
+    check_plan(w, info)
     live = w.live_rows
-    slots = torch.from_numpy(w.slot_mapping[live]).to(DEV)
+    say(f"{w.name}: oracle on all {len(live)} live rows, {ORACLE_THREADS} host threads")
+    ref = oracle_rows(st, live)
+    got = to_host(out, w.dtype)[live]
+    err = assert_close(got, ref, w.dtype, w.name)
+    # scatter: every live row's slots hold its new K/V bit-exactly, nothing else moved
+    nq = w.query_len
+    tokens = (live[:, None] * nq + np.arange(nq)[None, :]).reshape(-1)
+    slots = torch.from_numpy(w.slot_mapping[tokens]).to(DEV)
     blk, off = slots // w.block_size, slots % w.block_size
-    rows_dev = torch.from_numpy(live).to(DEV)
+    tok_dev = torch.from_numpy(tokens).to(DEV)
     sink_b = w.num_blocks
     for pool, before, new in ((st.k_cache, k_before, st.k_new),
                               (st.v_cache, v_before, st.v_new)):
         if w.layout == "HND":
-            assert torch.equal(bits(pool[blk, :, off, :]), bits(new[rows_dev]))
-            before[blk, :, off, :] = new[rows_dev]
+            assert torch.equal(bits(pool[blk, :, off, :]), bits(new[tok_dev]))
+            before[blk, :, off, :] = new[tok_dev]
             before[sink_b, :, 0, :] = pool[sink_b, :, 0, :]
         else:
-            assert torch.equal(bits(pool[blk, off]), bits(new[rows_dev]))
-            before[blk, off] = new[rows_dev]
+            assert torch.equal(bits(pool[blk, off]), bits(new[tok_dev]))
+            before[blk, off] = new[tok_dev]
             before[sink_b, 0] = pool[sink_b, 0]
         assert torch.equal(bits(before), bits(pool)), "the scatter touched another slot"
     # padding rows: zero output
     pads = w.pad_rows
     if len(pads):
         assert torch.count_nonzero(out[torch.from_numpy(pads).to(DEV)]).item() == 0
-    say(f"{w.name}: sampled max err {err:.3e}")
+    say(f"{w.name}: every row, max err {err:.3e}")
     del k_before, v_before, st
     torch.cuda.empty_cache()
 
 
-def test_config3_ragged_sampled():
-    def pick(w):
-        lens = w.context_lens
-        return sorted({int(np.argmax(lens)), int(np.argmin(np.where(lens > 0, lens, 10**9))),
-                       *w.pad_rows.tolist(), 5, 17})
-    _sampled(3, pick)
+def test_config3_ragged_every_row():
+    _full_size(3)
 
 
-def test_config4_long_tail_sampled():
-    def pick(w):
-        lens = w.context_lens
-        return sorted({w.meta["forced_row"], int(np.argmin(lens)), 0, 100, 200, 255,
-                       int(np.argsort(lens)[128])})
-    _sampled(4, pick)
+def test_config4_long_tail_every_row():
+    _full_size(4)
 
 
-def test_config5_full_width_sampled():
-    def pick(w):
-        lens = w.context_lens
-        full = np.nonzero(lens == 8192)[0]
-        mid = np.nonzero((lens > 256) & (lens < 8192))[0]
-        short = np.nonzero((lens > 0) & (lens <= 256))[0]
-        return sorted({int(full[0]), int(full[-1]), int(mid[0]), int(mid[len(mid) // 2]),
-                       int(short[0]), int(w.pad_rows[0]), int(w.pad_rows[-1])})
-    _sampled(5, pick)
+def test_config5_full_width_every_row():
+    _full_size(5)
+
+
+PLAN_TUNINGS = [
+    {},                                               # the plan's own choice
+    {"chunk_min": 512, "chunk_max": 512},             # pinned
+    {"chunk_min": 8192, "chunk_max": 8192},           # pinned: no row of width 8192 split
+    {"chunk_min": 32, "chunk_max": 2048, "solo_tokens": 1, "decode_waves": 4},
+]
+
+
+@pytest.mark.parametrize("tuning", PLAN_TUNINGS,
+                         ids=lambda t: "-".join(f"{k}{v}" for k, v in t.items()) or "default")
+@pytest.mark.parametrize("idx,kv_heads,query_len", [(2, None, 1), (3, None, 1), (4, None, 1),
+                                                    (5, None, 1), (5, 8, 1), (5, None, 4)])
+def test_plan_counts_equal_the_kernel_walk(idx, kv_heads, query_len, tuning):
+    """Day 59, "What I learned" 5: the host's tile accounting and the kernel's loop,
+    held to the same lengths.  The plan's entries are sum(cdiv(len, P)) plus the pad
+    rows; the decode kernel's own count of the tiles it streamed is the vector groups
+    times sum(cdiv(len, tile)).  The counts depend on the lengths alone, so the rows'
+    tables here name blocks of a small shared pool (rows may share blocks for a read)."""
+    w = wl.make_config(idx, kv_heads=kv_heads, query_len=query_len)
+    nb = 2048
+    j = np.arange(w.max_blocks, dtype=np.int64)[None, :]
+    r = np.arange(w.rows, dtype=np.int64)[:, None]
+    tables = to_dev(((j * 7 + r * 131) % nb).astype(np.int32))
+    shape = (nb + 1, w.kv_heads, w.block_size, w.head_dim)
+    gen = torch.Generator(device=DEV).manual_seed(idx)
+    k = torch.randn(shape, generator=gen, device=DEV).to(torch.bfloat16)
+    v = torch.randn(shape, generator=gen, device=DEV).to(torch.bfloat16)
+    q = to_dev(w.q, w.dtype)
+    lens = to_dev(w.context_lens)
+    saved = binding.get_tuning()
+    binding.set_tuning(**tuning)
+    try:
+        if query_len == 1:
+            n = binding.workspace_bytes(k, w.rows, w.heads, w.max_blocks)
+            read = binding.paged_attention
+        else:
+            n = binding.workspace_bytes_multi(k, w.rows, query_len, w.heads, w.max_blocks)
+            read = binding.paged_attention_multi
+        ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+        read(q, k, v, tables, lens, w.scale, workspace=ws, validate=False)
+        info = binding.plan_info(ws)
+    finally:
+        binding.set_tuning(**saved)
+    say(f"config {idx} kv_heads={w.kv_heads} query_len={query_len} {tuning}: {info}")
+    check_plan(w, info)
+    if "chunk_max" in tuning and tuning["chunk_min"] == tuning["chunk_max"]:
+        assert info["chunk_tokens"] == tuning["chunk_min"]
 
 
 # --------------------------------------------------------------------------- #
@@ -374,8 +496,19 @@ def test_bad_block_ids_without_validation_are_skipped_and_reported(kind):
     binding.set_tuning(groups_per_cu=1, solo_tokens=512 if solo else 1)
     try:
         binding.device_status(DEV, clear=True)
-        got = to_host(st.run(validate=False), "bf16")
+        ws = st.workspace()
+        clean_ws = st.workspace()
+        got = to_host(st.run(validate=False, workspace=ws), "bf16")
+        # the bit belongs to this call: its workspace has it, a clean call's has not,
+        # and the device-wide word keeps it until cleared
+        clean = Step(w, host_history=True)
+        clean.run(validate=False, workspace=clean_ws)
+        assert binding.workspace_status(ws) == _capi.DEVERR_BLOCK_ID
+        assert binding.workspace_status(clean_ws) == 0
         assert binding.device_status(DEV, clear=True) & _capi.DEVERR_BLOCK_ID
+        # a later clean call in the same workspace starts its status afresh
+        clean.run(validate=False, workspace=ws)
+        assert binding.workspace_status(ws) == 0
     finally:
         binding.set_tuning(**saved)
     ref, kw, vw = _oracle_by_rows(w, st.k_host, st.v_host)
@@ -646,21 +779,9 @@ def test_grouped_query_heads(case, max_group):
 
 
 @pytest.mark.parametrize("kv_heads", [8, 4])
-def test_config5_grouped_variant_sampled(kv_heads):
-    """The full-width batch with 32 query heads over 8 or 4 KV heads, sampled rows."""
-    w = wl.make_config(5, kv_heads=kv_heads)
-    say(f"{w.name}: building {w.pool_bytes / 1e9:.1f} GB of pools on the device")
-    st = Step(w, host_history=False)
-    out = st.run()
-    lens = w.context_lens
-    full = np.nonzero(lens == 8192)[0]
-    short = np.nonzero((lens > 0) & (lens <= 256))[0]
-    rows = sorted({int(full[0]), int(short[0]), int(w.pad_rows[0]), 3, 77})
-    ref = oracle_rows(st, rows)
-    err = assert_close(to_host(out, w.dtype)[rows], ref, w.dtype, w.name)
-    say(f"{w.name}: sampled max err {err:.3e}")
-    del st
-    torch.cuda.empty_cache()
+def test_config5_grouped_variant_every_row(kv_heads):
+    """The full-width batch with 32 query heads over 8 or 4 KV heads."""
+    _full_size(5, kv_heads=kv_heads)
 
 
 
@@ -1079,7 +1200,7 @@ def test_bad_live_slot_without_validation_is_skipped_and_reported():
 def test_config5_as_a_slot_window():
     """The full-width batch read through its slot window (256 x 8192 int64 cells, a
     view of a wider table): every output bit-identical to the block-table read, and
-    sampled rows against the oracle."""
+    every row against the oracle."""
     w = wl.make_config(5)
     width = w.max_blocks * w.block_size
     st = Step(w)
@@ -1094,11 +1215,9 @@ def test_config5_as_a_slot_window():
                                         st.lens, w.scale)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(got, "bf16"), blk)
-    rng = np.random.default_rng(12)
-    live = [r for r in range(w.rows) if w.context_lens[r] > 0]
-    rows = sorted(rng.choice(live, 6, replace=False).tolist())
-    ref = oracle_rows(st, rows)
-    assert_close(blk[rows], ref, "bf16", "config 5 slot window")
+    live = w.live_rows
+    ref = oracle_rows(st, live)
+    assert_close(blk[live], ref, "bf16", "config 5 slot window")
 
 
 def test_captured_slot_window_step():
@@ -1232,45 +1351,10 @@ def test_multi_refusals_touch_nothing():
     assert torch.all(out == 2.0)
 
 
-def test_config5_with_four_new_tokens_sampled():
+def test_config5_with_four_new_tokens_every_row():
     """The full-width batch with four new tokens per row (a speculative-decoding step
-    of three drafts): sampled rows against the oracle, from a host copy of just the
-    blocks those rows name."""
-    w = wl.make_config(5, query_len=4)
-    st = Step(w)
-    say(f"{w.name}: q {tuple(st.q.shape)}")
-    got = to_host(_multi_run(w, st, validate=False), "bf16")
-    assert binding.device_status(DEV, clear=True) == 0
-    rng = np.random.default_rng(21)
-    live = [r for r in range(w.rows) if w.context_lens[r] > 0]
-    longest = int(np.argmax(w.context_lens))
-    rows = sorted(set(rng.choice(live, 5, replace=False).tolist() + [longest]))
-    pads = [r for r in range(w.rows) if w.context_lens[r] == 0]
-    assert np.all(got[pads] == 0)
-    blocks = wl.live_blocks(w, rows)
-    remap = {int(b): i for i, b in enumerate(blocks)}
-    idx = torch.from_numpy(np.append(blocks, w.num_blocks).astype(np.int64)).to(DEV)
-    k = to_host(st.k_cache.index_select(0, idx), "bf16")
-    v = to_host(st.v_cache.index_select(0, idx), "bf16")
-    n = len(blocks)
-    bt = np.full((len(rows), w.max_blocks), -1, dtype=np.int32)
-    sm = []
-    for a, r in enumerate(rows):
-        live_b = wl.cdiv(w.context_lens[r], w.block_size)
-        bt[a, :live_b] = [remap[int(b)] for b in w.block_tables[r, :live_b]]
-        for i in range(4):
-            s = int(w.slot_mapping[r * 4 + i])
-            sm.append(remap[s // w.block_size] * w.block_size + s % w.block_size)
-    k_new = w.k_new.reshape(w.rows, 4, w.kv_heads, w.head_dim)[rows].reshape(-1, w.kv_heads,
-                                                                           w.head_dim)
-    v_new = w.v_new.reshape(w.rows, 4, w.kv_heads, w.head_dim)[rows].reshape(-1, w.kv_heads,
-                                                                           w.head_dim)
-    oracle.kv_write(k, v, k_new, v_new, np.array(sm, dtype=np.int64), num_blocks=n,
-                    block_size=w.block_size, layout=w.layout, dtype="bf16")
-    ref = oracle.paged_attention_multi(w.q[rows], k, v, bt, w.context_lens[rows], w.scale,
-                                       num_blocks=n, block_size=w.block_size, layout=w.layout,
-                                       dtype="bf16")
-    assert_close(got[rows], ref, "bf16", w.name)
+    of three drafts)."""
+    _full_size(5, query_len=4)
 
 
 # --------------------------------------------------------------------------- #
