@@ -175,6 +175,27 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
                                int32_t num_heads, float scale, void* workspace,
                                size_t workspace_bytes, int32_t validate, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): pkv_paged_attention with the
+ * library's own workspace, a static device array of PKV_NOALLOC_SCRATCH_BYTES on each
+ * device (held from the library's load until the process ends).  The caller passes
+ * the inputs and `out` as for pkv_paged_attention; the call allocates nothing, runs
+ * no host checks and copies nothing to the host (validate = 0 semantics: bad lengths
+ * are clamped, bad block ids skipped, each raising its bit in the device-wide status
+ * word, pkv_device_status), and records no timing events.
+ * Refuses (before touching anything) what pkv_paged_attention refuses from the shape,
+ * and with WORKSPACE a batch whose pkv_workspace_bytes exceeds the scratch.  Every
+ * call on a device shares that device's scratch: calls that overlap on one device
+ * (two streams, two host threads) race and give undefined results.  The scratch keeps
+ * the last call's work list; each call rewrites everything it reads. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pkv_status pkv_paged_attention_noalloc(const pkv_pool_desc* pool, void* out, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables,
+                                       int32_t max_blocks_per_row,
+                                       const int32_t* context_lens, int64_t num_rows,
+                                       int32_t num_heads, float scale, void* stream);
+
 /* The read with several new tokens (queries) per row: speculative decoding's draft
  * tokens, or a chunk of a prompt, over the same paged history (Day 59, "Why it
  * matters": the read's rectangle has a query_len axis beside rows and heads).

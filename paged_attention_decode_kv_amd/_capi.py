@@ -14,6 +14,7 @@ LAYOUT_CODES = {"HND": 0, "NHD": 1}
 STATUS_NAMES = ("OK", "EMPTY", "DTYPE", "SHAPE", "CONTEXT_BOUNDS", "BLOCK_ID", "SLOT",
                 "UNSUPPORTED", "WORKSPACE", "NULL", "HIP")
 DEVERR_SLOT, DEVERR_CONTEXT_BOUNDS, DEVERR_BLOCK_ID = 1, 2, 4
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 
 # every function include/pagedkv.h declares: name -> (restype, argtypes)
 _i32, _i64, _sz, _p, _f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p,
@@ -74,6 +75,8 @@ SIGNATURES = {
                                        _i64, _i32, _f, _p, _sz,
                                        ctypes.POINTER(ctypes.c_void_p)]),
     "pkv_graph_launch": (_i32, [_p, _p]),
+    "pkv_paged_attention_noalloc": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32,
+                                           _f, _p]),
     "pkv_workspace_bytes_multi": (_sz, [_PD, _i64, _i32, _i32, _i32]),
     "pkv_paged_attention_multi": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32, _i32,
                                          _f, _p, _sz, _i32, _p]),

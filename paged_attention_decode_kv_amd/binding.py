@@ -161,6 +161,35 @@ def paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     return out
 
 
+def paged_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            scale: float, out: torch.Tensor, *,
+                            layout: str = "HND") -> torch.Tensor:
+    """The decode read in the library's static scratch (pkv_paged_attention_noalloc):
+    nothing is allocated, by the library or here, so ``out`` must be given; no host
+    checks (bad inputs are clamped or skipped and reported in device_status)."""
+    rows = int(context_lens.shape[0]) if context_lens.dim() >= 1 else 0
+    if rows == 0:
+        _raise("EMPTY", "no rows")
+    desc = _pool_pair(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _device_tensor(q, "q", k_cache.dtype, dev)
+    _device_tensor(out, "out", k_cache.dtype, dev)
+    _device_tensor(block_tables, "block_tables", torch.int32, dev)
+    _device_tensor(context_lens, "context_lens", torch.int32, dev)
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[2] != desc.head_dim or \
+            out.shape != q.shape:
+        _raise("SHAPE", f"q and out must be [{rows}, heads, {desc.head_dim}]")
+    if context_lens.dim() != 1 or block_tables.dim() != 2 or block_tables.shape[0] != rows:
+        _raise("SHAPE", "block_tables must be [rows, max_blocks], context_lens [rows]")
+    with torch.cuda.device(dev):
+        _check(_capi.lib().pkv_paged_attention_noalloc(
+            ctypes.byref(desc), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), rows,
+            int(q.shape[1]), float(scale), _stream(k_cache)))
+    return out
+
+
 def workspace_bytes_multi(k_cache: torch.Tensor, num_rows: int, query_len: int,
                           num_heads: int, max_blocks: int, layout: str = "HND") -> int:
     desc = pool_desc(k_cache, layout)

@@ -489,6 +489,38 @@ pkv_status pkv_paged_attention(const pkv_pool_desc* pool, void* out, const void*
   return ok();
 }
 
+pkv_status pkv_paged_attention_noalloc(const pkv_pool_desc* pool, void* out, const void* q,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables,
+                                       int32_t max_blocks_per_row,
+                                       const int32_t* context_lens, int64_t num_rows,
+                                       int32_t num_heads, float scale, void* stream) {
+  static_assert(pkv::kScratchBytes == PKV_NOALLOC_SCRATCH_BYTES, "the header states it");
+  const pkv::Tuning t = pkv::tuning_snapshot();   // this call's one view of the tuning
+  pkv_status s = check_attention_shape(pool, max_blocks_per_row, num_rows, num_heads);
+  if (s != PKV_OK) return s;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  s = check_attention_items(pool, max_blocks_per_row, num_rows, num_heads, t);
+  if (s != PKV_OK) return s;
+  const size_t need = pkv::workspace_bytes(num_rows, num_heads, pool->head_dim,
+                                           max_blocks_per_row, pool->block_size, t);
+  if (need > pkv::kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE,
+                "this batch needs a workspace of %zu bytes; the static scratch holds %zu "
+                "(use pkv_paged_attention with a workspace of its own)",
+                need, pkv::kScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = pkv::scratch_pointer(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "looking up the static scratch");
+  const pkv::TimingPause untimed;   // timing would create events
+  e = launch_attention(pool, out, q, k_cache, v_cache, block_tables, max_blocks_per_row,
+                       context_lens, num_rows, num_heads, scale, scratch, t,
+                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching paged_attention_noalloc");
+  return ok();
+}
+
 size_t pkv_workspace_bytes_slots(const pkv_pool_desc* pool, int64_t num_rows,
                                  int32_t num_heads, int32_t width) {
   const pkv::Tuning t = pkv::tuning_snapshot();

@@ -205,6 +205,13 @@ hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& s,
                                         const Workspace& ws, const Tuning& t,
                                         hipStream_t stream);
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream);
+
+// The library's own workspace for callers that cannot allocate
+// (pkv_paged_attention_noalloc): a static device array of kScratchBytes on every
+// device the library runs on.  scratch_pointer gives the current device's copy: its
+// device address, looked up once per device with hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+hipError_t scratch_pointer(void** ptr);
 // which decode kernel (and query-vector group) a read of this shape runs under tuning t
 // (uses a.g, a.num_heads, a.query_len)
 const char* decode_kernel_name(const AttnArgs& a, const Tuning& t);
@@ -213,6 +220,12 @@ const char* decode_kernel_name(const AttnArgs& a, const Tuning& t);
 void timing_begin(int phase, hipStream_t stream);
 void timing_end(int phase, hipStream_t stream);
 void timing_enable(bool on);
+// While a TimingPause lives, this thread's launches record no events (a call that
+// must not create any).
+struct TimingPause {
+  TimingPause();
+  ~TimingPause();
+};
 hipError_t timing_read(int phase, double* total_ms, int64_t* launches, bool reset);
 
 }  // namespace pkv

@@ -47,6 +47,11 @@ namespace pkv {
 // pkv_device_status); each call also keeps its own bits in its workspace's counters.
 __device__ unsigned int g_status;
 
+// The workspace of pkv_paged_attention_noalloc, one per device.  Host code never uses
+// this name as an address (on the host it is a stand-in, not device memory): it uses
+// the device address scratch_pointer looks up.  Calls on one device share it.
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
@@ -2598,6 +2603,24 @@ const char* decode_kernel_name(const AttnArgs& a, const Tuning& t) {
     case 8: return kVec[3];
     default: return kVec[0];
   }
+}
+
+hipError_t scratch_pointer(void** ptr) {
+  static std::atomic<void*> addr[64];   // per device, looked up once
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // with the device current: its own copy of the array
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);   // racing threads store the same
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream) {

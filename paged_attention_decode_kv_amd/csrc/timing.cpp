@@ -51,6 +51,7 @@ struct PhaseLog {
 SpinLock g_mu;
 std::atomic<bool> g_on{false};
 PhaseLog g_log[kPhases];
+thread_local int g_paused = 0;   // TimingPause depth on this thread
 
 hipEvent_t take(PhaseLog& p) noexcept {
   if (!p.spare.empty()) {
@@ -92,6 +93,9 @@ void timing_enable(bool on) {
   g_on = on;
 }
 
+TimingPause::TimingPause() { ++g_paused; }
+TimingPause::~TimingPause() { --g_paused; }
+
 // A stream under capture records nodes, not work: events there would never complete
 // on their own, so captured launches go untimed.
 static bool capturing(hipStream_t stream) {
@@ -100,7 +104,7 @@ static bool capturing(hipStream_t stream) {
 }
 
 void timing_begin(int phase, hipStream_t stream) {
-  if (!g_on || capturing(stream)) return;
+  if (!g_on || g_paused || capturing(stream)) return;
   Guard lock(g_mu);
   PhaseLog& p = g_log[phase];
   // a start left open on this stream (a launch that failed before its stop) is dropped
@@ -119,7 +123,7 @@ void timing_begin(int phase, hipStream_t stream) {
 }
 
 void timing_end(int phase, hipStream_t stream) {
-  if (!g_on || capturing(stream)) return;
+  if (!g_on || g_paused || capturing(stream)) return;
   Guard lock(g_mu);
   PhaseLog& p = g_log[phase];
   hipEvent_t start = take_open(p, stream);
