@@ -14,8 +14,11 @@ per step.  The step is timed twice over the same tensors: as the two library cal
 per step (eager), and as replays of one HIP graph recorded from those calls (graph, the
 default ``value``; ``--launch eager`` reports the other).  ``roofline`` reports the
 decode kernel alone, timed with HIP events on its launch stream over a third pass of
-the same library-call steps, against MI355X's 8 TB/s HBM peak.
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same batch.
+the same library-call steps, against MI355X's 8 TB/s HBM peak, and beside the rate a
+plain streaming read of the same byte count reaches on the same GPU (``achievable``).
+``cpu_baseline`` times the CPU oracle over the same batch (every row by default) on a
+pool of host threads, one per core of the process's CPU affinity (at most 16); its
+outputs check every GPU output row.
 """
 
 from __future__ import annotations
@@ -47,8 +50,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5)")
     ap.add_argument("--layout", default="HND", choices=["HND", "NHD"])
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the batch the CPU oracle runs (a seeded sample; 0: every "
+                         "row)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads of the CPU oracle (0: the process's CPU affinity, "
+                         "at most 16)")
     ap.add_argument("--chunk-min", type=int, default=0,
                     help="shortest decode work-item length in tokens (0: library default)")
     ap.add_argument("--chunk-max", type=int, default=0,
@@ -119,13 +126,23 @@ def traffic_per_launch(config_name, layout):
     return None
 
 
-def blas_threads():
+MAX_ORACLE_THREADS = 16    # a one-GPU machine's share of its host's cores
+
+
+def cpu_info():
+    """Host CPUs as this process sees them: the model, the logical CPUs of the machine
+    and those of the process's affinity."""
+    model = None
     try:
-        from threadpoolctl import threadpool_info
-        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-        return max(n) if n else 1
-    except Exception:
-        return 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
 
 
 def _host(t, dtype):
@@ -136,31 +153,54 @@ def _host(t, dtype):
     return t.cpu().numpy()
 
 
-def cpu_baseline(w, k_cache, v_cache, budget_s, min_rows=0):
-    """The oracle (kv_write + masked-rectangle read) on rows of the batch, four rows per
-    oracle call, in a seeded order, until the wall-clock budget is spent (and at least
-    ``min_rows`` rows are done).  Runs on the pool before any GPU step touches it; host
-    copies of the rows' blocks are made before each call and are not timed.  Returns
-    the timing record and the oracle outputs of the rows it covered."""
+def _row_groups(lens, rows, per_row, cells=1 << 23):
+    """Rows sorted by length, cut into groups whose oracle rectangle (rows x longest
+    length x per_row elements) stays within `cells` (a longer row goes alone)."""
+    rows = sorted(rows, key=lambda r: int(lens[r]))
+    groups, at = [], 0
+    while at < len(rows):
+        end = at + 1
+        while end < len(rows) and (end + 1 - at) * max(1, int(lens[rows[end]])) * per_row <= cells:
+            end += 1
+        groups.append(rows[at:end])
+        at = end
+    return groups
+
+
+def cpu_baseline(w, k_cache, v_cache, sample_rows=0, threads=0):
+    """The oracle (kv_write + masked-rectangle read) over the batch's rows (every row,
+    or a seeded sample of ``sample_rows``), in groups of rows of similar length on a pool
+    of host threads (numpy releases the interpreter lock in its gathers, products and
+    loops; BLAS is held to one thread per worker).  Runs on the pool before any GPU
+    step touches it.  The host copies of each group's blocks are made first, untimed;
+    the wall clock from the first group's start to the last group's end is the time.
+    Returns the timing record and the oracle outputs of the rows it covered."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from paged_attention_decode_kv_amd import workloads as wl
 
-    order = np.random.default_rng(1234).permutation(w.rows)
-    spent, kv_bytes, row_heads, tokens = 0.0, 0, 0, 0
-    rows_done, outputs = [], []
-    elem = 2 if w.dtype == "bf16" else 4
-    for at in range(0, w.rows, 4):
-        part = order[at:at + 4]
+    info = cpu_info()
+    n_threads = threads or max(1, min(MAX_ORACLE_THREADS, info["affinity"]))
+    rows = list(range(w.rows))
+    if sample_rows and sample_rows < w.rows:
+        rows = sorted(np.random.default_rng(1234).permutation(w.rows)[:sample_rows].tolist())
+    nq = w.query_len
+    kv_shape = (w.rows, nq, w.kv_heads, w.head_dim)
+    read = oracle.paged_attention if nq == 1 else oracle.paged_attention_multi
+    groups = _row_groups(w.context_lens, rows, w.heads * w.head_dim * nq)
+    jobs = []
+    for part in groups:                     # host copies, untimed
         blocks = wl.live_blocks(w, part)
         remap = {int(b): i for i, b in enumerate(blocks)}
         n = len(blocks)
         idx = torch.from_numpy(np.append(blocks, w.num_blocks).astype(np.int64)).to(k_cache.device)
         kh = _host(k_cache.index_select(0, idx), w.dtype)
         vh = _host(v_cache.index_select(0, idx), w.dtype)
-        nq = w.query_len
         bt = np.full((len(part), w.max_blocks), -1, dtype=np.int32)
         sm = np.empty(len(part) * nq, dtype=np.int64)
         for i, r in enumerate(part):
@@ -170,36 +210,69 @@ def cpu_baseline(w, k_cache, v_cache, budget_s, min_rows=0):
                 s = int(w.slot_mapping[r * nq + j])
                 sm[i * nq + j] = (n * w.block_size if w.context_lens[r] == 0 else
                                   remap[s // w.block_size] * w.block_size + s % w.block_size)
-        kv_shape = (w.rows, nq, w.kv_heads, w.head_dim)
         k_new = w.k_new.reshape(kv_shape)[part].reshape(-1, w.kv_heads, w.head_dim)
         v_new = w.v_new.reshape(kv_shape)[part].reshape(-1, w.kv_heads, w.head_dim)
-        read = oracle.paged_attention if nq == 1 else oracle.paged_attention_multi
+        jobs.append((part, kh, vh, bt, sm, n, k_new, v_new))
+
+    def compute(job):
+        part, kh, vh, bt, sm, n, k_new, v_new = job
+        oracle.kv_write(kh, vh, k_new, v_new, sm, num_blocks=n, block_size=w.block_size,
+                        layout=w.layout, dtype=w.dtype)
+        return read(w.q[part], kh, vh, bt, w.context_lens[part], w.scale, num_blocks=n,
+                    block_size=w.block_size, layout=w.layout, dtype=w.dtype)
+
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(n_threads) as ex:
         t0 = time.perf_counter()
-        oracle.kv_write(kh, vh, k_new, v_new, sm, num_blocks=n,
-                        block_size=w.block_size, layout=w.layout, dtype=w.dtype)
-        out = read(w.q[part], kh, vh, bt, w.context_lens[part], w.scale, num_blocks=n,
-                   block_size=w.block_size, layout=w.layout, dtype=w.dtype)
-        spent += time.perf_counter() - t0
-        outputs.append(out)
-        lens = w.context_lens[part]
-        kv_bytes += int(lens.sum()) * w.kv_heads * w.head_dim * 2 * elem
-        tokens += int(lens.sum())
-        rows_done.extend(int(r) for r in part)
-        row_heads += int(np.count_nonzero(lens)) * w.heads
-        if spent >= budget_s and len(rows_done) >= min_rows:
-            break
+        outs = list(ex.map(compute, jobs))
+        spent = time.perf_counter() - t0
+    done = [r for part in groups for r in part]
+    lens = w.context_lens[done]
+    elem = 2 if w.dtype == "bf16" else 4
+    kv_bytes = int(lens.sum()) * w.kv_heads * w.head_dim * 2 * elem
+    row_heads = int(np.count_nonzero(lens)) * w.heads
     rec = {
         "value": round(kv_bytes / spent / 1e9, 4),
         "unit": "GB/s",
-        "cores": blas_threads(),
+        "cores": n_threads,
         "kind": "oracle",
-        "sample": (f"{len(rows_done)} of {w.rows} rows of the same batch ({tokens} tokens, "
-                   f"{row_heads} live (row, head) pairs), 4 rows per oracle call, float64 "
-                   f"numpy; {spent:.1f} s; {row_heads / spent:.1f} (row, head)/s"),
+        "sample": (f"{'every row' if len(done) == w.rows else f'{len(done)} seeded rows'} of "
+                   f"the same batch ({len(done)} rows, {int(lens.sum())} tokens, {row_heads} "
+                   f"live (row, head) pairs) in {len(groups)} row groups on {n_threads} host "
+                   f"threads (BLAS 1 thread each), float64 numpy; {spent:.2f} s wall; "
+                   f"{row_heads / spent:.1f} (row, head)/s"),
         "seconds": round(spent, 3),
         "row_heads_per_s": round(row_heads / spent, 3),
+        "cpu": info,
     }
-    return rec, np.array(rows_done), np.concatenate(outputs)
+    return rec, np.array(done), np.concatenate(outs)
+
+
+def achievable_read(nbytes, device, reps=5):
+    """The best rate (GB/s) a plain streaming read of ``nbytes`` reaches on this GPU
+    (pkv_stream_read, 1 to 8 workgroups of 256 threads per CU), each launch timed with
+    events on the stream it runs on; returns (GB/s, workgroups per CU, microseconds)."""
+    import torch
+
+    from paged_attention_decode_kv_amd import binding
+
+    nbytes = max(16, nbytes // 16 * 16)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    sink = torch.zeros(1, dtype=torch.int32, device=device)
+    best = None
+    for gpc in (1, 2, 4, 8):
+        for _ in range(2):
+            binding.stream_read(buf, sink, gpc)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            ev[2 * i].record()
+            binding.stream_read(buf, sink, gpc)
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        us = min(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) * 1e3
+        if best is None or us < best[2]:
+            best = (nbytes / us / 1e3, gpc, us)
+    del buf, sink
+    return best
 
 
 def check_outputs(out, rows, ref, dtype):
@@ -316,9 +389,14 @@ def main():
 
     # the CPU oracle runs first, on the untouched pool: its timing is the baseline and
     # its outputs check the GPU step's outputs afterwards
-    budget = 0.0 if args.no_cpu_baseline else args.cpu_seconds
-    log(f"cpu oracle on a sample of rows (budget {budget:.0f} s)")
-    base_rec, check_rows, check_ref = cpu_baseline(w, k_cache, v_cache, budget, min_rows=4)
+    if args.no_cpu_baseline:   # the oracle still checks a few rows
+        sample = min(w.rows, 8)
+    else:
+        sample = args.cpu_rows
+    log(f"cpu oracle on {sample or 'every'} row(s) of the batch")
+    base_rec, check_rows, check_ref = cpu_baseline(w, k_cache, v_cache, sample,
+                                                   args.cpu_threads)
+    log(f"cpu oracle: {base_rec['sample']}")
 
     def step(validate=False):
         binding.kv_write(k_new, v_new, slots, k_cache, v_cache, layout=w.layout,
@@ -448,6 +526,9 @@ def main():
             kern_bytes = acc.algorithmic_bytes(tok_lens, address="slots", **shape)["attention"]
         traffic = None        # the committed counters are for the unscattered batch
     achieved = kern_bytes / kern_s / 1e9
+    ach_gbps, ach_gpc, ach_us = achievable_read(kern_bytes, dev)
+    log(f"streaming read of {kern_bytes} B: {ach_us:.2f} us at {ach_gpc} workgroups/CU, "
+        f"{ach_gbps:.1f} GB/s")
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 2),
@@ -458,6 +539,11 @@ def main():
         "kernel": kernel,
         "kernel_avg_us": round(kern_s * 1e6, 2),
         "bytes_per_launch": kern_bytes,
+        # a plain streaming read of the same byte count on this GPU (best of 1-8
+        # workgroups/CU, fastest of 5 launches): the rate a kernel that only reads reaches
+        "achievable": round(ach_gbps, 2),
+        "achievable_kernel": f"stream_read_kernel, {ach_gpc} x 256-thread workgroups per CU",
+        "frac_of_achievable": round(achieved / ach_gbps, 4),
     }
     result = {
         "metric": METRIC,

@@ -317,6 +317,16 @@ typedef struct pkv_plan_info {
 pkv_status pkv_plan_info_read(const void* workspace, size_t workspace_bytes,
                               pkv_plan_info* info, void* stream);
 
+/* A plain streaming read of `bytes` bytes at device address `src`, with the decode
+ * kernels' 16-byte non-temporal loads, by groups_per_cu (1..16) workgroups of 256
+ * threads per compute unit, each reading 32 KB runs dealt round robin.  For
+ * benchmarks: the rate a kernel that does nothing but read reaches on this GPU, the
+ * achievable reference beside the decode kernel's rate.  `sink` is a 4-byte device
+ * word that is written only if the bytes read fold to one particular value (so no load
+ * can be skipped).  bytes: a positive multiple of 16.  Asynchronous on `stream`. */
+pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                           int32_t groups_per_cu, void* stream);
+
 /* Work split of the decode read (process-wide).  Each call cuts every row's history
  * into chunks; one (chunk, query head) is a work item of the persistent decode kernel,
  * shared by the waves of one workgroup, and rows longer than one chunk are merged

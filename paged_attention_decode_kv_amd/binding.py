@@ -450,6 +450,17 @@ def plan_info(workspace: torch.Tensor) -> dict:
     return {f: int(getattr(info, f)) for f, _ in _capi.PlanInfo._fields_}
 
 
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, groups_per_cu: int = 4) -> None:
+    """Enqueue a plain streaming read of ``buf`` (pkv_stream_read) on the current
+    stream; ``sink`` is a device int32/uint32 scalar tensor."""
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda:
+        _raise("SHAPE", "buf and sink must be contiguous device tensors")
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    with torch.cuda.device(buf.device):
+        _check(_capi.lib().pkv_stream_read(_ptr(buf), nbytes, _ptr(sink), int(groups_per_cu),
+                                           _stream(buf)))
+
+
 def decode_kernel_for(k_cache: torch.Tensor, num_heads: int, query_len: int = 1,
                       layout: str = "HND") -> str:
     """Which decode kernel (and query-vector group) a read of this shape runs."""

@@ -740,6 +740,19 @@ pkv_status pkv_workspace_status(const void* workspace, size_t workspace_bytes,
   return ok();
 }
 
+pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                           int32_t groups_per_cu, void* stream) {
+  if (!src || !sink) return fail(PKV_ERR_NULL, "src or sink is NULL");
+  if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+    return fail(PKV_ERR_SHAPE, "bytes %zu: a positive multiple of 16 up to 2^40", bytes);
+  if (groups_per_cu < 1 || groups_per_cu > 16)
+    return fail(PKV_ERR_SHAPE, "groups_per_cu %d outside [1, 16]", groups_per_cu);
+  hipError_t e = pkv::launch_stream_read(src, (int64_t)bytes, sink, groups_per_cu,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the streaming read");
+  return ok();
+}
+
 pkv_status pkv_set_tuning(const pkv_tuning* t) {
   if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
   if (!pkv::set_tuning(t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group,

@@ -205,6 +205,8 @@ hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& s,
                                         const Workspace& ws, const Tuning& t,
                                         hipStream_t stream);
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink,
+                              int groups_per_cu, hipStream_t stream);
 
 // The library's own workspace for callers that cannot allocate
 // (pkv_paged_attention_noalloc): a static device array of kScratchBytes on every

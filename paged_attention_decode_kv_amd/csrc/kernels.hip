@@ -2605,6 +2605,45 @@ const char* decode_kernel_name(const AttnArgs& a, const Tuning& t) {
   }
 }
 
+// ------------------------------------------------------------------------- //
+// a plain streaming read (the achievable-bandwidth reference of benchmarks)
+// ------------------------------------------------------------------------- //
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 8;
+
+// Each thread reads 16-byte pieces i, i + 256, ... of its workgroup's runs of
+// 256 x kStreamUnroll pieces (32 KB), runs dealt round robin over the grid, with the
+// decode kernels' non-temporal loads, and folds them into one word; a store that
+// depends on that word keeps every load.
+__global__ void __launch_bounds__(kStreamThreads)
+stream_read_kernel(const char* src, int64_t pieces, uint32_t* sink) {
+  constexpr int64_t kRun = (int64_t)kStreamThreads * kStreamUnroll;
+  uint32_t acc = 0;
+  for (int64_t run = (int64_t)blockIdx.x * kRun; run < pieces; run += (int64_t)gridDim.x * kRun) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      const int64_t i = run + u * kStreamThreads + threadIdx.x;
+      v[u] = i < pieces ? load16_stream(src + i * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x5EED5EEDu) sink[0] = acc;   // almost never taken; the loads must happen
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink,
+                              int groups_per_cu, hipStream_t stream) {
+  int cus = 0;
+  hipError_t err = device_cus(&cus);
+  if (err != hipSuccess) return err;
+  const int64_t pieces = bytes / 16;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)(cus * groups_per_cu)),
+                     dim3(kStreamThreads), 0, stream, static_cast<const char*>(src), pieces,
+                     sink);
+  return hipGetLastError();
+}
+
 hipError_t scratch_pointer(void** ptr) {
   static std::atomic<void*> addr[64];   // per device, looked up once
   int dev = 0;
