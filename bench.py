@@ -275,6 +275,56 @@ def achievable_read(nbytes, device, reps=5):
     return best
 
 
+def achievable_gather(w, k_cache, v_cache, reps=5):
+    """The best rate (GB/s) a plain read of exactly the (block, KV head) pieces of K and
+    V the decode streams reaches (pkv_gather_read), 1 to 8 workgroups of 256 threads
+    per CU.  The pieces go in the decode's order: row by row, in groups of 8 blocks (a
+    decode item's waves take one block each), every KV head of a group before the next
+    group, so that concurrent waves read all heads' pieces (one head's pieces sit at the
+    same offset of every 128 KB block, and reading them alone leaves most HBM channels
+    idle).  HND pools only (a piece is contiguous there); returns (GB/s, workgroups per
+    CU, microseconds, bytes) or None."""
+    import numpy as np
+    import torch
+
+    from paged_attention_decode_kv_amd import binding
+    from paged_attention_decode_kv_amd import workloads as wl
+
+    if w.layout != "HND":
+        return None
+    elem = 2 if w.dtype == "bf16" else 4
+    piece = w.block_size * w.head_dim * elem
+    blk_bytes = w.kv_heads * piece
+    offs = []
+    for r in range(w.rows):
+        nb = wl.cdiv(w.context_lens[r], w.block_size)
+        if nb == 0:
+            continue
+        blocks = w.block_tables[r, :nb].astype(np.int64)
+        heads = np.arange(w.kv_heads, dtype=np.int64)
+        for g0 in range(0, nb, 8):
+            grp = blocks[g0:g0 + 8]
+            offs.append((heads[:, None] * piece + grp[None, :] * blk_bytes).reshape(-1))
+    pieces = binding.GatherPieces(k_cache, v_cache, np.concatenate(offs), piece)
+    sink = torch.zeros(1, dtype=torch.int32, device=k_cache.device)
+    nbytes = pieces.offsets.numel() * piece * 2
+    best = None
+    for gpc in (1, 2, 4, 8):
+        for _ in range(2):
+            binding.gather_read(pieces, sink, gpc)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            ev[2 * i].record()
+            binding.gather_read(pieces, sink, gpc)
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        us = min(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) * 1e3
+        if best is None or us < best[2]:
+            best = (nbytes / us / 1e3, gpc, us, nbytes)
+    del pieces, sink
+    return best
+
+
 def check_outputs(out, rows, ref, dtype):
     """GPU outputs of the sampled rows against the oracle's (same tolerances as the
     parity tests: 2e-6 for float32, 2e-2 and 2^-8 relative + 2e-5 for bfloat16)."""
@@ -529,6 +579,10 @@ def main():
     ach_gbps, ach_gpc, ach_us = achievable_read(kern_bytes, dev)
     log(f"streaming read of {kern_bytes} B: {ach_us:.2f} us at {ach_gpc} workgroups/CU, "
         f"{ach_gbps:.1f} GB/s")
+    gather = achievable_gather(w, k_cache, v_cache) if not scattered else None
+    if gather:
+        log(f"gathering read of the decode's {gather[3]} B of 4 KB pieces: {gather[2]:.2f} us "
+            f"at {gather[1]} workgroups/CU, {gather[0]:.1f} GB/s")
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 2),
@@ -544,6 +598,12 @@ def main():
         "achievable": round(ach_gbps, 2),
         "achievable_kernel": f"stream_read_kernel, {ach_gpc} x 256-thread workgroups per CU",
         "frac_of_achievable": round(achieved / ach_gbps, 4),
+        # the same for a plain read of exactly the (block, KV head) pieces the decode
+        # reads, in their scattered order (HND pools)
+        "achievable_gather": round(gather[0], 2) if gather else None,
+        "achievable_gather_kernel": (f"gather_read_kernel, {gather[1]} x 256-thread "
+                                     f"workgroups per CU, {gather[3]} B") if gather else None,
+        "frac_of_gather": round(achieved / gather[0], 4) if gather else None,
     }
     result = {
         "metric": METRIC,

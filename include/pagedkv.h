@@ -327,6 +327,16 @@ pkv_status pkv_plan_info_read(const void* workspace, size_t workspace_bytes,
 pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
                            int32_t groups_per_cu, void* stream);
 
+/* The same loads over scattered pieces: piece i is piece_bytes bytes (a multiple of 16)
+ * at byte offset offsets[i] of both k_base and v_base (device addresses; `offsets` is a
+ * device array of n_pieces int64), each wave of the grid reading every (waves)-th
+ * piece, two at a time.  With the offsets of the (block, KV head) pieces a decode read
+ * streams, it is the rate a kernel that only reads reaches on that access pattern.
+ * Each piece's bytes must lie inside both allocations.  Asynchronous on `stream`. */
+pkv_status pkv_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,
+                           int64_t n_pieces, int32_t piece_bytes, uint32_t* sink,
+                           int32_t groups_per_cu, void* stream);
+
 /* Work split of the decode read (process-wide).  Each call cuts every row's history
  * into chunks; one (chunk, query head) is a work item of the persistent decode kernel,
  * shared by the waves of one workgroup, and rows longer than one chunk are merged

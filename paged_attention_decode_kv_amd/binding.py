@@ -461,6 +461,36 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, groups_per_cu: int = 4) -
                                            _stream(buf)))
 
 
+class GatherPieces:
+    """Byte offsets of pieces of both pools for gather_read, checked on the host to lie
+    inside the pools and then copied to the device."""
+
+    def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, offsets: np.ndarray,
+                 piece_bytes: int):
+        offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+        nbytes = min(k_cache.numel() * k_cache.element_size(),
+                     v_cache.numel() * v_cache.element_size())
+        if offsets.ndim != 1 or offsets.size == 0:
+            _raise("SHAPE", "offsets must be a non-empty 1-D array")
+        if piece_bytes < 16 or piece_bytes % 16 or offsets.min() < 0 or \
+                offsets.max() + piece_bytes > nbytes:
+            _raise("SHAPE", "a piece lies outside the pools")
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.offsets = torch.from_numpy(offsets).to(k_cache.device)
+        self.piece_bytes = int(piece_bytes)
+
+
+def gather_read(pieces: GatherPieces, sink: torch.Tensor, groups_per_cu: int = 4) -> None:
+    """Enqueue a plain read of checked pieces of both pools (pkv_gather_read) on the
+    current stream."""
+    k_cache, v_cache, offsets = pieces.k_cache, pieces.v_cache, pieces.offsets
+    piece_bytes = pieces.piece_bytes
+    with torch.cuda.device(k_cache.device):
+        _check(_capi.lib().pkv_gather_read(_ptr(k_cache), _ptr(v_cache), _ptr(offsets),
+                                           offsets.numel(), int(piece_bytes), _ptr(sink),
+                                           int(groups_per_cu), _stream(k_cache)))
+
+
 def decode_kernel_for(k_cache: torch.Tensor, num_heads: int, query_len: int = 1,
                       layout: str = "HND") -> str:
     """Which decode kernel (and query-vector group) a read of this shape runs."""

@@ -753,6 +753,22 @@ pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
   return ok();
 }
 
+pkv_status pkv_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,
+                           int64_t n_pieces, int32_t piece_bytes, uint32_t* sink,
+                           int32_t groups_per_cu, void* stream) {
+  if (!k_base || !v_base || !offsets || !sink)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  if (n_pieces < 1 || piece_bytes < 16 || piece_bytes % 16 != 0 || piece_bytes > (1 << 20))
+    return fail(PKV_ERR_SHAPE, "%lld pieces of %d bytes: at least one piece, each a multiple "
+                "of 16 bytes up to 1 MiB", (long long)n_pieces, piece_bytes);
+  if (groups_per_cu < 1 || groups_per_cu > 16)
+    return fail(PKV_ERR_SHAPE, "groups_per_cu %d outside [1, 16]", groups_per_cu);
+  hipError_t e = pkv::launch_gather_read(k_base, v_base, offsets, n_pieces, piece_bytes, sink,
+                                         groups_per_cu, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the gathering read");
+  return ok();
+}
+
 pkv_status pkv_set_tuning(const pkv_tuning* t) {
   if (!t) return fail(PKV_ERR_NULL, "tuning is NULL");
   if (!pkv::set_tuning(t->chunk_min, t->chunk_max, t->decode_waves, t->items_per_group,

@@ -207,6 +207,9 @@ hipError_t launch_paged_attention_slots(const AttnArgs& a, const SlotArgs& s,
 hipError_t read_device_status(uint32_t* flags, int clear, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink,
                               int groups_per_cu, hipStream_t stream);
+hipError_t launch_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,
+                              int64_t n_pieces, int32_t piece_bytes, uint32_t* sink,
+                              int groups_per_cu, hipStream_t stream);
 
 // The library's own workspace for callers that cannot allocate
 // (pkv_paged_attention_noalloc): a static device array of kScratchBytes on every
