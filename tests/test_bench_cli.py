@@ -72,15 +72,19 @@ def test_traffic_is_reported_only_for_the_current_kernel_source(tmp_path):
 def test_committed_traffic_records_are_consistent():
     """Every committed record taken on the current kernel source: fetch + write bytes
     make its per-launch figure, within a few percent of the algorithmic bytes (the
-    excess is split partials), from counters scaled by a 1 GiB copy's readings."""
+    excess is split partials) for launches of at least 100 MB (a launch of a few hundred
+    KB reads mostly its fixed bytes: arguments, counters, work list), from counters
+    scaled by a 1 GiB copy's readings."""
     b = _bench_module()
     with open(b.TRAFFIC_FILE) as f:
         records = json.load(f)["records"]
     src = b.kernel_source_hash()
     current = [r for r in records if r["kernel_source_sha256"] == src]
+    assert current, "no traffic record for the current kernel source"
     for r in current:
         assert r["bytes_per_launch"] == r["fetch_bytes"] + r["write_bytes"]
-        assert 0.99 < r["traffic_over_algorithmic"] < 1.05, r["tag"]
+        if r["algorithmic_bytes_per_launch"] >= 100e6:
+            assert 0.99 < r["traffic_over_algorithmic"] < 1.05, r["tag"]
         cal = r["calibration"]
         assert abs(cal["fetch_scale"] * cal["fetch_kib"] - 1048576) < 1024
         assert abs(cal["write_scale"] * cal["write_kib"] - 1048576) < 1024
