@@ -524,6 +524,18 @@ def test_bad_block_ids_without_validation_are_skipped_and_reported(kind):
     assert_close(got, ref, "bf16", kind)
 
 
+def test_first_launches_from_two_host_threads():
+    """A fresh process whose first decode launches come from two host threads at once
+    (each on its own stream; one shape on the vector units and one on the matrix cores,
+    then one shape from both): every output matches the oracle."""
+    import subprocess
+    import sys
+    helper = os.path.join(os.path.dirname(os.path.abspath(__file__)), "two_thread_first_launch.py")
+    r = subprocess.run([sys.executable, helper], capture_output=True, text=True, timeout=240)
+    say(r.stdout.strip().replace("\n", " | "))
+    assert r.returncode == 0 and "OK" in r.stdout, r.stdout + r.stderr[-2000:]
+
+
 def test_refusals_touch_nothing():
     w = wl.make_custom([37, 5, 16], heads=4, head_dim=128, dtype="bf16", seed=9)
     st = Step(w, host_history=True)
