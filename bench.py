@@ -567,6 +567,9 @@ def main():
     kernel, kern_s, kern_bytes = (binding.decode_kernel_for(k_cache, w.heads, w.query_len,
                                                             w.layout), dec_s, dec_bytes)
     traffic = traffic_per_launch(w.name, w.layout)
+    # the plan of the last step (every step plans the same batch): chunk length,
+    # workgroups taking part, entries, split rows
+    plan = binding.plan_info(ws)
     if scattered and avg.get("token_rows"):
         tok_lens = np.zeros_like(w.context_lens)
         tok_lens[scattered] = w.context_lens[scattered]
@@ -650,6 +653,9 @@ def main():
         "phase_avg_us": {ph: (round(v * 1e3, 2) if v is not None else None)
                          for ph, v in avg.items()},
         "algorithmic_bytes": b,
+        "plan": {k: plan[k] for k in ("chunk_tokens", "decode_groups", "entries",
+                                      "full_chunks", "split_rows", "records",
+                                      "record_capacity", "token_rows")},
         "roofline": roofline,
     }
     result["cpu_baseline"] = None if args.no_cpu_baseline else base_rec
