@@ -248,8 +248,9 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 }
 
 // exclusive prefix sum of one value per thread over the workgroup (kPlanThreads
-// threads); returns the thread's prefix and writes the total to *total
-__device__ int block_exclusive_scan(int x, int* s_wave, int* total) {
+// threads); returns the thread's prefix and writes the total to *total.  Without
+// sync_after the caller's own next barrier must come before s_wave is written again.
+__device__ int block_exclusive_scan(int x, int* s_wave, int* total, bool sync_after = true) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kWaves = kPlanThreads / 64;
   const int incl = wave_inclusive_scan(x);
@@ -263,14 +264,15 @@ __device__ int block_exclusive_scan(int x, int* s_wave, int* total) {
   __syncthreads();
   const int prefix = (wave > 0 ? s_wave[wave - 1] : 0) + incl - x;
   *total = s_wave[kWaves - 1];
-  __syncthreads();
+  if (sync_after) __syncthreads();
   return prefix;
 }
 
 // The same for N values per thread at once (one set of barriers): each x[k] becomes the
 // thread's exclusive prefix of value k, and total[k] the workgroup's sum of it.
 template <int N>
-__device__ void block_exclusive_scan_n(int (&x)[N], int (*s_wave)[N], int (&total)[N]) {
+__device__ void block_exclusive_scan_n(int (&x)[N], int (*s_wave)[N], int (&total)[N],
+                                       bool sync_after = true) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kWaves = kPlanThreads / 64;
   int incl[N];
@@ -296,7 +298,7 @@ __device__ void block_exclusive_scan_n(int (&x)[N], int (*s_wave)[N], int (&tota
     total[k] = s_wave[kWaves - 1][k];
     x[k] = prefix;
   }
-  __syncthreads();
+  if (sync_after) __syncthreads();
 }
 
 // A row's length as the block path reads it: clamped to what the table addresses (the
@@ -358,6 +360,7 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   __shared__ int s_status;
   __shared__ int s_cand[kCand];
   __shared__ int s_spl[kCand];
+  __shared__ int s_choice[2];              // chunk length's log2, narrow (8 waves per CU)
   const int t = threadIdx.x;
   const int lane = t & 63;
   if (t < kCand) {
@@ -402,15 +405,20 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
       spl[k] += n > 1 ? n : 0;
     }
   }
+  if ((t & ~63) < a.num_rows) {   // a wave without a row adds nothing
 #pragma unroll
-  for (int k = 0; k < kCand; ++k) {
-    const int v = wave_sum_i(cnt[k]);
-    const int vs = wave_sum_i(spl[k]);
-    if (lane == 0 && k < ncand) {
-      atomicAdd(&s_cand[k], v);
-      atomicAdd(&s_spl[k], vs);
+    for (int k = 0; k < kCand; ++k) {
+      if (k >= ncand) break;
+      const int v = wave_sum_i(cnt[k]);
+      const int vs = wave_sum_i(spl[k]);
+      if (lane == 0) {
+        atomicAdd(&s_cand[k], v);
+        atomicAdd(&s_spl[k], vs);
+      }
     }
   }
+  static_assert(kBins == kPlanThreads, "one remainder bin per thread");
+  s_bin_fill[t] = 0;
   __syncthreads();
   // Workgroups and chunk length.  A batch that gives 8 waves per compute unit enough
   // items of more than the shortest chunk is bandwidth-bound: then 8 waves per CU
@@ -419,54 +427,76 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   // stream).  Otherwise every workgroup takes part, with the chunk length that gives
   // them all enough items.
   const int64_t per_entry = a.query_len * a.num_heads / a.query_group;
-  // Balance: with G workgroups, the largest candidate whose chunks hold at most
-  // 1 / kBalance of a workgroup's share (tokens x items per entry / G); the work list
-  // runs longest first, so the last items to start are short ones.  The batch's tokens
-  // are taken as its chunk_min chunks x chunk_min (over by less than a chunk a row).
-  const int64_t work = ((int64_t)s_cand[0] << lmin) * per_entry;
-  auto balance_cap = [&](int64_t groups) {
-    int kc = 0;
-    for (int k = 1; k < ncand; ++k)
-      if ((int64_t{1} << (lmin + k)) * kBalance * groups <= work) kc = k;
-    return kc;
-  };
-  int lp = lmin;
-  bool narrow = false;
-  if (a.narrow_groups > 0) {
-    for (int k = min(ncand - 1, balance_cap(a.narrow_groups)); k > 0; --k) {
-      const int64_t items = (int64_t)s_cand[k] * per_entry;
-      // chunks shorter than solo_tokens are all single-wave items, which need only
-      // kSoloPerWave of them for each wave, not narrow_items for the workgroups
-      const bool solo = a.solo_tokens > 1 && (1 << (lmin + k)) < a.solo_tokens &&
-                        items >= (int64_t)kSoloPerWave * a.narrow_groups * a.group_waves;
-      if (items >= a.narrow_items || solo) {
-        lp = lmin + k;
-        narrow = true;
-        break;
+  // Wave 0 chooses alone (the counts are workgroup-uniform: scalar registers) and
+  // publishes the choice; the other waves wait at the barrier.
+  if (t < 64) {
+    int cand[kCand], cand_spl[kCand];   // candidates past ncand hold 0
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+      cand[k] = __builtin_amdgcn_readfirstlane(s_cand[k]);
+      cand_spl[k] = __builtin_amdgcn_readfirstlane(s_spl[k]);
+    }
+    // Balance: with G workgroups, the largest candidate whose chunks hold at most
+    // 1 / kBalance of a workgroup's share (tokens x items per entry / G); the work list
+    // runs longest first, so the last items to start are short ones.  The batch's tokens
+    // are taken as its chunk_min chunks x chunk_min (over by less than a chunk a row).
+    const int64_t work = ((int64_t)cand[0] << lmin) * per_entry;
+    auto balance_cap = [&](int64_t groups) {
+      int kc = 0;
+#pragma unroll
+      for (int k = 1; k < kCand; ++k)
+        if (k < ncand && (int64_t{1} << (lmin + k)) * kBalance * groups <= work) kc = k;
+      return kc;
+    };
+    int lp = lmin;
+    bool narrow = false;
+    if (a.narrow_groups > 0) {
+      const int kmax = min(ncand - 1, balance_cap(a.narrow_groups));
+#pragma unroll
+      for (int k = kCand - 1; k > 0; --k) {
+        const int64_t items = (int64_t)cand[k] * per_entry;
+        // chunks shorter than solo_tokens are all single-wave items, which need only
+        // kSoloPerWave of them for each wave, not narrow_items for the workgroups
+        const bool solo = a.solo_tokens > 1 && (1 << (lmin + k)) < a.solo_tokens &&
+                          items >= (int64_t)kSoloPerWave * a.narrow_groups * a.group_waves;
+        if (!narrow && k <= kmax && (items >= a.narrow_items || solo)) {
+          lp = lmin + k;
+          narrow = true;
+        }
       }
     }
+    if (!narrow) {
+      // A batch too small to give every workgroup its share even at the shortest chunk
+      // takes the longest that gives a quarter of it: each extra split of a row costs a
+      // float32 partial record per vector, and the shortest chunk splits the most.
+      const int kc = min(ncand - 1, balance_cap(a.grid_groups));
+      int found = -1;
+#pragma unroll
+      for (int k = kCand - 1; k >= 0; --k)
+        if (found < 0 && k <= kc && (int64_t)cand[k] * per_entry >= a.target_items) found = k;
+#pragma unroll
+      for (int k = kCand - 1; k >= 0; --k)
+        if (found < 0 && k <= kc && (int64_t)cand[k] * per_entry >= a.target_items / 4)
+          found = k;
+      lp = lmin + (found > 0 ? found : 0);
+    }
+    // the split rows' partial records must fit the workspace (they always do at the
+    // longest candidate, which the workspace is sized for)
+#pragma unroll
+    for (int k = 0; k < kCand - 1; ++k)
+      if (k == lp - lmin && k < ncand - 1 && cand_spl[k] > a.record_chunks) ++lp;
+    if (t == 0) {
+      s_choice[0] = lp;
+      s_choice[1] = narrow ? 1 : 0;
+    }
   }
-  if (!narrow) {
-    // A batch too small to give every workgroup its share even at the shortest chunk
-    // takes the longest that gives a quarter of it: each extra split of a row costs a
-    // float32 partial record per vector, and the shortest chunk splits the most.
-    const int kc = min(ncand - 1, balance_cap(a.grid_groups));
-    int found = -1;
-    for (int k = kc; k >= 0 && found < 0; --k)
-      if ((int64_t)s_cand[k] * per_entry >= a.target_items) found = k;
-    for (int k = kc; k >= 0 && found < 0; --k)
-      if ((int64_t)s_cand[k] * per_entry >= a.target_items / 4) found = k;
-    lp = lmin + (found > 0 ? found : 0);
-  }
-  // the split rows' partial records must fit the workspace (they always do at the
-  // longest candidate, which the workspace is sized for)
-  while (lp < lmin + ncand - 1 && s_spl[lp - lmin] > a.record_chunks) ++lp;
+  __syncthreads();
+  const int lp = s_choice[0];
+  const bool narrow = s_choice[1] != 0;
   const int P = 1 << lp;
   const int bshift = lp > 10 ? lp - 10 : 0;   // remainder -> bin (kBins = 1024)
   const int nbins = P >> bshift;
   static_assert(kBins == 1024, "bin shift assumes 1024 bins");
-  if (t < nbins) s_bin_fill[t] = 0;
-  __syncthreads();
 
   // a row's length as pass 0 found it
   auto row_len = [&](int64_t r) {
@@ -495,7 +525,8 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
     const int full = ctx >> lp;
     int v[4] = {full, in && ctx == 0 ? 1 : 0, split ? fnch : 0, split ? 1 : 0};
     int tot[4];
-    block_exclusive_scan_n<4>(v, s_scan, tot);
+    // (the last round's scan needs no closing barrier: the loop's own follows)
+    block_exclusive_scan_n<4>(v, s_scan, tot, base + kPlanThreads < a.num_rows);
     const int rec0 = split ? total_rec + v[2] : -1;
     for (int k = 0; k < full; ++k)
       ws.entries[total_a + v[0] + k] = make_int4((int)r, k, split ? rec0 + k : -1, ctx);
@@ -519,11 +550,12 @@ __device__ void plan_body(const AttnArgs& a, const Workspace& ws) {
   {
     const int bin = nbins - 1 - t;
     const int count = t < nbins ? s_bin_fill[bin] : 0;
-    const int start = block_exclusive_scan(count, s_wave, &total_b);
-    if (t < nbins) s_bin_start[bin] = start;
+    const int start = block_exclusive_scan(count, s_wave, &total_b, false);
+    if (t < nbins) {
+      s_bin_start[bin] = start;
+      s_bin_fill[t] = 0;   // every count was read before the scan's first barrier
+    }
   }
-  __syncthreads();
-  if (t < nbins) s_bin_fill[t] = 0;
   __syncthreads();
   // pass 2: place sections B and C
   for (int64_t r = t; r < a.num_rows; r += kPlanThreads) {
