@@ -1822,6 +1822,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Workspace ws) {
   constexpr int PER = D / 64;     // dims per lane
   constexpr int W = kCombineThreads / 64;
+  constexpr int kHeld = 8;        // a row of at most this many chunks: one round of loads
   const int lane = threadIdx.x & 63;
   const int n_vec = a.query_len * a.num_heads;
   const int64_t pairs = (int64_t)ws.counters[8] * n_vec;
@@ -1839,19 +1840,50 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(AttnArgs a, Wo
     const int64_t stride = (int64_t)n_vec * (D + 4);
 
     float mx = -INFINITY;
-    for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, rec[c * stride]);
-    mx = wave_max(mx);
-    if (mx == -INFINITY) mx = 0.f;   // only a row whose length was out of bounds
     float l = 0.f, acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < nch; ++c) {
-      const float* p = rec + c * stride;
-      const float f = __builtin_amdgcn_exp2f(p[0] - mx);
-      l += p[1] * f;
+    if (nch <= kHeld) {
+      // every chunk's (m, l, acc) at once, then the same sums in chunk order
+      float m[kHeld], lc[kHeld], y[kHeld][PER];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += p[4 + lane * PER + i] * f;
+      for (int c = 0; c < kHeld; ++c) {
+        m[c] = -INFINITY;
+        lc[c] = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) y[c][i] = 0.f;
+        if (c < nch) {
+          const float* p = rec + c * stride;
+          m[c] = p[0];
+          lc[c] = p[1];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) y[c][i] = p[4 + lane * PER + i];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kHeld; ++c) mx = fmaxf(mx, m[c]);
+      if (mx == -INFINITY) mx = 0.f;   // only a row whose length was out of bounds
+#pragma unroll
+      for (int c = 0; c < kHeld; ++c) {
+        if (c < nch) {
+          const float f = __builtin_amdgcn_exp2f(m[c] - mx);
+          l += lc[c] * f;
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] += y[c][i] * f;
+        }
+      }
+    } else {
+      for (int c = lane; c < nch; c += 64) mx = fmaxf(mx, rec[c * stride]);
+      mx = wave_max(mx);
+      if (mx == -INFINITY) mx = 0.f;   // only a row whose length was out of bounds
+#pragma unroll 4
+      for (int c = 0; c < nch; ++c) {
+        const float* p = rec + c * stride;
+        const float f = __builtin_amdgcn_exp2f(p[0] - mx);
+        l += p[1] * f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += p[4 + lane * PER + i] * f;
+      }
     }
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     T* outp = static_cast<T*>(a.out) + vec_slot(a, r, v) * D + lane * PER;
