@@ -366,6 +366,50 @@ def test_plan_counts_equal_the_kernel_walk(idx, kv_heads, query_len, tuning):
         assert info["chunk_tokens"] == tuning["chunk_min"]
 
 
+def _budget_batch():
+    """64 rows of 4096 tokens, float32 pools, 32 query heads over 4 KV heads (8 query
+    vectors to an item on the vector units).  8 waves per CU need 4096 items; 256-token
+    chunks are the longest that give them (64 x 16 entries x 4 head groups), and their
+    records (64 x 16 chunks of 32 vectors, 17.3 MB) exceed the workspace's cap of 992
+    record chunks, while 512-token chunks (512 record chunks) fit."""
+    return wl.make_custom([4096] * 64, heads=32, kv_heads=4, head_dim=128, block_size=16,
+                          dtype="f32", layout="HND", seed=64)
+
+
+@pytest.mark.parametrize("chunk_max", [0, 256], ids=["budget-binds", "budget-fits"])
+def test_record_budget_moves_the_plan_to_longer_chunks(chunk_max):
+    """The split rows' partial records have a fixed budget in the workspace: the
+    records every row needs at the longest chunk length, or 16 MiB, whichever is more.
+    With the default range the plan's first choice does not fit and it takes the next
+    longer chunk; with the range capped at 256 tokens the cap is that range's own need
+    and the first choice stands.  Every row against the oracle both ways."""
+    w = _budget_batch()
+    st = Step(w)
+    saved = binding.get_tuning()
+    if chunk_max:
+        binding.set_tuning(chunk_min=128, chunk_max=chunk_max)
+    try:
+        ws = st.workspace()
+        out = st.run(workspace=ws)
+        info = binding.plan_info(ws)
+    finally:
+        binding.set_tuning(**saved)
+    say(f"record budget, chunk_max {chunk_max or 'default'}: {info}")
+    check_plan(w, info)
+    lens = w.context_lens.astype(np.int64)
+    cap = info["record_capacity"]
+    if chunk_max:
+        assert cap == accounting.tiles_walked(lens, 256), info
+        assert info["chunk_tokens"] == 256 and info["records"] == cap, info
+    else:
+        assert cap == 992, info
+        assert accounting.tiles_walked(lens, 256) > cap, info    # the first choice
+        assert info["chunk_tokens"] == 512 and info["records"] == 512, info
+    ref = oracle_rows(st, w.live_rows)
+    err = assert_close(to_host(out, w.dtype)[w.live_rows], ref, w.dtype, "record budget")
+    say(f"record budget: every row, max err {err:.3e}")
+
+
 # --------------------------------------------------------------------------- #
 # shapes, ragged tails and edges at sizes the oracle finishes quickly
 # --------------------------------------------------------------------------- #
