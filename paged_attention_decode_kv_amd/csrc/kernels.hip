@@ -1487,8 +1487,10 @@ typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
 // 64 or 128, sub-chunks of 16 tokens), single-wave items first.  A single wave's tiles
 // hold whole vectors (lane (col, grp): dims 16 o + 4 grp .. + 3 of vector col), so it
 // writes its item's result from registers.  After its last fold of a wide item a wave
-// parks its state, [QG][D] floats, in its own stage, and the waves are merged from
-// there.
+// parks its state, [QG][D] floats, in a park area of its own, and the waves are merged
+// from there; its stage is free by then, so the next item's first sub-chunk streams in
+// while the waves meet and merge.  (At head_dim 128 these kernels hold one workgroup per
+// compute unit by registers, so the park area costs no occupancy.)
 template <int D, int WAVES, int QG>
 __global__ void __launch_bounds__(WAVES * 64)
 decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
@@ -1518,7 +1520,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   // 256-byte head vector all sit in the same 4 banks.
   constexpr int STAGE = 2 * U * 1024;      // K chunks, then V chunks
   __shared__ __attribute__((aligned(16))) char s_stage[WAVES][STAGE];
-  static_assert(QG * D * 4 <= STAGE, "a wave's merge state fits its stage");
+  __shared__ __attribute__((aligned(16))) float s_park[WAVES][QG * D];
   __shared__ int s_ticket[2];
   __shared__ float s_m[2][QG][WAVES], s_l[2][QG][WAVES];
   __shared__ int s_walk[WAVES];
@@ -1673,6 +1675,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
   int item, next;
   order.first_two(item, next, &ws.counters[1], s_ticket);
   int buf = 0;
+  bool first_staged = false;   // the item's first sub-chunk is already in this wave's stage
   Meta cur;
   if (item < n_wide)
     cur = finish_meta_mfma<D, QG, NR, WAVES>(a, issue_entry(ws, item, groups), item, lp,
@@ -1697,7 +1700,12 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 
     const int n_sub = (ca.t_end - ca.t_begin + CH - 1) / CH;
     if (wave == 0) walked += n_sub;
-    if (wave < n_sub) stage_in(ca, wave, 0, cur.blk);
+    if (wave < n_sub && !first_staged) stage_in(ca, wave, 0, cur.blk);
+    first_staged = false;
+    // the next item's query and block ids load after this wave's first fold (its entry
+    // has landed by then), in time for its first sub-chunk to be staged below
+    Meta nxt;
+    bool nxt_issued = false;
     for (int s = wave; s < n_sub; s += WAVES) {
       __amdgpu_buffer_rsrc_t ksrc, vsrc;
       const int i = (s - wave) / WAVES;
@@ -1709,16 +1717,30 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       if (s + WAVES < n_sub) stage_in(ca, s + WAVES, i + 1, cur.blk);
       mfma_tile_fold<NO>(sc, vt, min(nvalid, last_rel - s * CH + 1), grp, scale_log2, m, l,
                          acc);
+      if (!nxt_issued) {
+        nxt = finish_meta_mfma<D, QG, NR, WAVES>(a, next_ent, next, lp, log2_bs, lane, wave);
+        nxt_issued = true;
+      }
     }
-
-    const Meta nxt = finish_meta_mfma<D, QG, NR, WAVES>(a, next_ent, next, lp, log2_bs, lane,
-                                                        wave);
+    if (!nxt_issued)
+      nxt = finish_meta_mfma<D, QG, NR, WAVES>(a, next_ent, next, lp, log2_bs, lane, wave);
+    // the next item's first sub-chunk into this wave's stage (its last read of this
+    // item's stage has completed), to land while the waves merge this item
+    if (next < n_wide) {
+      const ChunkAddr cn = chunk_addr(__builtin_amdgcn_readfirstlane(nxt.chunk),
+                                      __builtin_amdgcn_readfirstlane(nxt.hg),
+                                      __builtin_amdgcn_readfirstlane(nxt.ctx));
+      if (wave < (cn.t_end - cn.t_begin + CH - 1) / CH) {
+        stage_in(cn, wave, 0, nxt.blk);
+        first_staged = true;
+      }
+    }
     l += __shfl_xor(l, 16);        // the four row groups' denominators
     l += __shfl_xor(l, 32);
-    // park this wave's state in its own stage (its last stage read has completed):
-    // vector c's dim d at c * D + (d ^ park_swizzle(c)), so that the 64 lanes of one
-    // write (16 vectors x 4 row groups) fall in distinct LDS banks
-    float* park = reinterpret_cast<float*>(&s_stage[wave][0]);
+    // park this wave's state: vector c's dim d at c * D + (d ^ park_swizzle(c)), so
+    // that the 64 lanes of one write (16 vectors x 4 row groups) fall in distinct LDS
+    // banks
+    float* park = &s_park[wave][0];
     if (col < QG) {
       const int sw = park_swizzle(col);
 #pragma unroll
@@ -1747,7 +1769,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
       for (int w = 0; w < WAVES; ++w) {
         const float f = __builtin_amdgcn_exp2f(s_m[buf][j][w] - mu);
         lj += s_l[buf][j][w] * f;
-        const float* pw = reinterpret_cast<const float*>(&s_stage[w][0]) + j * D;
+        const float* pw = &s_park[w][0] + j * D;
 #pragma unroll
         for (int i = 0; i < PER; ++i) y[i] += pw[(lane * PER + i) ^ sw] * f;
       }
@@ -1773,7 +1795,7 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
         for (int i = 0; i < PER; ++i) rec[4 + lane * PER + i] = y[i];
       }
     }
-    __syncthreads();     // every stage is free again before the next item streams in
+    __syncthreads();     // every park area is free again before the next item parks
     buf ^= 1;
     item = next;
     cur = nxt;
