@@ -410,6 +410,54 @@ def test_record_budget_moves_the_plan_to_longer_chunks(chunk_max):
     say(f"record budget: every row, max err {err:.3e}")
 
 
+@pytest.mark.parametrize("chunk", [0, 8192], ids=["default", "chunk8192"])
+def test_rows_longer_than_the_longest_chunk(chunk):
+    """Rows of up to 20000 tokens (a table 20000 wide): even at the longest chunk
+    (8192 tokens) they split, into up to 3 chunks, and the merge joins them.  8 query
+    heads over 2 KV heads (4 vectors to an item, the matrix cores), bf16."""
+    lens = [20000, 16384, 8193, 8192, 100, 0, 1]
+    w = wl.make_custom(lens, heads=8, kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                       layout="HND", seed=2000)
+    st = Step(w, host_history=False)
+    saved = binding.get_tuning()
+    if chunk:
+        binding.set_tuning(chunk_min=chunk, chunk_max=chunk)
+    try:
+        ws = st.workspace()
+        out = st.run(workspace=ws)
+        info = binding.plan_info(ws)
+    finally:
+        binding.set_tuning(**saved)
+    say(f"rows past the longest chunk, chunk {chunk or 'default'}: {info}")
+    check_plan(w, info)
+    if chunk:
+        assert info["chunk_tokens"] == chunk and info["split_rows"] == 3, info
+    ref = oracle_rows(st, w.live_rows)
+    err = assert_close(to_host(out, w.dtype)[w.live_rows], ref, w.dtype,
+                       "rows past the longest chunk")
+    assert torch.all(out[torch.from_numpy(w.pad_rows).to(DEV)] == 0)
+    say(f"rows past the longest chunk: max err {err:.3e}")
+
+
+def test_a_row_of_a_quarter_million_tokens():
+    """One row of 2^18 tokens beside a row of 3: a table 2^18 wide, the row cut into
+    about a thousand chunks and merged from as many partial records (the merge's loop
+    over more chunks than it holds at once).  2 query heads over 1 KV head, head_dim 64,
+    bf16; every output against the oracle."""
+    w = wl.make_custom([1 << 18, 3], heads=2, kv_heads=1, head_dim=64, block_size=16,
+                       dtype="bf16", layout="HND", seed=20)
+    st = Step(w, host_history=False)
+    ws = st.workspace()
+    out = st.run(workspace=ws)
+    info = binding.plan_info(ws)
+    say(f"2^18 tokens: {info}")
+    check_plan(w, info)
+    assert info["split_rows"] >= 1 and (1 << 18) // info["chunk_tokens"] > 8, info
+    ref = oracle_rows(st, w.live_rows)
+    err = assert_close(to_host(out, w.dtype)[w.live_rows], ref, w.dtype, "2^18 tokens")
+    say(f"2^18 tokens: max err {err:.3e}")
+
+
 # --------------------------------------------------------------------------- #
 # shapes, ragged tails and edges at sizes the oracle finishes quickly
 # --------------------------------------------------------------------------- #
