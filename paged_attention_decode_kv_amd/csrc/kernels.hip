@@ -1221,8 +1221,12 @@ decode_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 
   // ---- wide items: the workgroup's waves share each one ----
   ItemOrder order{xcd_order(G), G, n_dealt};
-  int item, next;
-  order.first_two(item, next, &ws.counters[1], s_ticket);
+  // A batch with no wide items takes no tickets: at the end of a kernel that has
+  // only single-wave items, one shared counter taking two returning atomics from every
+  // workgroup was the last thing each waited for.  n_wide is the same for every
+  // workgroup, so all of them skip the barriers together.
+  int item = n_wide, next = n_wide;
+  if (n_wide > 0) order.first_two(item, next, &ws.counters[1], s_ticket);
   int buf = 0;
   Meta cur;
   if (item < n_wide)
@@ -1672,8 +1676,12 @@ decode_mfma_kernel(AttnArgs a, Workspace ws, float scale_log2) {
 
   // ---- wide items: the workgroup's waves share each one ----
   ItemOrder order{xcd_order(G), G, n_dealt};
-  int item, next;
-  order.first_two(item, next, &ws.counters[1], s_ticket);
+  // A batch with no wide items takes no tickets: at the end of a kernel that has
+  // only single-wave items, one shared counter taking two returning atomics from every
+  // workgroup was the last thing each waited for.  n_wide is the same for every
+  // workgroup, so all of them skip the barriers together.
+  int item = n_wide, next = n_wide;
+  if (n_wide > 0) order.first_two(item, next, &ws.counters[1], s_ticket);
   int buf = 0;
   bool first_staged = false;   // the item's first sub-chunk is already in this wave's stage
   Meta cur;
