@@ -97,6 +97,47 @@ def test_no_alloc_read_matches_the_workspace_read_twice():
         say(f"no-alloc: bit-identical to the workspace call, max err {err:.3e}")
 
 
+def _named_step(idx):
+    """A named configuration's pools (built on the device), after its kv_write; returns
+    the read's tensors."""
+    w = wl.make_config(idx)
+    k_cache = torch.empty(w.pool_shape, dtype=TORCH_DT[w.dtype], device=DEV)
+    v_cache = torch.empty_like(k_cache)
+    wl.history_device(w, k_cache, v_cache)
+    binding.kv_write(to_dev(w.k_new, w.dtype), to_dev(w.v_new, w.dtype),
+                     to_dev(w.slot_mapping), k_cache, v_cache, layout=w.layout)
+    return (w, to_dev(w.q, w.dtype), k_cache, v_cache, to_dev(w.block_tables),
+            to_dev(w.context_lens))
+
+
+def test_no_alloc_at_the_full_width_step():
+    """The full-width batch (256 rows of up to 8192 tokens, 34 GB of pools; its
+    workspace is about 17 MB, inside the scratch) read both ways: bit-identical.  Then a
+    smaller batch (8 rows of 2048, every row split) over the scratch the first call
+    left: bit-identical again."""
+    for idx in (5, 2):
+        w, q, k_cache, v_cache, tables, lens = _named_step(idx)
+        need = binding.workspace_bytes(k_cache, w.rows, w.heads, w.max_blocks, w.layout)
+        assert 0 < need <= _capi.NOALLOC_SCRATCH_BYTES
+        say(f"no-alloc, config {idx}: workspace {need} bytes")
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        want = binding.paged_attention(q, k_cache, v_cache, tables, lens, w.scale,
+                                       layout=w.layout, workspace=ws, validate=True)
+        out = torch.full_like(q, 3.0)
+        binding.device_status(DEV, clear=True)
+        binding.paged_attention_noalloc(q, k_cache, v_cache, tables, lens, w.scale, out,
+                                        layout=w.layout)
+        torch.cuda.synchronize()
+        assert binding.device_status(DEV, clear=True) == 0
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), \
+            f"config {idx}: the scratch read differs from the workspace read"
+        pads = torch.from_numpy(w.pad_rows).to(DEV)
+        assert torch.all(out[pads] == 0)
+        say(f"no-alloc, config {idx}: bit-identical to the workspace read")
+        del k_cache, v_cache, ws
+        torch.cuda.empty_cache()
+
+
 def test_no_alloc_refuses_a_batch_larger_than_the_scratch():
     """A batch whose workspace exceeds the scratch is refused before anything runs."""
     w = wl.make_custom([8192] * 2, heads=32, kv_heads=32, head_dim=256, dtype="bf16",
