@@ -616,6 +616,33 @@ def test_bad_block_ids_without_validation_are_skipped_and_reported(kind):
     assert_close(got, ref, "bf16", kind)
 
 
+@pytest.mark.parametrize("kind", ["vector", "matrix"])
+def test_bad_lengths_without_validation_are_clamped_and_reported(kind):
+    """validate=False: a length below 0 reads as 0 (the row gives zeros), and one past
+    what its table addresses reads as the table's capacity (the whole table).  The
+    CONTEXT_BOUNDS status bit is raised in the call's workspace and in the device word.
+    Every row against the oracle over the clamped lengths."""
+    heads, kvh = (16, 4) if kind == "matrix" else (4, 4)
+    lens = [100, 0, 4096, 50, 0, 777]      # row 2 fills its table: 256 blocks of 16
+    w = wl.make_custom(lens, heads=heads, kv_heads=kvh, head_dim=128, dtype="bf16",
+                       max_blocks=256, seed=23)
+    st = Step(w, host_history=True)
+    binding.kv_write(st.k_new, st.v_new, st.slots, st.k_cache, st.v_cache, layout=w.layout)
+    bad = st.lens.clone()
+    bad[1] = -5                            # clamps to 0: the pad row it is
+    bad[2] = 4096 + 777                    # clamps to 4096: the row as it is
+    ws = st.workspace()
+    binding.device_status(DEV, clear=True)
+    out = binding.paged_attention(st.q, st.k_cache, st.v_cache, st.tables, bad, w.scale,
+                                  layout=w.layout, workspace=ws, validate=False)
+    torch.cuda.synchronize()
+    assert binding.workspace_status(ws) == _capi.DEVERR_CONTEXT_BOUNDS
+    assert binding.device_status(DEV, clear=True) & _capi.DEVERR_CONTEXT_BOUNDS
+    ref, _, _ = oracle_full(w, st.k_host, st.v_host)
+    err = assert_close(to_host(out, w.dtype), ref, w.dtype, f"clamped lengths, {kind}")
+    say(f"clamped lengths ({kind}): max err {err:.3e}")
+
+
 def test_first_launches_from_two_host_threads():
     """A fresh process whose first decode launches come from two host threads at once
     (each on its own stream; one shape on the vector units and one on the matrix cores,
