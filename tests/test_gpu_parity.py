@@ -643,6 +643,35 @@ def test_bad_lengths_without_validation_are_clamped_and_reported(kind):
     say(f"clamped lengths ({kind}): max err {err:.3e}")
 
 
+def test_bad_write_slots_without_validation_are_skipped_and_reported():
+    """validate=False: a write slot outside [0, sink] (below 0, past the sink) is
+    skipped, so its token's K/V go nowhere, every other token lands bit-exactly, the
+    rest of the pool is untouched, and the SLOT status bit is raised."""
+    w = wl.make_custom([40, 17, 0, 99, 5], heads=4, kv_heads=2, head_dim=128, dtype="bf16",
+                       layout="NHD", seed=29)
+    st = Step(w, host_history=True)
+    sink = binding.sink_slot(st.k_cache, w.layout)
+    assert sink == w.num_blocks * w.block_size
+    slots = w.slot_mapping.copy()
+    slots[1] = -3
+    slots[3] = sink + 5
+    binding.device_status(DEV, clear=True)
+    binding.kv_write(st.k_new, st.v_new, to_dev(slots), st.k_cache, st.v_cache,
+                     layout=w.layout, validate=False)
+    torch.cuda.synchronize()
+    assert binding.device_status(DEV, clear=True) & _capi.DEVERR_SLOT
+    keep = np.array([i for i in range(len(slots)) if 0 <= slots[i] <= sink])
+    kw, vw = st.k_host.copy(), st.v_host.copy()
+    oracle.kv_write(kw, vw, w.k_new[keep], w.v_new[keep], slots[keep],
+                    num_blocks=w.num_blocks, block_size=w.block_size, layout=w.layout,
+                    dtype=w.dtype)
+    for got, want in ((st.k_cache, kw), (st.v_cache, vw)):
+        g = to_host(got, w.dtype)
+        assert np.array_equal(g.view(np.uint16), want.view(np.uint16)), \
+            "a skipped token's K/V landed, or a slot other than the named ones changed"
+    say(f"bad write slots: tokens 1 and 3 skipped, {len(keep)} written")
+
+
 def test_first_launches_from_two_host_threads():
     """A fresh process whose first decode launches come from two host threads at once
     (each on its own stream; one shape on the vector units and one on the matrix cores,
