@@ -458,6 +458,40 @@ def test_a_row_of_a_quarter_million_tokens():
     say(f"2^18 tokens: max err {err:.3e}")
 
 
+@pytest.mark.parametrize("chunk", [0, 1024], ids=["default", "chunk1024"])
+def test_the_most_rows(chunk):
+    """65535 rows, the most the library takes: the plan walks them 1024 at a time and
+    keeps each thread's first four rows in registers, so rows past 4096 take its other
+    path (lengths and record offsets reloaded from memory).  Short rows with pad rows
+    among them, and long rows past index 4096; with 1024-token chunks those split, so
+    their record offsets come back from memory too.  Every row against the oracle, and
+    the plan against the host accounting."""
+    rng = np.random.default_rng(65535)
+    lens = rng.integers(0, 41, 65535)
+    for r in (5000, 30000, 65534, 4100):
+        lens[r] = 3000 + r % 7
+    w = wl.make_custom(lens.tolist(), heads=2, kv_heads=1, head_dim=64, dtype="bf16",
+                       layout="HND", seed=65535)
+    st = Step(w, host_history=False)
+    saved = binding.get_tuning()
+    if chunk:
+        binding.set_tuning(chunk_min=chunk, chunk_max=chunk)
+    try:
+        ws = st.workspace()
+        out = st.run(workspace=ws)
+        info = binding.plan_info(ws)
+    finally:
+        binding.set_tuning(**saved)
+    say(f"65535 rows, chunk {chunk or 'default'}: {info}")
+    check_plan(w, info)
+    if chunk:
+        assert info["chunk_tokens"] == chunk and info["split_rows"] == 4, info
+    ref = oracle_rows(st, w.live_rows)
+    err = assert_close(to_host(out, w.dtype)[w.live_rows], ref, w.dtype, "65535 rows")
+    assert torch.all(out[torch.from_numpy(w.pad_rows).to(DEV)] == 0)
+    say(f"65535 rows: every row, max err {err:.3e}")
+
+
 # --------------------------------------------------------------------------- #
 # shapes, ragged tails and edges at sizes the oracle finishes quickly
 # --------------------------------------------------------------------------- #
