@@ -342,8 +342,11 @@ pkv_status pkv_gather_read(const void* k_base, const void* v_base, const int64_t
  * shared by the waves of one workgroup, and rows longer than one chunk are merged
  * afterwards in chunk order.  The chunk length is chosen on the device per call: the
  * largest power of two in [chunk_min, chunk_max] that still yields items_per_group
- * items per decode workgroup (else the largest that yields a quarter of that, else
- * chunk_min).  Setting chunk_min == chunk_max pins it.
+ * items per decode workgroup (for chunks shorter than solo_tokens, one item per wave),
+ * and whose chunk holds at most a third of a workgroup's share of the batch (else the
+ * largest that yields a quarter of that, else chunk_min); then the next longer one
+ * while the split rows' partial records would not fit the workspace.  Setting
+ * chunk_min == chunk_max pins it.
  *   chunk_min, chunk_max  powers of two in [32, 8192], chunk_max/chunk_min <= 64
  *                         (defaults 128, 8192)
  *   decode_waves          64-lane waves per workgroup: 1, 2, 4 or 8 (default 8)
