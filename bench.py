@@ -15,7 +15,10 @@ per step (eager), and as replays of one HIP graph recorded from those calls (gra
 default ``value``; ``--launch eager`` reports the other).  ``roofline`` reports the
 decode kernel alone, timed with HIP events on its launch stream over a third pass of
 the same library-call steps, against MI355X's 8 TB/s HBM peak, and beside the rate a
-plain streaming read of the same byte count reaches on the same GPU (``achievable``).
+plain streaming read of the same byte count reaches on the same GPU (``achievable``)
+and the best rate a plain read of exactly the decode's scattered pieces reaches over
+every load shape of the gathering read (``achievable_gather``; ``--gather-sweep`` logs
+each shape, and the same pieces sorted by address).
 ``cpu_baseline`` times the CPU oracle over the same batch (every row by default) on a
 pool of host threads, one per core of the process's CPU affinity (at most 16); its
 outputs check every GPU output row.
@@ -97,6 +100,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise kernel over 1 GiB (for counter scaling)")
+    ap.add_argument("--gather-sweep", action="store_true",
+                    help="log the gathering read's rate for every load shape, in the decode's "
+                         "piece order and sorted by address")
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="read a buffer of this many MB before each event-timed step, so that "
                          "the per-kernel times see no K/V left in the 256 MB MALL by the step "
@@ -275,19 +281,15 @@ def achievable_read(nbytes, device, reps=5):
     return best
 
 
-def achievable_gather(w, k_cache, v_cache, reps=5):
-    """The best rate (GB/s) a plain read of exactly the (block, KV head) pieces of K and
-    V the decode streams reaches (pkv_gather_read), 1 to 8 workgroups of 256 threads
-    per CU.  The pieces go in the decode's order: row by row, in groups of 8 blocks (a
-    decode item's waves take one block each), every KV head of a group before the next
-    group, so that concurrent waves read all heads' pieces (one head's pieces sit at the
-    same offset of every 128 KB block, and reading them alone leaves most HBM channels
-    idle).  HND pools only (a piece is contiguous there); returns (GB/s, workgroups per
-    CU, microseconds, bytes) or None."""
+def gather_offsets(w):
+    """Byte offsets of the (block, KV head) pieces of K and V the decode streams, in its
+    order: row by row, in groups of 8 blocks (a decode item's waves take one block
+    each), every KV head of a group before the next group, so that concurrent waves
+    read all heads' pieces (one head's pieces sit at the same offset of every block, and
+    reading them alone leaves most HBM channels idle).  HND pools only (a piece is
+    contiguous there); returns (offsets, piece bytes) or None."""
     import numpy as np
-    import torch
 
-    from paged_attention_decode_kv_amd import binding
     from paged_attention_decode_kv_amd import workloads as wl
 
     if w.layout != "HND":
@@ -295,34 +297,88 @@ def achievable_gather(w, k_cache, v_cache, reps=5):
     elem = 2 if w.dtype == "bf16" else 4
     piece = w.block_size * w.head_dim * elem
     blk_bytes = w.kv_heads * piece
+    heads = np.arange(w.kv_heads, dtype=np.int64)
     offs = []
     for r in range(w.rows):
         nb = wl.cdiv(w.context_lens[r], w.block_size)
         if nb == 0:
             continue
         blocks = w.block_tables[r, :nb].astype(np.int64)
-        heads = np.arange(w.kv_heads, dtype=np.int64)
         for g0 in range(0, nb, 8):
             grp = blocks[g0:g0 + 8]
             offs.append((heads[:, None] * piece + grp[None, :] * blk_bytes).reshape(-1))
-    pieces = binding.GatherPieces(k_cache, v_cache, np.concatenate(offs), piece)
-    sink = torch.zeros(1, dtype=torch.int32, device=k_cache.device)
-    nbytes = pieces.offsets.numel() * piece * 2
-    best = None
-    for gpc in (1, 2, 4, 8):
-        for _ in range(2):
-            binding.gather_read(pieces, sink, gpc)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
-        for i in range(reps):
-            ev[2 * i].record()
-            binding.gather_read(pieces, sink, gpc)
-            ev[2 * i + 1].record()
-        torch.cuda.synchronize()
-        us = min(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) * 1e3
-        if best is None or us < best[2]:
-            best = (nbytes / us / 1e3, gpc, us, nbytes)
-    del pieces, sink
-    return best
+    return np.concatenate(offs), piece
+
+
+def gather_rates(pieces, reps=5):
+    """Every (waves per workgroup, pieces per wave, workgroups per CU) of the gathering
+    read over ``pieces``: a list of (GB/s, waves, pieces per wave, workgroups per CU,
+    microseconds), fastest of ``reps`` launches each, timed with events on the stream the
+    read runs on."""
+    import torch
+
+    from paged_attention_decode_kv_amd import binding
+
+    sink = torch.zeros(1, dtype=torch.int32, device=pieces.k_cache.device)
+    nbytes = pieces.offsets.numel() * pieces.piece_bytes * 2
+    out = []
+    for waves, ppw in binding.GATHER_SHAPES:
+        for gpc in (1, 2, 4) if waves == 8 else (1, 2, 4, 8):
+            def launch():
+                binding.gather_read(pieces, sink, gpc, waves, ppw)
+            for _ in range(2):
+                launch()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+            for i in range(reps):
+                ev[2 * i].record()
+                launch()
+                ev[2 * i + 1].record()
+            torch.cuda.synchronize()
+            us = min(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) * 1e3
+            out.append((nbytes / us / 1e3, waves, ppw, gpc, us))
+    del sink
+    return out
+
+
+def achievable_gather(w, k_cache, v_cache, sweep_log=None):
+    """The best rate (GB/s) a plain read of exactly the (block, KV head) pieces of K and
+    V the decode streams, in its order (gather_offsets), reaches over every load shape
+    of pkv_gather_read (4 or 8 waves per workgroup, 1, 2 or 4 pieces per wave, 1 to 8
+    workgroups per CU).  With ``sweep_log``, every shape's rate goes to it, and so do
+    those of the same pieces sorted by address (a locality the decode's order does not
+    have: context only).  HND pools only; returns (GB/s, description, microseconds,
+    bytes) or None."""
+    import numpy as np
+
+    from paged_attention_decode_kv_amd import binding
+
+    got = gather_offsets(w)
+    if got is None:
+        return None
+    offs, piece = got
+    pieces = binding.GatherPieces(k_cache, v_cache, offs, piece)
+    nbytes = offs.size * piece * 2
+    rates = gather_rates(pieces)
+    del pieces
+    best = max(rates)
+    if sweep_log:
+        sweep_log(f"gathering read of {nbytes} B in {offs.size} pieces of {piece} B "
+                  f"(GB/s by waves per workgroup x pieces per wave, workgroups per CU):")
+        orders = [("decode order", rates)]
+        sorted_pieces = binding.GatherPieces(k_cache, v_cache, np.sort(offs), piece)
+        orders.append(("sorted by address", gather_rates(sorted_pieces)))
+        del sorted_pieces
+        for name, rr in orders:
+            for waves, ppw in binding.GATHER_SHAPES:
+                cells = [f"{gpc}: {gbs:.0f}" for gbs, wv, pp, gpc, _ in rr
+                         if (wv, pp) == (waves, ppw)]
+                sweep_log(f"  {name}, {waves} waves x {ppw} pieces: " + ", ".join(cells))
+            top = max(rr)
+            sweep_log(f"  {name}: best {top[0]:.1f} GB/s ({top[1]} waves x {top[2]} pieces, "
+                      f"{top[3]} workgroups per CU)")
+    desc = (f"gather_read_kernel, {best[3]} x {best[1]}-wave workgroups per CU, "
+            f"{best[2]} pieces a wave, best of {len(rates)} shapes, {nbytes} B")
+    return best[0], desc, best[4], nbytes
 
 
 def check_outputs(out, rows, ref, dtype):
@@ -582,10 +638,11 @@ def main():
     ach_gbps, ach_gpc, ach_us = achievable_read(kern_bytes, dev)
     log(f"streaming read of {kern_bytes} B: {ach_us:.2f} us at {ach_gpc} workgroups/CU, "
         f"{ach_gbps:.1f} GB/s")
-    gather = achievable_gather(w, k_cache, v_cache) if not scattered else None
+    gather = (achievable_gather(w, k_cache, v_cache, log if args.gather_sweep else None)
+              if not scattered else None)
     if gather:
-        log(f"gathering read of the decode's {gather[3]} B of 4 KB pieces: {gather[2]:.2f} us "
-            f"at {gather[1]} workgroups/CU, {gather[0]:.1f} GB/s")
+        log(f"gathering read of the decode's {gather[3]} B of pieces: {gather[2]:.2f} us, "
+            f"{gather[0]:.1f} GB/s ({gather[1]})")
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 2),
@@ -602,10 +659,9 @@ def main():
         "achievable_kernel": f"stream_read_kernel, {ach_gpc} x 256-thread workgroups per CU",
         "frac_of_achievable": round(achieved / ach_gbps, 4),
         # the same for a plain read of exactly the (block, KV head) pieces the decode
-        # reads, in their scattered order (HND pools)
+        # reads, in its order (HND pools): the best of every load shape
         "achievable_gather": round(gather[0], 2) if gather else None,
-        "achievable_gather_kernel": (f"gather_read_kernel, {gather[1]} x 256-thread "
-                                     f"workgroups per CU, {gather[3]} B") if gather else None,
+        "achievable_gather_kernel": gather[1] if gather else None,
         "frac_of_gather": round(achieved / gather[0], 4) if gather else None,
     }
     result = {

@@ -327,15 +327,21 @@ pkv_status pkv_plan_info_read(const void* workspace, size_t workspace_bytes,
 pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
                            int32_t groups_per_cu, void* stream);
 
-/* The same loads over scattered pieces: piece i is piece_bytes bytes (a multiple of 16)
- * at byte offset offsets[i] of both k_base and v_base (device addresses; `offsets` is a
- * device array of n_pieces int64), each wave of the grid reading every (waves)-th
- * piece, two at a time.  With the offsets of the (block, KV head) pieces a decode read
- * streams, it is the rate a kernel that only reads reaches on that access pattern.
- * Each piece's bytes must lie inside both allocations.  Asynchronous on `stream`. */
+/* The same loads over scattered pieces: piece i is piece_bytes bytes (a multiple of 16,
+ * at most 1 MiB) at byte offset offsets[i] of both k_base and v_base (device addresses;
+ * `offsets` is a device array of n_pieces int64).  groups_per_cu (1..16) workgroups of
+ * waves_per_group (4 or 8) waves per compute unit; each wave reads pieces_per_wave (1, 2
+ * or 4) pieces at a time, every (waves in the grid)-th piece of the list, so that the
+ * grid reads one contiguous window of the list at a time.  With the offsets of the
+ * (block, KV head) pieces a decode read streams, in its order, it is the rate a kernel
+ * that only reads reaches on that access pattern; benchmarks take the best over these
+ * shapes.  Each piece's bytes must lie inside both allocations: the library cannot
+ * check device offsets, so the caller does.  Refused (PKV_ERR_SHAPE) for other shapes.
+ * Asynchronous on `stream`. */
 pkv_status pkv_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,
                            int64_t n_pieces, int32_t piece_bytes, uint32_t* sink,
-                           int32_t groups_per_cu, void* stream);
+                           int32_t groups_per_cu, int32_t waves_per_group,
+                           int32_t pieces_per_wave, void* stream);
 
 /* Work split of the decode read (process-wide).  Each call cuts every row's history
  * into chunks; one (chunk, query head) is a work item of the persistent decode kernel,

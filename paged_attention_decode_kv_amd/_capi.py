@@ -78,7 +78,7 @@ SIGNATURES = {
     "pkv_paged_attention_noalloc": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32,
                                            _f, _p]),
     "pkv_stream_read": (_i32, [_p, _sz, _p, _i32, _p]),
-    "pkv_gather_read": (_i32, [_p, _p, _p, _i64, _i32, _p, _i32, _p]),
+    "pkv_gather_read": (_i32, [_p, _p, _p, _i64, _i32, _p, _i32, _i32, _i32, _p]),
     "pkv_workspace_bytes_multi": (_sz, [_PD, _i64, _i32, _i32, _i32]),
     "pkv_paged_attention_multi": (_i32, [_PD, _p, _p, _p, _p, _p, _i32, _p, _i64, _i32, _i32,
                                          _f, _p, _sz, _i32, _p]),

@@ -480,7 +480,12 @@ class GatherPieces:
         self.piece_bytes = int(piece_bytes)
 
 
-def gather_read(pieces: GatherPieces, sink: torch.Tensor, groups_per_cu: int = 4) -> None:
+GATHER_SHAPES = ((4, 1), (4, 2), (4, 4), (8, 1), (8, 2), (8, 4))
+"""(waves per workgroup, pieces per wave) that pkv_gather_read takes."""
+
+
+def gather_read(pieces: GatherPieces, sink: torch.Tensor, groups_per_cu: int = 4,
+                waves_per_group: int = 4, pieces_per_wave: int = 2) -> None:
     """Enqueue a plain read of checked pieces of both pools (pkv_gather_read) on the
     current stream."""
     k_cache, v_cache, offsets = pieces.k_cache, pieces.v_cache, pieces.offsets
@@ -488,7 +493,8 @@ def gather_read(pieces: GatherPieces, sink: torch.Tensor, groups_per_cu: int = 4
     with torch.cuda.device(k_cache.device):
         _check(_capi.lib().pkv_gather_read(_ptr(k_cache), _ptr(v_cache), _ptr(offsets),
                                            offsets.numel(), int(piece_bytes), _ptr(sink),
-                                           int(groups_per_cu), _stream(k_cache)))
+                                           int(groups_per_cu), int(waves_per_group),
+                                           int(pieces_per_wave), _stream(k_cache)))
 
 
 def decode_kernel_for(k_cache: torch.Tensor, num_heads: int, query_len: int = 1,

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ("kernels.hip", "capi.cpp", "timing.cpp")
+SOURCES = ("kernels.hip", "reference_reads.hip", "capi.cpp", "timing.cpp")
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code: hipcc would otherwise

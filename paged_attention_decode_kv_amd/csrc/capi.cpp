@@ -755,7 +755,8 @@ pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
 
 pkv_status pkv_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,
                            int64_t n_pieces, int32_t piece_bytes, uint32_t* sink,
-                           int32_t groups_per_cu, void* stream) {
+                           int32_t groups_per_cu, int32_t waves_per_group,
+                           int32_t pieces_per_wave, void* stream) {
   if (!k_base || !v_base || !offsets || !sink)
     return fail(PKV_ERR_NULL, "a required pointer is NULL");
   if (n_pieces < 1 || piece_bytes < 16 || piece_bytes % 16 != 0 || piece_bytes > (1 << 20))
@@ -763,8 +764,13 @@ pkv_status pkv_gather_read(const void* k_base, const void* v_base, const int64_t
                 "of 16 bytes up to 1 MiB", (long long)n_pieces, piece_bytes);
   if (groups_per_cu < 1 || groups_per_cu > 16)
     return fail(PKV_ERR_SHAPE, "groups_per_cu %d outside [1, 16]", groups_per_cu);
+  if (waves_per_group != 4 && waves_per_group != 8)
+    return fail(PKV_ERR_SHAPE, "waves_per_group %d: 4 or 8", waves_per_group);
+  if (pieces_per_wave != 1 && pieces_per_wave != 2 && pieces_per_wave != 4)
+    return fail(PKV_ERR_SHAPE, "pieces_per_wave %d: 1, 2 or 4", pieces_per_wave);
   hipError_t e = pkv::launch_gather_read(k_base, v_base, offsets, n_pieces, piece_bytes, sink,
-                                         groups_per_cu, static_cast<hipStream_t>(stream));
+                                         groups_per_cu, waves_per_group, pieces_per_wave,
+                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "launching the gathering read");
   return ok();
 }

@@ -209,7 +209,10 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink,
                               int groups_per_cu, hipStream_t stream);
 hipError_t launch_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,
                               int64_t n_pieces, int32_t piece_bytes, uint32_t* sink,
-                              int groups_per_cu, hipStream_t stream);
+                              int groups_per_cu, int waves_per_group, int pieces_per_wave,
+                              hipStream_t stream);
+// compute units of the current device (looked up once per device)
+hipError_t device_cus(int* cus);
 
 // The library's own workspace for callers that cannot allocate
 // (pkv_paged_attention_noalloc): a static device array of kScratchBytes on every

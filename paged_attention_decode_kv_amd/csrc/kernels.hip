@@ -2600,7 +2600,7 @@ static void launch_combine(const AttnArgs& a, const Workspace& ws, hipStream_t s
   }
 }
 
-static hipError_t device_cus(int* cus) {
+hipError_t device_cus(int* cus) {
   static std::atomic<int> count[64];   // per device, computed once
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -2697,99 +2697,6 @@ const char* decode_kernel_name(const AttnArgs& a, const Tuning& t) {
     case 8: return kVec[3];
     default: return kVec[0];
   }
-}
-
-// ------------------------------------------------------------------------- //
-// a plain streaming read (the achievable-bandwidth reference of benchmarks)
-// ------------------------------------------------------------------------- //
-constexpr int kStreamThreads = 256;
-constexpr int kStreamUnroll = 8;
-
-// Each thread reads 16-byte pieces i, i + 256, ... of its workgroup's runs of
-// 256 x kStreamUnroll pieces (32 KB), runs dealt round robin over the grid, with the
-// decode kernels' non-temporal loads, and folds them into one word; a store that
-// depends on that word keeps every load.
-__global__ void __launch_bounds__(kStreamThreads)
-stream_read_kernel(const char* src, int64_t pieces, uint32_t* sink) {
-  constexpr int64_t kRun = (int64_t)kStreamThreads * kStreamUnroll;
-  uint32_t acc = 0;
-  for (int64_t run = (int64_t)blockIdx.x * kRun; run < pieces; run += (int64_t)gridDim.x * kRun) {
-    uint4 v[kStreamUnroll];
-#pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) {
-      const int64_t i = run + u * kStreamThreads + threadIdx.x;
-      v[u] = i < pieces ? load16_stream(src + i * 16) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  if (acc == 0x5EED5EEDu) sink[0] = acc;   // almost never taken; the loads must happen
-}
-
-// The same loads over pieces scattered in two pools: wave w of the grid reads pieces
-// w, w + waves, ... of the offset list, each piece `piece16` 16-byte words at that byte
-// offset of both pools.  Two pieces at a time, in passes of 4 KB of each piece and pool
-// (16 KB a wave in flight: every load of a pass is issued before any is folded); the
-// next offsets load while a pass is read.
-__global__ void __launch_bounds__(kStreamThreads)
-gather_read_kernel(const char* kb, const char* vb, const int64_t* offsets, int64_t n,
-                   int piece16, uint32_t* sink) {
-  constexpr int kWaves = kStreamThreads / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t waves = (int64_t)gridDim.x * kWaves;
-  int64_t p = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  uint32_t acc = 0;
-  int64_t off0 = p < n ? offsets[p] : 0;
-  int64_t off1 = p + waves < n ? offsets[p + waves] : 0;
-  for (; p < n; p += 2 * waves) {
-    const bool two = p + waves < n;
-    const int64_t o0 = off0, o1 = off1;
-    off0 = p + 2 * waves < n ? offsets[p + 2 * waves] : 0;
-    off1 = p + 3 * waves < n ? offsets[p + 3 * waves] : 0;
-    for (int base = 0; base < piece16; base += 4 * 64) {
-      uint4 v[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = base + u * 64 + lane;
-        const bool in = i < piece16;
-        const int64_t b = (int64_t)i * 16;
-        v[u][0] = in ? load16_stream(kb + o0 + b) : make_uint4(0, 0, 0, 0);
-        v[u][1] = in ? load16_stream(vb + o0 + b) : make_uint4(0, 0, 0, 0);
-        v[u][2] = in && two ? load16_stream(kb + o1 + b) : make_uint4(0, 0, 0, 0);
-        v[u][3] = in && two ? load16_stream(vb + o1 + b) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc ^= v[u][k].x ^ v[u][k].y ^ v[u][k].z ^ v[u][k].w;
-    }
-  }
-  if (acc == 0x5EED5EEDu) sink[0] = acc;   // almost never taken; the loads must happen
-}
-
-hipError_t launch_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,
-                              int64_t n_pieces, int32_t piece_bytes, uint32_t* sink,
-                              int groups_per_cu, hipStream_t stream) {
-  int cus = 0;
-  hipError_t err = device_cus(&cus);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gather_read_kernel, dim3((unsigned)(cus * groups_per_cu)),
-                     dim3(kStreamThreads), 0, stream, static_cast<const char*>(k_base),
-                     static_cast<const char*>(v_base), offsets, n_pieces, piece_bytes / 16,
-                     sink);
-  return hipGetLastError();
-}
-
-hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink,
-                              int groups_per_cu, hipStream_t stream) {
-  int cus = 0;
-  hipError_t err = device_cus(&cus);
-  if (err != hipSuccess) return err;
-  const int64_t pieces = bytes / 16;
-  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)(cus * groups_per_cu)),
-                     dim3(kStreamThreads), 0, stream, static_cast<const char*>(src), pieces,
-                     sink);
-  return hipGetLastError();
 }
 
 hipError_t scratch_pointer(void** ptr) {
