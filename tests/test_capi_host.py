@@ -275,6 +275,34 @@ def test_graph_capture_refusals_need_no_gpu(lib):
     assert _capi.STATUS_NAMES[lib.pkv_graph_destroy(None)] == "OK"
 
 
+def test_reference_read_refusals_need_no_gpu(lib):
+    """pkv_stream_read and pkv_gather_read refuse bad sizes and shapes before launching."""
+    p = ctypes.c_void_p(16)         # never dereferenced: every case below is refused first
+
+    def gather(n=4, piece=4096, gpc=1, waves=4, ppw=2, ptr=p):
+        return _capi.STATUS_NAMES[lib.pkv_gather_read(ptr, p, p, n, piece, p, gpc, waves, ppw,
+                                                      None)]
+
+    def stream(nbytes=4096, gpc=1, ptr=p):
+        return _capi.STATUS_NAMES[lib.pkv_stream_read(ptr, nbytes, p, gpc, None)]
+
+    assert gather(ptr=None) == "NULL"
+    assert gather(n=0) == "SHAPE"
+    assert gather(piece=8) == "SHAPE"
+    assert gather(piece=4100) == "SHAPE"
+    assert gather(piece=(1 << 20) + 16) == "SHAPE"
+    assert gather(gpc=0) == "SHAPE" and gather(gpc=17) == "SHAPE"
+    for waves, ppw, field in ((2, 2, "waves_per_group 2"), (16, 1, "waves_per_group 16"),
+                              (4, 3, "pieces_per_wave 3"), (8, 8, "pieces_per_wave 8"),
+                              (4, 0, "pieces_per_wave 0")):
+        assert gather(waves=waves, ppw=ppw) == "SHAPE"
+        assert field in lib.pkv_last_error_detail().decode()
+    assert stream(ptr=None) == "NULL"
+    assert stream(nbytes=0) == "SHAPE" and stream(nbytes=24) == "SHAPE"
+    assert stream(gpc=0) == "SHAPE" and stream(gpc=17) == "SHAPE"
+    assert len(binding.GATHER_SHAPES) == 6
+
+
 def test_row_buckets():
     from paged_attention_decode_kv_amd.graphs import bucket_for, default_buckets
     assert default_buckets(1) == [1]
