@@ -303,6 +303,29 @@ def test_reference_read_refusals_need_no_gpu(lib):
     assert len(binding.GATHER_SHAPES) == 6
 
 
+def test_a_c99_program_includes_the_header_and_links_the_library(lib, tmp_path):
+    """The boundary is plain C: tests/c_abi_consumer.c compiles as C99 with -pedantic
+    -Werror against include/pagedkv.h, links libpagedkv.so, and its host-only calls
+    return what the header states."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    src = os.path.join(ROOT, "tests", "c_abi_consumer.c")
+    exe = str(tmp_path / "c_abi_consumer")
+    libdir = os.path.dirname(_capi.LIB_PATH)
+    build = subprocess.run(
+        [gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I",
+         os.path.join(ROOT, "include"), src, "-o", exe, "-L", libdir, "-lpagedkv",
+         f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "0 failure(s)" in run.stdout
+
+
 def test_row_buckets():
     from paged_attention_decode_kv_amd.graphs import bucket_for, default_buckets
     assert default_buckets(1) == [1]
