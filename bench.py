@@ -281,33 +281,59 @@ def achievable_read(nbytes, device, reps=5):
     return best
 
 
-def gather_offsets(w):
-    """Byte offsets of the (block, KV head) pieces of K and V the decode streams, in its
-    order: row by row, in groups of 8 blocks (a decode item's waves take one block
-    each), every KV head of a group before the next group, so that concurrent waves
-    read all heads' pieces (one head's pieces sit at the same offset of every block, and
-    reading them alone leaves most HBM channels idle).  HND pools only (a piece is
-    contiguous there); returns (offsets, piece bytes) or None."""
+def gather_offsets(w, rows=None, slot_rows=None):
+    """Byte offsets of the pieces of K and V a decode read streams, in its order, with the
+    piece size: (offsets, piece bytes), or None.
+    * Block tables, HND pool: one (block, KV head) piece of block_size x head_dim
+      elements per block and KV head, row by row, in groups of 8 blocks (a decode item's
+      waves take one block each), every KV head of a group before the next group, so that
+      concurrent waves read all heads' pieces (one head's pieces sit at the same offset of
+      every block, and reading them alone leaves most HBM channels idle).
+    * Block tables, NHD pool: a (block, KV head) is block_size separate token vectors, so
+      each live token's head vector is a piece, in the same order.
+    * ``slot_rows`` ({row: its live slots, in window order}): the rows read token by
+      token; a piece per (row, KV head, token), in that order.
+    ``rows`` limits the block-table rows (default: every row)."""
     import numpy as np
 
     from paged_attention_decode_kv_amd import workloads as wl
 
-    if w.layout != "HND":
-        return None
     elem = 2 if w.dtype == "bf16" else 4
-    piece = w.block_size * w.head_dim * elem
-    blk_bytes = w.kv_heads * piece
+    vec = w.head_dim * elem
     heads = np.arange(w.kv_heads, dtype=np.int64)
+
+    def token_offset(slot, h):     # byte offset of (slot, KV head h) in either layout
+        if w.layout == "NHD":
+            return (slot * w.kv_heads + h) * vec
+        blk, off = slot // w.block_size, slot % w.block_size
+        return ((blk * w.kv_heads + h) * w.block_size + off) * vec
+
     offs = []
-    for r in range(w.rows):
-        nb = wl.cdiv(w.context_lens[r], w.block_size)
+    if slot_rows is not None:
+        for r, sl in slot_rows.items():
+            sl = np.asarray(sl, dtype=np.int64)
+            offs.append(token_offset(sl[None, :], heads[:, None]).reshape(-1))
+        return (np.concatenate(offs), vec) if offs else None
+    t_in = np.arange(w.block_size, dtype=np.int64)
+    for r in (range(w.rows) if rows is None else rows):
+        n = int(w.context_lens[r])
+        nb = wl.cdiv(n, w.block_size)
         if nb == 0:
             continue
         blocks = w.block_tables[r, :nb].astype(np.int64)
         for g0 in range(0, nb, 8):
             grp = blocks[g0:g0 + 8]
-            offs.append((heads[:, None] * piece + grp[None, :] * blk_bytes).reshape(-1))
-    return np.concatenate(offs), piece
+            if w.layout == "HND":
+                offs.append(((grp[None, :] * w.kv_heads + heads[:, None]) * w.block_size *
+                             vec).reshape(-1))
+            else:   # live tokens only: position g0 * block_size + j * block_size + t
+                pos = (g0 + np.arange(len(grp), dtype=np.int64))[:, None] * w.block_size + t_in
+                slot = grp[:, None] * w.block_size + t_in
+                o = token_offset(slot[None, :, :], heads[:, None, None])
+                offs.append(o[:, pos < n].reshape(-1))
+    if not offs:
+        return None
+    return np.concatenate(offs), (w.block_size * vec if w.layout == "HND" else vec)
 
 
 def gather_rates(pieces, reps=5):
@@ -340,19 +366,18 @@ def gather_rates(pieces, reps=5):
     return out
 
 
-def achievable_gather(w, k_cache, v_cache, sweep_log=None):
-    """The best rate (GB/s) a plain read of exactly the (block, KV head) pieces of K and
-    V the decode streams, in its order (gather_offsets), reaches over every load shape
-    of pkv_gather_read (4 or 8 waves per workgroup, 1, 2 or 4 pieces per wave, 1 to 8
-    workgroups per CU).  With ``sweep_log``, every shape's rate goes to it, and so do
+def achievable_gather(w, k_cache, v_cache, sweep_log=None, rows=None, slot_rows=None):
+    """The best rate (GB/s) a plain read of exactly the pieces of K and V the dominant
+    kernel streams, in its order (gather_offsets), reaches over every load shape of
+    pkv_gather_read (4 or 8 waves per workgroup, 1, 2 or 4 loads in flight per wave, 1 to
+    8 workgroups per CU).  With ``sweep_log``, every shape's rate goes to it, and so do
     those of the same pieces sorted by address (a locality the decode's order does not
-    have: context only).  HND pools only; returns (GB/s, description, microseconds,
-    bytes) or None."""
+    have: context only).  Returns (GB/s, description, microseconds, bytes) or None."""
     import numpy as np
 
     from paged_attention_decode_kv_amd import binding
 
-    got = gather_offsets(w)
+    got = gather_offsets(w, rows=rows, slot_rows=slot_rows)
     if got is None:
         return None
     offs, piece = got
@@ -362,8 +387,10 @@ def achievable_gather(w, k_cache, v_cache, sweep_log=None):
     del pieces
     best = max(rates)
     if sweep_log:
+        per = 1024 // piece if piece <= 1024 and 1024 % piece == 0 else 1
         sweep_log(f"gathering read of {nbytes} B in {offs.size} pieces of {piece} B "
-                  f"(GB/s by waves per workgroup x pieces per wave, workgroups per CU):")
+                  f"(GB/s by waves per workgroup x loads in flight per wave, a load being "
+                  f"{per} piece(s), and workgroups per CU):")
         orders = [("decode order", rates)]
         sorted_pieces = binding.GatherPieces(k_cache, v_cache, np.sort(offs), piece)
         orders.append(("sorted by address", gather_rates(sorted_pieces)))
@@ -376,8 +403,11 @@ def achievable_gather(w, k_cache, v_cache, sweep_log=None):
             top = max(rr)
             sweep_log(f"  {name}: best {top[0]:.1f} GB/s ({top[1]} waves x {top[2]} pieces, "
                       f"{top[3]} workgroups per CU)")
-    desc = (f"gather_read_kernel, {best[3]} x {best[1]}-wave workgroups per CU, "
-            f"{best[2]} pieces a wave, best of {len(rates)} shapes, {nbytes} B")
+    kern = "gather_small_kernel" if piece <= 1024 and 1024 % piece == 0 else "gather_read_kernel"
+    loads = (f"{best[2]} loads of {1024 // piece} pieces a wave" if kern == "gather_small_kernel"
+             else f"{best[2]} pieces a wave")
+    desc = (f"{kern}, {best[3]} x {best[1]}-wave workgroups per CU, {loads}, best of "
+            f"{len(rates)} shapes, {nbytes} B in pieces of {piece} B")
     return best[0], desc, best[4], nbytes
 
 
@@ -638,11 +668,19 @@ def main():
     ach_gbps, ach_gpc, ach_us = achievable_read(kern_bytes, dev)
     log(f"streaming read of {kern_bytes} B: {ach_us:.2f} us at {ach_gpc} workgroups/CU, "
         f"{ach_gbps:.1f} GB/s")
-    gather = (achievable_gather(w, k_cache, v_cache, log if args.gather_sweep else None)
-              if not scattered else None)
+    # the reference read takes the dominant kernel's pieces: the rows read token by token
+    # (their live slots, in window order) or the rows read through block tables
+    sweep = log if args.gather_sweep else None
+    if kernel == "token_rows_kernel":
+        win = slot_win[scattered].cpu().numpy()
+        slot_rows = {r: win[i, :int(w.context_lens[r])] for i, r in enumerate(scattered)}
+        gather = achievable_gather(w, k_cache, v_cache, sweep, slot_rows=slot_rows)
+    else:
+        gather = achievable_gather(w, k_cache, v_cache, sweep,
+                                   rows=[r for r in range(w.rows) if r not in set(scattered)])
     if gather:
-        log(f"gathering read of the decode's {gather[3]} B of pieces: {gather[2]:.2f} us, "
-            f"{gather[0]:.1f} GB/s ({gather[1]})")
+        log(f"gathering read of the dominant kernel's {gather[3]} B of pieces: "
+            f"{gather[2]:.2f} us, {gather[0]:.1f} GB/s ({gather[1]})")
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 2),
@@ -658,8 +696,8 @@ def main():
         "achievable": round(ach_gbps, 2),
         "achievable_kernel": f"stream_read_kernel, {ach_gpc} x 256-thread workgroups per CU",
         "frac_of_achievable": round(achieved / ach_gbps, 4),
-        # the same for a plain read of exactly the (block, KV head) pieces the decode
-        # reads, in its order (HND pools): the best of every load shape
+        # the same for a plain read of exactly the pieces the dominant kernel reads, in
+        # its order: the best of every load shape
         "achievable_gather": round(gather[0], 2) if gather else None,
         "achievable_gather_kernel": gather[1] if gather else None,
         "frac_of_gather": round(achieved / gather[0], 4) if gather else None,

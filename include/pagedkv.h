@@ -335,7 +335,10 @@ pkv_status pkv_stream_read(const void* src, size_t bytes, uint32_t* sink,
  * grid reads one contiguous window of the list at a time.  With the offsets of the
  * (block, KV head) pieces a decode read streams, in its order, it is the rate a kernel
  * that only reads reaches on that access pattern; benchmarks take the best over these
- * shapes.  Each piece's bytes must lie inside both allocations: the library cannot
+ * shapes.  Pieces of at most 1 KB that divide 1 KB (a token's head vector in a
+ * slot-major pool, or a token read through a slot window) are read by lane groups, 1024 /
+ * piece_bytes pieces a wave load; larger pieces one wave each, 4 KB of each piece and
+ * pool a pass.  Each piece's bytes must lie inside both allocations: the library cannot
  * check device offsets, so the caller does.  Refused (PKV_ERR_SHAPE) for other shapes.
  * Asynchronous on `stream`. */
 pkv_status pkv_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,

@@ -1,6 +1,7 @@
 // Read-only reference kernels for benchmarks: the rate a kernel that does nothing but
 // read reaches on this GPU, over a contiguous range (stream_read_kernel) and over the
-// scattered (block, KV head) pieces a decode read streams (gather_read_kernel).  They
+// scattered pieces a decode read streams (gather_read_kernel for (block, KV head) pieces
+// of a few KB, gather_small_kernel for token pieces of at most 1 KB).  They
 // touch no decode state and sit in a file of their own, so that changing them leaves the
 // decode kernels' source unchanged.
 //
@@ -104,6 +105,52 @@ gather_read_kernel(const char* kb, const char* vb, const int64_t* offsets, int64
   if (acc == kSinkValue) sink[0] = acc;   // almost never taken; the loads must happen
 }
 
+// Pieces of at most 64 16-byte words that divide a wave's 64 lanes (piece16 = 1, 2, 4,
+// ..., 64): lane l reads word l % piece16 of piece l / piece16 of its group, so one
+// wave load covers 64 / piece16 whole pieces (a one-wave-a-piece read of a 256-byte
+// piece would leave 48 of 64 lanes idle).  Group q of the list is pieces
+// q * per .. q * per + per - 1 (per = 64 / piece16); wave w of the grid's `waves` takes,
+// in pass k, groups w + (NP k + j) waves (j = 0 .. NP - 1), all NP loads of a pass issued
+// before any is folded, and the next pass's offsets load while a pass is read.
+template <int WAVES, int NP>
+__global__ void __launch_bounds__(WAVES * 64)
+gather_small_kernel(const char* kb, const char* vb, const int64_t* offsets, int64_t n,
+                    int piece16, uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int per = 64 / piece16;
+  const int64_t part = lane / piece16;             // this lane's piece within a group
+  const int64_t word = (int64_t)(lane % piece16) * 16;
+  const int64_t waves = (int64_t)gridDim.x * WAVES;
+  const int64_t groups = (n + per - 1) / per;
+  int64_t q = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+  uint32_t acc = 0;
+  int64_t off[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int64_t p = (q + j * waves) * per + part;
+    off[j] = p < n ? offsets[p] : -1;
+  }
+  for (; q < groups; q += NP * waves) {
+    int64_t o[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      o[j] = off[j];
+      const int64_t p = (q + (NP + j) * waves) * per + part;
+      off[j] = p < n ? offsets[p] : -1;
+    }
+    u32x4_t v[NP][2];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const bool in = o[j] >= 0;
+      v[j][0] = in ? load16_nt(kb + o[j] + word) : u32x4_t{0, 0, 0, 0};
+      v[j][1] = in ? load16_nt(vb + o[j] + word) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) acc ^= fold4(v[j][0]) ^ fold4(v[j][1]);
+  }
+  if (acc == kSinkValue) sink[0] = acc;   // almost never taken; the loads must happen
+}
+
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink,
                               int groups_per_cu, hipStream_t stream) {
   int cus = 0;
@@ -118,8 +165,12 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink,
 template <int WAVES, int NP>
 static void launch_gather(const char* kb, const char* vb, const int64_t* offsets, int64_t n,
                           int piece16, uint32_t* sink, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gather_read_kernel<WAVES, NP>), dim3(grid), dim3(WAVES * 64), 0, stream,
-                     kb, vb, offsets, n, piece16, sink);
+  if (piece16 <= 64 && 64 % piece16 == 0)
+    hipLaunchKernelGGL((gather_small_kernel<WAVES, NP>), dim3(grid), dim3(WAVES * 64), 0,
+                       stream, kb, vb, offsets, n, piece16, sink);
+  else
+    hipLaunchKernelGGL((gather_read_kernel<WAVES, NP>), dim3(grid), dim3(WAVES * 64), 0,
+                       stream, kb, vb, offsets, n, piece16, sink);
 }
 
 hipError_t launch_gather_read(const void* k_base, const void* v_base, const int64_t* offsets,

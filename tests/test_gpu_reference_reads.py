@@ -41,13 +41,16 @@ def _gather_sink(k, v, offsets, piece_bytes, gpc, waves, ppw):
 
 
 @pytest.mark.parametrize("waves,ppw", binding.GATHER_SHAPES)
-@pytest.mark.parametrize("piece_bytes", [256, 4096 + 256])
+@pytest.mark.parametrize("piece_bytes", [64, 256, 4096 + 256])
 def test_gather_read_reaches_the_last_piece(waves, ppw, piece_bytes):
-    # more pieces than one pass of the largest grid takes (256 CUs x 3 x 8 waves x 4
-    # pieces = 24576), and a count no shape divides; 4352-byte pieces leave a second
-    # 4 KB step with 16 of 64 lanes live
-    n_slots = 40000 if piece_bytes == 256 else 30000
-    n = 24576 + 24576 // 2 + 7 if piece_bytes == 256 else 24576 + 11
+    # 2.5 passes of the largest grid used here (CUs x 3 workgroups x 8 waves x 4 loads,
+    # each load a whole piece of 4352 bytes or 1024 / piece_bytes pieces of 64 and 256),
+    # plus a count no shape divides; 4352-byte pieces leave a second 4 KB step with 16 of
+    # 64 lanes live, and pieces of at most 1 KB are read by lane groups
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    per = 1024 // piece_bytes if piece_bytes <= 1024 else 1
+    n = cus * 3 * 8 * 4 * per * 5 // 2 + 7
+    n_slots = n + 1000
     rng = np.random.default_rng(piece_bytes * 16 + waves * 4 + ppw)
     order = rng.permutation(n_slots)
     listed = order[:n].astype(np.int64) * piece_bytes
