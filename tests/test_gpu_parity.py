@@ -1634,7 +1634,7 @@ def _random_case(seed):
     rng = np.random.default_rng(1000 + seed)
     dtype = ["bf16", "f32"][int(rng.integers(2))]
     d = [64, 128, 256][int(rng.integers(3))]
-    bs = [16, 32, 64][int(rng.integers(3))]
+    bs = [16, 32, 64, 128, 256][int(rng.integers(5))]
     kvh = [1, 2, 4][int(rng.integers(3))]
     group = [1, 2, 4, 8][int(rng.integers(4))]
     n_q = [1, 1, 2, 4][int(rng.integers(4))]
@@ -1658,7 +1658,7 @@ def _random_case(seed):
                 seed=seed), tuning
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_configurations(seed):
     """Drawn shapes (dtype, head_dim, block size, head grouping, new tokens per row,
     layout, lengths) under drawn work splits (chunk range, waves, staging, matrix cores,
