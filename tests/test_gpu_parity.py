@@ -1653,6 +1653,10 @@ def _random_case(seed):
                   mfma=[1, 2][int(rng.integers(2))],
                   solo_tokens=[1, 64, 256, 1024][int(rng.integers(4))],
                   groups_per_cu=1 if many else [1, 2, 16][int(rng.integers(3))])
+    # drawn after the rest, so that the draws above stay what they were
+    tuning.update(deal=[1, 2][int(rng.integers(2))],
+                  items_per_group=[1, 4, 16, 64][int(rng.integers(4))],
+                  max_query_group=[16, 8, 4, 1][int(rng.integers(4))])
     return dict(context_lens=lens, heads=kvh * group, kv_heads=kvh, head_dim=d, block_size=bs,
                 dtype=dtype, layout=["HND", "NHD"][int(rng.integers(2))], query_len=n_q,
                 seed=seed), tuning
@@ -1662,8 +1666,9 @@ def _random_case(seed):
 def test_random_configurations(seed):
     """Drawn shapes (dtype, head_dim, block size, head grouping, new tokens per row,
     layout, lengths) under drawn work splits (chunk range, waves, staging, matrix cores,
-    single-wave bound, workgroups per CU): every output against the oracle, the
-    scatter bit-exact."""
+    single-wave bound, workgroups per CU, static deal or all tickets, items per
+    workgroup, query-group cap): every output against the oracle, the scatter
+    bit-exact."""
     kw, tuning = _random_case(seed)
     w = wl.make_custom(**kw)
     say(f"random {seed}: rows {w.rows} heads {w.heads}/{w.kv_heads} d {w.head_dim} "
