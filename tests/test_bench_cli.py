@@ -89,3 +89,49 @@ def test_committed_traffic_records_are_consistent():
         assert abs(cal["fetch_scale"] * cal["fetch_kib"] - 1048576) < 1024
         assert abs(cal["write_scale"] * cal["write_kib"] - 1048576) < 1024
         assert all("rocprofv3 --pmc" in c and "bench.py" in c for c in r["commands"])
+
+
+@pytest.mark.parametrize("layout", ["HND", "NHD"])
+def test_gather_pieces_are_the_pieces_the_read_streams(layout):
+    """The reference read's piece list (gather_offsets) holds each piece the decode reads
+    exactly once and nothing else: for an HND pool every (live block, KV head) piece, for
+    an NHD pool every live (position, KV head) token vector, and for rows read token by
+    token every (listed slot, KV head) token vector; all inside the pool."""
+    import numpy as np
+
+    from paged_attention_decode_kv_amd import workloads as wl
+
+    bench = _bench_module()
+    w = wl.make_custom([37, 0, 16, 100, 1], heads=8, kv_heads=2, head_dim=64, block_size=16,
+                       dtype="bf16", layout=layout, seed=5)
+    vec = w.head_dim * 2
+    pool_bytes = int(np.prod(w.pool_shape)) * 2
+
+    def token_bytes(slot, h):       # from the pool shape, independently of the bench
+        blk, off = divmod(int(slot), w.block_size)
+        idx = (blk, h, off) if layout == "HND" else (blk, off, h)
+        return int(np.ravel_multi_index(idx, w.pool_shape[:3])) * vec
+
+    offs, piece = bench.gather_offsets(w)
+    want = []
+    for r in range(w.rows):
+        n = int(w.context_lens[r])
+        for t in range(n):
+            slot = int(w.block_tables[r, t // w.block_size]) * w.block_size + t % w.block_size
+            for h in range(w.kv_heads):
+                if layout == "NHD":
+                    want.append(token_bytes(slot, h))
+                elif t % w.block_size == 0:          # a whole (block, KV head) piece
+                    want.append(token_bytes(slot, h))
+    assert piece == (w.block_size * vec if layout == "HND" else vec)
+    assert sorted(offs.tolist()) == sorted(want)
+    assert offs.min() >= 0 and offs.max() + piece <= pool_bytes
+
+    rng = np.random.default_rng(1)
+    slot_rows = {3: rng.permutation(np.arange(40, 140)), 0: np.array([5, 200, 17])}
+    offs, piece = bench.gather_offsets(w, slot_rows=slot_rows)
+    want = [token_bytes(s, h) for r in slot_rows for h in range(w.kv_heads)
+            for s in slot_rows[r]]
+    assert piece == vec
+    assert offs.tolist() == want                      # row by row, head by head, in order
+    assert bench.gather_offsets(w, rows=[1]) is None  # a padding row reads nothing
